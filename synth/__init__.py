@@ -1,0 +1,114 @@
+"""Seeded synthetic inputs for C = A·Bᵀ, shared by the oracle side and the GPU side.
+
+This module draws random numbers and rounds them to the 16-bit input format.
+It holds none of the product's arithmetic: no dot products, no accumulation,
+no output rounding.  Each generator returns raw bit patterns (uint16 arrays),
+so the very same bits feed the GPU kernel and the CPU oracle.
+
+Recipe (also stated in the design notes):
+  * ``numpy.random.default_rng(seed)`` (PCG64); A is drawn first (M×K, row-major
+    order), then B (N×K, row-major order — B is stored transposed).
+  * distributions: ``normal`` N(0, 1); ``normal_scaled`` N(0, σ=1/√K);
+    ``uniform`` U[-1, 1) via ``rng.uniform(-1, 1)``; ``int`` uniform integers in
+    [-4, 4] (exact in bf16 and f16, so fp32 accumulation is exact).
+  * rounding: bf16 values go float64 → float32 (numpy, round-to-nearest-even)
+    → bfloat16 (torch CPU conversion, round-to-nearest-even); f16 values go
+    float64 → float16 directly (numpy, round-to-nearest-even).
+
+The workloads are the matrix products the pages measure: 4096³ square
+("Optimizing Blackwell matrix multiplication in Mojo (part 2)", section
+"Starting from the 4-line kernel") and M=1024, K=N=4096 f16 with normally
+distributed data ("Collective matrix multiplication", the single-device
+timing in its introduction), plus a small square case, a ragged case and a
+skinny memory-bound case.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+IN_DTYPES = ("bf16", "f16")
+OUT_DTYPES = ("f32", "f16", "bf16")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    in_dtype: str
+    out_dtype: str
+    dist: str
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def compulsory_bytes(self) -> int:
+        osz = 4 if self.out_dtype == "f32" else 2
+        return (self.M * self.K + self.N * self.K) * 2 + self.M * self.N * osz
+
+    def integer_twin(self) -> "Workload":
+        return dataclasses.replace(self, name=self.name + "_int", dist="int", seed=self.seed + 100)
+
+
+# The five measured shapes, seeds 0..4 in this order.
+WORKLOADS = {
+    "sq512_bf16_f32": Workload("sq512_bf16_f32", 512, 512, 512, "bf16", "f32", "normal", 0),
+    "m1024_n4096_k4096_f16_f16": Workload("m1024_n4096_k4096_f16_f16", 1024, 4096, 4096, "f16", "f16",
+                                          "normal", 1),
+    "sq4096_bf16_bf16": Workload("sq4096_bf16_bf16", 4096, 4096, 4096, "bf16", "bf16", "normal", 2),
+    "ragged_m1000_n3000_k2050_bf16_f32": Workload("ragged_m1000_n3000_k2050_bf16_f32", 1000, 3000, 2050,
+                                                  "bf16", "f32", "uniform", 3),
+    "skinny_m16_n8192_k8192_bf16_bf16": Workload("skinny_m16_n8192_k8192_bf16_bf16", 16, 8192, 8192,
+                                                 "bf16", "bf16", "normal_scaled", 4),
+}
+
+
+def _to_bf16_bits(x64: np.ndarray) -> np.ndarray:
+    import torch  # CPU conversion only
+
+    f32 = np.ascontiguousarray(x64, dtype=np.float32)
+    t = torch.from_numpy(f32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _to_f16_bits(x64: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x64).astype(np.float16).view(np.uint16)
+
+
+def round_bits(x64: np.ndarray, in_dtype: str) -> np.ndarray:
+    """Round float64 values to the 16-bit input format, returning raw bits."""
+    if in_dtype == "bf16":
+        return _to_bf16_bits(x64)
+    if in_dtype == "f16":
+        return _to_f16_bits(x64)
+    raise ValueError("in_dtype must be bf16 or f16")
+
+
+def _draw(rng: np.random.Generator, shape, dist: str, K: int) -> np.ndarray:
+    if dist == "normal":
+        return rng.standard_normal(shape)
+    if dist == "normal_scaled":
+        return rng.normal(0.0, 1.0 / np.sqrt(K), shape)
+    if dist == "uniform":
+        return rng.uniform(-1.0, 1.0, shape)
+    if dist == "int":
+        return rng.integers(-4, 5, shape).astype(np.float64)
+    raise ValueError("unknown distribution %r" % dist)
+
+
+def make(M: int, N: int, K: int, in_dtype: str, dist: str, seed: int):
+    """Return (a_bits (M,K) uint16, b_bits (N,K) uint16)."""
+    rng = np.random.default_rng(seed)
+    a = _draw(rng, (M, K), dist, K)
+    b = _draw(rng, (N, K), dist, K)
+    return round_bits(a, in_dtype), round_bits(b, in_dtype)
+
+
+def make_workload(w: Workload):
+    return make(w.M, w.N, w.K, w.in_dtype, w.dist, w.seed)

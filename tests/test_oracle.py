@@ -1,0 +1,415 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself:
+  * hand-computed products (tests/golden/hand_products.txt);
+  * the IEEE-754 definitions of the 16-bit formats (tests/golden/*.txt) and the
+    library conversions of numpy (float16) and torch-CPU (bfloat16), exhaustively
+    over all 65536 bit patterns for decoding;
+  * exact rational brute force (fractions.Fraction) on tiny shapes, within the
+    fp64 summation bound, and equal on integer inputs;
+  * closed forms: identity, all-ones, zero and permutation operands;
+  * a library routine: numpy float64 matmul on independently decoded inputs.
+A mistake planted in a copy of the oracle's result (transposed operand, dropped
+last term, wrong sign) must fail these pins.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import tolerance
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+U64 = 2.0 ** -53
+
+
+def gamma(k):
+    return k * U64 / (1 - k * U64)
+
+
+def parse_products():
+    cases = []
+    lines = [l.strip() for l in open(os.path.join(GOLDEN, "hand_products.txt"))]
+    lines = [l for l in lines if l and not l.startswith("#")]
+    i = 0
+    while i < len(lines):
+        tag, name, M, N, K = lines[i].split()
+        assert tag == "case"
+        M, N, K = int(M), int(N), int(K)
+        rows = [[float(v) for v in l.split()] for l in lines[i + 1:i + 1 + M + N + M]]
+        A = np.array(rows[:M])
+        B = np.array(rows[M:M + N])
+        C = np.array(rows[M + N:])
+        assert A.shape == (M, K) and B.shape == (N, K) and C.shape == (M, N)
+        cases.append((name, A, B, C))
+        i += 1 + M + N + M
+    return cases
+
+
+def indep_decode(bits, in_dtype):
+    """Library decode (numpy float16 / torch bfloat16), independent of the oracle's C decoders."""
+    b = np.ascontiguousarray(bits).view(np.uint16)
+    if in_dtype == "f16":
+        return b.view(np.float16).astype(np.float64)
+    t = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- golden fixtures
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+def test_hand_products(in_dtype):
+    for name, A, B, C in parse_products():
+        a = synth.round_bits(A, in_dtype)
+        b = synth.round_bits(B, in_dtype)
+        assert np.array_equal(indep_decode(a, in_dtype), A), name  # inputs exact in the format
+        c, nA, nB = oracle.gemm_bt_ref(a, b, in_dtype)
+        assert np.array_equal(c, C), (name, c, C)
+        assert np.allclose(nA, np.sqrt((A * A).sum(1)), rtol=1e-15)
+        assert np.allclose(nB, np.sqrt((B * B).sum(1)), rtol=1e-15)
+        for out in ("f32", "bf16", "f16"):
+            got = oracle.round_to(c, out)
+            back = indep_decode(got, out) if out != "f32" else got.view(np.float32).astype(np.float64)
+            assert np.array_equal(back, C), (name, out)
+
+
+def test_golden_bit_patterns():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "ieee_16bit_patterns.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        d, h, v = line.split()
+        bits = np.array([int(h, 16)], dtype=np.uint16)
+        got = oracle.decode(bits, d)[0]
+        want = float(v)
+        if math.isnan(want):
+            assert math.isnan(got)
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), (d, h, got, want)
+        n += 1
+    assert n >= 20
+
+
+def test_golden_rne_cases():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "rne_cases.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        d, v, h = line.split()
+        got = int(oracle.round_to(np.array([float(v)]), d)[0])
+        assert got == int(h, 16), (d, v, hex(got), h)
+        n += 1
+    assert n >= 25
+
+
+# ---------------------------------------------------------------- decoders / encoders vs libraries
+
+def test_decode_exhaustive_vs_libraries():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for d in ("bf16", "f16"):
+        got = oracle.decode(allbits, d)
+        want = indep_decode(allbits, d)
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], want[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_round_f16_vs_numpy():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([
+        rng.standard_normal(200000) * 10.0 ** rng.integers(-9, 6, 200000),
+        rng.uniform(-70000, 70000, 20000),
+        (rng.integers(-4096, 4096, 20000) + 0.5) * 2.0 ** rng.integers(-30, 5, 20000),  # many ties
+    ])
+    got = oracle.round_to(x, "f16")
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_round_bf16_vs_torch_on_fp32_values():
+    rng = np.random.default_rng(12)
+    x32 = np.concatenate([
+        (rng.standard_normal(200000) * 10.0 ** rng.integers(-40, 38, 200000)).astype(np.float32),
+        ((rng.integers(-65536, 65536, 20000) + 0.5) * 2.0 ** rng.integers(-140, 100, 20000)).astype(np.float32),
+    ])
+    x32 = x32[np.isfinite(x32)]
+    got = oracle.round_to(x32.astype(np.float64), "bf16")
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_round_f32_vs_numpy():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal(100000) * 10.0 ** rng.integers(-40, 38, 100000)
+    got = oracle.round_to(x, "f32")
+    want = x.astype(np.float32).view(np.uint32)
+    assert np.array_equal(got, want)
+
+
+def _rne_exact(x, p, emin, maxfin):
+    """Nearest-even rounding by exact rational arithmetic (brute force, tiny inputs)."""
+    if x == 0:
+        return 0.0
+    a = abs(Fraction(x))
+    e = 0
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** (max(e, emin) - p)
+    n = a / q
+    fl = n.numerator // n.denominator
+    fr = n - fl
+    if fr > Fraction(1, 2) or (fr == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * q
+    r = math.inf if r > maxfin else float(r)
+    return math.copysign(r, x)
+
+
+def test_round_vs_exact_rationals():
+    rng = np.random.default_rng(14)
+    xs = rng.standard_normal(3000) * 10.0 ** rng.integers(-8, 5, 3000)
+    for d, p, emin, mx in (("bf16", 7, -126, (2 - Fraction(1, 128)) * Fraction(2) ** 127),
+                           ("f16", 10, -14, Fraction(65504))):
+        got = oracle.decode(oracle.round_to(xs, d), d)
+        for x, g in zip(xs, got):
+            assert g == _rne_exact(float(x), p, emin, mx), (d, x, g)
+
+
+# ---------------------------------------------------------------- brute force on tiny shapes
+
+def _exact_products(a_val, b_val):
+    M, K = a_val.shape
+    N = b_val.shape[0]
+    C = [[sum((Fraction(float(a_val[i, k])) * Fraction(float(b_val[j, k])) for k in range(K)), Fraction(0))
+          for j in range(N)] for i in range(M)]
+    S = np.abs(a_val) @ np.abs(b_val).T
+    return C, S
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+def test_brute_force_random_tiny(in_dtype):
+    rng = np.random.default_rng(21)
+    for trial in range(25):
+        M, N, K = (int(v) for v in rng.integers(1, 9, 3))
+        a, b = synth.make(M, N, K, in_dtype, "normal", seed=1000 + trial)
+        c, _, _ = oracle.gemm_bt_ref(a, b, in_dtype)
+        av, bv = indep_decode(a, in_dtype), indep_decode(b, in_dtype)
+        C, S = _exact_products(av, bv)
+        for i in range(M):
+            for j in range(N):
+                assert abs(Fraction(c[i, j]) - C[i][j]) <= Fraction(gamma(K) * S[i, j]), (trial, i, j)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+def test_brute_force_integer_exact(in_dtype):
+    for trial in range(10):
+        M, N, K = 3 + trial % 4, 2 + trial % 5, 1 + 3 * trial
+        a, b = synth.make(M, N, K, in_dtype, "int", seed=2000 + trial)
+        c, _, _ = oracle.gemm_bt_ref(a, b, in_dtype)
+        av, bv = indep_decode(a, in_dtype), indep_decode(b, in_dtype)
+        C, _ = _exact_products(av, bv)
+        assert all(c[i, j] == C[i][j] for i in range(M) for j in range(N))
+
+
+def test_brute_force_cancellation():
+    # rows whose terms cancel to a small remainder: fp64 keeps it exactly at this size
+    A = np.array([[256.0, 1.0, -256.0, 0.0078125], [1024.0, -1024.0, 3.0, -3.0]])
+    B = np.array([[1.0, 1.0, 1.0, 1.0], [0.5, 0.5, 0.5, 0.5]])
+    a, b = synth.round_bits(A, "bf16"), synth.round_bits(B, "bf16")
+    c, _, _ = oracle.gemm_bt_ref(a, b, "bf16")
+    assert np.array_equal(c, np.array([[1.0078125, 0.50390625], [0.0, 0.0]]))
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+def test_identity_B(in_dtype):
+    M, K = 37, 45
+    a, _ = synth.make(M, 1, K, in_dtype, "normal", seed=5)
+    for N in (K, 20, 60):  # N = K, N < K, N > K
+        B = np.eye(N, K)
+        b = synth.round_bits(B, in_dtype)
+        c, _, _ = oracle.gemm_bt_ref(a, b, in_dtype)
+        av = indep_decode(a, in_dtype)
+        want = np.zeros((M, N))
+        want[:, :min(N, K)] = av[:, :min(N, K)]
+        assert np.array_equal(c, want)
+
+
+@pytest.mark.parametrize("K", [1, 7, 64, 2050, 4096])
+def test_all_ones(K):
+    M, N = 3, 5
+    ones = np.ones((max(M, N), K))
+    for d in ("bf16", "f16"):
+        a = synth.round_bits(ones[:M], d)
+        b = synth.round_bits(ones[:N], d)
+        c, nA, nB = oracle.gemm_bt_ref(a, b, d)
+        assert np.all(c == K)
+        assert np.allclose(nA, math.sqrt(K)) and np.allclose(nB, math.sqrt(K))
+    # the downcast of K: e.g. 2050 -> 2048 in bf16 (spacing 16 there)
+    if K == 2050:
+        assert oracle.decode(oracle.round_to(np.array([2050.0]), "bf16"), "bf16")[0] == 2048.0
+        assert oracle.decode(oracle.round_to(np.array([2050.0]), "f16"), "f16")[0] == 2050.0
+
+
+def test_zero_operand():
+    a, b = synth.make(9, 11, 13, "bf16", "normal", seed=6)
+    z = np.zeros_like(b)
+    c, _, nB = oracle.gemm_bt_ref(a, z, "bf16")
+    assert np.all(c == 0) and np.all(nB == 0)
+    c, nA, _ = oracle.gemm_bt_ref(np.zeros_like(a), b, "bf16")
+    assert np.all(c == 0) and np.all(nA == 0)
+
+
+def test_permutation_B():
+    M, K = 10, 12
+    a, _ = synth.make(M, 1, K, "f16", "normal", seed=7)
+    perm = np.random.default_rng(3).permutation(K)
+    P = np.zeros((K, K))
+    P[np.arange(K), perm] = 1.0  # row j of stored B picks column perm[j] of A
+    c, _, _ = oracle.gemm_bt_ref(a, synth.round_bits(P, "f16"), "f16")
+    assert np.array_equal(c, indep_decode(a, "f16")[:, perm])
+
+
+def test_empty_shapes():
+    a = np.zeros((0, 5), np.uint16)
+    b = np.zeros((3, 5), np.uint16)
+    c, nA, nB = oracle.gemm_bt_ref(a, b, "bf16")
+    assert c.shape == (0, 3)
+    a = np.zeros((4, 0), np.uint16)
+    b = np.zeros((3, 0), np.uint16)
+    c, nA, nB = oracle.gemm_bt_ref(a, b, "bf16")
+    assert c.shape == (4, 3) and np.all(c == 0)  # empty sum
+
+
+# ---------------------------------------------------------------- library cross-check
+
+@pytest.mark.parametrize("in_dtype,shape", [("bf16", (64, 80, 96)), ("f16", (33, 65, 127)),
+                                            ("bf16", (512, 512, 512))])
+def test_vs_numpy_matmul(in_dtype, shape):
+    M, N, K = shape
+    a, b = synth.make(M, N, K, in_dtype, "normal", seed=8)
+    c, nA, nB = oracle.gemm_bt_ref(a, b, in_dtype)
+    av, bv = indep_decode(a, in_dtype), indep_decode(b, in_dtype)
+    ref = av @ bv.T
+    S = np.abs(av) @ np.abs(bv).T
+    # both sides carry fp64 summation error
+    assert np.all(np.abs(c - ref) <= 2 * gamma(K) * S + 1e-300)
+    assert np.allclose(nA, np.linalg.norm(av, axis=1), rtol=1e-13)
+    assert np.allclose(nB, np.linalg.norm(bv, axis=1), rtol=1e-13)
+
+
+def test_entries_and_norms_match_full():
+    a, b = synth.make(70, 90, 130, "bf16", "uniform", seed=9)
+    c, nA, nB = oracle.gemm_bt_ref(a, b, "bf16")
+    rng = np.random.default_rng(0)
+    I = rng.integers(0, 70, 500)
+    J = rng.integers(0, 90, 500)
+    e = oracle.gemm_bt_entries(a, b, "bf16", I, J)
+    assert np.array_equal(e, c[I, J])
+    assert np.array_equal(oracle.row_norms(a, "bf16"), nA)
+    assert np.array_equal(oracle.row_norms(b, "bf16"), nB)
+    with pytest.raises(ValueError):
+        oracle.gemm_bt_entries(a, b, "bf16", np.array([70]), np.array([0]))
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def test_planted_mistakes_fail_the_pins():
+    """A plausible oracle bug must be caught: compare each corrupted variant to the exact result."""
+    M = N = K = 7  # square, so a transposed operand still has the right shape
+    a, b = synth.make(M, N, K, "bf16", "normal", seed=31)
+    av, bv = indep_decode(a, "bf16"), indep_decode(b, "bf16")
+    C, S = _exact_products(av, bv)
+    good, _, _ = oracle.gemm_bt_ref(a, b, "bf16")
+    variants = {
+        "transposed result": good.T,
+        "B read as K x N": av @ bv,
+        "A read as K x M": av.T @ bv.T,
+        "dropped last term": av[:, :-1] @ bv[:, :-1].T,
+        "sign of one term": good - 2 * np.outer(av[:, 3], bv[:, 3]),
+        "off-by-one k": av[:, 1:] @ bv[:, :-1].T,
+    }
+
+    def pins_ok(c):
+        return all(abs(Fraction(float(c[i, j])) - C[i][j]) <= Fraction(gamma(K) * S[i, j])
+                   for i in range(M) for j in range(N))
+
+    assert pins_ok(good)
+    for name, bad in variants.items():
+        assert not pins_ok(bad), name
+
+
+# ---------------------------------------------------------------- tolerance checker
+
+def test_tolerance_rules():
+    rng = np.random.default_rng(41)
+    cref = rng.standard_normal((50, 60)) * 10
+    d = np.full_like(cref, 1e-6)  # tiny D: the ulp term dominates for 16-bit outputs
+    for out in ("bf16", "f16"):
+        u = tolerance.ulp(cref, out)
+        assert tolerance.check(cref + 0.9 * u, cref, d, out)
+        assert not tolerance.check(cref + 3 * u, cref, d, out)
+    D = np.abs(rng.standard_normal((50, 60))) + 1
+    for out in ("f32", "bf16", "f16"):
+        lim = tolerance.bound(cref, D, out)
+        assert tolerance.check(cref + 0.99 * lim, cref, D, out)
+        assert not tolerance.check(cref - 1.5 * lim, cref, D, out)
+    # zero D requires an exact zero
+    z = np.zeros((2, 2))
+    assert tolerance.check(z, z, z, "bf16")
+    assert not tolerance.check(z + 1e-30, z, z, "bf16")
+    # non-finite handling
+    inf = np.array([[np.inf, 1.0]])
+    assert tolerance.check(inf, inf, np.ones_like(inf), "f16")
+    assert not tolerance.check(np.array([[np.nan, 1.0]]), inf, np.ones_like(inf), "f16")
+    assert not tolerance.check(np.array([[1.0, np.inf]]), np.array([[1.0, 1.0]]), np.ones((1, 2)), "f32")
+
+
+def test_ulp_values():
+    assert tolerance.ulp(np.array([1.0]), "bf16")[0] == 2.0 ** -7
+    assert tolerance.ulp(np.array([1.5]), "f16")[0] == 2.0 ** -10
+    assert tolerance.ulp(np.array([4096.0]), "bf16")[0] == 32.0
+    assert tolerance.ulp(np.array([0.0]), "f16")[0] == 2.0 ** -24
+    assert tolerance.ulp(np.array([0.0]), "bf16")[0] == 2.0 ** -133
+    assert tolerance.ulp(np.array([1e-40]), "bf16")[0] == 2.0 ** -133
+
+
+def test_bit_exact_helper():
+    r = np.array([0x3F80, 0x8000, 0x4000], np.uint16)
+    g = np.array([0x3F80, 0x0000, 0x4000], np.uint16)
+    assert tolerance.bit_exact(g, r, "bf16")
+    g[2] = 0x4001
+    assert not tolerance.bit_exact(g, r, "bf16")
+
+
+# ---------------------------------------------------------------- input recipe
+
+def test_synth_recipe():
+    w = synth.WORKLOADS["sq512_bf16_f32"]
+    a1, b1 = synth.make_workload(w)
+    a2, b2 = synth.make_workload(w)
+    assert a1.dtype == np.uint16 and a1.shape == (512, 512) and b1.shape == (512, 512)
+    assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+    av = indep_decode(a1, "bf16")
+    assert abs(av.mean()) < 0.02 and abs(av.std() - 1) < 0.02
+    ai, bi = synth.make_workload(w.integer_twin())
+    vi = indep_decode(ai, "bf16")
+    assert set(np.unique(vi)) <= set(range(-4, 5)) and len(np.unique(vi)) == 9
+    ws = synth.WORKLOADS["skinny_m16_n8192_k8192_bf16_bf16"]
+    a, _ = synth.make(ws.M, 4, ws.K, "bf16", ws.dist, ws.seed)
+    assert abs(indep_decode(a, "bf16").std() - 1 / math.sqrt(ws.K)) < 0.001
+    wu = synth.WORKLOADS["ragged_m1000_n3000_k2050_bf16_f32"]
+    a, _ = synth.make(50, 4, wu.K, "bf16", wu.dist, wu.seed)
+    v = indep_decode(a, "bf16")
+    assert v.min() >= -1 and v.max() <= 1 and abs(v.std() - 1 / math.sqrt(3)) < 0.01
+    assert [x.seed for x in synth.WORKLOADS.values()] == [0, 1, 2, 3, 4]
