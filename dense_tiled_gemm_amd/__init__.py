@@ -1,0 +1,156 @@
+"""Python binding of libgemm_bt.so: C = A·Bᵀ on an MI355X (gfx950).
+
+Argument marshalling only.  Every arithmetic step runs in the library's HIP
+kernels; PyTorch supplies device memory and the stream.  There is no CPU or
+PyTorch fallback: if the shared library is missing, every call raises.
+
+Entry points (same names as the C-ABI in ``include/gemm_bt.h``):
+  gemm_bt(A, B, C, M, N, K, in_dtype, out_dtype, stream)   raw device pointers
+  gemm_bt_status_string(status), gemm_bt_version()
+  gemm_bt_plan(M, N, K, in_dtype, out_dtype, a_align, b_align, c_align)
+  gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m)
+and a torch convenience wrapper ``mm_bt(a, b, out_dtype)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+F32, F16, BF16 = 0, 1, 2
+OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_LAUNCH = 0, 1, 2, 3, 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm_bt.so")
+EXPORTS = ("gemm_bt", "gemm_bt_status_string", "gemm_bt_version", "gemm_bt_plan", "gemm_bt_tile_coord")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GemmBtError(RuntimeError):
+    def __init__(self, status, what="gemm_bt"):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int),
+                ("threads", ctypes.c_int), ("vec", ctypes.c_int), ("group_m", ctypes.c_int),
+                ("ksplit", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("tiles_m", ctypes.c_int64),
+                ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+def load():
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libgemm_bt.so is not built (expected at %s); run "
+                                   "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+            lib = ctypes.CDLL(LIB_PATH)
+            vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+            lib.gemm_bt.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+            lib.gemm_bt.restype = ci
+            lib.gemm_bt_status_string.argtypes = [ci]
+            lib.gemm_bt_status_string.restype = ctypes.c_char_p
+            lib.gemm_bt_version.argtypes = []
+            lib.gemm_bt_version.restype = ci
+            lib.gemm_bt_plan.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
+            lib.gemm_bt_plan.restype = ci
+            lib.gemm_bt_tile_coord.argtypes = [i64, i64, i64, ci, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+            lib.gemm_bt_tile_coord.restype = ci
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().gemm_bt_status_string(int(status)).decode()
+
+
+gemm_bt_status_string = status_string
+
+
+def gemm_bt_version() -> int:
+    return int(load().gemm_bt_version())
+
+
+def gemm_bt(A: int, B: int, C: int, M: int, N: int, K: int, in_dtype: int, out_dtype: int,
+            stream: int | None) -> int:
+    """Raw call: device pointers as integers, returns the status code."""
+    return int(load().gemm_bt(A or None, B or None, C or None, M, N, K, in_dtype, out_dtype, stream or None))
+
+
+def gemm_bt_plan(M, N, K, in_dtype, out_dtype, a_align=256, b_align=256, c_align=256):
+    p = Plan()
+    st = load().gemm_bt_plan(M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, ctypes.byref(p))
+    if st != OK:
+        raise GemmBtError(st, "gemm_bt_plan")
+    return p
+
+
+def gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m):
+    tm, tn = ctypes.c_int64(), ctypes.c_int64()
+    st = load().gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m, ctypes.byref(tm), ctypes.byref(tn))
+    if st != OK:
+        raise GemmBtError(st, "gemm_bt_tile_coord")
+    return tm.value, tn.value
+
+
+# ---------------------------------------------------------------- torch convenience
+
+def _torch_code(dt):
+    import torch
+
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float16:
+        return F16
+    if dt == torch.float32:
+        return F32
+    raise TypeError("unsupported dtype %s" % dt)
+
+
+def _torch_dtype(code):
+    import torch
+
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[code]
+
+
+def mm_bt(a, b, out_dtype=None, out=None, stream=None):
+    """C = a @ b.T for CUDA/HIP tensors a (M×K) and b (N×K) of one 16-bit dtype.
+
+    ``out_dtype`` defaults to a's dtype; ``out`` may be a preallocated
+    contiguous M×N tensor.  The call is asynchronous on ``stream`` (default:
+    torch's current stream of a's device).
+    """
+    import torch
+
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("expected a (M,K) and b (N,K), got %s and %s" % (tuple(a.shape), tuple(b.shape)))
+    if a.dtype != b.dtype:
+        raise TypeError("a and b must share one dtype")
+    if not a.is_cuda or not b.is_cuda or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    in_code = _torch_code(a.dtype)
+    out_code = in_code if out_dtype is None else (_torch_code(out_dtype) if not isinstance(out_dtype, int)
+                                                  else out_dtype)
+    a = a.contiguous()
+    b = b.contiguous()
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=_torch_dtype(out_code), device=a.device)
+    elif out.shape != (M, N) or not out.is_contiguous() or out.dtype != _torch_dtype(out_code):
+        raise ValueError("out must be a contiguous %dx%d %s tensor" % (M, N, _torch_dtype(out_code)))
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    with torch.cuda.device(a.device):
+        st = gemm_bt(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, in_code, out_code, stream)
+    if st != OK:
+        raise GemmBtError(st)
+    return out

@@ -1,0 +1,139 @@
+// common.hpp -- types and small device helpers shared by the gemm_bt kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_bt.h"
+
+namespace gbt {
+
+typedef unsigned short u16;
+typedef unsigned int u32;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Buffer-resource word 3 for gfx9-family raw buffers (32-bit data format,
+// no swizzle, no index stride).  With stride 0 the hardware range-checks each
+// access against num_records bytes: an out-of-range load returns zero and an
+// out-of-range store is dropped.  The kernels rely on this for the rows past
+// M or N of a ragged tile and as a safety net for everything else.
+constexpr int kRsrcWord3 = 0x00020000;
+// A byte offset that is always out of range (num_records is kept below 2^31).
+constexpr u32 kOutOfRange = 0x80000000u;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Whole-value reinterpretations.  Arguments are taken by value on purpose:
+// __builtin_bit_cast applied directly to an element of an ext_vector_type
+// reads the vector's first element in this compiler, so always go through a
+// plain local.
+__device__ inline float as_f32(u32 u) { return __builtin_bit_cast(float, u); }
+__device__ inline u32 as_u32(float f) { return __builtin_bit_cast(u32, f); }
+
+// fp32 -> 16-bit, round to nearest even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32),
+// two values packed into one dword, the first in the low half.
+template <int OUT>
+__device__ inline u32 pack2(float a, float b);
+template <>
+__device__ inline u32 pack2<GEMM_BT_BF16>(float a, float b) {
+    bf16x2 p = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(u32, p);
+}
+template <>
+__device__ inline u32 pack2<GEMM_BT_F16>(float a, float b) {
+    f16x2 p = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(u32, p);
+}
+
+// MFMA wrappers over raw 16-byte operands (8 elements of the input type).
+template <int IN>
+struct Mfma;
+template <>
+struct Mfma<GEMM_BT_BF16> {
+    __device__ static inline f32x16 m32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static inline f32x4 m16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma<GEMM_BT_F16> {
+    __device__ static inline f32x16 m32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ static inline f32x4 m16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+
+// 8 consecutive 16-bit elements of one row, starting at byte offset `off`
+// inside the buffer `r`, with every element at index >= `valid` (0..8)
+// replaced by zero.  VEC is the widest access the alignment allows:
+// 8 -> one 16-byte load (then `valid` is 0 or 8), 2 -> four 4-byte loads,
+// 1 -> eight 2-byte loads.
+template <int VEC>
+__device__ inline u32x4 load8(__amdgpu_buffer_rsrc_t r, u32 off, int valid);
+
+template <>
+__device__ inline u32x4 load8<8>(__amdgpu_buffer_rsrc_t r, u32 off, int valid) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, valid > 0 ? off : kOutOfRange, 0, 0);
+}
+template <>
+__device__ inline u32x4 load8<2>(__amdgpu_buffer_rsrc_t r, u32 off, int valid) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32 d = __builtin_amdgcn_raw_buffer_load_b32(r, 2 * i < valid ? off + 4 * i : kOutOfRange, 0, 0);
+        v[i] = d;
+    }
+    return v;
+}
+template <>
+__device__ inline u32x4 load8<1>(__amdgpu_buffer_rsrc_t r, u32 off, int valid) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32 lo = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * i < valid ? off + 4 * i : kOutOfRange, 0, 0);
+        const u32 hi = __builtin_amdgcn_raw_buffer_load_b16(r, 2 * i + 1 < valid ? off + 4 * i + 2 : kOutOfRange, 0, 0);
+        v[i] = lo | (hi << 16);
+    }
+    return v;
+}
+
+// Tile order: XCD regrouping followed by banded (grouped) order.  Identical
+// on host and device so the host can verify it is a bijection.
+__host__ __device__ inline void tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m,
+                                           int64_t* tm, int64_t* tn) {
+    const int64_t total = tiles_m * tiles_n;
+    // Workgroup pid is dispatched to die pid % 8.  Give die x the contiguous
+    // run [start_x, start_x + count_x) of the tile sequence.
+    constexpr int64_t kXcd = 8;
+    const int64_t q = total / kXcd, rem = total % kXcd;
+    const int64_t x = pid % kXcd, i = pid / kXcd;
+    const int64_t seq = x * q + (x < rem ? x : rem) + i;
+    // Banded order over the tile grid: bands of group_m tile-rows, walked
+    // column by column, rows fastest inside a band.
+    const int64_t band_tiles = (int64_t)group_m * tiles_n;
+    const int64_t band = seq / band_tiles;
+    const int64_t first_m = band * group_m;
+    const int64_t rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int64_t in_band = seq - band * band_tiles;
+    *tm = first_m + in_band % rows;
+    *tn = in_band / rows;
+}
+
+}  // namespace gbt

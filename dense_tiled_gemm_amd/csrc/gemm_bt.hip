@@ -1,0 +1,279 @@
+// gemm_bt.hip -- C-ABI entry points of libgemm_bt.so: argument checks, launch
+// planning and kernel dispatch for C = A * B^T on gfx950.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "common.hpp"
+#include "skinny_kernel.hpp"
+#include "tiled_kernel.hpp"
+
+namespace gbt {
+
+// Zero fill of C for K == 0 (every entry is an empty sum).
+__global__ void zero_fill_kernel(u16* __restrict__ c, size_t n16) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) c[i] = 0;
+}
+
+enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3 };
+
+// Tile shapes of the LDS-tiled kernel.
+//   L: 256 x 256, 8 waves as 2 x 4 (each wave 128 x 64 of C), 128 KiB LDS.
+//   M: 128 x 128, 4 waves as 2 x 2 (each wave 64 x 64 of C), 64 KiB LDS.
+// The skinny kernel: 32 rows of B per workgroup (NB = 2), K split over 4 waves.
+struct TileCfg {
+    int bm, bn, wm, wn;
+};
+constexpr TileCfg kCfgL = {256, 256, 2, 4};
+constexpr TileCfg kCfgM = {128, 128, 2, 2};
+constexpr int kSkinnyNB = 2, kSkinnyKS = 4;
+constexpr int kSwz = 1;
+constexpr int kGroupM = 4;
+
+static int forced_cfg() {
+    // Benchmarking aid: GEMM_BT_FORCE_TILE=L|M pins the tiled kernel's shape.
+    static std::atomic<int> cached{-2};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v == -2) {
+        const char* e = std::getenv("GEMM_BT_FORCE_TILE");
+        v = -1;
+        if (e && (e[0] == 'L' || e[0] == 'l')) v = 0;
+        if (e && (e[0] == 'M' || e[0] == 'm')) v = 1;
+        cached.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+static int pick_vec(int64_t K, int a_align, int b_align) {
+    if (K % 8 == 0 && a_align % 16 == 0 && b_align % 16 == 0) return 8;
+    if (K % 2 == 0 && a_align % 4 == 0 && b_align % 4 == 0) return 2;
+    return 1;
+}
+
+static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
+                     int b_align, int c_align, int num_cu, gemm_bt_plan_t* p) {
+    if (!p) return GEMM_BT_ERR_INVALID_VALUE;
+    std::memset(p, 0, sizeof(*p));
+    if (M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
+    if (in_dtype != GEMM_BT_BF16 && in_dtype != GEMM_BT_F16) return GEMM_BT_ERR_UNSUPPORTED;
+    if (out_dtype != GEMM_BT_F32 && out_dtype != GEMM_BT_BF16 && out_dtype != GEMM_BT_F16)
+        return GEMM_BT_ERR_UNSUPPORTED;
+    const int osz = out_dtype == GEMM_BT_F32 ? 4 : 2;
+    // 32-bit buffer offsets inside one 256-row panel of A, B and C.
+    if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
+    if (256 * K * 2 >= 0x7FFFFFFFLL || 256 * N * (int64_t)osz >= 0x7FFFFFFFLL) return GEMM_BT_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) {
+        p->kernel = KIND_NONE;
+        return GEMM_BT_OK;
+    }
+    if (K == 0) {
+        p->kernel = KIND_FILL;
+        p->threads = 256;
+        const int64_t n16 = M * N * osz / 2;
+        int64_t g = (n16 + 255) / 256;
+        p->grid = g < 4096 ? g : 4096;
+        return GEMM_BT_OK;
+    }
+    p->vec = pick_vec(K, a_align, b_align);
+    p->bk = 64;
+    if (M <= 16) {
+        p->kernel = KIND_SKINNY;
+        p->bm = 16;
+        p->bn = 16 * kSkinnyNB;
+        p->bk = 32;
+        p->ksplit = kSkinnyKS;
+        p->threads = 64 * kSkinnyKS;
+        p->lds_bytes = kSkinnyKS * kSkinnyNB * 64 * 16;
+        p->tiles_m = 1;
+        p->tiles_n = (N + p->bn - 1) / p->bn;
+        p->grid = p->tiles_n;
+        return GEMM_BT_OK;
+    }
+    const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256);
+    int use = tiles_l >= num_cu ? 0 : 1;
+    const int f = forced_cfg();
+    if (f >= 0) use = f;
+    const TileCfg c = use == 0 ? kCfgL : kCfgM;
+    p->kernel = KIND_TILED;
+    p->bm = c.bm;
+    p->bn = c.bn;
+    p->threads = 64 * c.wm * c.wn;
+    p->group_m = kGroupM;
+    p->ksplit = 1;
+    p->lds_bytes = 2 * (c.bm + c.bn) * 64 * 2;
+    p->tiles_m = (M + c.bm - 1) / c.bm;
+    p->tiles_n = (N + c.bn - 1) / c.bn;
+    p->grid = p->tiles_m * p->tiles_n;
+    (void)c_align;
+    return GEMM_BT_OK;
+}
+
+// ---- kernel selection --------------------------------------------------------
+
+typedef void (*TiledFn)(const u16*, const u16*, void*, int, int, int, int, int, int, int);
+typedef void (*SkinnyFn)(const u16*, const u16*, void*, int, int, int, int);
+
+template <int IN, int OUT, int VEC>
+static const void* tiled_fn(int cfg) {
+    if (cfg == 0)
+        return (const void*)&tiled_kernel<IN, OUT, kCfgL.bm, kCfgL.bn, kCfgL.wm, kCfgL.wn, VEC, kSwz>;
+    return (const void*)&tiled_kernel<IN, OUT, kCfgM.bm, kCfgM.bn, kCfgM.wm, kCfgM.wn, VEC, kSwz>;
+}
+
+template <int IN, int OUT>
+static const void* tiled_fn_vec(int cfg, int vec) {
+    if (vec == 8) return tiled_fn<IN, OUT, 8>(cfg);
+    if (vec == 2) return tiled_fn<IN, OUT, 2>(cfg);
+    return tiled_fn<IN, OUT, 1>(cfg);
+}
+
+template <int IN>
+static const void* tiled_fn_out(int out, int cfg, int vec) {
+    if (out == GEMM_BT_F32) return tiled_fn_vec<IN, GEMM_BT_F32>(cfg, vec);
+    if (out == GEMM_BT_BF16) return tiled_fn_vec<IN, GEMM_BT_BF16>(cfg, vec);
+    return tiled_fn_vec<IN, GEMM_BT_F16>(cfg, vec);
+}
+
+template <int IN, int OUT>
+static const void* skinny_fn_vec(int vec) {
+    if (vec == 8) return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 8>;
+    if (vec == 2) return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 2>;
+    return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 1>;
+}
+
+template <int IN>
+static const void* skinny_fn_out(int out, int vec) {
+    if (out == GEMM_BT_F32) return skinny_fn_vec<IN, GEMM_BT_F32>(vec);
+    if (out == GEMM_BT_BF16) return skinny_fn_vec<IN, GEMM_BT_BF16>(vec);
+    return skinny_fn_vec<IN, GEMM_BT_F16>(vec);
+}
+
+// ---- device checks -------------------------------------------------------------
+
+constexpr int kMaxDev = 64;
+static std::atomic<int> g_dev_state[kMaxDev];  // 0 unknown, 1 gfx950, 2 other
+static std::atomic<int> g_dev_cus[kMaxDev];
+
+static int check_device(int* num_cu) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return GEMM_BT_ERR_NO_DEVICE;
+    }
+    if (dev >= kMaxDev) return GEMM_BT_ERR_NO_DEVICE;
+    int st = g_dev_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return GEMM_BT_ERR_NO_DEVICE;
+        }
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        g_dev_state[dev].store(st, std::memory_order_release);
+    }
+    if (st != 1) return GEMM_BT_ERR_NO_DEVICE;
+    *num_cu = g_dev_cus[dev].load(std::memory_order_relaxed);
+    return GEMM_BT_OK;
+}
+
+static int align_of(const void* p) {
+    const uintptr_t v = (uintptr_t)p;
+    if (v % 16 == 0) return 16;
+    if (v % 8 == 0) return 8;
+    if (v % 4 == 0) return 4;
+    if (v % 2 == 0) return 2;
+    return 1;
+}
+
+}  // namespace gbt
+
+using namespace gbt;
+
+extern "C" {
+
+int gemm_bt_version(void) { return 100; }
+
+const char* gemm_bt_status_string(int status) {
+    switch (status) {
+        case GEMM_BT_OK: return "ok";
+        case GEMM_BT_ERR_INVALID_VALUE: return "invalid value";
+        case GEMM_BT_ERR_UNSUPPORTED: return "unsupported dtype or size";
+        case GEMM_BT_ERR_NO_DEVICE: return "no gfx950 HIP device";
+        case GEMM_BT_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align, int b_align,
+                 int c_align, gemm_bt_plan_t* plan) {
+    return plan_impl(M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
+}
+
+int gemm_bt_tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m, int64_t* tm, int64_t* tn) {
+    if (!tm || !tn || tiles_m <= 0 || tiles_n <= 0 || group_m <= 0) return GEMM_BT_ERR_INVALID_VALUE;
+    if (pid < 0 || pid >= tiles_m * tiles_n) return GEMM_BT_ERR_INVALID_VALUE;
+    tile_coord(pid, tiles_m, tiles_n, group_m, tm, tn);
+    return GEMM_BT_OK;
+}
+
+int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
+            void* stream) {
+    gemm_bt_plan_t p;
+    const int a_al = align_of(A), b_al = align_of(B), c_al = align_of(C);
+    // Plan against the default CU count first: it validates the arguments
+    // without touching the device.
+    int st = plan_impl(M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
+    if (st != GEMM_BT_OK) return st;
+    if (p.kernel == KIND_NONE) return GEMM_BT_OK;
+    const int osz = out_dtype == GEMM_BT_F32 ? 4 : 2;
+    if (!C) return GEMM_BT_ERR_INVALID_VALUE;
+    if (p.kernel != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
+    if ((uintptr_t)A % 2 || (uintptr_t)B % 2 || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
+
+    int num_cu = 256;
+    st = check_device(&num_cu);
+    if (st != GEMM_BT_OK) return st;
+    if (num_cu != 256) {
+        st = plan_impl(M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, num_cu, &p);
+        if (st != GEMM_BT_OK) return st;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+
+    if (p.kernel == KIND_FILL) {
+        u16* c16 = (u16*)C;
+        size_t n16 = (size_t)M * (size_t)N * osz / 2;
+        void* args[] = {&c16, &n16};
+        e = hipLaunchKernel((const void*)&zero_fill_kernel, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+    } else {
+        const u16* a = (const u16*)A;
+        const u16* b = (const u16*)B;
+        // Vector stores need 4 consecutive outputs inside one row, aligned.
+        int vec_store = (N % 4 == 0) && c_al >= 4 * osz ? 1 : 0;
+        if (p.kernel == KIND_TILED) {
+            const int cfg = p.bm == kCfgL.bm ? 0 : 1;
+            const void* fn = in_dtype == GEMM_BT_BF16 ? tiled_fn_out<GEMM_BT_BF16>(out_dtype, cfg, p.vec)
+                                                      : tiled_fn_out<GEMM_BT_F16>(out_dtype, cfg, p.vec);
+            int tm = (int)p.tiles_m, tn = (int)p.tiles_n, gm = p.group_m;
+            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store};
+            e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+        } else {
+            const void* fn = in_dtype == GEMM_BT_BF16 ? skinny_fn_out<GEMM_BT_BF16>(out_dtype, p.vec)
+                                                      : skinny_fn_out<GEMM_BT_F16>(out_dtype, p.vec);
+            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &vec_store};
+            e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+        }
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_BT_ERR_LAUNCH;
+    }
+    return GEMM_BT_OK;
+}
+
+}  // extern "C"

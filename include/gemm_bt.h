@@ -1,0 +1,120 @@
+/*
+ * gemm_bt.h -- C = A * B^T on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  C[i][j] = sum_k A[i][k] * B[j][k] for 0 <= i < M, 0 <= j < N,
+ * with A stored M x K row-major and B stored N x K row-major, i.e. B is kept
+ * transposed so both operands are read along K ("Optimizing Blackwell matrix
+ * multiplication in Mojo (part 2)", sections "Starting from the 4-line kernel"
+ * and "Kernel 2: TMA and Tensor Core", where B is laid out row_major(N, K) so
+ * its loads coalesce).  Inputs are bf16 or f16 (both operands the same type,
+ * as the MMA contract of "Writing Mosaic GPU kernels with Pallas", section
+ * "MMA (TensorCore)", requires); products are accumulated in fp32 and the
+ * result is rounded once, to nearest even, into the output type ("Chapter 7:
+ * Writing custom kernels with Pallas", section 4.1': fp32 accumulator, cast
+ * only after the last K step).  C is overwritten: there is no alpha/beta.
+ *
+ * Layout.  Dense and contiguous: lda = ldb = K elements, ldc = N elements.
+ * Pointers need only element alignment (2 bytes for 16-bit data, 4 bytes for
+ * fp32 output); 16-byte alignment together with K % 8 == 0 selects the
+ * widest loads and is a performance matter only.
+ *
+ * Ownership.  The caller owns A, B and C (device memory, e.g. from PyTorch).
+ * The library allocates nothing per call, keeps no pointer after it returns
+ * and holds no state beyond a per-device cache of device attributes.
+ *
+ * Asynchrony and errors.  gemm_bt enqueues its kernel on `stream` and returns
+ * without waiting.  Argument errors are reported before anything is
+ * enqueued.  A launch failure is reported as GEMM_BT_ERR_LAUNCH; a fault
+ * inside the kernel shows at the caller's next synchronisation.  No call
+ * throws, exits or aborts.  Calls are thread-safe.  C must not overlap A or B.
+ */
+#ifndef GEMM_BT_H
+#define GEMM_BT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum {
+    GEMM_BT_F32 = 0,  /* IEEE binary32 (output only) */
+    GEMM_BT_F16 = 1,  /* IEEE binary16 */
+    GEMM_BT_BF16 = 2  /* bfloat16: the upper 16 bits of a binary32 */
+} gemm_bt_dtype;
+
+/* Status codes returned by every entry point. */
+typedef enum {
+    GEMM_BT_OK = 0,
+    GEMM_BT_ERR_INVALID_VALUE = 1, /* negative size, null pointer with data, bad plan pointer */
+    GEMM_BT_ERR_UNSUPPORTED = 2,   /* dtype combination or size outside the supported range */
+    GEMM_BT_ERR_NO_DEVICE = 3,     /* no HIP device, or it is not a gfx950 */
+    GEMM_BT_ERR_LAUNCH = 4         /* the kernel launch failed */
+} gemm_bt_status;
+
+/*
+ * C = A * B^T.
+ *   A          device pointer, M x K elements of in_dtype, row-major
+ *   B          device pointer, N x K elements of in_dtype, row-major (B^T stored)
+ *   C          device pointer, M x N elements of out_dtype, row-major; overwritten
+ *   M, N, K    sizes, each in [0, 2^31 - 1]; M*K, N*K and M*N elements must each
+ *              fit below 2^31 bytes per 256-row panel (checked: UNSUPPORTED)
+ *   in_dtype   GEMM_BT_BF16 or GEMM_BT_F16
+ *   out_dtype  GEMM_BT_F32, GEMM_BT_BF16 or GEMM_BT_F16
+ *   stream     hipStream_t to enqueue on; NULL means the default stream
+ * M == 0 or N == 0: nothing is enqueued, returns GEMM_BT_OK.
+ * K == 0: C is filled with zeros (the empty sum) on `stream`.
+ * The device is the caller's current HIP device.
+ */
+int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+            int in_dtype, int out_dtype, void* stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* gemm_bt_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gemm_bt_version(void);
+
+/*
+ * Launch plan: which kernel and tile shape gemm_bt would use for a problem.
+ * Host-only (no device call); lets callers and tests see the tiling and the
+ * grid.  `a_align`, `b_align`, `c_align` are the byte alignments of the
+ * pointers that would be passed (e.g. 256 for fresh allocations).
+ */
+typedef struct {
+    int kernel;       /* 0 = none (empty), 1 = zero fill (K == 0), 2 = LDS-tiled MFMA, 3 = skinny streaming */
+    int bm, bn, bk;   /* workgroup tile (rows of C, columns of C, K step) */
+    int threads;      /* threads per workgroup */
+    int vec;          /* elements per global load: 8 (16 bytes), 2 or 1 */
+    int group_m;      /* tile-rows per group in the grouped tile order */
+    int ksplit;       /* waves that split K inside a workgroup (skinny kernel) */
+    int lds_bytes;    /* LDS per workgroup */
+    int64_t tiles_m, tiles_n;
+    int64_t grid;     /* workgroups launched */
+} gemm_bt_plan_t;
+
+int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
+                 int b_align, int c_align, gemm_bt_plan_t* plan);
+
+/*
+ * Tile order used by the tiled kernel: workgroup `pid` (0 <= pid < tiles_m *
+ * tiles_n) computes output tile (tm, tn).  Workgroups are first regrouped by
+ * the XCD (accelerator die, 8 on MI355X, each with its own L2) that the
+ * hardware dispatches them to, round-robin, so that each die receives a
+ * contiguous run of tiles; that run is then walked in bands of `group_m`
+ * tile-rows, column by column inside a band, so that tiles running at the
+ * same time share A-row and B-row panels in L2 ("Writing Mosaic GPU kernels
+ * with Pallas", section "Using the L2 cache": reorder the grid into bands of
+ * mt rows so that concurrently scheduled blocks touch less data).
+ * Host-callable copy of the device function; returns INVALID_VALUE for a pid
+ * outside the grid.
+ */
+int gemm_bt_tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m, int64_t* tm,
+                       int64_t* tn);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_BT_H */

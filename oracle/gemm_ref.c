@@ -169,18 +169,37 @@ void orc_round(const double* x, int64_t n, int out_dtype, void* out) {
     }
 }
 
+/* Exact value of every 16-bit pattern, filled once from the decoders above so
+   the loops below index a table instead of re-decoding each operand. */
+static double g_table[2][65536];
+static int g_table_ready[2];
+
+static const double* table_for(int dtype) {
+    const int t = dtype == ORC_BF16 ? 1 : 0;
+    if (!g_table_ready[t]) {
+#pragma omp critical(orc_table)
+        {
+            if (!g_table_ready[t]) {
+                for (int h = 0; h < 65536; ++h) g_table[t][h] = decode((uint16_t)h, dtype);
+                g_table_ready[t] = 1;
+            }
+        }
+    }
+    return g_table[t];
+}
+
 /* One output entry: the increasing-k fp64 dot product of row i of A and
    row j of stored B. */
-static double dot_row(const uint16_t* a, const uint16_t* b, int64_t K, int dtype) {
+static double dot_row(const uint16_t* a, const uint16_t* b, int64_t K, const double* tab) {
     double s = 0.0;
-    for (int64_t k = 0; k < K; ++k) s += decode(a[k], dtype) * decode(b[k], dtype);
+    for (int64_t k = 0; k < K; ++k) s += tab[a[k]] * tab[b[k]];
     return s;
 }
 
-static double norm_row(const uint16_t* a, int64_t K, int dtype) {
+static double norm_row(const uint16_t* a, int64_t K, const double* tab) {
     double s = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        const double v = decode(a[k], dtype);
+        const double v = tab[a[k]];
         s += v * v;
     }
     return sqrt(s);
@@ -199,16 +218,17 @@ int orc_gemm_bt(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int6
 #else
     (void)nthreads;
 #endif
+    const double* tab = table_for(in_dtype);
     int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
     for (i = 0; i < M; ++i) {
         const uint16_t* a = A + i * K;
-        for (int64_t j = 0; j < N; ++j) C[i * N + j] = dot_row(a, B + j * K, K, in_dtype);
-        if (nA) nA[i] = norm_row(a, K, in_dtype);
+        for (int64_t j = 0; j < N; ++j) C[i * N + j] = dot_row(a, B + j * K, K, tab);
+        if (nA) nA[i] = norm_row(a, K, tab);
     }
     if (nB) {
 #pragma omp parallel for schedule(static)
-        for (i = 0; i < N; ++i) nB[i] = norm_row(B + i * K, K, in_dtype);
+        for (i = 0; i < N; ++i) nB[i] = norm_row(B + i * K, K, tab);
     }
     return 0;
 }
@@ -229,9 +249,10 @@ int orc_gemm_bt_entries(const uint16_t* A, const uint16_t* B, int64_t M, int64_t
 #else
     (void)nthreads;
 #endif
+    const double* tab = table_for(in_dtype);
     int64_t t;
 #pragma omp parallel for schedule(dynamic, 64)
-    for (t = 0; t < n; ++t) out[t] = dot_row(A + I[t] * K, B + J[t] * K, K, in_dtype);
+    for (t = 0; t < n; ++t) out[t] = dot_row(A + I[t] * K, B + J[t] * K, K, tab);
     return 0;
 }
 
@@ -245,8 +266,9 @@ int orc_row_norms(const uint16_t* X, int64_t R, int64_t K, int in_dtype, double*
 #else
     (void)nthreads;
 #endif
+    const double* tab = table_for(in_dtype);
     int64_t r;
 #pragma omp parallel for schedule(static)
-    for (r = 0; r < R; ++r) out[r] = norm_row(X + r * K, K, in_dtype);
+    for (r = 0; r < R; ++r) out[r] = norm_row(X + r * K, K, tab);
     return 0;
 }

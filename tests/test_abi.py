@@ -1,0 +1,108 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, validates arguments before touching a device, and its host-side
+planning and tile order behave as documented."""
+import os
+import re
+
+import pytest
+
+import dense_tiled_gemm_amd as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gemm_bt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gemm_bt\w*)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = gb.load()
+    names = declared_functions()
+    assert set(names) == set(gb.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert gb.gemm_bt_version() >= 100
+    for st in range(5):
+        s = gb.status_string(st)
+        assert s and s != "unknown status"
+    assert gb.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("args,want", [
+    ((1, 1, 1, -1, 4, 4, gb.BF16, gb.F32), gb.ERR_INVALID_VALUE),
+    ((1, 1, 1, 4, -1, 4, gb.BF16, gb.F32), gb.ERR_INVALID_VALUE),
+    ((1, 1, 1, 4, 4, -1, gb.BF16, gb.F32), gb.ERR_INVALID_VALUE),
+    ((1, 1, 1, 4, 4, 4, gb.F32, gb.F32), gb.ERR_UNSUPPORTED),   # fp32 inputs are not offered
+    ((1, 1, 1, 4, 4, 4, gb.BF16, 7), gb.ERR_UNSUPPORTED),
+    ((1, 1, 1, 4, 4, 1 << 31, gb.BF16, gb.F32), gb.ERR_UNSUPPORTED),
+    ((1, 1, 1, 4, 1 << 23, 4, gb.BF16, gb.F32), gb.ERR_UNSUPPORTED),
+    ((0, 0, 0, 0, 5, 5, gb.BF16, gb.F32), gb.OK),               # empty: nothing enqueued
+    ((0, 0, 0, 5, 0, 5, gb.F16, gb.F16), gb.OK),
+    ((16, 16, 0, 4, 4, 4, gb.BF16, gb.F32), gb.ERR_INVALID_VALUE),  # null C
+    ((0, 16, 16, 4, 4, 4, gb.BF16, gb.F32), gb.ERR_INVALID_VALUE),  # null A
+    ((17, 16, 16, 4, 4, 4, gb.BF16, gb.F32), gb.ERR_INVALID_VALUE),  # misaligned A
+    ((16, 16, 18, 4, 4, 4, gb.BF16, gb.F32), gb.ERR_INVALID_VALUE),  # misaligned fp32 C
+])
+def test_argument_validation_before_any_device_call(args, want):
+    A, B, C, M, N, K, i, o = args
+    assert gb.gemm_bt(A, B, C, M, N, K, i, o, None) == want
+
+
+def test_no_device_status_without_gpu():
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; this checks the no-device path only")
+    # valid-looking arguments: the call must stop at the device query
+    assert gb.gemm_bt(256, 256, 256, 4, 4, 4, gb.BF16, gb.F32, None) == gb.ERR_NO_DEVICE
+
+
+def test_plan_choices():
+    p = gb.gemm_bt_plan(4096, 4096, 4096, gb.BF16, gb.BF16)
+    assert (p.kernel, p.bm, p.bn, p.bk, p.vec, p.grid) == (2, 256, 256, 64, 8, 256)
+    p = gb.gemm_bt_plan(1024, 4096, 4096, gb.F16, gb.F16)
+    assert (p.kernel, p.bm, p.bn, p.grid) == (2, 128, 128, 256)
+    p = gb.gemm_bt_plan(1000, 3000, 2050, gb.BF16, gb.F32)
+    assert (p.kernel, p.bm, p.bn, p.vec, p.tiles_m, p.tiles_n) == (2, 128, 128, 2, 8, 24)
+    p = gb.gemm_bt_plan(16, 8192, 8192, gb.BF16, gb.BF16)
+    assert (p.kernel, p.bm, p.bn, p.ksplit, p.grid) == (3, 16, 32, 4, 256)
+    p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)
+    assert (p.kernel, p.bm, p.grid) == (2, 128, 16)
+    assert gb.gemm_bt_plan(7, 9, 0, gb.BF16, gb.F32).kernel == 1   # K == 0: zero fill
+    assert gb.gemm_bt_plan(0, 9, 5, gb.BF16, gb.F32).kernel == 0   # empty
+    # alignment decides the load width
+    assert gb.gemm_bt_plan(64, 64, 64, gb.BF16, gb.F32, a_align=4).vec == 2
+    assert gb.gemm_bt_plan(64, 64, 63, gb.BF16, gb.F32).vec == 1
+    assert gb.gemm_bt_plan(64, 64, 66, gb.BF16, gb.F32).vec == 2
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,group_m", [(16, 16, 4), (8, 32, 4), (8, 24, 4), (4, 4, 4),
+                                                     (3, 5, 4), (1, 256, 4), (7, 13, 2), (33, 1, 8)])
+def test_tile_order_is_a_bijection(tiles_m, tiles_n, group_m):
+    seen = set()
+    for pid in range(tiles_m * tiles_n):
+        tm, tn = gb.gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m)
+        assert 0 <= tm < tiles_m and 0 <= tn < tiles_n
+        seen.add((tm, tn))
+    assert len(seen) == tiles_m * tiles_n
+    with pytest.raises(gb.GemmBtError):
+        gb.gemm_bt_tile_coord(tiles_m * tiles_n, tiles_m, tiles_n, group_m)
+
+
+def test_tile_order_keeps_each_die_on_a_compact_block():
+    # 16 x 16 tiles (4096^2 with 256^2 tiles): workgroups pid = x (mod 8) run on
+    # die x; each die should get a 4-row x 8-column block, so it reads 4 A
+    # panels and 8 B panels instead of 1 x 32 or 32 x 1.
+    for x in range(8):
+        tiles = [gb.gemm_bt_tile_coord(pid, 16, 16, 4) for pid in range(x, 256, 8)]
+        rows = {t[0] for t in tiles}
+        cols = {t[1] for t in tiles}
+        assert len(tiles) == 32 and len(rows) == 4 and len(cols) == 8
+    # the first 8 workgroups (one per die, dispatched together) start 8 different blocks
+    firsts = [gb.gemm_bt_tile_coord(pid, 16, 16, 4) for pid in range(8)]
+    assert len(set(firsts)) == 8

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP kernels, called through the C-ABI, against the CPU oracle.
+
+Every case prints its name, shape and seed before it touches the GPU.  Outputs
+are poisoned with NaN before each call so a missed store cannot pass.  The
+rules (oracle.tolerance): fp32 out |err| <= 1e-3·‖A_i‖‖B_j‖; 16-bit out adds one
+ulp of the oracle value; integer-valued inputs must match bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import tolerance
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits, in_dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to("cuda").view(TORCH_DT[in_dtype])
+
+
+def run_gpu(gb, a_bits, b_bits, in_dtype, out_dtype):
+    a = to_dev(a_bits, in_dtype)
+    b = to_dev(b_bits, in_dtype)
+    M, N = a.shape[0], b.shape[0]
+    c = torch.full((M, N), float("nan"), dtype=TORCH_DT[out_dtype], device="cuda")
+    gb.mm_bt(a, b, out_dtype=TORCH_DT[out_dtype], out=c)
+    torch.cuda.synchronize()
+    return c.cpu()
+
+
+def f64(c):
+    return c.to(torch.float64).numpy()
+
+
+def out_bits(c):
+    if c.dtype == torch.float32:
+        return c.view(torch.int32).numpy().view(np.uint32)
+    return c.view(torch.int16).numpy().view(np.uint16)
+
+
+def check_full(c, a_bits, b_bits, in_dtype, out_dtype, what):
+    cref, nA, nB = oracle.gemm_bt_ref(a_bits, b_bits, in_dtype)
+    rep = tolerance.check(f64(c), cref, np.outer(nA, nB), out_dtype)
+    assert rep.ok, (what, rep)
+    return cref
+
+
+def check_bits_full(c, a_bits, b_bits, in_dtype, out_dtype, what):
+    cref, _, _ = oracle.gemm_bt_ref(a_bits, b_bits, in_dtype)
+    rep = tolerance.bit_exact(out_bits(c), oracle.round_to(cref, out_dtype), out_dtype)
+    assert rep.ok, (what, rep)
+
+
+SHAPES = [
+    (1, 1, 1), (1, 7, 3), (2, 3, 8), (16, 16, 16), (17, 33, 65), (31, 63, 127), (64, 64, 64),
+    (65, 129, 200), (127, 255, 64), (128, 128, 128), (130, 260, 72), (200, 100, 300),
+    (257, 513, 129), (300, 700, 1000), (129, 1031, 64), (513, 257, 520),
+]
+SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200)]
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_shape_sweep(gpu, in_dtype, out_dtype):
+    for i, (M, N, K) in enumerate(SHAPES + SKINNY):
+        seed = 500 + i
+        say("sweep", in_dtype, out_dtype, M, N, K, "seed", seed)
+        a, b = synth.make(M, N, K, in_dtype, "normal", seed)
+        c = run_gpu(gpu, a, b, in_dtype, out_dtype)
+        check_full(c, a, b, in_dtype, out_dtype, (M, N, K))
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_integer_bit_exact_sweep(gpu, in_dtype, out_dtype):
+    for i, (M, N, K) in enumerate(SHAPES + SKINNY):
+        seed = 700 + i
+        say("int sweep", in_dtype, out_dtype, M, N, K, "seed", seed)
+        a, b = synth.make(M, N, K, in_dtype, "int", seed)
+        c = run_gpu(gpu, a, b, in_dtype, out_dtype)
+        check_bits_full(c, a, b, in_dtype, out_dtype, (M, N, K))
+
+
+def sample_entries(M, N, rng, tile=256):
+    """Rows and columns at every tile edge plus random ones; returns (I, J)."""
+    edge_r = sorted({0, M - 1} | {min(M - 1, t + d) for t in range(0, M, tile) for d in (-1, 0)} - {-1})
+    edge_c = sorted({0, N - 1} | {min(N - 1, t + d) for t in range(0, N, tile) for d in (-1, 0)} - {-1})
+    rows = np.unique(np.concatenate([edge_r[:64], rng.integers(0, M, 24)]))
+    cols = np.unique(np.concatenate([edge_c[:64], rng.integers(0, N, 24)]))
+    I1, J1 = np.meshgrid(rows, np.arange(N), indexing="ij")
+    I2, J2 = np.meshgrid(np.arange(M), cols, indexing="ij")
+    I3 = rng.integers(0, M, 20000)
+    J3 = rng.integers(0, N, 20000)
+    I = np.concatenate([I1.ravel(), I2.ravel(), I3])
+    J = np.concatenate([J1.ravel(), J2.ravel(), J3])
+    return I, J
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_full_size(gpu, name):
+    """Each measured workload at its full size, in the launch configuration the benchmark times."""
+    w = synth.WORKLOADS[name]
+    say("workload", name, w.M, w.N, w.K, w.in_dtype, w.out_dtype, "seed", w.seed)
+    a, b = synth.make_workload(w)
+    c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
+    cf = f64(c)
+    assert np.isfinite(cf).all(), name
+    if w.M * w.N * w.K <= 8e9:
+        check_full(c, a, b, w.in_dtype, w.out_dtype, name)
+    else:
+        rng = np.random.default_rng(w.seed)
+        I, J = sample_entries(w.M, w.N, rng)
+        ref = oracle.gemm_bt_entries(a, b, w.in_dtype, I, J)
+        nA = oracle.row_norms(a, w.in_dtype)
+        nB = oracle.row_norms(b, w.in_dtype)
+        rep = tolerance.check(cf[I, J], ref, nA[I] * nB[J], w.out_dtype)
+        assert rep.ok, (name, rep)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_integer_twin_bit_exact(gpu, name):
+    w = synth.WORKLOADS[name].integer_twin()
+    say("workload int twin", w.name, w.M, w.N, w.K, "seed", w.seed)
+    a, b = synth.make_workload(w)
+    c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
+    if w.M * w.N * w.K <= 8e9:
+        check_bits_full(c, a, b, w.in_dtype, w.out_dtype, w.name)
+    else:
+        rng = np.random.default_rng(w.seed)
+        I, J = sample_entries(w.M, w.N, rng)
+        ref = oracle.gemm_bt_entries(a, b, w.in_dtype, I, J)
+        rep = tolerance.bit_exact(out_bits(c)[I, J], oracle.round_to(ref, w.out_dtype), w.out_dtype)
+        assert rep.ok, (w.name, rep)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+def test_closed_forms(gpu, in_dtype):
+    M, K = 300, 264
+    a, _ = synth.make(M, 1, K, in_dtype, "normal", 41)
+    av = oracle.decode(a, in_dtype)
+    for N in (K, 100, 400):
+        say("identity B", in_dtype, M, N, K)
+        eye = synth.round_bits(np.eye(N, K), in_dtype)
+        for out in ("f32", in_dtype):
+            c = run_gpu(gpu, a, eye, in_dtype, out)
+            want = np.zeros((M, N))
+            want[:, :min(N, K)] = av[:, :min(N, K)]
+            assert np.array_equal(f64(c), want), (N, out)
+    for K in (1, 63, 2050, 4096):
+        say("all ones", in_dtype, K)
+        ones_a = synth.round_bits(np.ones((70, K)), in_dtype)
+        ones_b = synth.round_bits(np.ones((90, K)), in_dtype)
+        for out in ("f32", "bf16", "f16"):
+            c = run_gpu(gpu, ones_a, ones_b, in_dtype, out)
+            want = oracle.decode(oracle.round_to(np.array([float(K)]), out), out)[0] if out != "f32" else float(K)
+            assert np.all(f64(c) == want), (K, out)
+    say("zero operand", in_dtype)
+    a, b = synth.make(129, 257, 96, in_dtype, "normal", 42)
+    c = run_gpu(gpu, a, np.zeros_like(b), in_dtype, "f32")
+    assert np.all(f64(c) == 0)
+    say("permutation B", in_dtype)
+    perm = np.random.default_rng(5).permutation(K := 192)
+    P = np.zeros((K, K))
+    P[np.arange(K), perm] = 1.0
+    a, _ = synth.make(77, 1, K, in_dtype, "normal", 43)
+    c = run_gpu(gpu, a, synth.round_bits(P, in_dtype), in_dtype, "f32")
+    assert np.array_equal(f64(c), oracle.decode(a, in_dtype)[:, perm])
+
+
+def test_k_zero_and_empty(gpu):
+    for out in ("f32", "bf16", "f16"):
+        say("K=0", out)
+        a = torch.empty((33, 0), dtype=torch.bfloat16, device="cuda")
+        b = torch.empty((65, 0), dtype=torch.bfloat16, device="cuda")
+        c = torch.full((33, 65), float("nan"), dtype=TORCH_DT[out], device="cuda")
+        gpu.mm_bt(a, b, out_dtype=TORCH_DT[out], out=c)
+        torch.cuda.synchronize()
+        assert torch.all(c == 0).item()
+    say("M=0")
+    a = torch.empty((0, 16), dtype=torch.bfloat16, device="cuda")
+    b = torch.ones((8, 16), dtype=torch.bfloat16, device="cuda")
+    c = gpu.mm_bt(a, b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert c.shape == (0, 8)
+
+
+def test_buffer_end_is_never_read(gpu):
+    """A and B sit at the very start of allocations whose remainder is NaN: any
+    read past an operand's last element would poison the result."""
+    for (M, N, K) in [(65, 130, 70), (300, 200, 66), (16, 300, 130), (257, 257, 257)]:
+        say("tail poison", M, N, K)
+        a_bits, b_bits = synth.make(M, N, K, "bf16", "uniform", 77)
+        big_a = torch.full((M * K + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        big_b = torch.full((N * K + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        big_a[:M * K] = to_dev(a_bits, "bf16").reshape(-1)
+        big_b[:N * K] = to_dev(b_bits, "bf16").reshape(-1)
+        c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        st = gpu.gemm_bt(big_a.data_ptr(), big_b.data_ptr(), c.data_ptr(), M, N, K, gpu.BF16, gpu.F32,
+                         torch.cuda.current_stream().cuda_stream)
+        assert st == gpu.OK
+        torch.cuda.synchronize()
+        check_full(c.cpu(), a_bits, b_bits, "bf16", "f32", (M, N, K))
+
+
+def test_unaligned_pointers_and_odd_k(gpu):
+    """Operands starting 2 or 4 bytes past an aligned address, and odd K, select the narrow loaders."""
+    for (M, N, K, off) in [(70, 90, 64, 1), (70, 90, 64, 2), (40, 300, 33, 0), (130, 66, 130, 1), (9, 77, 101, 1)]:
+        say("unaligned", M, N, K, "offset elems", off)
+        a_bits, b_bits = synth.make(M, N, K, "f16", "normal", 88)
+        ba = torch.zeros(M * K + 8, dtype=torch.float16, device="cuda")
+        bb = torch.zeros(N * K + 8, dtype=torch.float16, device="cuda")
+        ba[off:off + M * K] = to_dev(a_bits, "f16").reshape(-1)
+        bb[off:off + N * K] = to_dev(b_bits, "f16").reshape(-1)
+        bc = torch.full((M * N + 8,), float("nan"), dtype=torch.float16, device="cuda")
+        st = gpu.gemm_bt(ba.data_ptr() + 2 * off, bb.data_ptr() + 2 * off, bc.data_ptr() + 2 * off, M, N, K,
+                         gpu.F16, gpu.F16, torch.cuda.current_stream().cuda_stream)
+        assert st == gpu.OK
+        torch.cuda.synchronize()
+        c = bc[off:off + M * N].reshape(M, N).cpu()
+        check_full(c, a_bits, b_bits, "f16", "f16", (M, N, K, off))
+        # neighbours of C untouched
+        assert torch.isnan(bc[:off].cpu()).all() and torch.isnan(bc[off + M * N:].cpu()).all()
+
+
+def test_deterministic_and_stream(gpu):
+    w = synth.WORKLOADS["ragged_m1000_n3000_k2050_bf16_f32"]
+    say("determinism", w.name)
+    a_bits, b_bits = synth.make_workload(w)
+    a, b = to_dev(a_bits, "bf16"), to_dev(b_bits, "bf16")
+    c1 = gpu.mm_bt(a, b, out_dtype=torch.float32)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c2 = gpu.mm_bt(a, b, out_dtype=torch.float32)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
