@@ -35,9 +35,10 @@ class GemmBtError(RuntimeError):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("kernel", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int),
-                ("threads", ctypes.c_int), ("vec", ctypes.c_int), ("group_m", ctypes.c_int),
-                ("ksplit", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("tiles_m", ctypes.c_int64),
+    _fields_ = [("kernel", ctypes.c_int), ("variant", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int),
+                ("bk", ctypes.c_int), ("threads", ctypes.c_int), ("vec", ctypes.c_int), ("group_m", ctypes.c_int),
+                ("ksplit", ctypes.c_int), ("stages", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("tiles_m", ctypes.c_int64),
                 ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64)]
 
     def as_dict(self):

@@ -136,4 +136,62 @@ __host__ __device__ inline void tile_coord(int64_t pid, int64_t tiles_m, int64_t
     *tn = in_band / rows;
 }
 
+// Store a wave's FN x FM grid of 32x32 accumulator blocks (MFMA 32x32x16 with
+// the B tile as first operand, so block (i, j) holds C^T: register r of lane
+// l is C[row mw + 32j + l%32][col nw + 32i + 8(r/4) + 4(l/32) + r%4]).  Each
+// lane writes 4 consecutive outputs of one row of C per store: one 16-byte
+// (fp32) or 8-byte (16-bit) store when vec_store, else element by element.
+// Rows >= M and columns >= N are not written.  The fp32 -> 16-bit conversion
+// rounds to nearest even, once.
+template <int OUT, int FN, int FM>
+__device__ inline void store_tile_32x32(const f32x16 (&acc)[FN][FM], void* C, int M, int N, int m0, int n0,
+                                        int mw, int nw, int lane, int vec_store) {
+    constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
+    const size_t c_origin = (size_t)m0 * N + n0;
+    const size_t c_rest = (size_t)M * N - c_origin;
+    const u32 c_bytes = (u32)min(c_rest * OSZ, (size_t)0x7FFFFFFF);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const char*)C + c_origin * OSZ, c_bytes);
+    const int mlim = M - m0, nlim = N - n0;
+    const int fr = lane & 31, fhi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int ml = mw + 32 * j + fr;
+            if (ml >= mlim) continue;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = nw + 32 * i + 8 * g + 4 * fhi;
+                const u32 off = ((u32)ml * (u32)N + (u32)nl) * OSZ;
+                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                if (vec_store) {
+                    if (nl < nlim) {
+                        if constexpr (OUT == GEMM_BT_F32) {
+                            u32x4 w = {as_u32(v0), as_u32(v1), as_u32(v2), as_u32(v3)};
+                            __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, 0, 0);
+                        } else {
+                            u32x2 w = {pack2<OUT>(v0, v1), pack2<OUT>(v2, v3)};
+                            __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
+                        }
+                    }
+                } else {
+                    const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (nl + e < nlim) {
+                            if constexpr (OUT == GEMM_BT_F32) {
+                                __builtin_amdgcn_raw_buffer_store_b32(as_u32(vv[e]), rc, off + 4u * e, 0, 0);
+                            } else {
+                                const u32 p = pack2<OUT>(vv[e], 0.0f);
+                                __builtin_amdgcn_raw_buffer_store_b16((u16)(p & 0xFFFFu), rc, off + 2u * e, 0, 0);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 }  // namespace gbt

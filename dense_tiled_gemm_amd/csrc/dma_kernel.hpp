@@ -1,0 +1,204 @@
+// dma_kernel.hpp -- LDS-tiled MFMA kernel for C = A * B^T with direct
+// global->LDS loads and a multi-stage LDS ring (gfx950, 16-byte aligned rows).
+//
+// Same computation and lane maps as staged_kernel (tiled_kernel.hpp); what
+// changes is how tiles reach LDS:
+//   * loader: buffer_load_dwordx4 ... lds (16 bytes per lane, new on gfx950)
+//     moves each 16-byte chunk from global memory straight into LDS with no
+//     register staging.  One wave instruction fills 1 KiB of LDS, i.e. 1024 /
+//     (2*BK) whole tile rows; lane L writes LDS bytes [16L, 16L+16) of that
+//     KiB, so the XOR swizzle is applied on the global side: lane L fetches the
+//     logical chunk (L mod CPR) XOR swz(row), which lands where the MFMA reads
+//     expect it ("Optimizing Blackwell matrix multiplication in Mojo (part
+//     2)", section "Kernel 3: Swizzling" and the appendix's swizzle math: XOR
+//     bits of the row into the 16-byte-chunk bits of the address);
+//   * pipeline: STAGES LDS buffers in a ring.  Tile kt+STAGES-1 is requested
+//     while tile kt is multiplied, so STAGES-1 K steps of MFMA work cover the
+//     load latency ("Writing Mosaic GPU kernels with Pallas", section "Hopper
+//     (wgmma)": multi-buffered pipeline that refills a slot as soon as the MMA
+//     reading it has finished).  Per step: wait until this wave's loads of
+//     tile kt have landed (s_waitcnt vmcnt(N) with N = loads of the younger
+//     tiles), one s_barrier so every wave's loads have landed and every wave
+//     is done reading the slot about to be refilled, refill, compute.  The
+//     barrier is issued without a memory fence (a fence would force
+//     vmcnt(0) and drain the ring); compiler-only fences keep LDS accesses on
+//     their side of it;
+//   * K tail and ragged edges: rows past M or N and chunks at k >= K are
+//     fetched with an out-of-range offset, which the buffer unit turns into
+//     zeros in LDS ("Chapter 7: Writing custom kernels with Pallas", section
+//     4.3: zero the K overhang of both operands).  The ring always issues the
+//     same number of loads per step (out-of-range ones past the last tile) so
+//     the vmcnt bound is a compile-time constant.
+#pragma once
+
+#include "common.hpp"
+
+namespace gbt {
+
+// 16-byte-chunk swizzle for tile rows of CPR chunks.  SWZ 0 disables it (for
+// measuring bank conflicts); SWZ 1 and 2 XOR 3 (CPR 8) or 2 (CPR 4) row bits
+// into the chunk index, starting at row bit 0/1 (CPR 8) or 1/2 (CPR 4).
+template <int CPR, int SWZ>
+__device__ inline int swz_row(int row) {
+    if constexpr (SWZ == 0) return 0;
+    else if constexpr (CPR == 8) return SWZ == 1 ? (row & 7) : ((row >> 1) & 7);
+    else return SWZ == 1 ? ((row >> 1) & 3) : ((row >> 2) & 3);
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+__device__ inline void barrier_no_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One 16-byte-per-lane global->LDS transfer: lane L's 16 bytes from buffer
+// offset voff + soff land at LDS address dst + 16 L (dst is wave-uniform and
+// goes to M0).  Kept out of the kernel's lambdas: this compiler drops the
+// host-side launch stub of a kernel template whose lambda calls the builtin
+// directly.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, u32 voff, u32 soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+}
+
+template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ>
+__global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
+                                                          void* __restrict__ C, int M, int N, int K,
+                                                          int tiles_m, int tiles_n, int group_m,
+                                                          int vec_store) {
+    constexpr int W = WM * WN;
+    constexpr int CPR = BK / 8;          // 16-byte chunks per tile row
+    constexpr int ROWB = BK * 2;         // bytes per tile row
+    constexpr int RPI = 1024 / ROWB;     // tile rows per wave load instruction
+    constexpr int LA = BM / (RPI * W);   // A load instructions per wave per stage
+    constexpr int LB = BN / (RPI * W);
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+    constexpr int PEND = (STAGES - 2) * (LA + LB);
+    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static_assert(STAGES >= 2, "at least double buffering");
+    static_assert(LA * RPI * W == BM && LB * RPI * W == BN, "tile rows must split evenly over waves");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(PEND < 64, "vmcnt range");
+    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * STAGE_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    int64_t tm64, tn64;
+    tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
+    const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (u32)rows_a * (u32)K * 2u);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (u32)rows_b * (u32)K * 2u);
+    const u32 row_bytes = (u32)K * 2u;
+
+    // Loader geometry.  Wave instruction i of this wave fills row block
+    // j = wave + i*W (rows j*RPI .. j*RPI+RPI-1 of the tile); lane L writes
+    // row j*RPI + L/CPR at physical chunk L%CPR and so fetches logical chunk
+    // (L%CPR) ^ swz(row).
+    const int lrow = lane / CPR, lphys = lane % CPR;
+    u32 a_off[LA], b_off[LB];
+    int a_kc[LA], b_kc[LB];  // first K index (within a tile) of the lane's chunk
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int row = (wave + i * W) * RPI + lrow;
+        const int c = lphys ^ swz_row<CPR, SWZ>(row);
+        a_off[i] = (u32)row * row_bytes + (u32)c * 16u;
+        a_kc[i] = c * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int row = (wave + i * W) * RPI + lrow;
+        const int c = lphys ^ swz_row<CPR, SWZ>(row);
+        b_off[i] = (u32)row * row_bytes + (u32)c * 16u;
+        b_kc[i] = c * 8;
+    }
+
+    auto issue = [&](int stage, int kt) {
+        unsigned char* sbase = lds + stage * STAGE_BYTES;
+        const u32 kbytes = (u32)kt * (u32)ROWB;
+        const int kleft = K - kt * BK;  // valid K elements in this tile (may be <= 0)
+        if (kleft >= BK) {
+#pragma unroll
+            for (int i = 0; i < LA; ++i)
+                dma16(ra, sbase + (wave + i * W) * 1024, a_off[i], kbytes);
+#pragma unroll
+            for (int i = 0; i < LB; ++i)
+                dma16(rb, sbase + BM * ROWB + (wave + i * W) * 1024, b_off[i], kbytes);
+        } else {
+#pragma unroll
+            for (int i = 0; i < LA; ++i)
+                dma16(ra, sbase + (wave + i * W) * 1024, a_kc[i] < kleft ? a_off[i] : kOutOfRange, kbytes);
+#pragma unroll
+            for (int i = 0; i < LB; ++i)
+                dma16(rb, sbase + BM * ROWB + (wave + i * W) * 1024, b_kc[i] < kleft ? b_off[i] : kOutOfRange,
+                      kbytes);
+        }
+    };
+
+    // Operand reads: row (lane % 32) of each 32-row block, logical chunk
+    // 2*ks + lane/32 for k-substep ks; block bases are multiples of 32, so the
+    // swizzle term depends on the lane only.
+    const int fr = lane & 31, fhi = lane >> 5;
+    const int fsw = swz_row<CPR, SWZ>(fr);
+    const int a_base = (wm * TM + fr) * ROWB;
+    const int b_base = BM * ROWB + (wn * TN + fr) * ROWB;
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto compute = [&](int stage) {
+        const unsigned char* s = lds + stage * STAGE_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int ch = ((2 * ks + fhi) ^ fsw) * 16;
+            u32x4 fb[FN], fa[FM];
+#pragma unroll
+            for (int i = 0; i < FN; ++i) fb[i] = *(const u32x4*)(s + b_base + 32 * ROWB * i + ch);
+#pragma unroll
+            for (int j = 0; j < FM; ++j) fa[j] = *(const u32x4*)(s + a_base + 32 * ROWB * j + ch);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] = Mfma<IN>::m32x32x16(fb[i], fa[j], acc[i][j]);
+        }
+    };
+
+    const int nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
+    int cs = 0;               // stage holding tile kt
+    int ls = STAGES - 1;      // stage receiving tile kt + STAGES - 1
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<PEND>();
+        barrier_no_fence();
+        issue(ls, kt + STAGES - 1);
+        compute(cs);
+        cs = cs + 1 == STAGES ? 0 : cs + 1;
+        ls = ls + 1 == STAGES ? 0 : ls + 1;
+    }
+    wait_vmcnt<0>();  // the ring's last (out-of-range) loads still write LDS
+
+    store_tile_32x32<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+}
+
+}  // namespace gbt

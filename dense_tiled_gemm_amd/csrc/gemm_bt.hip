@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "common.hpp"
+#include "dma_kernel.hpp"
 #include "skinny_kernel.hpp"
 #include "tiled_kernel.hpp"
 
@@ -18,11 +19,12 @@ __global__ void zero_fill_kernel(u16* __restrict__ c, size_t n16) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) c[i] = 0;
 }
 
-enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3 };
+enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3, KIND_DMA = 4 };
 
-// Tile shapes of the LDS-tiled kernel.
-//   L: 256 x 256, 8 waves as 2 x 4 (each wave 128 x 64 of C), 128 KiB LDS.
-//   M: 128 x 128, 4 waves as 2 x 2 (each wave 64 x 64 of C), 64 KiB LDS.
+// Tile shapes.  The aligned path (16-byte loads) uses dma_kernel; rows that
+// are not 16-byte aligned use the register-staged kernel with narrower loads.
+//   staged L: 256 x 256, 8 waves as 2 x 4 (each wave 128 x 64), BK 64, 2 stages.
+//   staged M: 128 x 128, 4 waves as 2 x 2 (each wave 64 x 64), BK 64, 2 stages.
 // The skinny kernel: 32 rows of B per workgroup (NB = 2), K split over 4 waves.
 struct TileCfg {
     int bm, bn, wm, wn;
@@ -33,15 +35,62 @@ constexpr int kSkinnyNB = 2, kSkinnyKS = 4;
 constexpr int kSwz = 1;
 constexpr int kGroupM = 4;
 
-static int forced_cfg() {
-    // Benchmarking aid: GEMM_BT_FORCE_TILE=L|M pins the tiled kernel's shape.
+// DMA-kernel variants: [in: bf16, f16][out: f32, bf16, f16] entry points.
+struct DmaVariant {
+    const char* name;
+    int bm, bn, bk, stages, wm, wn, swz;
+    const void* fn[2][3];
+};
+
+static int in_index(int in_dtype) { return in_dtype == GEMM_BT_BF16 ? 0 : 1; }
+static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out_dtype == GEMM_BT_BF16 ? 1 : 2); }
+
+template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ>
+static DmaVariant dma_variant(const char* name, bool all_dtypes) {
+    DmaVariant v = {name, BM, BN, BK, S, WM, WN, SWZ, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
+    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ>;
+    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ>;
+    if (all_dtypes) {
+        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ>;
+        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ>;
+        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ>;
+        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ>;
+    }
+    return v;
+}
+
+// Index 0 is the default for large grids, 1 the default for small ones; the
+// rest exist for tuning (GEMM_BT_FORCE_TILE=<name>) and are built for the
+// bf16->bf16 and f16->f16 combinations only.
+static const DmaVariant* dma_variants(int* count) {
+    static const DmaVariant v[] = {
+        dma_variant<256, 256, 64, 2, 2, 4, 1>("L64S2", true),
+        dma_variant<128, 128, 64, 4, 2, 2, 1>("M64S4", true),
+        dma_variant<256, 256, 32, 4, 2, 4, 1>("L32S4", false),
+        dma_variant<256, 256, 32, 3, 2, 4, 1>("L32S3", false),
+        dma_variant<256, 256, 64, 2, 2, 2, 1>("L64S2W4", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 0>("L64S2X0", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2X2", false),
+        dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4X2", false),
+        dma_variant<128, 128, 64, 2, 2, 2, 1>("M64S2", false),
+        dma_variant<128, 128, 32, 4, 2, 2, 1>("M32S4", false),
+        dma_variant<128, 256, 64, 3, 2, 4, 1>("T64S3", false),
+    };
+    *count = (int)(sizeof(v) / sizeof(v[0]));
+    return v;
+}
+
+static int forced_variant() {
+    // Benchmarking aid: GEMM_BT_FORCE_TILE=<variant name> pins the DMA kernel shape.
     static std::atomic<int> cached{-2};
     int v = cached.load(std::memory_order_relaxed);
     if (v == -2) {
-        const char* e = std::getenv("GEMM_BT_FORCE_TILE");
         v = -1;
-        if (e && (e[0] == 'L' || e[0] == 'l')) v = 0;
-        if (e && (e[0] == 'M' || e[0] == 'm')) v = 1;
+        const char* e = std::getenv("GEMM_BT_FORCE_TILE");
+        int n = 0;
+        const DmaVariant* vs = dma_variants(&n);
+        for (int i = 0; e && i < n; ++i)
+            if (std::strcmp(e, vs[i].name) == 0) v = i;
         cached.store(v, std::memory_order_relaxed);
     }
     return v;
@@ -93,19 +142,36 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         return GEMM_BT_OK;
     }
     const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256);
-    int use = tiles_l >= num_cu ? 0 : 1;
-    const int f = forced_cfg();
-    if (f >= 0) use = f;
-    const TileCfg c = use == 0 ? kCfgL : kCfgM;
-    p->kernel = KIND_TILED;
-    p->bm = c.bm;
-    p->bn = c.bn;
-    p->threads = 64 * c.wm * c.wn;
+    const bool big = tiles_l >= num_cu;
     p->group_m = kGroupM;
     p->ksplit = 1;
-    p->lds_bytes = 2 * (c.bm + c.bn) * 64 * 2;
-    p->tiles_m = (M + c.bm - 1) / c.bm;
-    p->tiles_n = (N + c.bn - 1) / c.bn;
+    if (p->vec == 8) {
+        int n = 0;
+        const DmaVariant* vs = dma_variants(&n);
+        int use = big ? 0 : 1;
+        const int f = forced_variant();
+        if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
+        const DmaVariant& v = vs[use];
+        p->kernel = KIND_DMA;
+        p->variant = use;
+        p->bm = v.bm;
+        p->bn = v.bn;
+        p->bk = v.bk;
+        p->stages = v.stages;
+        p->threads = 64 * v.wm * v.wn;
+        p->lds_bytes = v.stages * (v.bm + v.bn) * v.bk * 2;
+    } else {
+        const TileCfg c = big ? kCfgL : kCfgM;
+        p->kernel = KIND_TILED;
+        p->variant = big ? 0 : 1;
+        p->bm = c.bm;
+        p->bn = c.bn;
+        p->stages = 2;
+        p->threads = 64 * c.wm * c.wn;
+        p->lds_bytes = 2 * (c.bm + c.bn) * 64 * 2;
+    }
+    p->tiles_m = (M + p->bm - 1) / p->bm;
+    p->tiles_n = (N + p->bn - 1) / p->bn;
     p->grid = p->tiles_m * p->tiles_n;
     (void)c_align;
     return GEMM_BT_OK;
@@ -119,8 +185,8 @@ typedef void (*SkinnyFn)(const u16*, const u16*, void*, int, int, int, int);
 template <int IN, int OUT, int VEC>
 static const void* tiled_fn(int cfg) {
     if (cfg == 0)
-        return (const void*)&tiled_kernel<IN, OUT, kCfgL.bm, kCfgL.bn, kCfgL.wm, kCfgL.wn, VEC, kSwz>;
-    return (const void*)&tiled_kernel<IN, OUT, kCfgM.bm, kCfgM.bn, kCfgM.wm, kCfgM.wn, VEC, kSwz>;
+        return (const void*)&staged_kernel<IN, OUT, kCfgL.bm, kCfgL.bn, kCfgL.wm, kCfgL.wn, VEC, kSwz>;
+    return (const void*)&staged_kernel<IN, OUT, kCfgM.bm, kCfgM.bn, kCfgM.wm, kCfgM.wn, VEC, kSwz>;
 }
 
 template <int IN, int OUT>
@@ -255,10 +321,15 @@ int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
         const u16* b = (const u16*)B;
         // Vector stores need 4 consecutive outputs inside one row, aligned.
         int vec_store = (N % 4 == 0) && c_al >= 4 * osz ? 1 : 0;
-        if (p.kernel == KIND_TILED) {
-            const int cfg = p.bm == kCfgL.bm ? 0 : 1;
-            const void* fn = in_dtype == GEMM_BT_BF16 ? tiled_fn_out<GEMM_BT_BF16>(out_dtype, cfg, p.vec)
-                                                      : tiled_fn_out<GEMM_BT_F16>(out_dtype, cfg, p.vec);
+        if (p.kernel == KIND_TILED || p.kernel == KIND_DMA) {
+            const void* fn;
+            if (p.kernel == KIND_DMA) {
+                int n = 0;
+                fn = dma_variants(&n)[p.variant].fn[in_index(in_dtype)][out_index(out_dtype)];
+            } else {
+                fn = in_dtype == GEMM_BT_BF16 ? tiled_fn_out<GEMM_BT_BF16>(out_dtype, p.variant, p.vec)
+                                              : tiled_fn_out<GEMM_BT_F16>(out_dtype, p.variant, p.vec);
+            }
             int tm = (int)p.tiles_m, tn = (int)p.tiles_n, gm = p.group_m;
             void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store};
             e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);

@@ -1,4 +1,6 @@
-// tiled_kernel.hpp -- LDS-tiled, double-buffered MFMA kernel for C = A * B^T (gfx950).
+// tiled_kernel.hpp -- LDS-tiled, double-buffered MFMA kernel for C = A * B^T (gfx950),
+// register-staged variant used when rows are not 16-byte aligned (K % 8 != 0
+// or operands offset by 2 or 4 bytes); the aligned fast path is dma_kernel.hpp.
 //
 // One workgroup computes one BM x BN tile of C.  Per K step of BK = 64:
 //   * loader: every thread moves 16-byte chunks of the A tile (BM x 64) and
@@ -50,7 +52,7 @@ __device__ inline int swz(int row) {
 }
 
 template <int IN, int OUT, int BM, int BN, int WM, int WN, int VEC, int SWZ>
-__global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const u16* __restrict__ A,
+__global__ __launch_bounds__(64 * WM * WN) void staged_kernel(const u16* __restrict__ A,
                                                             const u16* __restrict__ B,
                                                             void* __restrict__ C, int M, int N, int K,
                                                             int tiles_m, int tiles_n, int group_m,
@@ -62,7 +64,6 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const u16* __restri
     constexpr int LA = BM * 8 / T, LB = BN * 8 / T;  // 16-byte chunks per thread per step
     constexpr int ROWS_PER_PASS = T / 8;
     constexpr int STAGE = (BM + BN) * 8;  // chunks per LDS stage
-    constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert((BM * 8) % T == 0 && (BN * 8) % T == 0, "tile rows must split evenly over threads");
     static_assert(ROWS_PER_PASS % 16 == 0, "row step must keep the swizzle phase");
@@ -157,51 +158,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(const u16* __restri
         __syncthreads();
     }
 
-    // Epilogue.  C buffer based at the tile origin; range = the rest of C.
-    const size_t c_origin = (size_t)m0 * N + n0;
-    const size_t c_rest = (size_t)M * N - c_origin;
-    const u32 c_bytes = (u32)min(c_rest * OSZ, (size_t)0x7FFFFFFF);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const char*)C + c_origin * OSZ, c_bytes);
-    const int mlim = M - m0, nlim = N - n0;
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int ml = wm * TM + 32 * j + fr;
-            if (ml >= mlim) continue;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = wn * TN + 32 * i + 8 * g + 4 * fhi;
-                const u32 off = ((u32)ml * (u32)N + (u32)nl) * OSZ;
-                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                if (vec_store) {
-                    if (nl < nlim) {
-                        if constexpr (OUT == GEMM_BT_F32) {
-                            u32x4 w = {as_u32(v0), as_u32(v1), as_u32(v2), as_u32(v3)};
-                            __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, 0, 0);
-                        } else {
-                            u32x2 w = {pack2<OUT>(v0, v1), pack2<OUT>(v2, v3)};
-                            __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
-                        }
-                    }
-                } else {
-                    const float vv[4] = {v0, v1, v2, v3};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (nl + e < nlim) {
-                            if constexpr (OUT == GEMM_BT_F32) {
-                                __builtin_amdgcn_raw_buffer_store_b32(as_u32(vv[e]), rc, off + 4u * e, 0, 0);
-                            } else {
-                                const u32 p = pack2<OUT>(vv[e], 0.0f);
-                                __builtin_amdgcn_raw_buffer_store_b16((u16)(p & 0xFFFFu), rc, off + 2u * e, 0, 0);
-                            }
-                        }
-                    }
-                }
-            }
-        }
-    }
+    store_tile_32x32<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
 }
 
 }  // namespace gbt

@@ -83,12 +83,16 @@ int gemm_bt_version(void);
  * pointers that would be passed (e.g. 256 for fresh allocations).
  */
 typedef struct {
-    int kernel;       /* 0 = none (empty), 1 = zero fill (K == 0), 2 = LDS-tiled MFMA, 3 = skinny streaming */
+    int kernel;       /* 0 = none (empty), 1 = zero fill (K == 0), 2 = LDS-tiled MFMA with register-staged
+                         loads (rows not 16-byte aligned), 3 = skinny streaming (M <= 16), 4 = LDS-tiled
+                         MFMA with direct global->LDS loads (16-byte aligned rows) */
+    int variant;      /* tile-shape variant index within the kernel family */
     int bm, bn, bk;   /* workgroup tile (rows of C, columns of C, K step) */
     int threads;      /* threads per workgroup */
     int vec;          /* elements per global load: 8 (16 bytes), 2 or 1 */
     int group_m;      /* tile-rows per group in the grouped tile order */
     int ksplit;       /* waves that split K inside a workgroup (skinny kernel) */
+    int stages;       /* LDS pipeline depth (tiled kernels) */
     int lds_bytes;    /* LDS per workgroup */
     int64_t tiles_m, tiles_n;
     int64_t grid;     /* workgroups launched */

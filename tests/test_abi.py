@@ -64,15 +64,16 @@ def test_no_device_status_without_gpu():
 
 def test_plan_choices():
     p = gb.gemm_bt_plan(4096, 4096, 4096, gb.BF16, gb.BF16)
-    assert (p.kernel, p.bm, p.bn, p.bk, p.vec, p.grid) == (2, 256, 256, 64, 8, 256)
+    assert (p.kernel, p.bm, p.bn, p.vec, p.grid) == (4, 256, 256, 8, 256)
+    assert p.lds_bytes == p.stages * (p.bm + p.bn) * p.bk * 2 <= 160 * 1024
     p = gb.gemm_bt_plan(1024, 4096, 4096, gb.F16, gb.F16)
-    assert (p.kernel, p.bm, p.bn, p.grid) == (2, 128, 128, 256)
+    assert (p.kernel, p.bm, p.bn, p.grid) == (4, 128, 128, 256)
     p = gb.gemm_bt_plan(1000, 3000, 2050, gb.BF16, gb.F32)
     assert (p.kernel, p.bm, p.bn, p.vec, p.tiles_m, p.tiles_n) == (2, 128, 128, 2, 8, 24)
     p = gb.gemm_bt_plan(16, 8192, 8192, gb.BF16, gb.BF16)
     assert (p.kernel, p.bm, p.bn, p.ksplit, p.grid) == (3, 16, 32, 4, 256)
     p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)
-    assert (p.kernel, p.bm, p.grid) == (2, 128, 16)
+    assert (p.kernel, p.bm, p.grid) == (4, 128, 16)
     assert gb.gemm_bt_plan(7, 9, 0, gb.BF16, gb.F32).kernel == 1   # K == 0: zero fill
     assert gb.gemm_bt_plan(0, 9, 5, gb.BF16, gb.F32).kernel == 0   # empty
     # alignment decides the load width
