@@ -38,6 +38,12 @@ namespace gbt {
 // 16-byte-chunk swizzle for tile rows of CPR chunks.  SWZ 0 disables it (for
 // measuring bank conflicts); SWZ 1 and 2 XOR 3 (CPR 8) or 2 (CPR 4) row bits
 // into the chunk index, starting at row bit 0/1 (CPR 8) or 1/2 (CPR 4).
+// gfx950's LDS has 64 four-byte banks (256 bytes per cycle): a ds_read_b128
+// is served 16 lanes at a time, so the 16 lanes of one MFMA operand read
+// (16 rows, same logical chunk) must hit 16 different 16-byte bank groups.
+// With 128-byte rows, row r starts at bank group 8*(r%2); XORing bits 1..3
+// of r into the chunk (SWZ 2) spreads rows r..r+15 over all 16 groups, while
+// bits 0..2 (SWZ 1, the form that suits 32 banks) leaves 2-way conflicts.
 template <int CPR, int SWZ>
 __device__ inline int swz_row(int row) {
     if constexpr (SWZ == 0) return 0;
@@ -166,20 +172,33 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // Operand fragments are double-buffered in registers: the LDS reads for
+    // k-substep ks+1 are issued before the MFMAs of substep ks, so their
+    // latency hides behind 8 MFMAs instead of stalling the wave.
+    auto read_frags = [&](const unsigned char* s, int ks, u32x4 (&fb)[FN], u32x4 (&fa)[FM]) {
+        const int ch = ((2 * ks + fhi) ^ fsw) * 16;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) fb[i] = *(const u32x4*)(s + b_base + 32 * ROWB * i + ch);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) fa[j] = *(const u32x4*)(s + a_base + 32 * ROWB * j + ch);
+    };
+    auto mma = [&](const u32x4 (&fb)[FN], const u32x4 (&fa)[FM]) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = Mfma<IN>::m32x32x16(fb[i], fa[j], acc[i][j]);
+    };
     auto compute = [&](int stage) {
         const unsigned char* s = lds + stage * STAGE_BYTES;
+        constexpr int KS = BK / 16;
+        u32x4 fb0[FN], fa0[FM], fb1[FN], fa1[FM];
+        read_frags(s, 0, fb0, fa0);
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = ((2 * ks + fhi) ^ fsw) * 16;
-            u32x4 fb[FN], fa[FM];
-#pragma unroll
-            for (int i = 0; i < FN; ++i) fb[i] = *(const u32x4*)(s + b_base + 32 * ROWB * i + ch);
-#pragma unroll
-            for (int j = 0; j < FM; ++j) fa[j] = *(const u32x4*)(s + a_base + 32 * ROWB * j + ch);
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] = Mfma<IN>::m32x32x16(fb[i], fa[j], acc[i][j]);
+        for (int ks = 0; ks < KS; ks += 2) {
+            read_frags(s, ks + 1, fb1, fa1);
+            mma(fb0, fa0);
+            if (ks + 2 < KS) read_frags(s, ks + 2, fb0, fa0);
+            mma(fb1, fa1);
         }
     };
 

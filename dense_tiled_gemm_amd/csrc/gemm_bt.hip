@@ -32,7 +32,7 @@ struct TileCfg {
 constexpr TileCfg kCfgL = {256, 256, 2, 4};
 constexpr TileCfg kCfgM = {128, 128, 2, 2};
 constexpr int kSkinnyNB = 2, kSkinnyKS = 4;
-constexpr int kSwz = 1;
+constexpr int kSwz = 2;
 constexpr int kGroupM = 4;
 
 // DMA-kernel variants: [in: bf16, f16][out: f32, bf16, f16] entry points.
@@ -64,17 +64,15 @@ static DmaVariant dma_variant(const char* name, bool all_dtypes) {
 // bf16->bf16 and f16->f16 combinations only.
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
-        dma_variant<256, 256, 64, 2, 2, 4, 1>("L64S2", true),
-        dma_variant<128, 128, 64, 4, 2, 2, 1>("M64S4", true),
-        dma_variant<256, 256, 32, 4, 2, 4, 1>("L32S4", false),
-        dma_variant<256, 256, 32, 3, 2, 4, 1>("L32S3", false),
-        dma_variant<256, 256, 64, 2, 2, 2, 1>("L64S2W4", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2", true),
+        dma_variant<128, 128, 64, 4, 2, 2, 2>("M64S4", true),
+        dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4", false),
         dma_variant<256, 256, 64, 2, 2, 4, 0>("L64S2X0", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2X2", false),
-        dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4X2", false),
-        dma_variant<128, 128, 64, 2, 2, 2, 1>("M64S2", false),
-        dma_variant<128, 128, 32, 4, 2, 2, 1>("M32S4", false),
-        dma_variant<128, 256, 64, 3, 2, 4, 1>("T64S3", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 1>("L64S2X1", false),
+        dma_variant<128, 128, 64, 2, 2, 2, 2>("M64S2", false),
+        dma_variant<128, 128, 32, 4, 2, 2, 2>("M32S4", false),
+        dma_variant<128, 256, 64, 3, 2, 4, 2>("T64S3", false),
+        dma_variant<128, 128, 64, 4, 2, 2, 1>("M64S4X1", false),
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
