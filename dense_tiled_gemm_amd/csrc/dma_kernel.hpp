@@ -66,15 +66,41 @@ __device__ inline void barrier_no_fence() {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource as four SGPRs for inline assembly (same fields as
+// make_rsrc: base address, stride 0, num_records bytes, word 3).
+__device__ inline i32x4 rsrc_words(const void* base, u32 bytes) {
+    const uint64_t p = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int)(u32)p;
+    r[1] = (int)((u32)(p >> 32) & 0xFFFFu);
+    r[2] = (int)bytes;
+    r[3] = kRsrcWord3;
+    return r;
+}
 
 // One 16-byte-per-lane global->LDS transfer: lane L's 16 bytes from buffer
-// offset voff + soff land at LDS address dst + 16 L (dst is wave-uniform and
-// goes to M0).  Kept out of the kernel's lambdas: this compiler drops the
-// host-side launch stub of a kernel template whose lambda calls the builtin
-// directly.
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* dst, u32 voff, u32 soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+// offset voff + soff land at LDS byte address m0 + 16 L, where m0 = `dst`
+// (wave-uniform).  Written as inline assembly on purpose: the instruction
+// then stays invisible to the compiler's wait-count insertion, which would
+// otherwise treat every in-flight transfer as aliasing the ds_reads of the
+// stage being computed and drain the whole ring (s_waitcnt vmcnt(0)) before
+// them.  The kernels order these transfers with explicit s_waitcnt vmcnt(N)
+// and barriers instead.  The s_nop covers the M0-write -> LDS-DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved: the clobber documents the write
+__device__ inline void dma16(const i32x4& r, unsigned char* dst, u32 voff, u32 soff) {
+    const u32 m0 = (u32)(uintptr_t)(lds_ptr_t)dst;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+        : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ>
 __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
@@ -108,8 +134,8 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
     const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (u32)rows_a * (u32)K * 2u);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (u32)rows_b * (u32)K * 2u);
+    const i32x4 ra = rsrc_words(A + (size_t)m0 * K, (u32)rows_a * (u32)K * 2u);
+    const i32x4 rb = rsrc_words(B + (size_t)n0 * K, (u32)rows_b * (u32)K * 2u);
     const u32 row_bytes = (u32)K * 2u;
 
     // Loader geometry.  Wave instruction i of this wave fills row block

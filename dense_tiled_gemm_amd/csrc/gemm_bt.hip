@@ -8,6 +8,7 @@
 
 #include "common.hpp"
 #include "dma_kernel.hpp"
+#include "skinny_dma.hpp"
 #include "skinny_kernel.hpp"
 #include "tiled_kernel.hpp"
 
@@ -25,13 +26,17 @@ enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3, KIND_
 // are not 16-byte aligned use the register-staged kernel with narrower loads.
 //   staged L: 256 x 256, 8 waves as 2 x 4 (each wave 128 x 64), BK 64, 2 stages.
 //   staged M: 128 x 128, 4 waves as 2 x 2 (each wave 64 x 64), BK 64, 2 stages.
-// The skinny kernel: 32 rows of B per workgroup (NB = 2), K split over 4 waves.
+// Skinny (M <= 16): aligned rows use skinny_dma_kernel (32 rows of B per
+// workgroup, 256-element K stages in a 6-deep LDS ring, 4 waves); other
+// alignments use the register-streaming skinny_kernel (32 rows, K split over
+// 4 waves).
 struct TileCfg {
     int bm, bn, wm, wn;
 };
 constexpr TileCfg kCfgL = {256, 256, 2, 4};
 constexpr TileCfg kCfgM = {128, 128, 2, 2};
 constexpr int kSkinnyNB = 2, kSkinnyKS = 4;
+constexpr int kSdBN = 32, kSdKB = 256, kSdStages = 6, kSdWaves = 4;
 constexpr int kSwz = 2;
 constexpr int kGroupM = 4;
 
@@ -129,12 +134,24 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
     if (M <= 16) {
         p->kernel = KIND_SKINNY;
         p->bm = 16;
-        p->bn = 16 * kSkinnyNB;
-        p->bk = 32;
-        p->ksplit = kSkinnyKS;
-        p->threads = 64 * kSkinnyKS;
-        p->lds_bytes = kSkinnyKS * kSkinnyNB * 64 * 16;
         p->tiles_m = 1;
+        if (p->vec == 8) {
+            p->variant = 1;
+            p->bn = kSdBN;
+            p->bk = kSdKB;
+            p->stages = kSdStages;
+            p->ksplit = kSdWaves;
+            p->threads = 64 * kSdWaves;
+            p->lds_bytes = kSdStages * (16 + kSdBN) * kSdKB * 2 + kSdWaves * (kSdBN / 16) * 64 * 16;
+        } else {
+            p->variant = 0;
+            p->bn = 16 * kSkinnyNB;
+            p->bk = 32;
+            p->stages = 2;
+            p->ksplit = kSkinnyKS;
+            p->threads = 64 * kSkinnyKS;
+            p->lds_bytes = kSkinnyKS * kSkinnyNB * 64 * 16;
+        }
         p->tiles_n = (N + p->bn - 1) / p->bn;
         p->grid = p->tiles_n;
         return GEMM_BT_OK;
@@ -203,7 +220,7 @@ static const void* tiled_fn_out(int out, int cfg, int vec) {
 
 template <int IN, int OUT>
 static const void* skinny_fn_vec(int vec) {
-    if (vec == 8) return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 8>;
+    if (vec == 8) return (const void*)&skinny_dma_kernel<IN, OUT, kSdBN, kSdKB, kSdStages, kSdWaves>;
     if (vec == 2) return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 2>;
     return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 1>;
 }
