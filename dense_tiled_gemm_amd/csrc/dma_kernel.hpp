@@ -90,15 +90,28 @@ __device__ inline i32x4 rsrc_words(const void* base, u32 bytes) {
 // and barriers instead.  The s_nop covers the M0-write -> LDS-DMA hazard.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved: the clobber documents the write
+// NT = true marks the load non-temporal (streaming data read once: it should
+// not displace reusable lines in L2).
+template <bool NT = false>
 __device__ inline void dma16(const i32x4& r, unsigned char* dst, u32 voff, u32 soff) {
     const u32 m0 = (u32)(uintptr_t)(lds_ptr_t)dst;
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
-        :
-        : "s"(m0), "v"(voff), "s"(r), "s"(soff)
-        : "memory", "m0");
+    if constexpr (NT) {
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen nt lds"
+            :
+            : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+            : "memory", "m0");
+    } else {
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen lds"
+            :
+            : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+            : "memory", "m0");
+    }
 }
 #pragma clang diagnostic pop
 

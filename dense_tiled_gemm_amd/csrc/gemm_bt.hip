@@ -36,7 +36,6 @@ struct TileCfg {
 constexpr TileCfg kCfgL = {256, 256, 2, 4};
 constexpr TileCfg kCfgM = {128, 128, 2, 2};
 constexpr int kSkinnyNB = 2, kSkinnyKS = 4;
-constexpr int kSdBN = 32, kSdKB = 256, kSdStages = 6, kSdWaves = 4;
 constexpr int kSwz = 2;
 constexpr int kGroupM = 4;
 
@@ -80,6 +79,57 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<128, 128, 64, 4, 2, 2, 1>("M64S4X1", false),
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
+    return v;
+}
+
+// Skinny DMA-kernel variants [in][out]; index 0 is the default.
+struct SkinnyVariant {
+    const char* name;
+    int bn, kb, stages, waves;
+    const void* fn[2][3];
+};
+
+template <int BN, int KB, int S, int W>
+static SkinnyVariant skinny_variant(const char* name, bool all_dtypes) {
+    SkinnyVariant v = {name, BN, KB, S, W, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
+    v.fn[0][1] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BN, KB, S, W>;
+    v.fn[1][2] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BN, KB, S, W>;
+    if (all_dtypes) {
+        v.fn[0][0] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BN, KB, S, W>;
+        v.fn[0][2] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BN, KB, S, W>;
+        v.fn[1][0] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BN, KB, S, W>;
+        v.fn[1][1] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BN, KB, S, W>;
+    }
+    return v;
+}
+
+static const SkinnyVariant* skinny_variants(int* count) {
+    static const SkinnyVariant v[] = {
+        skinny_variant<16, 256, 4, 4>("S16K256x4", true),
+        skinny_variant<8, 256, 4, 4>("S8K256x4", false),
+        skinny_variant<8, 256, 6, 4>("S8K256x6", false),
+        skinny_variant<8, 512, 4, 4>("S8K512x4", false),
+        skinny_variant<16, 256, 6, 4>("S16K256x6", false),
+        skinny_variant<32, 256, 6, 4>("S32K256x6", false),
+        skinny_variant<16, 128, 8, 4>("S16K128x8", false),
+    };
+    *count = (int)(sizeof(v) / sizeof(v[0]));
+    return v;
+}
+
+static int forced_skinny() {
+    // Benchmarking aid: GEMM_BT_FORCE_SKINNY=<variant name>.
+    static std::atomic<int> cached{-2};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = -1;
+        const char* e = std::getenv("GEMM_BT_FORCE_SKINNY");
+        int n = 0;
+        const SkinnyVariant* vs = skinny_variants(&n);
+        for (int i = 0; e && i < n; ++i)
+            if (std::strcmp(e, vs[i].name) == 0) v = i;
+        cached.store(v, std::memory_order_relaxed);
+    }
     return v;
 }
 
@@ -136,13 +186,20 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         p->bm = 16;
         p->tiles_m = 1;
         if (p->vec == 8) {
-            p->variant = 1;
-            p->bn = kSdBN;
-            p->bk = kSdKB;
-            p->stages = kSdStages;
-            p->ksplit = kSdWaves;
-            p->threads = 64 * kSdWaves;
-            p->lds_bytes = kSdStages * (16 + kSdBN) * kSdKB * 2 + kSdWaves * (kSdBN / 16) * 64 * 16;
+            int n = 0;
+            const SkinnyVariant* vs = skinny_variants(&n);
+            int use = 0;
+            const int f = forced_skinny();
+            if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
+            const SkinnyVariant& v = vs[use];
+            p->variant = 1 + use;
+            p->bn = v.bn;
+            p->bk = v.kb;
+            p->stages = v.stages;
+            p->ksplit = v.waves;
+            p->threads = 64 * v.waves;
+            const int bnp = v.bn < 16 ? 16 : v.bn;
+            p->lds_bytes = v.stages * (16 + bnp) * v.kb * 2 + v.waves * (bnp / 16) * 64 * 16;
         } else {
             p->variant = 0;
             p->bn = 16 * kSkinnyNB;
@@ -220,7 +277,6 @@ static const void* tiled_fn_out(int out, int cfg, int vec) {
 
 template <int IN, int OUT>
 static const void* skinny_fn_vec(int vec) {
-    if (vec == 8) return (const void*)&skinny_dma_kernel<IN, OUT, kSdBN, kSdKB, kSdStages, kSdWaves>;
     if (vec == 2) return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 2>;
     return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 1>;
 }
@@ -349,8 +405,14 @@ int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
             void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store};
             e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
         } else {
-            const void* fn = in_dtype == GEMM_BT_BF16 ? skinny_fn_out<GEMM_BT_BF16>(out_dtype, p.vec)
-                                                      : skinny_fn_out<GEMM_BT_F16>(out_dtype, p.vec);
+            const void* fn;
+            if (p.variant >= 1) {
+                int n = 0;
+                fn = skinny_variants(&n)[p.variant - 1].fn[in_index(in_dtype)][out_index(out_dtype)];
+            } else {
+                fn = in_dtype == GEMM_BT_BF16 ? skinny_fn_out<GEMM_BT_BF16>(out_dtype, p.vec)
+                                              : skinny_fn_out<GEMM_BT_F16>(out_dtype, p.vec);
+            }
             void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &vec_store};
             e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
         }

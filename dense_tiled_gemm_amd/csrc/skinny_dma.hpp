@@ -10,7 +10,10 @@
 //   * each workgroup owns BN rows of B and the whole K range; B and the 16
 //     rows of A stream through an STAGES-deep LDS ring, KB elements of K per
 //     stage, with buffer_load_dwordx4 ... lds (no register staging), so about
-//     (STAGES-1) * (16 + BN) * KB * 2 bytes per workgroup are in flight;
+//     (STAGES-1) * (16 + BN) * KB * 2 bytes per workgroup are in flight.  HBM
+//     streams B fastest when each workgroup walks few rows at a time, so BN
+//     may be 8: the MFMA's first operand then has 8 padding rows whose
+//     outputs are never stored (the matrix cores have ample slack here);
 //   * rows are 2*KB bytes long in LDS; the 16-byte chunk index is XORed with
 //     the low 4 row bits so the 16 rows read by one MFMA operand load fall
 //     in 16 different bank groups of the 64-bank LDS (the same swizzle idea as
@@ -39,20 +42,23 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
     constexpr int CPR = KB / 8;            // 16-byte chunks per row per stage
     constexpr int ROWB = KB * 2;           // bytes per row per stage
     constexpr int RPI = 1024 / ROWB;       // rows per wave load instruction
+    constexpr int BNP = BN < 16 ? 16 : BN;  // B rows held in LDS (BN loaded, the rest padding)
     constexpr int A_LOADS = AR / RPI, B_LOADS = BN / RPI;
     constexpr int LOADS = (A_LOADS + B_LOADS) / W;  // per wave per stage
-    constexpr int STAGE_BYTES = (AR + BN) * ROWB;
+    constexpr int STAGE_BYTES = (AR + BNP) * ROWB;
     constexpr int KBLK = KB / 32;          // MFMA k-blocks per stage
     constexpr int KPW = KBLK / W;          // k-blocks per wave per stage
-    constexpr int NBLK = BN / 16;
+    constexpr int NBLK = BNP / 16;
     constexpr int PEND = (STAGES - 2) * LOADS;
     constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
     static_assert(RPI >= 1 && ROWB * RPI == 1024, "stage rows must tile 1 KiB loads");
+    static_assert(BN % RPI == 0 && (BN % 16 == 0 || BN < 16), "B rows per workgroup");
     static_assert((A_LOADS + B_LOADS) % W == 0, "loads split evenly over waves");
     static_assert(KBLK % W == 0, "k-blocks split evenly over waves");
     static_assert(CPR >= 16, "swizzle needs 16 chunks per row");
     static_assert(PEND < 64, "vmcnt range");
     static_assert(STAGES * STAGE_BYTES + W * NBLK * 64 * 16 <= 160 * 1024, "LDS budget");
+    static_assert(LOADS * W == A_LOADS + B_LOADS, "loads split evenly");
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * STAGE_BYTES];
     __shared__ f32x4 red[W][NBLK][64];
@@ -93,8 +99,10 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
             const int j = wave + i * W;
             const u32 o = kc[i] < kleft ? off[i] : kOutOfRange;
             // whether load i reads A or B is fixed per (wave, i) and uniform
-            if (is_a[i]) dma16(ra, sbase + j * 1024, o, kbytes);
-            else dma16(rb, sbase + j * 1024, o, kbytes);
+            // B is read exactly once: non-temporal; A is re-read by every
+            // workgroup and should stay in L2
+            if (is_a[i]) dma16<false>(ra, sbase + j * 1024, o, kbytes);
+            else dma16<true>(rb, sbase + j * 1024, o, kbytes);
         }
     };
 
@@ -146,9 +154,11 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
         f32x4 sum = red[0][b][lane];
 #pragma unroll
         for (int w = 1; w < W; ++w) sum += red[w][b][lane];
-        const int n = n0 + 16 * b + 4 * q;
+        const int nl = 16 * b + 4 * q;  // padding rows (nl >= BN) are not stored
+        const int n = n0 + nl;
         const u32 o = ((u32)m * (u32)N + (u32)n) * OSZ;
         const float v0 = sum[0], v1 = sum[1], v2 = sum[2], v3 = sum[3];
+        if (nl >= BN) continue;
         if (vec_store) {
             if (n < N) {
                 if constexpr (OUT == GEMM_BT_F32) {
