@@ -113,9 +113,35 @@ __device__ inline void dma16(const i32x4& r, unsigned char* dst, u32 voff, u32 s
             : "memory", "m0");
     }
 }
+// 4 bytes per lane into LDS at m0 + 4 L: used only to pull cache lines into
+// L2 ahead of the 16-byte loads that will need them (the LDS bytes are not
+// read).
+__device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, u32 soff) {
+    const u32 m0 = (u32)(uintptr_t)(lds_ptr_t)dst;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, %3 offen lds"
+        :
+        : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+        : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
-template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ>
+// SCHED 0: every wave loads fragments and multiplies in the same K step
+//          (fragment reads double-buffered in registers);
+// SCHED 1: ping-pong.  The two wave rows (wm = 0, 1) are offset by one
+//          barrier: waves w and w+4 share a SIMD, so on every SIMD one wave
+//          issues its whole K step of MFMAs from registers while the other
+//          reads its next fragments from LDS (and the wm = 0 group issues the
+//          next tile's global->LDS loads); the roles swap at each barrier.
+//
+// PF > 0 (SCHED 0 only): L2 prefetch.  With each refill the waves also touch
+// the 128-byte lines of tile kt + STAGES - 1 + PF (one line per tile row when
+// BK = 64) with 4-byte LDS-DMA loads into a scratch corner of LDS, so that the
+// refill PF steps later finds its lines in L2 instead of paying the full
+// HBM / Infinity-Cache latency with only STAGES - 1 steps of cover.
+template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0>
 __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                           void* __restrict__ C, int M, int N, int K,
                                                           int tiles_m, int tiles_n, int group_m,
@@ -129,15 +155,17 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int STAGE_BYTES = (BM + BN) * ROWB;
-    constexpr int PEND = (STAGES - 2) * (LA + LB);
+    constexpr int PFI = PF > 0 ? (BM + BN) / (64 * W) : 0;  // prefetch instructions per wave per step
+    constexpr int PEND = (STAGES - 2) * (LA + LB + PFI) + PFI;
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert(LA * RPI * W == BM && LB * RPI * W == BN, "tile rows must split evenly over waves");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(PEND < 64, "vmcnt range");
-    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(PF == 0 || (BK == 64 && (BM + BN) % (64 * W) == 0 && SCHED == 0), "prefetch layout");
+    static_assert(STAGES * STAGE_BYTES + (PF > 0 ? W * 256 : 0) <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * STAGE_BYTES + (PF > 0 ? W * 256 : 0)];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -195,6 +223,25 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         }
     };
 
+    // L2 prefetch: lane l of instruction p of this wave touches tile row
+    // (wave * PFI + p) * 64 + l (A rows first, then B rows), first line of the
+    // tile's 128-byte K segment.
+    auto prefetch = [&](int kt) {
+        if constexpr (PF > 0) {
+            unsigned char* pbase = lds + STAGES * STAGE_BYTES + wave * 256;
+            const u32 kbytes = (u32)kt * (u32)ROWB;
+            const bool live = kt * BK < K;
+#pragma unroll
+            for (int p = 0; p < PFI; ++p) {
+                const int row = (wave * PFI + p) * 64 + lane;
+                if (row < BM)
+                    dma4_touch(ra, pbase, live ? (u32)row * row_bytes : kOutOfRange, kbytes);
+                else
+                    dma4_touch(rb, pbase, live ? (u32)(row - BM) * row_bytes : kOutOfRange, kbytes);
+            }
+        }
+    };
+
     // Operand reads: row (lane % 32) of each 32-row block, logical chunk
     // 2*ks + lane/32 for k-substep ks; block bases are multiples of 32, so the
     // swizzle term depends on the lane only.
@@ -242,17 +289,91 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     };
 
     const int nk = (K + BK - 1) / BK;
+    if constexpr (SCHED == 1) {
+        static_assert(W == 8 && WM == 2, "ping-pong pairs the two wave rows");
+        constexpr int KS = BK / 16;
+        constexpr int L2 = 2 * (LA + LB);  // loads of one whole tile, issued by one wm = 0 wave
+        const int grp = wm;  // waves 0..3 and 4..7; wave w and w + 4 share a SIMD
+        // The wm = 0 group issues every load of a tile (block rows `wave` and
+        // `wave + 4`); the wm = 1 group never loads from global memory.
+        auto issue_g0 = [&](int stage, int kt) {
+            unsigned char* sbase = lds + stage * STAGE_BYTES;
+            const u32 kbytes = (u32)kt * (u32)ROWB;
+            const int kleft = K - kt * BK;
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
+            for (int h = 0; h < 2; ++h) {
+                const int blk = wave + 4 * h;
+#pragma unroll
+                for (int i = 0; i < LA; ++i) {
+                    const int row = (blk + i * W) * RPI + lrow;
+                    const int c = lphys ^ swz_row<CPR, SWZ>(row);
+                    const u32 o = (u32)row * row_bytes + (u32)c * 16u;
+                    dma16(ra, sbase + (blk + i * W) * 1024, c * 8 < kleft ? o : kOutOfRange, kbytes);
+                }
+#pragma unroll
+                for (int i = 0; i < LB; ++i) {
+                    const int row = (blk + i * W) * RPI + lrow;
+                    const int c = lphys ^ swz_row<CPR, SWZ>(row);
+                    const u32 o = (u32)row * row_bytes + (u32)c * 16u;
+                    dma16(rb, sbase + BM * ROWB + (blk + i * W) * 1024, c * 8 < kleft ? o : kOutOfRange, kbytes);
+                }
+            }
+        };
+        // Tile t lives in stage t % STAGES.  Barriers alternate between the
+        // groups' phases: between barriers 2t+1 and 2t+2 the wm = 0 group
+        // reads tile t while the wm = 1 group multiplies tile t-1; between
+        // 2t+2 and 2t+3 the roles swap.  The refill of stage (t-1) % STAGES
+        // with tile t + STAGES - 1 is issued by wm = 0 right after barrier
+        // 2t+1, when both groups are done reading tile t-1; wm = 0 waits for
+        // tile t+1 (allowing STAGES-2 younger tiles in flight) before barrier
+        // 2t+3, after which it reads tile t+1.
+        u32x4 fb[KS][FN], fa[KS][FM];
+        if (grp == 0) {
+#pragma unroll
+            for (int t = 0; t < STAGES - 1; ++t) issue_g0(t, t);
+            wait_vmcnt<(STAGES - 2) * L2>();
+        }
+        barrier_no_fence();
+        if (grp == 1) barrier_no_fence();
+        int cs = 0;              // stage of tile kt
+        int ls = STAGES - 1;     // stage refilled during tile kt's read phase
+        for (int kt = 0; kt < nk; ++kt) {
+            // memory phase: this group's fragments of tile kt (+ a refill)
+            const unsigned char* sc = lds + cs * STAGE_BYTES;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) read_frags(sc, ks, fb[ks], fa[ks]);
+            if (grp == 0) issue_g0(ls, kt + STAGES - 1);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading stage cs
+            barrier_no_fence();
+            // compute phase: the whole K step from registers
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) mma(fb[ks], fa[ks]);
+            if (grp == 0) wait_vmcnt<(STAGES - 2) * L2>();  // tile kt + 1 has landed
+            barrier_no_fence();
+            cs = cs + 1 == STAGES ? 0 : cs + 1;
+            ls = ls + 1 == STAGES ? 0 : ls + 1;
+        }
+        if (grp == 0) barrier_no_fence();
+    } else {
+    // Every step issues the same pair, (refill of tile t, prefetch of tile
+    // t + PF), prologue included, so the loads younger than tile kt's are
+    // always PEND instructions.
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+        issue(s, s);
+        prefetch(s + PF);
+    }
     int cs = 0;               // stage holding tile kt
     int ls = STAGES - 1;      // stage receiving tile kt + STAGES - 1
     for (int kt = 0; kt < nk; ++kt) {
         wait_vmcnt<PEND>();
         barrier_no_fence();
         issue(ls, kt + STAGES - 1);
+        prefetch(kt + STAGES - 1 + PF);
         compute(cs);
         cs = cs + 1 == STAGES ? 0 : cs + 1;
         ls = ls + 1 == STAGES ? 0 : ls + 1;
+    }
     }
     wait_vmcnt<0>();  // the ring's last (out-of-range) loads still write LDS
 

@@ -49,16 +49,16 @@ struct DmaVariant {
 static int in_index(int in_dtype) { return in_dtype == GEMM_BT_BF16 ? 0 : 1; }
 static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out_dtype == GEMM_BT_BF16 ? 1 : 2); }
 
-template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ>
+template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0>
 static DmaVariant dma_variant(const char* name, bool all_dtypes) {
     DmaVariant v = {name, BM, BN, BK, S, WM, WN, SWZ, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
-    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ>;
-    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ>;
+    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
+    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
     if (all_dtypes) {
-        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ>;
-        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ>;
-        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ>;
-        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ>;
+        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
+        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
+        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
+        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
     }
     return v;
 }
@@ -77,6 +77,15 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<128, 128, 32, 4, 2, 2, 2>("M32S4", false),
         dma_variant<128, 256, 64, 3, 2, 4, 2>("T64S3", false),
         dma_variant<128, 128, 64, 4, 2, 2, 1>("M64S4X1", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP", true),
+        dma_variant<256, 256, 32, 4, 2, 4, 2, 1>("L32PPS4", false),
+        dma_variant<256, 256, 32, 3, 2, 4, 2, 1>("L32PPS3", false),
+        dma_variant<128, 256, 64, 2, 2, 4, 2, 1>("T64PP", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 1>("L64P1", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 2>("L64P2", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 3>("L64P3", false),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 0, 1>("M64S4P1", false),
+        dma_variant<128, 128, 64, 2, 2, 2, 2, 0, 2>("M64S2P2", false),
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
