@@ -9,7 +9,9 @@ Prints ONE JSON line on stdout:
   cpu_baseline the CPU oracle timed on a bounded sample of the same product
   secondary    µs of the 1024×4096×4096 f16 workload and GB/s of the
                16×8192×8192 skinny workload (same timing method)
-Diagnostics go to stderr.
+Diagnostics go to stderr.  The default 400 untimed warm-up launches matter:
+from idle, an MI355X needs about 25 ms of sustained GEMM launches before its
+clocks settle, and launches inside that ramp run up to 15% slower.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
   python bench.py --mode copy     # plain device copy of known size (counter calibration)
@@ -165,8 +167,8 @@ def copy_mode(torch, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="sq4096_bf16_bf16")
     ap.add_argument("--rotate", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")

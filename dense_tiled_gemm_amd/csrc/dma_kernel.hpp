@@ -130,6 +130,10 @@ __device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, 
 
 // SCHED 0: every wave loads fragments and multiplies in the same K step
 //          (fragment reads double-buffered in registers);
+// SCHED 2: early barrier (the default): as SCHED 0, but the barrier of a K
+//          step sits before the MFMAs of the tile's last k-substep, which then
+//          cover the first LDS reads of the next tile and the refill loads
+//          (see the SCHED == 2 branch);
 // SCHED 1: ping-pong.  The two wave rows (wm = 0, 1) are offset by one
 //          barrier: waves w and w+4 share a SIMD, so on every SIMD one wave
 //          issues its whole K step of MFMAs from registers while the other
@@ -289,7 +293,79 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     };
 
     const int nk = (K + BK - 1) / BK;
-    if constexpr (SCHED == 1) {
+    if constexpr (SCHED == 2) {
+        // Early barrier: each wave reads the fragments of a tile's last
+        // k-substep, then waits for the next tile and joins the barrier
+        // before issuing that substep's MFMAs.  After the barrier the
+        // MFMAs of the last substep run from registers while the first
+        // fragments of the next tile come out of LDS, and the refill of the
+        // freed stage is interleaved with them, one or two global->LDS
+        // loads after each MFMA: the load queue then fills while the matrix
+        // core is busy instead of stalling the wave in one burst.  The
+        // sched_barrier pins keep the compiler from regrouping the LDS
+        // reads, loads and MFMAs.
+        constexpr int KS = BK / 16;
+        constexpr int L = LA + LB;
+        constexpr int NMMA = FN * FM;
+        static_assert(KS % 2 == 0 && PF == 0, "fragment buffers alternate per substep");
+        u32x4 fb[2][FN], fa[2][FM];
+        auto mma_all = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM]) {
+#pragma unroll
+            for (int t = 0; t < NMMA; ++t)
+                acc[t / FM][t % FM] = Mfma<IN>::m32x32x16(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
+        };
+        // load d of this wave's share of tile kt into stage `stage` (A rows
+        // first), k >= K masked as in issue()
+        auto load_one = [&](int stage, int kt, int d) {
+            unsigned char* sbase = lds + stage * STAGE_BYTES;
+            const u32 kbytes = (u32)kt * (u32)ROWB;
+            const int kleft = K - kt * BK;
+            if (d < LA)
+                dma16(ra, sbase + (wave + d * W) * 1024, a_kc[d] < kleft ? a_off[d] : kOutOfRange, kbytes);
+            else
+                dma16(rb, sbase + BM * ROWB + (wave + (d - LA) * W) * 1024,
+                      b_kc[d - LA] < kleft ? b_off[d - LA] : kOutOfRange, kbytes);
+        };
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
+        wait_vmcnt<(STAGES - 2) * L>();
+        barrier_no_fence();
+        issue(STAGES - 1, STAGES - 1);
+        read_frags(lds, 0, fb[0], fa[0]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // both ways into the loop carry no pending LDS reads
+        int cs = 0;  // stage holding tile kt; tiles up to kt + STAGES - 1 are issued
+        for (int kt = 0; kt < nk; ++kt) {
+            const unsigned char* s = lds + cs * STAGE_BYTES;
+            const int ns = cs + 1 == STAGES ? 0 : cs + 1;
+#pragma unroll
+            for (int ks = 0; ks < KS - 1; ++ks) {
+                read_frags(s, ks + 1, fb[(ks + 1) & 1], fa[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_all(fb[ks & 1], fa[ks & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_vmcnt<(STAGES - 2) * L>();       // this wave's part of tile kt + 1 has landed
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading stage cs
+            barrier_no_fence();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(lds + ns * STAGE_BYTES, 0, fb[0], fa[0]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < NMMA; ++t) {
+                acc[t / FM][t % FM] = Mfma<IN>::m32x32x16(fb[1][t / FM], fa[1][t % FM], acc[t / FM][t % FM]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int d = 0; d < L; ++d)
+                    if (d * NMMA / L == t) load_one(cs, kt + STAGES, d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the next tile's first fragments arrived behind those MFMAs;
+            // saying so here keeps the next iteration from waiting on the
+            // reads it issues first
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            cs = ns;
+        }
+    } else if constexpr (SCHED == 1) {
         static_assert(W == 8 && WM == 2, "ping-pong pairs the two wave rows");
         constexpr int KS = BK / 16;
         constexpr int L2 = 2 * (LA + LB);  // loads of one whole tile, issued by one wm = 0 wave

@@ -68,24 +68,16 @@ static DmaVariant dma_variant(const char* name, bool all_dtypes) {
 // bf16->bf16 and f16->f16 combinations only.
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
-        dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2", true),
-        dma_variant<128, 128, 64, 4, 2, 2, 2>("M64S4", true),
-        dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E", true),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 2>("M64E4", true),
+        dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2", false),
+        dma_variant<128, 128, 64, 4, 2, 2, 2>("M64S4", false),
         dma_variant<256, 256, 64, 2, 2, 4, 0>("L64S2X0", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 1>("L64S2X1", false),
-        dma_variant<128, 128, 64, 2, 2, 2, 2>("M64S2", false),
-        dma_variant<128, 128, 32, 4, 2, 2, 2>("M32S4", false),
-        dma_variant<128, 256, 64, 3, 2, 4, 2>("T64S3", false),
-        dma_variant<128, 128, 64, 4, 2, 2, 1>("M64S4X1", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP", true),
-        dma_variant<256, 256, 32, 4, 2, 4, 2, 1>("L32PPS4", false),
-        dma_variant<256, 256, 32, 3, 2, 4, 2, 1>("L32PPS3", false),
-        dma_variant<128, 256, 64, 2, 2, 4, 2, 1>("T64PP", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 1>("L64P1", false),
+        dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4", false),
+        dma_variant<256, 256, 32, 4, 2, 4, 2, 2>("L32E4", false),
+        dma_variant<256, 256, 64, 2, 2, 2, 2, 2>("L64EW4", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP", false),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 2>("L64P2", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 3>("L64P3", false),
-        dma_variant<128, 128, 64, 4, 2, 2, 2, 0, 1>("M64S4P1", false),
-        dma_variant<128, 128, 64, 2, 2, 2, 2, 0, 2>("M64S2P2", false),
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
