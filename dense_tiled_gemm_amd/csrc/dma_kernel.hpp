@@ -293,27 +293,26 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     };
 
     const int nk = (K + BK - 1) / BK;
-    if constexpr (SCHED == 2) {
+    if constexpr (SCHED >= 2) {
         // Early barrier: each wave reads the fragments of a tile's last
         // k-substep, then waits for the next tile and joins the barrier
         // before issuing that substep's MFMAs.  After the barrier the
         // MFMAs of the last substep run from registers while the first
-        // fragments of the next tile come out of LDS, and the refill of the
-        // freed stage is interleaved with them, one or two global->LDS
-        // loads after each MFMA: the load queue then fills while the matrix
-        // core is busy instead of stalling the wave in one burst.  The
+        // fragments of the next tile come out of LDS.  The refill of the
+        // freed stage is spread over SPREAD substeps (the last one of this
+        // tile and the first SPREAD - 1 of the next), one or two
+        // global->LDS loads after each MFMA, so the load queues and the L2
+        // see a steady stream instead of one burst per K step.  The
         // sched_barrier pins keep the compiler from regrouping the LDS
         // reads, loads and MFMAs.
         constexpr int KS = BK / 16;
         constexpr int L = LA + LB;
         constexpr int NMMA = FN * FM;
+        constexpr int SPREAD = SCHED == 2 ? 1 : (SCHED == 3 ? 2 : KS);
+        constexpr int CH = L / SPREAD;  // loads per chunk
         static_assert(KS % 2 == 0 && PF == 0, "fragment buffers alternate per substep");
+        static_assert(L % SPREAD == 0 && SPREAD <= KS, "refill chunks");
         u32x4 fb[2][FN], fa[2][FM];
-        auto mma_all = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM]) {
-#pragma unroll
-            for (int t = 0; t < NMMA; ++t)
-                acc[t / FM][t % FM] = Mfma<IN>::m32x32x16(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
-        };
         // load d of this wave's share of tile kt into stage `stage` (A rows
         // first), k >= K masked as in issue()
         auto load_one = [&](int stage, int kt, int d) {
@@ -326,14 +325,29 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
                 dma16(rb, sbase + BM * ROWB + (wave + (d - LA) * W) * 1024,
                       b_kc[d - LA] < kleft ? b_off[d - LA] : kOutOfRange, kbytes);
         };
+        // the NMMA MFMAs of one substep with chunk c of a refill interleaved
+        auto mma_refill = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], int stage, int kt, int c) {
+#pragma unroll
+            for (int t = 0; t < NMMA; ++t) {
+                acc[t / FM][t % FM] = Mfma<IN>::m32x32x16(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int d = 0; d < CH; ++d)
+                    if (c >= 0 && d * NMMA / CH == t) load_one(stage, kt, c * CH + d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
         wait_vmcnt<(STAGES - 2) * L>();
         barrier_no_fence();
-        issue(STAGES - 1, STAGES - 1);
+#pragma unroll
+        for (int d = 0; d < CH; ++d) load_one(STAGES - 1, STAGES - 1, d);  // chunk 0 of tile STAGES - 1
         read_frags(lds, 0, fb[0], fa[0]);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // both ways into the loop carry no pending LDS reads
-        int cs = 0;  // stage holding tile kt; tiles up to kt + STAGES - 1 are issued
+        // stage cs holds tile kt; chunk 0 of tile kt + STAGES - 1 (stage ps)
+        // is issued, its other chunks go out during this tile's substeps
+        int cs = 0, ps = STAGES - 1;
         for (int kt = 0; kt < nk; ++kt) {
             const unsigned char* s = lds + cs * STAGE_BYTES;
             const int ns = cs + 1 == STAGES ? 0 : cs + 1;
@@ -341,8 +355,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             for (int ks = 0; ks < KS - 1; ++ks) {
                 read_frags(s, ks + 1, fb[(ks + 1) & 1], fa[(ks + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);
-                mma_all(fb[ks & 1], fa[ks & 1]);
-                __builtin_amdgcn_sched_barrier(0);
+                mma_refill(fb[ks & 1], fa[ks & 1], ps, kt + STAGES - 1, ks + 1 < SPREAD ? ks + 1 : -1);
             }
             wait_vmcnt<(STAGES - 2) * L>();       // this wave's part of tile kt + 1 has landed
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading stage cs
@@ -350,19 +363,12 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             __builtin_amdgcn_sched_barrier(0);
             read_frags(lds + ns * STAGE_BYTES, 0, fb[0], fa[0]);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int t = 0; t < NMMA; ++t) {
-                acc[t / FM][t % FM] = Mfma<IN>::m32x32x16(fb[1][t / FM], fa[1][t % FM], acc[t / FM][t % FM]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int d = 0; d < L; ++d)
-                    if (d * NMMA / L == t) load_one(cs, kt + STAGES, d);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            mma_refill(fb[1], fa[1], cs, kt + STAGES, 0);  // chunk 0 of the refill of stage cs
             // the next tile's first fragments arrived behind those MFMAs;
             // saying so here keeps the next iteration from waiting on the
             // reads it issues first
             __builtin_amdgcn_s_waitcnt(0xC07F);
+            ps = cs;
             cs = ns;
         }
     } else if constexpr (SCHED == 1) {
