@@ -194,4 +194,69 @@ __device__ inline void store_tile_32x32(const f32x16 (&acc)[FN][FM], void* C, in
     }
 }
 
+// Store the workgroup's BM x BN tile through LDS so that each global store
+// instruction writes whole rows: every wave first parks its accumulator
+// blocks (rounded to OUT) in LDS as a row-major tile, then the NT threads of
+// the workgroup copy rows to C with 16 bytes per lane, so 64 lanes write 1 KiB
+// of consecutive row bytes (full cache lines instead of 16-byte pieces from
+// 32 rows at a time).  The 16-byte chunk c of tile row r sits at physical
+// chunk c ^ (r mod 32) (mod 16 for 16-chunk rows): the column-wise parking
+// writes of 32 rows then spread over the banks, and the row-wise reads stay
+// whole chunks.  A tile larger than LDS_BYTES goes in WM passes of one wave
+// row each.  Requires 16-byte aligned rows of C (N * sizeof(OUT) a multiple of
+// 16 and C 16-byte aligned); rows >= M and columns >= N are not written.  The
+// caller guarantees that no wave still reads or fills `lds`.
+template <int OUT, int FN, int FM, int BM, int BN, int WM, int NT, int LDS_BYTES>
+__device__ inline void store_tile_lds(const f32x16 (&acc)[FN][FM], unsigned char* lds, void* C, int M, int N,
+                                      int m0, int n0, int mw, int nw, int wm, int tid) {
+    constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
+    constexpr int ROWB = BN * OSZ;  // bytes per tile row
+    constexpr int CPR = ROWB / 16;  // 16-byte chunks per tile row
+    constexpr int SWM = (CPR < 32 ? CPR : 32) - 1;
+    constexpr int P = BM * ROWB <= LDS_BYTES ? 1 : WM;
+    constexpr int RP = BM / P;  // tile rows per pass
+    static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "row chunks");
+    static_assert(RP * ROWB <= LDS_BYTES, "a pass must fit in LDS");
+    const size_t c_origin = (size_t)m0 * N + n0;
+    const size_t c_rest = (size_t)M * N - c_origin;
+    const u32 c_bytes = (u32)min(c_rest * OSZ, (size_t)0x7FFFFFFF);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const char*)C + c_origin * OSZ, c_bytes);
+    const int mlim = M - m0, nlim = N - n0;
+    const int lane = tid & 63, fr = lane & 31, fhi = lane >> 5;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        if (P == 1 || wm == p) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const int r = mw + 32 * j + fr - p * RP;  // tile row within the pass
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = nw + 32 * i + 8 * g + 4 * fhi;
+                        const int c = col * OSZ / 16;
+                        unsigned char* dst = lds + r * ROWB + ((c ^ (r & SWM)) * 16) + (OSZ == 2 ? 8 * fhi : 0);
+                        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                        if constexpr (OUT == GEMM_BT_F32)
+                            *(u32x4*)dst = u32x4{as_u32(v0), as_u32(v1), as_u32(v2), as_u32(v3)};
+                        else
+                            *(u32x2*)dst = u32x2{pack2<OUT>(v0, v1), pack2<OUT>(v2, v3)};
+                    }
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q0 = 0; q0 < RP * CPR; q0 += NT) {
+            const int q = q0 + tid;
+            const int r = q / CPR, c = q % CPR;
+            const u32x4 v = *(const u32x4*)(lds + r * ROWB + ((c ^ (r & SWM)) * 16));
+            const int row = p * RP + r, col = c * (16 / OSZ);
+            if (row < mlim && col < nlim)
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ((u32)row * (u32)N + (u32)col) * OSZ, 0, 0);
+        }
+        if (p + 1 < P) __syncthreads();
+    }
+}
+
 }  // namespace gbt

@@ -459,7 +459,14 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     }
     wait_vmcnt<0>();  // the ring's last (out-of-range) loads still write LDS
 
-    store_tile_32x32<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+    if (vec_store == 2) {
+        // every wave is past its last LDS read and its loads have landed
+        barrier_no_fence();
+        store_tile_lds<OUT, FN, FM, BM, BN, WM, 64 * W, STAGES * STAGE_BYTES>(acc, lds, C, M, N, m0, n0, wm * TM,
+                                                                             wn * TN, wm, threadIdx.x);
+    } else {
+        store_tile_32x32<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+    }
 }
 
 }  // namespace gbt

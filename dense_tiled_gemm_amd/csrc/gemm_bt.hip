@@ -393,8 +393,11 @@ int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
     } else {
         const u16* a = (const u16*)A;
         const u16* b = (const u16*)B;
-        // Vector stores need 4 consecutive outputs inside one row, aligned.
+        // Vector stores need 4 consecutive outputs inside one row, aligned;
+        // 2 = rows of C are also whole 16-byte chunks (the DMA kernel then
+        // stores through LDS, whole rows per instruction).
         int vec_store = (N % 4 == 0) && c_al >= 4 * osz ? 1 : 0;
+        if (vec_store && (N * osz) % 16 == 0 && c_al >= 16) vec_store = 2;
         if (p.kernel == KIND_TILED || p.kernel == KIND_DMA) {
             const void* fn;
             if (p.kernel == KIND_DMA) {
