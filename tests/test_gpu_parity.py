@@ -67,6 +67,8 @@ SHAPES = [
     (1, 1, 1), (1, 7, 3), (2, 3, 8), (16, 16, 16), (17, 33, 65), (31, 63, 127), (64, 64, 64),
     (65, 129, 200), (127, 255, 64), (128, 128, 128), (130, 260, 72), (200, 100, 300),
     (257, 513, 129), (300, 700, 1000), (129, 1031, 64), (513, 257, 520),
+    # 16-byte rows of C with ragged tile edges (whole-row epilogue), long K
+    (130, 264, 72), (520, 1032, 264), (256, 256, 4096),
 ]
 SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200)]
 
