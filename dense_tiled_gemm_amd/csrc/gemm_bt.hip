@@ -136,6 +136,19 @@ static int forced_skinny() {
     return v;
 }
 
+static bool forced_staged() {
+    // Benchmarking aid: GEMM_BT_FORCE_TILE=STAGED runs the register-staged
+    // kernel on 16-byte aligned rows too.
+    static std::atomic<int> cached{-1};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = std::getenv("GEMM_BT_FORCE_TILE");
+        v = (e && std::strcmp(e, "STAGED") == 0) ? 1 : 0;
+        cached.store(v, std::memory_order_relaxed);
+    }
+    return v == 1;
+}
+
 static int forced_variant() {
     // Benchmarking aid: GEMM_BT_FORCE_TILE=<variant name> pins the DMA kernel shape.
     static std::atomic<int> cached{-2};
@@ -220,7 +233,7 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
     const bool big = tiles_l >= num_cu;
     p->group_m = kGroupM;
     p->ksplit = 1;
-    if (p->vec == 8) {
+    if (p->vec == 8 && !forced_staged()) {
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
         int use = big ? 0 : 1;

@@ -28,7 +28,9 @@
 //     section 4.3: mask A's columns and B's rows); rows past M or N load as
 //     zero through the buffer range check and are never stored;
 //   * epilogue: fp32 -> output type once, round to nearest even, stores
-//     masked to i < M, j < N (section 4.3: out-of-range writes dropped).
+//     masked to i < M, j < N (section 4.3: out-of-range writes dropped); when
+//     rows of C are whole 16-byte chunks the tile goes out through LDS as
+//     whole rows (store_tile_lds).
 //
 // Operand roles: the MFMA's first operand is taken from the B tile and the
 // second from the A tile, so the MFMA computes a block of C^T.  Its
@@ -158,7 +160,12 @@ __global__ __launch_bounds__(64 * WM * WN) void staged_kernel(const u16* __restr
         __syncthreads();
     }
 
-    store_tile_32x32<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+    // the loop ended on a barrier: LDS is free for the whole-row epilogue
+    if (vec_store == 2)
+        store_tile_lds<OUT, FN, FM, BM, BN, WM, T, 2 * STAGE * 16>(acc, (unsigned char*)lds, C, M, N, m0, n0, wm * TM,
+                                                                  wn * TN, wm, tid);
+    else
+        store_tile_32x32<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
 }
 
 }  // namespace gbt
