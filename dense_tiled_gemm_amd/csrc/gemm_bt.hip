@@ -108,13 +108,12 @@ static SkinnyVariant skinny_variant(const char* name, bool all_dtypes) {
 
 static const SkinnyVariant* skinny_variants(int* count) {
     static const SkinnyVariant v[] = {
-        skinny_variant<16, 256, 4, 4>("S16K256x4", true),
-        skinny_variant<8, 256, 4, 4>("S8K256x4", false),
-        skinny_variant<8, 256, 6, 4>("S8K256x6", false),
-        skinny_variant<8, 512, 4, 4>("S8K512x4", false),
-        skinny_variant<16, 256, 6, 4>("S16K256x6", false),
+        skinny_variant<8, 256, 3, 1>("S8K256x3w1", true),
+        skinny_variant<16, 256, 4, 4>("S16K256x4", false),
+        skinny_variant<8, 256, 3, 2>("S8K256x3w2", false),
+        skinny_variant<8, 128, 4, 1>("S8K128x4w1", false),
+        skinny_variant<16, 256, 3, 1>("S16K256x3w1", false),
         skinny_variant<32, 256, 6, 4>("S32K256x6", false),
-        skinny_variant<16, 128, 8, 4>("S16K128x8", false),
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
@@ -214,8 +213,8 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
             p->stages = v.stages;
             p->ksplit = v.waves;
             p->threads = 64 * v.waves;
-            const int bnp = v.bn < 16 ? 16 : v.bn;
-            p->lds_bytes = v.stages * (16 + bnp) * v.kb * 2 + v.waves * (bnp / 16) * 64 * 16;
+            const int nblk = v.bn < 16 ? 1 : v.bn / 16;
+            p->lds_bytes = v.stages * (16 + v.bn) * v.kb * 2 + v.waves * nblk * 64 * 16;
         } else {
             p->variant = 0;
             p->bn = 16 * kSkinnyNB;

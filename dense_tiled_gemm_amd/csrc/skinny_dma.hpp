@@ -12,8 +12,9 @@
 //     stage, with buffer_load_dwordx4 ... lds (no register staging), so about
 //     (STAGES-1) * (16 + BN) * KB * 2 bytes per workgroup are in flight.  HBM
 //     streams B fastest when each workgroup walks few rows at a time, so BN
-//     may be 8: the MFMA's first operand then has 8 padding rows whose
-//     outputs are never stored (the matrix cores have ample slack here);
+//     may be 8: the MFMA's first operand then repeats those 8 rows and the
+//     repeated outputs are never stored (the matrix cores have ample slack
+//     here), and LDS holds only the 8 real rows, so more workgroups fit;
 //   * rows are 2*KB bytes long in LDS; the 16-byte chunk index is XORed with
 //     the low 4 row bits so the 16 rows read by one MFMA operand load fall
 //     in 16 different bank groups of the 64-bank LDS (the same swizzle idea as
@@ -42,13 +43,14 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
     constexpr int CPR = KB / 8;            // 16-byte chunks per row per stage
     constexpr int ROWB = KB * 2;           // bytes per row per stage
     constexpr int RPI = 1024 / ROWB;       // rows per wave load instruction
-    constexpr int BNP = BN < 16 ? 16 : BN;  // B rows held in LDS (BN loaded, the rest padding)
+    constexpr int BR = BN < 16 ? BN : 16;   // distinct B rows under one 16-row MFMA operand
+    constexpr int BNP = BN;                 // B rows held in LDS
     constexpr int A_LOADS = AR / RPI, B_LOADS = BN / RPI;
     constexpr int LOADS = (A_LOADS + B_LOADS) / W;  // per wave per stage
     constexpr int STAGE_BYTES = (AR + BNP) * ROWB;
     constexpr int KBLK = KB / 32;          // MFMA k-blocks per stage
     constexpr int KPW = KBLK / W;          // k-blocks per wave per stage
-    constexpr int NBLK = BNP / 16;
+    constexpr int NBLK = BN < 16 ? 1 : BN / 16;
     constexpr int PEND = (STAGES - 2) * LOADS;
     constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
     static_assert(RPI >= 1 && ROWB * RPI == 1024, "stage rows must tile 1 KiB loads");
@@ -58,6 +60,7 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
     static_assert(CPR >= 16, "swizzle needs 16 chunks per row");
     static_assert(PEND < 64, "vmcnt range");
     static_assert(STAGES * STAGE_BYTES + W * NBLK * 64 * 16 <= 160 * 1024, "LDS budget");
+    static_assert(16 % BR == 0, "B rows repeat evenly under a 16-row operand");
     static_assert(LOADS * W == A_LOADS + B_LOADS, "loads split evenly");
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * STAGE_BYTES];
@@ -118,11 +121,15 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
 #pragma unroll
         for (int t = 0; t < KPW; ++t) {
             const int kb = wave * KPW + t;
-            const int ch = ((4 * kb + q) ^ r16) * 16;  // stage rows of every block start at a multiple of 16
+            const int ch = ((4 * kb + q) ^ r16) * 16;  // A rows 0..15: swizzle term r16
             const u32x4 fa = *(const u32x4*)(s + r16 * ROWB + ch);
 #pragma unroll
             for (int b = 0; b < NBLK; ++b) {
-                const u32x4 fb = *(const u32x4*)(s + (AR + 16 * b + r16) * ROWB + ch);
+                // with BN < 16 the operand's rows r16 and r16 + BN repeat B row r16 % BN;
+                // the repeated output columns are never stored
+                const int brow = AR + 16 * b + (r16 % BR);
+                const int chb = ((4 * kb + q) ^ (brow & 15)) * 16;
+                const u32x4 fb = *(const u32x4*)(s + brow * ROWB + chb);
                 acc[b] = Mfma<IN>::m16x16x32(fb, fa, acc[b]);
             }
         }

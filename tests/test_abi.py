@@ -71,8 +71,9 @@ def test_plan_choices():
     p = gb.gemm_bt_plan(1000, 3000, 2050, gb.BF16, gb.F32)
     assert (p.kernel, p.bm, p.bn, p.vec, p.tiles_m, p.tiles_n) == (2, 128, 128, 2, 8, 24)
     p = gb.gemm_bt_plan(16, 8192, 8192, gb.BF16, gb.BF16)
-    assert (p.kernel, p.bm, p.bn, p.ksplit, p.grid) == (3, 16, 16, 4, 512)
-    assert p.lds_bytes <= 160 * 1024 and p.stages >= 4
+    assert (p.kernel, p.bm, p.bn, p.ksplit, p.grid) == (3, 16, 8, 1, 1024)
+    # several streaming workgroups fit on one CU
+    assert 4 * p.lds_bytes <= 160 * 1024 and p.stages >= 3
     assert gb.gemm_bt_plan(16, 8192, 8190, gb.BF16, gb.BF16).variant == 0  # narrow loads: register streaming
     p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)
     assert (p.kernel, p.bm, p.grid) == (4, 128, 16)
