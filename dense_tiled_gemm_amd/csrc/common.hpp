@@ -114,6 +114,13 @@ __device__ inline u32x4 load8<1>(__amdgpu_buffer_rsrc_t r, u32 off, int valid) {
     return v;
 }
 
+// One bf16 / f16 bit pattern (low 16 bits of v) to fp32, exactly.
+template <int IN>
+__device__ inline float decode16(u32 v) {
+    if constexpr (IN == GEMM_BT_BF16) return __uint_as_float(v << 16);
+    else return (float)__builtin_bit_cast(_Float16, (u16)v);
+}
+
 // Tile order: XCD regrouping followed by banded (grouped) order.  Identical
 // on host and device so the host can verify it is a bijection.
 __host__ __device__ inline void tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m,

@@ -182,6 +182,10 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     const i32x4 ra = rsrc_words(A + (size_t)m0 * K, (u32)rows_a * (u32)K * 2u);
     const i32x4 rb = rsrc_words(B + (size_t)n0 * K, (u32)rows_b * (u32)K * 2u);
     const u32 row_bytes = (u32)K * 2u;
+    // Only whole 16-byte chunks go through the LDS DMA: k < Kf.  When rows are
+    // 4-byte aligned but K % 8 != 0, the last K - Kf (2, 4 or 6) elements of
+    // every row are added after the loop (see the tail below).
+    const int Kf = K & ~7;
 
     // Loader geometry.  Wave instruction i of this wave fills row block
     // j = wave + i*W (rows j*RPI .. j*RPI+RPI-1 of the tile); lane L writes
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     auto issue = [&](int stage, int kt) {
         unsigned char* sbase = lds + stage * STAGE_BYTES;
         const u32 kbytes = (u32)kt * (u32)ROWB;
-        const int kleft = K - kt * BK;  // valid K elements in this tile (may be <= 0)
+        const int kleft = Kf - kt * BK;  // valid K elements in this tile (may be <= 0)
         if (kleft >= BK) {
 #pragma unroll
             for (int i = 0; i < LA; ++i)
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         if constexpr (PF > 0) {
             unsigned char* pbase = lds + STAGES * STAGE_BYTES + wave * 256;
             const u32 kbytes = (u32)kt * (u32)ROWB;
-            const bool live = kt * BK < K;
+            const bool live = kt * BK < Kf;
 #pragma unroll
             for (int p = 0; p < PFI; ++p) {
                 const int row = (wave * PFI + p) * 64 + lane;
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         }
     };
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (Kf + BK - 1) / BK;
     if constexpr (SCHED >= 2) {
         // Early barrier: each wave reads the fragments of a tile's last
         // k-substep, then waits for the next tile and joins the barrier
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         auto load_one = [&](int stage, int kt, int d) {
             unsigned char* sbase = lds + stage * STAGE_BYTES;
             const u32 kbytes = (u32)kt * (u32)ROWB;
-            const int kleft = K - kt * BK;
+            const int kleft = Kf - kt * BK;
             if (d < LA)
                 dma16(ra, sbase + (wave + d * W) * 1024, a_kc[d] < kleft ? a_off[d] : kOutOfRange, kbytes);
             else
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         auto issue_g0 = [&](int stage, int kt) {
             unsigned char* sbase = lds + stage * STAGE_BYTES;
             const u32 kbytes = (u32)kt * (u32)ROWB;
-            const int kleft = K - kt * BK;
+            const int kleft = Kf - kt * BK;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int blk = wave + 4 * h;
@@ -458,6 +462,52 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     }
     }
     wait_vmcnt<0>();  // the ring's last (out-of-range) loads still write LDS
+
+    if (Kf != K) {
+        // K tail: the last K - Kf elements of the tile's A and B rows are
+        // staged in LDS as zero-padded 8-element rows, then every lane adds
+        // their products to its accumulators with fp32 FMAs in increasing k,
+        // after all whole chunks (so each sum still runs over k in order).
+        barrier_no_fence();  // every wave is past its last read of the ring
+        u16* tl = (u16*)lds;
+        for (int q = threadIdx.x; q < (BM + BN) * 8; q += 64 * W) {
+            const int r = q >> 3, k = Kf + (q & 7);
+            u16 v = 0;
+            if (k < K) {
+                if (r < BM) {
+                    if (r < rows_a) v = A[(size_t)(m0 + r) * K + k];
+                } else if (r - BM < rows_b) {
+                    v = B[(size_t)(n0 + r - BM) * K + k];
+                }
+            }
+            tl[q] = v;
+        }
+        __syncthreads();
+        float at[FM][8];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const u32x4 w = *(const u32x4*)(tl + (wm * TM + 32 * j + fr) * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) at[j][e] = decode16<IN>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int nl = wn * TN + 32 * i + 8 * (r / 4) + 4 * fhi + (r % 4);
+                const u32x4 w = *(const u32x4*)(tl + (BM + nl) * 8);
+                float bt[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bt[e] = decode16<IN>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    float x = acc[i][j][r];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x = __builtin_fmaf(at[j][e], bt[e], x);
+                    acc[i][j][r] = x;
+                }
+            }
+    }
 
     if (vec_store == 2) {
         // every wave is past its last LDS read and its loads have landed

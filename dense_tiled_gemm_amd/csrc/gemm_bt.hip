@@ -232,7 +232,9 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
     const bool big = tiles_l >= num_cu;
     p->group_m = kGroupM;
     p->ksplit = 1;
-    if (p->vec == 8 && !forced_staged()) {
+    // the DMA kernel needs 4-byte aligned rows; a K tail that is not a whole
+    // 16-byte chunk is added after its loop
+    if (p->vec >= 2 && !forced_staged()) {
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
         int use = big ? 0 : 1;

@@ -68,8 +68,9 @@ def test_plan_choices():
     assert p.lds_bytes == p.stages * (p.bm + p.bn) * p.bk * 2 <= 160 * 1024
     p = gb.gemm_bt_plan(1024, 4096, 4096, gb.F16, gb.F16)
     assert (p.kernel, p.bm, p.bn, p.grid) == (4, 128, 128, 256)
-    p = gb.gemm_bt_plan(1000, 3000, 2050, gb.BF16, gb.F32)
-    assert (p.kernel, p.bm, p.bn, p.vec, p.tiles_m, p.tiles_n) == (2, 128, 128, 2, 8, 24)
+    p = gb.gemm_bt_plan(1000, 3000, 2050, gb.BF16, gb.F32)  # 4-byte rows: DMA kernel + K tail
+    assert (p.kernel, p.bm, p.bn, p.vec, p.tiles_m, p.tiles_n) == (4, 128, 128, 2, 8, 24)
+    assert gb.gemm_bt_plan(1000, 3000, 2049, gb.BF16, gb.F32).kernel == 2  # 2-byte rows: register-staged
     p = gb.gemm_bt_plan(16, 8192, 8192, gb.BF16, gb.BF16)
     assert (p.kernel, p.bm, p.bn, p.ksplit, p.grid) == (3, 16, 8, 1, 1024)
     # several streaming workgroups fit on one CU

@@ -69,6 +69,8 @@ SHAPES = [
     (257, 513, 129), (300, 700, 1000), (129, 1031, 64), (513, 257, 520),
     # 16-byte rows of C with ragged tile edges (whole-row epilogue), long K
     (130, 264, 72), (520, 1032, 264), (256, 256, 4096),
+    # 4-byte rows whose K is not a whole number of 8-element chunks (K tail), and K < 8
+    (130, 264, 74), (96, 200, 36), (300, 520, 1006), (64, 64, 6), (257, 300, 2050),
 ]
 SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200)]
 
@@ -218,7 +220,8 @@ def test_buffer_end_is_never_read(gpu):
 
 def test_unaligned_pointers_and_odd_k(gpu):
     """Operands starting 2 or 4 bytes past an aligned address, and odd K, select the narrow loaders."""
-    for (M, N, K, off) in [(70, 90, 64, 1), (70, 90, 64, 2), (40, 300, 33, 0), (130, 66, 130, 1), (9, 77, 101, 1)]:
+    for (M, N, K, off) in [(70, 90, 64, 1), (70, 90, 64, 2), (40, 300, 33, 0), (130, 66, 130, 1), (9, 77, 101, 1),
+                           (130, 66, 130, 2), (70, 90, 66, 2)]:
         say("unaligned", M, N, K, "offset elems", off)
         a_bits, b_bits = synth.make(M, N, K, "f16", "normal", 88)
         ba = torch.zeros(M * K + 8, dtype=torch.float16, device="cuda")
