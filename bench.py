@@ -7,8 +7,9 @@ Prints ONE JSON line on stdout:
   value        TFLOP/s of the whole job (2·M·N·K per step / step time)
   roofline     the tiled MFMA kernel against the MI355X dense bf16 peak
   cpu_baseline the CPU oracle timed on a bounded sample of the same product
-  secondary    µs of the 1024×4096×4096 f16 workload and GB/s of the
-               16×8192×8192 skinny workload (same timing method)
+  secondary    µs / TFLOP/s / GB/s of the other four workloads (1024×4096×4096
+               f16, 16×8192×8192 skinny, 512³, 1000×3000×2050), same timing
+  copy_GBps    a plain 1 GiB device copy, as context for achievable HBM
 Diagnostics go to stderr.  The default 400 untimed warm-up launches matter:
 from idle, an MI355X needs about 25 ms of sustained GEMM launches before its
 clocks settle, and launches inside that ramp run up to 15% slower.
@@ -144,6 +145,25 @@ def cpu_baseline(w, target_s=12.0):
                       "threads), %.2f s" % (rows - 1, w.M, w.N, w.K, w.in_dtype, rows * w.N * w.K, threads, dt)}
 
 
+def copy_rate(torch, n=1 << 30, reps=10):
+    """GB/s (read + write) of a plain 1 GiB device-to-device copy: the achievable-HBM context."""
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / ms / 1e6
+
+
 def copy_mode(torch, steps, warmup):
     """Plain device-to-device copy of 1 GiB, for scaling the HBM byte counters."""
     n = 1 << 30
@@ -229,7 +249,8 @@ def main():
     }
     if not args.no_secondary:
         sec = {}
-        for name in ("m1024_n4096_k4096_f16_f16", "skinny_m16_n8192_k8192_bf16_bf16"):
+        for name in ("m1024_n4096_k4096_f16_f16", "skinny_m16_n8192_k8192_bf16_bf16", "sq512_bf16_f32",
+                     "ragged_m1000_n3000_k2050_bf16_f32"):
             w2 = synth.WORKLOADS[name]
             c2 = Case(w2, torch, gb)
             _, ms2 = c2.time(max(50, args.steps // 2), args.warmup)
@@ -245,6 +266,8 @@ def main():
             del c2
             torch.cuda.empty_cache()
         out["secondary"] = sec
+        out["copy_GBps"] = round(copy_rate(torch), 1)
+        log("copy GB/s", out["copy_GBps"])
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
         log("cpu_baseline", out["cpu_baseline"])
