@@ -130,10 +130,11 @@ __device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, 
 
 // SCHED 0: every wave loads fragments and multiplies in the same K step
 //          (fragment reads double-buffered in registers);
-// SCHED 2: early barrier (the default): as SCHED 0, but the barrier of a K
-//          step sits before the MFMAs of the tile's last k-substep, which then
-//          cover the first LDS reads of the next tile and the refill loads
-//          (see the SCHED == 2 branch);
+// SCHED 2-5: early barrier (the default): as SCHED 0, but the barrier of a
+//          K step sits before the MFMAs of the tile's last k-substep(s), which
+//          then cover the first LDS reads of the next tile and the refill
+//          loads; 3 and 4 spread the refill over 2 or all substeps, 5 also
+//          reads fragments two substeps ahead (see the SCHED >= 2 branch);
 // SCHED 1: ping-pong.  The two wave rows (wm = 0, 1) are offset by one
 //          barrier: waves w and w+4 share a SIMD, so on every SIMD one wave
 //          issues its whole K step of MFMAs from registers while the other
@@ -298,25 +299,29 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
 
     const int nk = (Kf + BK - 1) / BK;
     if constexpr (SCHED >= 2) {
-        // Early barrier: each wave reads the fragments of a tile's last
-        // k-substep, then waits for the next tile and joins the barrier
-        // before issuing that substep's MFMAs.  After the barrier the
-        // MFMAs of the last substep run from registers while the first
-        // fragments of the next tile come out of LDS.  The refill of the
-        // freed stage is spread over SPREAD substeps (the last one of this
-        // tile and the first SPREAD - 1 of the next), one or two
-        // global->LDS loads after each MFMA, so the load queues and the L2
-        // see a steady stream instead of one burst per K step.  The
-        // sched_barrier pins keep the compiler from regrouping the LDS
-        // reads, loads and MFMAs.
+        // Early barrier: each wave reads the fragments of a tile's last FD
+        // k-substeps, then waits for the next tile and joins the barrier
+        // before issuing those substeps' MFMAs.  After the barrier these
+        // MFMAs run from registers while the first FD fragment sets of the
+        // next tile come out of LDS.  The refill of the freed stage is
+        // spread over SPREAD substeps (the FD after the barrier and the
+        // first SPREAD - FD of the next tile), one or two global->LDS loads
+        // after each MFMA, so the load queues and the L2 see a steady stream
+        // instead of one burst per K step.  FD = 2 (fragments read two
+        // substeps ahead) is for one wave per SIMD, where no second wave
+        // covers the LDS latency.  The sched_barrier pins keep the compiler
+        // from regrouping the LDS reads, loads and MFMAs.
         constexpr int KS = BK / 16;
         constexpr int L = LA + LB;
         constexpr int NMMA = FN * FM;
+        constexpr int FD = SCHED == 5 ? 2 : 1;
+        constexpr int NSLOT = 2 * FD;  // fragment buffers, used round robin
         constexpr int SPREAD = SCHED == 2 ? 1 : (SCHED == 3 ? 2 : KS);
         constexpr int CH = L / SPREAD;  // loads per chunk
-        static_assert(KS % 2 == 0 && PF == 0, "fragment buffers alternate per substep");
+        constexpr int HEADC = FD < SPREAD ? FD : SPREAD;  // chunks issued after the barrier
+        static_assert(KS % NSLOT == 0 && KS > FD && PF == 0, "fragment buffers rotate per substep");
         static_assert(L % SPREAD == 0 && SPREAD <= KS, "refill chunks");
-        u32x4 fb[2][FN], fa[2][FM];
+        u32x4 fb[NSLOT][FN], fa[NSLOT][FM];
         // load d of this wave's share of tile kt into stage `stage` (A rows
         // first), k >= K masked as in issue()
         auto load_one = [&](int stage, int kt, int d) {
@@ -346,28 +351,33 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         wait_vmcnt<(STAGES - 2) * L>();
         barrier_no_fence();
 #pragma unroll
-        for (int d = 0; d < CH; ++d) load_one(STAGES - 1, STAGES - 1, d);  // chunk 0 of tile STAGES - 1
-        read_frags(lds, 0, fb[0], fa[0]);
+        for (int d = 0; d < CH * HEADC; ++d) load_one(STAGES - 1, STAGES - 1, d);  // head chunks of tile STAGES - 1
+#pragma unroll
+        for (int j = 0; j < FD; ++j) read_frags(lds, j, fb[j], fa[j]);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // both ways into the loop carry no pending LDS reads
-        // stage cs holds tile kt; chunk 0 of tile kt + STAGES - 1 (stage ps)
-        // is issued, its other chunks go out during this tile's substeps
+        // stage cs holds tile kt; the head chunks of tile kt + STAGES - 1
+        // (stage ps) are issued, its other chunks go out during this tile's
+        // first substeps
         int cs = 0, ps = STAGES - 1;
         for (int kt = 0; kt < nk; ++kt) {
             const unsigned char* s = lds + cs * STAGE_BYTES;
             const int ns = cs + 1 == STAGES ? 0 : cs + 1;
 #pragma unroll
-            for (int ks = 0; ks < KS - 1; ++ks) {
-                read_frags(s, ks + 1, fb[(ks + 1) & 1], fa[(ks + 1) & 1]);
+            for (int ks = 0; ks < KS - FD; ++ks) {
+                read_frags(s, ks + FD, fb[(ks + FD) % NSLOT], fa[(ks + FD) % NSLOT]);
                 __builtin_amdgcn_sched_barrier(0);
-                mma_refill(fb[ks & 1], fa[ks & 1], ps, kt + STAGES - 1, ks + 1 < SPREAD ? ks + 1 : -1);
+                mma_refill(fb[ks % NSLOT], fa[ks % NSLOT], ps, kt + STAGES - 1, ks + FD < SPREAD ? ks + FD : -1);
             }
             wait_vmcnt<(STAGES - 2) * L>();       // this wave's part of tile kt + 1 has landed
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading stage cs
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);
-            read_frags(lds + ns * STAGE_BYTES, 0, fb[0], fa[0]);
+#pragma unroll
+            for (int j = 0; j < FD; ++j) read_frags(lds + ns * STAGE_BYTES, j, fb[j], fa[j]);
             __builtin_amdgcn_sched_barrier(0);
-            mma_refill(fb[1], fa[1], cs, kt + STAGES, 0);  // chunk 0 of the refill of stage cs
+#pragma unroll
+            for (int j = 0; j < FD; ++j)  // head chunks of the refill of stage cs
+                mma_refill(fb[(KS - FD + j) % NSLOT], fa[(KS - FD + j) % NSLOT], cs, kt + STAGES, j < SPREAD ? j : -1);
             // the next tile's first fragments arrived behind those MFMAs;
             // saying so here keeps the next iteration from waiting on the
             // reads it issues first

@@ -71,6 +71,7 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E", true),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4", true),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 2>("M64E4", false),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 5>("M64E4f2", false),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 3>("L64E2", false),
         dma_variant<256, 256, 32, 4, 2, 4, 2, 4>("L32E4s", false),
         dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2", false),
@@ -78,6 +79,7 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<256, 256, 64, 2, 2, 4, 0>("L64S2X0", false),
         dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4", false),
         dma_variant<256, 256, 64, 2, 2, 2, 2, 2>("L64EW4", false),
+        dma_variant<256, 256, 64, 2, 2, 2, 2, 3>("L64EW4s2", false),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP", false),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 2>("L64P2", false),
     };
