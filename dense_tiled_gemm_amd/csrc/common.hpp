@@ -143,32 +143,53 @@ __host__ __device__ inline void tile_coord(int64_t pid, int64_t tiles_m, int64_t
     *tn = in_band / rows;
 }
 
-// Store a wave's FN x FM grid of 32x32 accumulator blocks (MFMA 32x32x16 with
-// the B tile as first operand, so block (i, j) holds C^T: register r of lane
-// l is C[row mw + 32j + l%32][col nw + 32i + 8(r/4) + 4(l/32) + r%4]).  Each
-// lane writes 4 consecutive outputs of one row of C per store: one 16-byte
+// Accumulator blocks of the tiled kernels.  The MFMA takes the B tile as its
+// first operand, so block (i, j) of a wave holds a block of C^T, and each
+// lane owns 4 consecutive columns of one row of C per group of 4 registers:
+//   MF = 32 (v_mfma_f32_32x32x16, 16 registers): register r of lane l is
+//     C[mw + 32j + l%32][nw + 32i + 8(r/4) + 4(l/32) + r%4];
+//   MF = 16 (v_mfma_f32_16x16x32, 4 registers): register r of lane l is
+//     C[mw + 16j + l%16][nw + 16i + 4(l/16) + r].
+template <int MF>
+struct AccBlock {
+    typedef f32x16 type;
+    static constexpr int regs = 16;
+    __device__ static int row(int lane) { return lane & 31; }
+    // first column of register group g (registers 4g .. 4g+3), relative to the block
+    __device__ static int col(int lane, int g) { return 8 * g + 4 * (lane >> 5); }
+};
+template <>
+struct AccBlock<16> {
+    typedef f32x4 type;
+    static constexpr int regs = 4;
+    __device__ static int row(int lane) { return lane & 15; }
+    __device__ static int col(int lane, int g) { return 4 * (lane >> 4) + 0 * g; }
+};
+
+// Store a wave's FN x FM grid of MF x MF accumulator blocks directly: each
+// lane writes the 4 consecutive outputs of a register group with one 16-byte
 // (fp32) or 8-byte (16-bit) store when vec_store, else element by element.
 // Rows >= M and columns >= N are not written.  The fp32 -> 16-bit conversion
 // rounds to nearest even, once.
-template <int OUT, int FN, int FM>
-__device__ inline void store_tile_32x32(const f32x16 (&acc)[FN][FM], void* C, int M, int N, int m0, int n0,
-                                        int mw, int nw, int lane, int vec_store) {
+template <int OUT, int FN, int FM, int MF = 32>
+__device__ inline void store_tile(const typename AccBlock<MF>::type (&acc)[FN][FM], void* C, int M, int N, int m0,
+                                  int n0, int mw, int nw, int lane, int vec_store) {
+    typedef AccBlock<MF> AB;
     constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
     const size_t c_origin = (size_t)m0 * N + n0;
     const size_t c_rest = (size_t)M * N - c_origin;
     const u32 c_bytes = (u32)min(c_rest * OSZ, (size_t)0x7FFFFFFF);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc((const char*)C + c_origin * OSZ, c_bytes);
     const int mlim = M - m0, nlim = N - n0;
-    const int fr = lane & 31, fhi = lane >> 5;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
-            const int ml = mw + 32 * j + fr;
+            const int ml = mw + MF * j + AB::row(lane);
             if (ml >= mlim) continue;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = nw + 32 * i + 8 * g + 4 * fhi;
+            for (int g = 0; g < AB::regs / 4; ++g) {
+                const int nl = nw + MF * i + AB::col(lane, g);
                 const u32 off = ((u32)ml * (u32)N + (u32)nl) * OSZ;
                 const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
                 const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
@@ -208,14 +229,15 @@ __device__ inline void store_tile_32x32(const f32x16 (&acc)[FN][FM], void* C, in
 // of consecutive row bytes (full cache lines instead of 16-byte pieces from
 // 32 rows at a time).  The 16-byte chunk c of tile row r sits at physical
 // chunk c ^ (r mod 32) (mod 16 for 16-chunk rows): the column-wise parking
-// writes of 32 rows then spread over the banks, and the row-wise reads stay
-// whole chunks.  A tile larger than LDS_BYTES goes in WM passes of one wave
-// row each.  Requires 16-byte aligned rows of C (N * sizeof(OUT) a multiple of
-// 16 and C 16-byte aligned); rows >= M and columns >= N are not written.  The
-// caller guarantees that no wave still reads or fills `lds`.
-template <int OUT, int FN, int FM, int BM, int BN, int WM, int NT, int LDS_BYTES>
-__device__ inline void store_tile_lds(const f32x16 (&acc)[FN][FM], unsigned char* lds, void* C, int M, int N,
-                                      int m0, int n0, int mw, int nw, int wm, int tid) {
+// writes of 16 or 32 rows then spread over the banks, and the row-wise reads
+// stay whole chunks.  A tile larger than LDS_BYTES goes in WM passes of one
+// wave row each.  Requires 16-byte aligned rows of C (N * sizeof(OUT) a
+// multiple of 16 and C 16-byte aligned); rows >= M and columns >= N are not
+// written.  The caller guarantees that no wave still reads or fills `lds`.
+template <int OUT, int FN, int FM, int BM, int BN, int WM, int NT, int LDS_BYTES, int MF = 32>
+__device__ inline void store_tile_lds(const typename AccBlock<MF>::type (&acc)[FN][FM], unsigned char* lds, void* C,
+                                      int M, int N, int m0, int n0, int mw, int nw, int wm, int tid) {
+    typedef AccBlock<MF> AB;
     constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
     constexpr int ROWB = BN * OSZ;  // bytes per tile row
     constexpr int CPR = ROWB / 16;  // 16-byte chunks per tile row
@@ -229,7 +251,7 @@ __device__ inline void store_tile_lds(const f32x16 (&acc)[FN][FM], unsigned char
     const u32 c_bytes = (u32)min(c_rest * OSZ, (size_t)0x7FFFFFFF);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc((const char*)C + c_origin * OSZ, c_bytes);
     const int mlim = M - m0, nlim = N - n0;
-    const int lane = tid & 63, fr = lane & 31, fhi = lane >> 5;
+    const int lane = tid & 63;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         if (P == 1 || wm == p) {
@@ -237,12 +259,12 @@ __device__ inline void store_tile_lds(const f32x16 (&acc)[FN][FM], unsigned char
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int j = 0; j < FM; ++j) {
-                    const int r = mw + 32 * j + fr - p * RP;  // tile row within the pass
+                    const int r = mw + MF * j + AB::row(lane) - p * RP;  // tile row within the pass
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int col = nw + 32 * i + 8 * g + 4 * fhi;
+                    for (int g = 0; g < AB::regs / 4; ++g) {
+                        const int col = nw + MF * i + AB::col(lane, g);
                         const int c = col * OSZ / 16;
-                        unsigned char* dst = lds + r * ROWB + ((c ^ (r & SWM)) * 16) + (OSZ == 2 ? 8 * fhi : 0);
+                        unsigned char* dst = lds + r * ROWB + ((c ^ (r & SWM)) * 16) + (OSZ == 2 ? 8 * ((col >> 2) & 1) : 0);
                         const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
                         const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
                         if constexpr (OUT == GEMM_BT_F32)

@@ -146,7 +146,8 @@ __device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, 
 // BK = 64) with 4-byte LDS-DMA loads into a scratch corner of LDS, so that the
 // refill PF steps later finds its lines in L2 instead of paying the full
 // HBM / Infinity-Cache latency with only STAGES - 1 steps of cover.
-template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0>
+template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0,
+          int MF = 32>
 __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                           void* __restrict__ C, int M, int N, int K,
                                                           int tiles_m, int tiles_n, int group_m,
@@ -158,14 +159,17 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     constexpr int LA = BM / (RPI * W);   // A load instructions per wave per stage
     constexpr int LB = BN / (RPI * W);
     constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int FM = TM / MF, FN = TN / MF;
+    constexpr int KSUB = 512 / MF;       // K per MFMA: 16 (32x32x16) or 32 (16x16x32)
     constexpr int STAGE_BYTES = (BM + BN) * ROWB;
     constexpr int PFI = PF > 0 ? (BM + BN) / (64 * W) : 0;  // prefetch instructions per wave per step
     constexpr int PEND = (STAGES - 2) * (LA + LB + PFI) + PFI;
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert(LA * RPI * W == BM && LB * RPI * W == BN, "tile rows must split evenly over waves");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(MF == 32 || MF == 16, "MFMA 32x32x16 or 16x16x32");
+    static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be whole MFMA blocks");
+    static_assert(BK % (2 * KSUB) == 0, "two or more MFMA k-substeps per K step");
     static_assert(PEND < 64, "vmcnt range");
     static_assert(PF == 0 || (BK == 64 && (BM + BN) % (64 * W) == 0 && SCHED == 0), "prefetch layout");
     static_assert(STAGES * STAGE_BYTES + (PF > 0 ? W * 256 : 0) <= 160 * 1024, "LDS budget");
@@ -251,41 +255,46 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         }
     };
 
-    // Operand reads: row (lane % 32) of each 32-row block, logical chunk
-    // 2*ks + lane/32 for k-substep ks; block bases are multiples of 32, so the
-    // swizzle term depends on the lane only.
-    const int fr = lane & 31, fhi = lane >> 5;
+    // Operand reads: row (lane % MF) of each MF-row block, logical chunk
+    // (KSUB/8)*ks + lane/MF for k-substep ks; block bases are multiples of MF
+    // (>= 16), so the swizzle term depends on the lane only.
+    typedef AccBlock<MF> AB;
+    const int fr = lane % MF, fhi = lane / MF;
     const int fsw = swz_row<CPR, SWZ>(fr);
     const int a_base = (wm * TM + fr) * ROWB;
     const int b_base = BM * ROWB + (wn * TN + fr) * ROWB;
 
-    f32x16 acc[FN][FM];
+    typename AB::type acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < AB::regs; ++r) acc[i][j][r] = 0.0f;
 
     // Operand fragments are double-buffered in registers: the LDS reads for
     // k-substep ks+1 are issued before the MFMAs of substep ks, so their
     // latency hides behind 8 MFMAs instead of stalling the wave.
     auto read_frags = [&](const unsigned char* s, int ks, u32x4 (&fb)[FN], u32x4 (&fa)[FM]) {
-        const int ch = ((2 * ks + fhi) ^ fsw) * 16;
+        const int ch = (((KSUB / 8) * ks + fhi) ^ fsw) * 16;
 #pragma unroll
-        for (int i = 0; i < FN; ++i) fb[i] = *(const u32x4*)(s + b_base + 32 * ROWB * i + ch);
+        for (int i = 0; i < FN; ++i) fb[i] = *(const u32x4*)(s + b_base + MF * ROWB * i + ch);
 #pragma unroll
-        for (int j = 0; j < FM; ++j) fa[j] = *(const u32x4*)(s + a_base + 32 * ROWB * j + ch);
+        for (int j = 0; j < FM; ++j) fa[j] = *(const u32x4*)(s + a_base + MF * ROWB * j + ch);
+    };
+    auto mfma1 = [&](const u32x4& b, const u32x4& a, typename AB::type& c) {
+        if constexpr (MF == 32) c = Mfma<IN>::m32x32x16(b, a, c);
+        else c = Mfma<IN>::m16x16x32(b, a, c);
     };
     auto mma = [&](const u32x4 (&fb)[FN], const u32x4 (&fa)[FM]) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int j = 0; j < FM; ++j) acc[i][j] = Mfma<IN>::m32x32x16(fb[i], fa[j], acc[i][j]);
+            for (int j = 0; j < FM; ++j) mfma1(fb[i], fa[j], acc[i][j]);
     };
     auto compute = [&](int stage) {
         const unsigned char* s = lds + stage * STAGE_BYTES;
-        constexpr int KS = BK / 16;
+        constexpr int KS = BK / KSUB;
         u32x4 fb0[FN], fa0[FM], fb1[FN], fa1[FM];
         read_frags(s, 0, fb0, fa0);
 #pragma unroll
@@ -311,7 +320,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         // substeps ahead) is for one wave per SIMD, where no second wave
         // covers the LDS latency.  The sched_barrier pins keep the compiler
         // from regrouping the LDS reads, loads and MFMAs.
-        constexpr int KS = BK / 16;
+        constexpr int KS = BK / KSUB;
         constexpr int L = LA + LB;
         constexpr int NMMA = FN * FM;
         constexpr int FD = SCHED == 5 ? 2 : 1;
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         auto mma_refill = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], int stage, int kt, int c) {
 #pragma unroll
             for (int t = 0; t < NMMA; ++t) {
-                acc[t / FM][t % FM] = Mfma<IN>::m32x32x16(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
+                mfma1(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int d = 0; d < CH; ++d)
@@ -387,7 +396,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         }
     } else if constexpr (SCHED == 1) {
         static_assert(W == 8 && WM == 2, "ping-pong pairs the two wave rows");
-        constexpr int KS = BK / 16;
+        constexpr int KS = BK / KSUB;
         constexpr int L2 = 2 * (LA + LB);  // loads of one whole tile, issued by one wm = 0 wave
         const int grp = wm;  // waves 0..3 and 4..7; wave w and w + 4 share a SIMD
         // The wm = 0 group issues every load of a tile (block rows `wave` and
@@ -496,15 +505,15 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         float at[FM][8];
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
-            const u32x4 w = *(const u32x4*)(tl + (wm * TM + 32 * j + fr) * 8);
+            const u32x4 w = *(const u32x4*)(tl + (wm * TM + MF * j + fr) * 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) at[j][e] = decode16<IN>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
         }
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int nl = wn * TN + 32 * i + 8 * (r / 4) + 4 * fhi + (r % 4);
+            for (int r = 0; r < AB::regs; ++r) {
+                const int nl = wn * TN + MF * i + AB::col(lane, r / 4) + (r % 4);
                 const u32x4 w = *(const u32x4*)(tl + (BM + nl) * 8);
                 float bt[8];
 #pragma unroll
@@ -522,10 +531,10 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     if (vec_store == 2) {
         // every wave is past its last LDS read and its loads have landed
         barrier_no_fence();
-        store_tile_lds<OUT, FN, FM, BM, BN, WM, 64 * W, STAGES * STAGE_BYTES>(acc, lds, C, M, N, m0, n0, wm * TM,
+        store_tile_lds<OUT, FN, FM, BM, BN, WM, 64 * W, STAGES * STAGE_BYTES, MF>(acc, lds, C, M, N, m0, n0, wm * TM,
                                                                              wn * TN, wm, threadIdx.x);
     } else {
-        store_tile_32x32<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+        store_tile<OUT, FN, FM, MF>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
     }
 }
 

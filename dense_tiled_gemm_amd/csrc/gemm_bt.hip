@@ -49,16 +49,16 @@ struct DmaVariant {
 static int in_index(int in_dtype) { return in_dtype == GEMM_BT_BF16 ? 0 : 1; }
 static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out_dtype == GEMM_BT_BF16 ? 1 : 2); }
 
-template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0>
+template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32>
 static DmaVariant dma_variant(const char* name, bool all_dtypes) {
     DmaVariant v = {name, BM, BN, BK, S, WM, WN, SWZ, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
-    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
-    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
+    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
+    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
     if (all_dtypes) {
-        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
-        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
-        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
-        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF>;
+        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
+        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
+        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
+        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
     }
     return v;
 }
@@ -68,8 +68,10 @@ static DmaVariant dma_variant(const char* name, bool all_dtypes) {
 // bf16->bf16 and f16->f16 combinations only.
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E", true),
-        dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4", true),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16", true),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16", true),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E", false),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4", false),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 2>("M64E4", false),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 5>("M64E4f2", false),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 3>("L64E2", false),

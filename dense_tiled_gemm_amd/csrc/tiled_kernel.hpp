@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64 * WM * WN) void staged_kernel(const u16* __restr
         store_tile_lds<OUT, FN, FM, BM, BN, WM, T, 2 * STAGE * 16>(acc, (unsigned char*)lds, C, M, N, m0, n0, wm * TM,
                                                                   wn * TN, wm, tid);
     else
-        store_tile_32x32<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+        store_tile<OUT, FN, FM>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
 }
 
 }  // namespace gbt
