@@ -483,49 +483,36 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     wait_vmcnt<0>();  // the ring's last (out-of-range) loads still write LDS
 
     if (Kf != K) {
-        // K tail: the last K - Kf elements of the tile's A and B rows are
-        // staged in LDS as zero-padded 8-element rows, then every lane adds
-        // their products to its accumulators with fp32 FMAs in increasing k,
-        // after all whole chunks (so each sum still runs over k in order).
+        // K tail: the last K - Kf (2, 4 or 6) elements of every row form one
+        // more K tile, zero-padded, written into LDS stage 0 in the same
+        // swizzled layout and multiplied like the others.  It comes after all
+        // whole chunks, so each sum still runs over k in order.
         barrier_no_fence();  // every wave is past its last read of the ring
-        u16* tl = (u16*)lds;
-        for (int q = threadIdx.x; q < (BM + BN) * 8; q += 64 * W) {
-            const int r = q >> 3, k = Kf + (q & 7);
-            u16 v = 0;
-            if (k < K) {
+        for (int q = threadIdx.x; q < (BM + BN) * CPR; q += 64 * W) {
+            const int r = q / CPR, c = q % CPR;
+            u32 v[4] = {0u, 0u, 0u, 0u};
+            if (c == 0) {
+                const u16* src = nullptr;
                 if (r < BM) {
-                    if (r < rows_a) v = A[(size_t)(m0 + r) * K + k];
+                    if (r < rows_a) src = A + (size_t)(m0 + r) * K;
                 } else if (r - BM < rows_b) {
-                    v = B[(size_t)(n0 + r - BM) * K + k];
+                    src = B + (size_t)(n0 + r - BM) * K;
+                }
+                if (src) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (Kf + e < K) v[e >> 1] |= (u32)src[Kf + e] << (16 * (e & 1));
                 }
             }
-            tl[q] = v;
+            *(u32x4*)(lds + r * ROWB + ((c ^ swz_row<CPR, SWZ>(r)) * 16)) = u32x4{v[0], v[1], v[2], v[3]};
         }
         __syncthreads();
-        float at[FM][8];
+        u32x4 tb[FN], ta[FM];
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const u32x4 w = *(const u32x4*)(tl + (wm * TM + MF * j + fr) * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) at[j][e] = decode16<IN>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        for (int ks = 0; ks < BK / KSUB; ++ks) {
+            read_frags(lds, ks, tb, ta);
+            mma(tb, ta);
         }
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int r = 0; r < AB::regs; ++r) {
-                const int nl = wn * TN + MF * i + AB::col(lane, r / 4) + (r % 4);
-                const u32x4 w = *(const u32x4*)(tl + (BM + nl) * 8);
-                float bt[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bt[e] = decode16<IN>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-#pragma unroll
-                for (int j = 0; j < FM; ++j) {
-                    float x = acc[i][j][r];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x = __builtin_fmaf(at[j][e], bt[e], x);
-                    acc[i][j][r] = x;
-                }
-            }
     }
 
     if (vec_store == 2) {
