@@ -49,12 +49,13 @@ struct DmaVariant {
 static int in_index(int in_dtype) { return in_dtype == GEMM_BT_BF16 ? 0 : 1; }
 static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out_dtype == GEMM_BT_BF16 ? 1 : 2); }
 
-template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32>
-static DmaVariant dma_variant(const char* name, bool all_dtypes) {
+template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32,
+          bool ALL = false>
+static DmaVariant dma_variant(const char* name) {
     DmaVariant v = {name, BM, BN, BK, S, WM, WN, SWZ, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
     v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
     v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
-    if (all_dtypes) {
+    if constexpr (ALL) {
         v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
         v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
         v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
@@ -68,22 +69,17 @@ static DmaVariant dma_variant(const char* name, bool all_dtypes) {
 // bf16->bf16 and f16->f16 combinations only.
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16", true),
-        dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16", true),
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E", false),
-        dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4", false),
-        dma_variant<128, 128, 64, 4, 2, 2, 2, 2>("M64E4", false),
-        dma_variant<128, 128, 64, 4, 2, 2, 2, 5>("M64E4f2", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 3>("L64E2", false),
-        dma_variant<256, 256, 32, 4, 2, 4, 2, 4>("L32E4s", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2", false),
-        dma_variant<128, 128, 64, 4, 2, 2, 2>("M64S4", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 0>("L64S2X0", false),
-        dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4", false),
-        dma_variant<256, 256, 64, 2, 2, 2, 2, 2>("L64EW4", false),
-        dma_variant<256, 256, 64, 2, 2, 2, 2, 3>("L64EW4s2", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP", false),
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 2>("L64P2", false),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16, true>("L64E16"),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16, true>("M64E4s4m16"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E"),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4"),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 5>("M64E4f2"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2"),
+        dma_variant<256, 256, 64, 2, 2, 4, 0>("L64S2X0"),
+        dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4"),
+        dma_variant<256, 256, 64, 2, 2, 2, 2, 3>("L64EW4s2"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 2>("L64P2"),
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
@@ -96,12 +92,12 @@ struct SkinnyVariant {
     const void* fn[2][3];
 };
 
-template <int BN, int KB, int S, int W>
-static SkinnyVariant skinny_variant(const char* name, bool all_dtypes) {
+template <int BN, int KB, int S, int W, bool ALL = false>
+static SkinnyVariant skinny_variant(const char* name) {
     SkinnyVariant v = {name, BN, KB, S, W, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
     v.fn[0][1] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BN, KB, S, W>;
     v.fn[1][2] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BN, KB, S, W>;
-    if (all_dtypes) {
+    if constexpr (ALL) {
         v.fn[0][0] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BN, KB, S, W>;
         v.fn[0][2] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BN, KB, S, W>;
         v.fn[1][0] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BN, KB, S, W>;
@@ -112,12 +108,12 @@ static SkinnyVariant skinny_variant(const char* name, bool all_dtypes) {
 
 static const SkinnyVariant* skinny_variants(int* count) {
     static const SkinnyVariant v[] = {
-        skinny_variant<8, 256, 3, 1>("S8K256x3w1", true),
-        skinny_variant<16, 256, 4, 4>("S16K256x4", false),
-        skinny_variant<8, 256, 3, 2>("S8K256x3w2", false),
-        skinny_variant<8, 128, 4, 1>("S8K128x4w1", false),
-        skinny_variant<16, 256, 3, 1>("S16K256x3w1", false),
-        skinny_variant<32, 256, 6, 4>("S32K256x6", false),
+        skinny_variant<8, 256, 3, 1, true>("S8K256x3w1"),
+        skinny_variant<16, 256, 4, 4>("S16K256x4"),
+        skinny_variant<8, 256, 3, 2>("S8K256x3w2"),
+        skinny_variant<8, 128, 4, 1>("S8K128x4w1"),
+        skinny_variant<16, 256, 3, 1>("S16K256x3w1"),
+        skinny_variant<32, 256, 6, 4>("S32K256x6"),
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
