@@ -228,7 +228,7 @@ __device__ inline void store_tile(const typename AccBlock<MF>::type (&acc)[FN][F
 // the workgroup copy rows to C with 16 bytes per lane, so 64 lanes write 1 KiB
 // of consecutive row bytes (full cache lines instead of 16-byte pieces from
 // 32 rows at a time).  The 16-byte chunk c of tile row r sits at physical
-// chunk c ^ (r mod 32) (mod 16 for 16-chunk rows): the column-wise parking
+// chunk c ^ (r mod min(32, chunks per row)): the column-wise parking
 // writes of 16 or 32 rows then spread over the banks, and the row-wise reads
 // stay whole chunks.  A tile larger than LDS_BYTES goes in WM passes of one
 // wave row each.  Requires 16-byte aligned rows of C (N * sizeof(OUT) a
@@ -244,7 +244,7 @@ __device__ inline void store_tile_lds(const typename AccBlock<MF>::type (&acc)[F
     constexpr int SWM = (CPR < 32 ? CPR : 32) - 1;
     constexpr int P = BM * ROWB <= LDS_BYTES ? 1 : WM;
     constexpr int RP = BM / P;  // tile rows per pass
-    static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "row chunks");
+    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "row chunks");
     static_assert(RP * ROWB <= LDS_BYTES, "a pass must fit in LDS");
     const size_t c_origin = (size_t)m0 * N + n0;
     const size_t c_rest = (size_t)M * N - c_origin;

@@ -64,13 +64,15 @@ static DmaVariant dma_variant(const char* name) {
     return v;
 }
 
-// Index 0 is the default for large grids, 1 the default for small ones; the
+// Index 0 is the default for large grids, 1 for smaller ones, 2 for the
+// smallest (see plan_impl); the
 // rest exist for tuning (GEMM_BT_FORCE_TILE=<name>) and are built for the
 // bf16->bf16 and f16->f16 combinations only.
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16, true>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16, true>("M64E4s4m16"),
+        dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true>("Q64E4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 5>("M64E4f2"),
@@ -237,7 +239,10 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
     if (p->vec >= 2 && !forced_staged()) {
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
-        int use = big ? 0 : 1;
+        // 256x256 when that fills every CU; else 128x128 unless it leaves
+        // three quarters of the CUs idle, then 64x64
+        const int64_t tiles_m128 = ((M + 127) / 128) * ((N + 127) / 128);
+        int use = big ? 0 : (tiles_m128 * 4 >= num_cu ? 1 : 2);
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];

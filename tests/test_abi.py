@@ -76,8 +76,9 @@ def test_plan_choices():
     # several streaming workgroups fit on one CU
     assert 4 * p.lds_bytes <= 160 * 1024 and p.stages >= 3
     assert gb.gemm_bt_plan(16, 8192, 8190, gb.BF16, gb.BF16).variant == 0  # narrow loads: register streaming
-    p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)
-    assert (p.kernel, p.bm, p.grid) == (4, 128, 16)
+    p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)  # 16 tiles of 128: 64x64 tiles fill more CUs
+    assert (p.kernel, p.bm, p.grid) == (4, 64, 64)
+    assert gb.gemm_bt_plan(1024, 1024, 200, gb.BF16, gb.F32).bm == 128
     assert gb.gemm_bt_plan(7, 9, 0, gb.BF16, gb.F32).kernel == 1   # K == 0: zero fill
     assert gb.gemm_bt_plan(0, 9, 5, gb.BF16, gb.F32).kernel == 0   # empty
     # alignment decides the load width

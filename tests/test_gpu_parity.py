@@ -71,6 +71,8 @@ SHAPES = [
     (130, 264, 72), (520, 1032, 264), (256, 256, 4096),
     # 4-byte rows whose K is not a whole number of 8-element chunks (K tail), and K < 8
     (130, 264, 74), (96, 200, 36), (300, 520, 1006), (64, 64, 6), (257, 300, 2050),
+    # shapes that select the 128x128 and 256x256 tiles (the ones above take 64x64)
+    (1024, 1024, 200), (1030, 1030, 202), (4096, 4096, 72),
 ]
 SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200)]
 
