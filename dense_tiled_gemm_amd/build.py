@@ -19,6 +19,12 @@ FLAGS = [
     "-shared",
     # keep the compiler from forming packed-fp32 VALU ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMAs read and write their accumulators in VGPRs.  For a 256-thread
+    # workgroup the compiler otherwise assumes a wave may need more than 256
+    # registers, picks the AGPR form and then rotates the accumulator blocks
+    # through copies inside the K loop (1024x4096x4096: 48 -> 40 us).  Every
+    # kernel here keeps its accumulators within 256 registers.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
     "-Wno-unused-function",
 ]

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm_bt.h"
 
 namespace gbt {
@@ -18,6 +20,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1.
+// Used where a body must be replicated whatever its size: the unroll pragma
+// gives up above a size limit, and a loop left rolled turns the accumulator
+// array's constant indices into dynamic ones, which moves it to scratch.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 // Buffer-resource word 3 for gfx9-family raw buffers (32-bit data format,
 // no swizzle, no index stride).  With stride 0 the hardware range-checks each

@@ -135,6 +135,8 @@ __device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, 
 //          then cover the first LDS reads of the next tile and the refill
 //          loads; 3 and 4 spread the refill over 2 or all substeps, 5 also
 //          reads fragments two substeps ahead (see the SCHED >= 2 branch);
+// SCHED 6-8: as 2-4, with each substep's fragment reads spread over the
+//          MFMAs of the one before instead of issued as a burst;
 // SCHED 1: ping-pong.  The two wave rows (wm = 0, 1) are offset by one
 //          barrier: waves w and w+4 share a SIMD, so on every SIMD one wave
 //          issues its whole K step of MFMAs from registers while the other
@@ -197,22 +199,17 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     // row j*RPI + L/CPR at physical chunk L%CPR and so fetches logical chunk
     // (L%CPR) ^ swz(row).
     const int lrow = lane / CPR, lphys = lane % CPR;
-    u32 a_off[LA], b_off[LB];
-    int a_kc[LA], b_kc[LB];  // first K index (within a tile) of the lane's chunk
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-        const int row = (wave + i * W) * RPI + lrow;
-        const int c = lphys ^ swz_row<CPR, SWZ>(row);
-        a_off[i] = (u32)row * row_bytes + (u32)c * 16u;
-        a_kc[i] = c * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int row = (wave + i * W) * RPI + lrow;
-        const int c = lphys ^ swz_row<CPR, SWZ>(row);
-        b_off[i] = (u32)row * row_bytes + (u32)c * 16u;
-        b_kc[i] = c * 8;
-    }
+    // The rows of a wave's instructions are W * RPI apart, a multiple of the
+    // swizzle period (16 rows), so all of them fetch the same logical chunk
+    // and instruction i only adds i * W * RPI rows to the byte offset.  A and
+    // B tiles use the same row mapping.  The offsets are recomputed per load
+    // rather than held in registers (they are one add each).
+    static_assert((W * RPI) % 16 == 0, "a wave's row blocks share one swizzle");
+    const int lchunk = lphys ^ swz_row<CPR, SWZ>(wave * RPI + lrow);
+    const int l_kc = lchunk * 8;  // first K index (within a tile) of the lane's chunk
+    u32 l_off = (u32)(wave * RPI + lrow) * row_bytes + (u32)lchunk * 16u;
+    const u32 i_stride = (u32)(W * RPI) * row_bytes;
+    auto ld_off = [&](int i) { return l_off + (u32)i * i_stride; };
 
     auto issue = [&](int stage, int kt) {
         unsigned char* sbase = lds + stage * STAGE_BYTES;
@@ -221,17 +218,17 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         if (kleft >= BK) {
 #pragma unroll
             for (int i = 0; i < LA; ++i)
-                dma16(ra, sbase + (wave + i * W) * 1024, a_off[i], kbytes);
+                dma16(ra, sbase + (wave + i * W) * 1024, ld_off(i), kbytes);
 #pragma unroll
             for (int i = 0; i < LB; ++i)
-                dma16(rb, sbase + BM * ROWB + (wave + i * W) * 1024, b_off[i], kbytes);
+                dma16(rb, sbase + BM * ROWB + (wave + i * W) * 1024, ld_off(i), kbytes);
         } else {
 #pragma unroll
             for (int i = 0; i < LA; ++i)
-                dma16(ra, sbase + (wave + i * W) * 1024, a_kc[i] < kleft ? a_off[i] : kOutOfRange, kbytes);
+                dma16(ra, sbase + (wave + i * W) * 1024, l_kc < kleft ? ld_off(i) : kOutOfRange, kbytes);
 #pragma unroll
             for (int i = 0; i < LB; ++i)
-                dma16(rb, sbase + BM * ROWB + (wave + i * W) * 1024, b_kc[i] < kleft ? b_off[i] : kOutOfRange,
+                dma16(rb, sbase + BM * ROWB + (wave + i * W) * 1024, l_kc < kleft ? ld_off(i) : kOutOfRange,
                       kbytes);
         }
     };
@@ -323,9 +320,19 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         constexpr int KS = BK / KSUB;
         constexpr int L = LA + LB;
         constexpr int NMMA = FN * FM;
-        constexpr int FD = SCHED == 5 ? 2 : 1;
+        constexpr bool ILR = SCHED >= 6;  // fragment reads interleaved with the MFMAs
+        constexpr int BASE = ILR ? SCHED - 4 : SCHED;
+        static_assert(BASE >= 2 && BASE <= 5 && !(ILR && BASE == 5), "schedule");
+        constexpr int FD = BASE == 5 ? 2 : 1;
         constexpr int NSLOT = 2 * FD;  // fragment buffers, used round robin
-        constexpr int SPREAD = SCHED == 2 ? 1 : (SCHED == 3 ? 2 : KS);
+        constexpr int SPREAD = BASE == 2 ? 1 : (BASE == 3 ? 2 : KS);
+        // ILR: the FN + FM fragment reads of the next substep go out one
+        // every RS MFMAs over the first half of the current substep, in the
+        // order the next substep consumes them (b0, a0 .. a[FM-1], b1 ..), so
+        // that with one wave per SIMD the MFMA pipe is not left idle while a
+        // burst of reads issues.
+        constexpr int NRD = FN + FM;
+        constexpr int RS = NMMA / (2 * NRD) > 0 ? NMMA / (2 * NRD) : 1;
         constexpr int CH = L / SPREAD;  // loads per chunk
         constexpr int HEADC = FD < SPREAD ? FD : SPREAD;  // chunks issued after the barrier
         static_assert(KS % NSLOT == 0 && KS > FD && PF == 0, "fragment buffers rotate per substep");
@@ -338,22 +345,41 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             const u32 kbytes = (u32)kt * (u32)ROWB;
             const int kleft = Kf - kt * BK;
             if (d < LA)
-                dma16(ra, sbase + (wave + d * W) * 1024, a_kc[d] < kleft ? a_off[d] : kOutOfRange, kbytes);
+                dma16(ra, sbase + (wave + d * W) * 1024, l_kc < kleft ? ld_off(d) : kOutOfRange, kbytes);
             else
                 dma16(rb, sbase + BM * ROWB + (wave + (d - LA) * W) * 1024,
-                      b_kc[d - LA] < kleft ? b_off[d - LA] : kOutOfRange, kbytes);
+                      l_kc < kleft ? ld_off(d - LA) : kOutOfRange, kbytes);
+        };
+        // fragment r of substep ks in consumption order: b0, a0 .. a[FM-1], b1 ..
+        auto read_one = [&](const unsigned char* st, int ks, auto rc, u32x4 (&fb)[FN], u32x4 (&fa)[FM]) {
+            constexpr int r = decltype(rc)::value;
+            const int ch = (((KSUB / 8) * ks + fhi) ^ fsw) * 16;
+            if constexpr (r == 0)
+                fb[0] = *(const u32x4*)(st + b_base + ch);
+            else if constexpr (r <= FM)
+                fa[r - 1] = *(const u32x4*)(st + a_base + MF * ROWB * (r - 1) + ch);
+            else
+                fb[r - FM] = *(const u32x4*)(st + b_base + MF * ROWB * (r - FM) + ch);
         };
         // the NMMA MFMAs of one substep with chunk c of a refill interleaved
-        auto mma_refill = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], int stage, int kt, int c) {
-#pragma unroll
-            for (int t = 0; t < NMMA; ++t) {
+        // (and, with ILR, the reads of substep rks of stage rst into rfb/rfa)
+        auto mma_refill = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], int stage, int kt, int c,
+                              const unsigned char* rst, int rks, u32x4 (&rfb)[FN], u32x4 (&rfa)[FM]) {
+            static_for<0, NMMA>([&](auto tc) {
+                constexpr int t = decltype(tc)::value;
                 mfma1(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int d = 0; d < CH; ++d)
-                    if (c >= 0 && d * NMMA / CH == t) load_one(stage, kt, c * CH + d);
+                if constexpr (ILR)
+                    static_for<0, NRD>([&](auto rc) {
+                        if constexpr (decltype(rc)::value * RS == t) read_one(rst, rks, rc, rfb, rfa);
+                    });
+                static_for<0, CH>([&](auto dc) {
+                    constexpr int d = decltype(dc)::value;
+                    if constexpr (d * NMMA / CH == t)
+                        if (c >= 0) load_one(stage, kt, c * CH + d);
+                });
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
         };
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
@@ -373,20 +399,23 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             const int ns = cs + 1 == STAGES ? 0 : cs + 1;
 #pragma unroll
             for (int ks = 0; ks < KS - FD; ++ks) {
-                read_frags(s, ks + FD, fb[(ks + FD) % NSLOT], fa[(ks + FD) % NSLOT]);
+                if constexpr (!ILR) read_frags(s, ks + FD, fb[(ks + FD) % NSLOT], fa[(ks + FD) % NSLOT]);
                 __builtin_amdgcn_sched_barrier(0);
-                mma_refill(fb[ks % NSLOT], fa[ks % NSLOT], ps, kt + STAGES - 1, ks + FD < SPREAD ? ks + FD : -1);
+                mma_refill(fb[ks % NSLOT], fa[ks % NSLOT], ps, kt + STAGES - 1, ks + FD < SPREAD ? ks + FD : -1,
+                           s, ks + FD, fb[(ks + FD) % NSLOT], fa[(ks + FD) % NSLOT]);
             }
             wait_vmcnt<(STAGES - 2) * L>();       // this wave's part of tile kt + 1 has landed
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading stage cs
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!ILR)
 #pragma unroll
-            for (int j = 0; j < FD; ++j) read_frags(lds + ns * STAGE_BYTES, j, fb[j], fa[j]);
+                for (int j = 0; j < FD; ++j) read_frags(lds + ns * STAGE_BYTES, j, fb[j], fa[j]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < FD; ++j)  // head chunks of the refill of stage cs
-                mma_refill(fb[(KS - FD + j) % NSLOT], fa[(KS - FD + j) % NSLOT], cs, kt + STAGES, j < SPREAD ? j : -1);
+                mma_refill(fb[(KS - FD + j) % NSLOT], fa[(KS - FD + j) % NSLOT], cs, kt + STAGES, j < SPREAD ? j : -1,
+                           lds + ns * STAGE_BYTES, j, fb[j], fa[j]);
             // the next tile's first fragments arrived behind those MFMAs;
             // saying so here keeps the next iteration from waiting on the
             // reads it issues first

@@ -70,16 +70,17 @@ static DmaVariant dma_variant(const char* name) {
 // bf16->bf16 and f16->f16 combinations only.
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16, true>("L64E16"),
-        dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16, true>("M64E4s4m16"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true>("L64E16i"),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 8, 0, 16, true>("M64E4s4i"),
         dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true>("Q64E4m16"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 5>("M64E4f2"),
         dma_variant<256, 256, 64, 2, 2, 4, 2>("L64S2"),
         dma_variant<256, 256, 64, 2, 2, 4, 0>("L64S2X0"),
         dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4"),
-        dma_variant<256, 256, 64, 2, 2, 2, 2, 3>("L64EW4s2"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 2>("L64P2"),
     };
