@@ -149,7 +149,7 @@ __device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, 
 // refill PF steps later finds its lines in L2 instead of paying the full
 // HBM / Infinity-Cache latency with only STAGES - 1 steps of cover.
 template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0,
-          int MF = 32>
+          int MF = 32, int LDW = 0>
 __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                           void* __restrict__ C, int M, int N, int K,
                                                           int tiles_m, int tiles_n, int group_m,
@@ -318,7 +318,15 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         // covers the LDS latency.  The sched_barrier pins keep the compiler
         // from regrouping the LDS reads, loads and MFMAs.
         constexpr int KS = BK / KSUB;
-        constexpr int L = LA + LB;
+        // LDW > 0: only waves 0 .. LDW-1 issue the global->LDS loads (each a
+        // W/LDW times larger share); the others only read LDS and multiply.
+        constexpr int LW = LDW > 0 ? LDW : W;
+        static_assert(W % LW == 0 && (LW * RPI) % 16 == 0, "loader waves share the swizzle");
+        constexpr int LAW = BM / (RPI * LW), LBW = BN / (RPI * LW);
+        static_assert(LAW * RPI * LW == BM && LBW * RPI * LW == BN, "tile rows split evenly over loader waves");
+        constexpr int L = LAW + LBW;
+        const bool loader = LW == W || wave < LW;
+        const u32 lw_stride = (u32)(LW * RPI) * row_bytes;
         constexpr int NMMA = FN * FM;
         constexpr bool ILR = SCHED >= 6;  // fragment reads interleaved with the MFMAs
         constexpr int BASE = ILR ? SCHED - 4 : SCHED;
@@ -341,14 +349,16 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         // load d of this wave's share of tile kt into stage `stage` (A rows
         // first), k >= K masked as in issue()
         auto load_one = [&](int stage, int kt, int d) {
+            if (!loader) return;
             unsigned char* sbase = lds + stage * STAGE_BYTES;
             const u32 kbytes = (u32)kt * (u32)ROWB;
             const int kleft = Kf - kt * BK;
-            if (d < LA)
-                dma16(ra, sbase + (wave + d * W) * 1024, l_kc < kleft ? ld_off(d) : kOutOfRange, kbytes);
+            if (d < LAW)
+                dma16(ra, sbase + (wave + d * LW) * 1024, l_kc < kleft ? l_off + (u32)d * lw_stride : kOutOfRange,
+                      kbytes);
             else
-                dma16(rb, sbase + BM * ROWB + (wave + (d - LA) * W) * 1024,
-                      l_kc < kleft ? ld_off(d - LA) : kOutOfRange, kbytes);
+                dma16(rb, sbase + BM * ROWB + (wave + (d - LAW) * LW) * 1024,
+                      l_kc < kleft ? l_off + (u32)(d - LAW) * lw_stride : kOutOfRange, kbytes);
         };
         // fragment r of substep ks in consumption order: b0, a0 .. a[FM-1], b1 ..
         auto read_one = [&](const unsigned char* st, int ks, auto rc, u32x4 (&fb)[FN], u32x4 (&fa)[FM]) {
@@ -382,7 +392,9 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             });
         };
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
+        for (int s = 0; s < STAGES - 1; ++s)
+#pragma unroll
+            for (int d = 0; d < L; ++d) load_one(s, s, d);
         wait_vmcnt<(STAGES - 2) * L>();
         barrier_no_fence();
 #pragma unroll

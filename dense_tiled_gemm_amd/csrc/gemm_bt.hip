@@ -50,16 +50,16 @@ static int in_index(int in_dtype) { return in_dtype == GEMM_BT_BF16 ? 0 : 1; }
 static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out_dtype == GEMM_BT_BF16 ? 1 : 2); }
 
 template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32,
-          bool ALL = false>
+          bool ALL = false, int LDW = 0>
 static DmaVariant dma_variant(const char* name) {
     DmaVariant v = {name, BM, BN, BK, S, WM, WN, SWZ, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
-    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
-    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
+    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
+    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
     if constexpr (ALL) {
-        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
-        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
-        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
-        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF>;
+        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
+        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
+        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
+        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
     }
     return v;
 }
@@ -70,11 +70,12 @@ static DmaVariant dma_variant(const char* name) {
 // bf16->bf16 and f16->f16 combinations only.
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true>("L64E16i"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 4>("L64E16iL4"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 8, 0, 16, true>("M64E4s4i"),
         dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true>("Q64E4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16>("L64E16i"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 5>("M64E4f2"),
@@ -95,16 +96,16 @@ struct SkinnyVariant {
     const void* fn[2][3];
 };
 
-template <int BN, int KB, int S, int W, bool ALL = false>
+template <int BN, int KB, int S, int W, bool ALL = false, int ROT = 0>
 static SkinnyVariant skinny_variant(const char* name) {
     SkinnyVariant v = {name, BN, KB, S, W, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
-    v.fn[0][1] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BN, KB, S, W>;
-    v.fn[1][2] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BN, KB, S, W>;
+    v.fn[0][1] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BN, KB, S, W, ROT>;
+    v.fn[1][2] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BN, KB, S, W, ROT>;
     if constexpr (ALL) {
-        v.fn[0][0] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BN, KB, S, W>;
-        v.fn[0][2] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BN, KB, S, W>;
-        v.fn[1][0] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BN, KB, S, W>;
-        v.fn[1][1] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BN, KB, S, W>;
+        v.fn[0][0] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BN, KB, S, W, ROT>;
+        v.fn[0][2] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BN, KB, S, W, ROT>;
+        v.fn[1][0] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BN, KB, S, W, ROT>;
+        v.fn[1][1] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BN, KB, S, W, ROT>;
     }
     return v;
 }
@@ -117,6 +118,7 @@ static const SkinnyVariant* skinny_variants(int* count) {
         skinny_variant<8, 128, 4, 1>("S8K128x4w1"),
         skinny_variant<16, 256, 3, 1>("S16K256x3w1"),
         skinny_variant<32, 256, 6, 4>("S32K256x6"),
+        skinny_variant<16, 256, 3, 1, false, 1>("S16K256x3w1r1"),
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;

@@ -35,7 +35,7 @@
 
 namespace gbt {
 
-template <int IN, int OUT, int BN, int KB, int STAGES, int W>
+template <int IN, int OUT, int BN, int KB, int STAGES, int W, int ROT = 0>
 __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                            void* __restrict__ C, int M, int N, int K,
                                                            int vec_store) {
@@ -93,7 +93,12 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
         kc[i] = c * 8;
         is_a[i] = a;
     }
-    auto issue = [&](int stage, int kt) {
+    const int nk = (K + KB - 1) / KB;
+    // ROT > 0: workgroup g walks the K steps starting at (g * ROT) mod nk and
+    // wraps around, so that concurrent workgroups read different K offsets
+    const int k0 = ROT > 0 ? (int)(((long long)blockIdx.x * ROT) % nk) : 0;
+    auto issue = [&](int stage, int kstep) {
+        const int kt = ROT > 0 ? (kstep + k0 >= nk ? kstep + k0 - nk : kstep + k0) : kstep;
         unsigned char* sbase = lds + stage * STAGE_BYTES;
         const u32 kbytes = (u32)kt * (u32)ROWB;
         const int kleft = K - kt * KB;
@@ -135,7 +140,6 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
         }
     };
 
-    const int nk = (K + KB - 1) / KB;
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
     int cs = 0, ls = STAGES - 1;
