@@ -149,7 +149,7 @@ __device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, 
 // refill PF steps later finds its lines in L2 instead of paying the full
 // HBM / Infinity-Cache latency with only STAGES - 1 steps of cover.
 template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0,
-          int MF = 32, int LDW = 0>
+          int MF = 32, int LDW = 0, int RING5 = 0>
 __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                           void* __restrict__ C, int M, int N, int K,
                                                           int tiles_m, int tiles_n, int group_m,
@@ -174,9 +174,13 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     static_assert(BK % (2 * KSUB) == 0, "two or more MFMA k-substeps per K step");
     static_assert(PEND < 64, "vmcnt range");
     static_assert(PF == 0 || (BK == 64 && (BM + BN) % (64 * W) == 0 && SCHED == 0), "prefetch layout");
-    static_assert(STAGES * STAGE_BYTES + (PF > 0 ? W * 256 : 0) <= 160 * 1024, "LDS budget");
+    // RING5: five slots of one operand tile each instead of STAGES stages
+    constexpr int SLOT_BYTES = BM * ROWB;
+    constexpr int RING_BYTES = RING5 ? 5 * SLOT_BYTES : STAGES * STAGE_BYTES;
+    static_assert(!RING5 || (BM == BN && STAGES == 2 && SCHED == 6 && PF == 0 && RING5 <= 2), "five-slot ring layout");
+    static_assert(RING_BYTES + (PF > 0 ? W * 256 : 0) <= 160 * 1024, "LDS budget");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * STAGE_BYTES + (PF > 0 ? W * 256 : 0)];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[RING_BYTES + (PF > 0 ? W * 256 : 0)];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -260,6 +264,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     const int fsw = swz_row<CPR, SWZ>(fr);
     const int a_base = (wm * TM + fr) * ROWB;
     const int b_base = BM * ROWB + (wn * TN + fr) * ROWB;
+    const int b_base0 = (wn * TN + fr) * ROWB;  // relative to the B tile
 
     typename AB::type acc[FN][FM];
 #pragma unroll
@@ -361,36 +366,103 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
                       l_kc < kleft ? l_off + (u32)(d - LAW) * lw_stride : kOutOfRange, kbytes);
         };
         // fragment r of substep ks in consumption order: b0, a0 .. a[FM-1], b1 ..
-        auto read_one = [&](const unsigned char* st, int ks, auto rc, u32x4 (&fb)[FN], u32x4 (&fa)[FM]) {
+        // (sta, stb: the A and B tiles)
+        auto read_one = [&](const unsigned char* sta, const unsigned char* stb, int ks, auto rc, u32x4 (&fb)[FN],
+                            u32x4 (&fa)[FM]) {
             constexpr int r = decltype(rc)::value;
             const int ch = (((KSUB / 8) * ks + fhi) ^ fsw) * 16;
             if constexpr (r == 0)
-                fb[0] = *(const u32x4*)(st + b_base + ch);
+                fb[0] = *(const u32x4*)(stb + b_base0 + ch);
             else if constexpr (r <= FM)
-                fa[r - 1] = *(const u32x4*)(st + a_base + MF * ROWB * (r - 1) + ch);
+                fa[r - 1] = *(const u32x4*)(sta + a_base + MF * ROWB * (r - 1) + ch);
             else
-                fb[r - FM] = *(const u32x4*)(st + b_base + MF * ROWB * (r - FM) + ch);
+                fb[r - FM] = *(const u32x4*)(stb + b_base0 + MF * ROWB * (r - FM) + ch);
         };
-        // the NMMA MFMAs of one substep with chunk c of a refill interleaved
-        // (and, with ILR, the reads of substep rks of stage rst into rfb/rfa)
-        auto mma_refill = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], int stage, int kt, int c,
-                              const unsigned char* rst, int rks, u32x4 (&rfb)[FN], u32x4 (&rfa)[FM]) {
+        // the NMMA MFMAs of one substep; after MFMA t it issues load d of the
+        // refill if d * NMMA / CH == t (when do_load), and with ILR fragment
+        // read r of the next substep if r * RS == t
+        auto mma_step = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], bool do_load, auto&& load_d, auto&& read_r) {
             static_for<0, NMMA>([&](auto tc) {
                 constexpr int t = decltype(tc)::value;
                 mfma1(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (ILR)
                     static_for<0, NRD>([&](auto rc) {
-                        if constexpr (decltype(rc)::value * RS == t) read_one(rst, rks, rc, rfb, rfa);
+                        if constexpr (decltype(rc)::value * RS == t) read_r(rc);
                     });
                 static_for<0, CH>([&](auto dc) {
                     constexpr int d = decltype(dc)::value;
                     if constexpr (d * NMMA / CH == t)
-                        if (c >= 0) load_one(stage, kt, c * CH + d);
+                        if (do_load) load_d(d);
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
+        // chunk c of the refill of stage `stage` with tile kt, and with ILR
+        // the reads of substep rks of stage rst into rfb/rfa
+        auto mma_refill = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], int stage, int kt, int c,
+                              const unsigned char* rst, int rks, u32x4 (&rfb)[FN], u32x4 (&rfa)[FM]) {
+            mma_step(b, a, c >= 0, [&](int d) { load_one(stage, kt, c * CH + d); },
+                     [&](auto rc) { read_one(rst, rst + BM * ROWB, rks, rc, rfb, rfa); });
+        };
+        if constexpr (RING5) {
+        // Five slots of one operand tile each: A(j) sits in slot 2j mod 5 and
+        // B(j) in slot 2j + 1 mod 5.  After the barrier of step kt the slots
+        // of A(kt) and B(kt) are free; the refill then issues B(kt + 2) into
+        // A(kt)'s slot first and A(kt + 3) into B(kt)'s slot after it, so the
+        // next wait needs only the first half of the burst (the A loads are
+        // requested one step earlier than in the two-stage ring).
+        auto slot = [&](int sl) { return lds + sl * SLOT_BYTES; };
+        auto load_a = [&](int sl, int kt, int d) {
+            if (!loader) return;
+            const int kleft = Kf - kt * BK;
+            dma16(ra, slot(sl) + (wave + d * LW) * 1024, l_kc < kleft ? l_off + (u32)d * lw_stride : kOutOfRange,
+                  (u32)kt * (u32)ROWB);
+        };
+        auto load_b = [&](int sl, int kt, int d) {
+            if (!loader) return;
+            const int kleft = Kf - kt * BK;
+            dma16(rb, slot(sl) + (wave + d * LW) * 1024, l_kc < kleft ? l_off + (u32)d * lw_stride : kOutOfRange,
+                  (u32)kt * (u32)ROWB);
+        };
+        static_assert(SPREAD == 1 && FD == 1 && CH == LAW + LBW, "one refill burst per step");
+        // RING5 == 2: A(kt + 2) goes out during the first substep of step kt
+        // instead of with the refill burst after the barrier of step kt - 1
+        constexpr bool SPLIT = RING5 == 2;
+#pragma unroll
+        for (int j = 0; j < (SPLIT ? 2 : 3); ++j) {  // A0 B0 A1 B1 (A2)
+#pragma unroll
+            for (int d = 0; d < LAW; ++d) load_a(2 * j, j, d);
+            if (j < 2)
+#pragma unroll
+                for (int d = 0; d < LBW; ++d) load_b(2 * j + 1, j, d);
+        }
+        wait_vmcnt<(SPLIT ? 1 : 2) * LAW + LBW>();  // A0 and B0 have landed
+        barrier_no_fence();
+        static_for<0, NRD>([&](auto rc) { read_one(slot(0), slot(1), 0, rc, fb[0], fa[0]); });
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        int sa = 0;  // slot of A(kt); B(kt) is in the next slot
+        for (int kt = 0; kt < nk; ++kt) {
+            const int sb = sa == 4 ? 0 : sa + 1;
+            const int na = sa >= 3 ? sa - 3 : sa + 2, nb = sb >= 3 ? sb - 3 : sb + 2;
+            __builtin_amdgcn_sched_barrier(0);
+            const int sp = sa == 0 ? 4 : sa - 1;  // slot of B(kt - 1), free since the last barrier
+            mma_step(fb[0], fa[0], SPLIT, [&](int d) { if (d < LAW) load_a(sp, kt + 2, d); },
+                     [&](auto rc) { read_one(slot(sa), slot(sb), 1, rc, fb[1], fa[1]); });
+            wait_vmcnt<LAW>();                   // A(kt + 1), B(kt + 1) have landed; A(kt + 2) may not
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading A(kt), B(kt)
+            barrier_no_fence();
+            __builtin_amdgcn_sched_barrier(0);
+            mma_step(fb[1], fa[1], true,
+                     [&](int d) {
+                         if (d < LBW) load_b(sa, kt + 2, d);
+                         else if (!SPLIT) load_a(sb, kt + 3, d - LBW);
+                     },
+                     [&](auto rc) { read_one(slot(na), slot(nb), 0, rc, fb[0], fa[0]); });
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            sa = na;
+        }
+        } else {
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
 #pragma unroll
@@ -434,6 +506,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             __builtin_amdgcn_s_waitcnt(0xC07F);
             ps = cs;
             cs = ns;
+        }
         }
     } else if constexpr (SCHED == 1) {
         static_assert(W == 8 && WM == 2, "ping-pong pairs the two wave rows");

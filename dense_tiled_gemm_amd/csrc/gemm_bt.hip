@@ -50,16 +50,16 @@ static int in_index(int in_dtype) { return in_dtype == GEMM_BT_BF16 ? 0 : 1; }
 static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out_dtype == GEMM_BT_BF16 ? 1 : 2); }
 
 template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32,
-          bool ALL = false, int LDW = 0>
+          bool ALL = false, int LDW = 0, int RING5 = 0>
 static DmaVariant dma_variant(const char* name) {
     DmaVariant v = {name, BM, BN, BK, S, WM, WN, SWZ, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
-    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
-    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
+    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
     if constexpr (ALL) {
-        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
-        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
-        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
-        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW>;
+        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
     }
     return v;
 }
@@ -70,12 +70,15 @@ static DmaVariant dma_variant(const char* name) {
 // bf16->bf16 and f16->f16 combinations only.
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
-        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 4>("L64E16iL4"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 8, 0, 16, true>("M64E4s4i"),
         dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true>("Q64E4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16>("L64E16i"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, false, 4>("L64E16iL4"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, false, 0, 1>("L64E16iR5"),
+        dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, false, 4, 2>("L64E16iL4R5s"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2>("L64E"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4>("M64E4s4"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 5>("M64E4f2"),
