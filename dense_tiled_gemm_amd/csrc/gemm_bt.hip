@@ -43,6 +43,7 @@ constexpr int kGroupM = 4;
 struct DmaVariant {
     const char* name;
     int bm, bn, bk, stages, wm, wn, swz;
+    int lds_bytes;  // the ring: `stages` A+B stages, or five operand-tile slots
     const void* fn[2][3];
 };
 
@@ -52,7 +53,8 @@ static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out
 template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32,
           bool ALL = false, int LDW = 0, int RING5 = 0>
 static DmaVariant dma_variant(const char* name) {
-    DmaVariant v = {name, BM, BN, BK, S, WM, WN, SWZ, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
+    DmaVariant v = {name, BM, BN, BK, RING5 ? 5 : S, WM, WN, SWZ, RING5 ? 5 * BM * BK * 2 : S * (BM + BN) * BK * 2,
+                    {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
     v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
     v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
     if constexpr (ALL) {
@@ -259,7 +261,7 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         p->bk = v.bk;
         p->stages = v.stages;
         p->threads = 64 * v.wm * v.wn;
-        p->lds_bytes = v.stages * (v.bm + v.bn) * v.bk * 2;
+        p->lds_bytes = v.lds_bytes;
     } else {
         const TileCfg c = big ? kCfgL : kCfgM;
         p->kernel = KIND_TILED;

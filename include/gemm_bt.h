@@ -92,7 +92,8 @@ typedef struct {
     int vec;          /* elements per global load: 8 (16 bytes), 2 or 1 */
     int group_m;      /* tile-rows per group in the grouped tile order */
     int ksplit;       /* waves that split K inside a workgroup (skinny kernel) */
-    int stages;       /* LDS pipeline depth (tiled kernels) */
+    int stages;       /* LDS pipeline depth: A+B stages (tiled kernels), or for the 256x256 tile the 5 slots of
+                         its ring of single-operand tiles */
     int lds_bytes;    /* LDS per workgroup */
     int64_t tiles_m, tiles_n;
     int64_t grid;     /* workgroups launched */

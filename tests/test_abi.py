@@ -65,7 +65,10 @@ def test_no_device_status_without_gpu():
 def test_plan_choices():
     p = gb.gemm_bt_plan(4096, 4096, 4096, gb.BF16, gb.BF16)
     assert (p.kernel, p.bm, p.bn, p.vec, p.grid) == (4, 256, 256, 8, 256)
-    assert p.lds_bytes == p.stages * (p.bm + p.bn) * p.bk * 2 <= 160 * 1024
+    # five-slot ring: one A or B tile (256 rows x 64 K) per slot, all of LDS
+    assert (p.stages, p.lds_bytes) == (5, 5 * p.bm * p.bk * 2) and p.lds_bytes == 160 * 1024
+    p = gb.gemm_bt_plan(1024, 1024, 4096, gb.BF16, gb.BF16)  # 128x128 tiles: A+B stages
+    assert p.bm == 128 and p.lds_bytes == p.stages * (p.bm + p.bn) * p.bk * 2 <= 160 * 1024
     p = gb.gemm_bt_plan(1024, 4096, 4096, gb.F16, gb.F16)
     assert (p.kernel, p.bm, p.bn, p.grid) == (4, 128, 128, 256)
     p = gb.gemm_bt_plan(1000, 3000, 2050, gb.BF16, gb.F32)  # 4-byte rows: DMA kernel + K tail
