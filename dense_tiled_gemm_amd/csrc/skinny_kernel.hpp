@@ -79,16 +79,27 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(const u16* __restrict__
             for (int b = 0; b < NB; ++b) acc[b] = Mfma<IN>::m16x16x32(fb[buf][u][b], fa[buf][u], acc[b]);
     };
 
+    // The loop is unrolled by two so that the register buffer index is a
+    // constant: indexed by a variable, fa/fb would be placed in scratch.
     int kb = kb_begin;
     if (kb < kb_end) {
         load_batch(0, kb);
-        int buf = 0;
-        for (; kb + U < kb_end; kb += U) {
-            load_batch(buf ^ 1, kb + U);
-            mma_batch(buf);
-            buf ^= 1;
+        for (;;) {
+            if (kb + U >= kb_end) {
+                mma_batch(0);
+                break;
+            }
+            load_batch(1, kb + U);
+            mma_batch(0);
+            kb += U;
+            if (kb + U >= kb_end) {
+                mma_batch(1);
+                break;
+            }
+            load_batch(0, kb + U);
+            mma_batch(1);
+            kb += U;
         }
-        mma_batch(buf);
     }
 
 #pragma unroll
