@@ -5,7 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 links or calls it, and the two share no code.
 
 The arithmetic lives in ``gemm_ref.c`` (plain C, fp64 accumulation in
-increasing k, exact 16-bit decoders, IEEE round-to-nearest-even encoders);
+increasing k, exact decoders for the 16-bit and OCP 8-bit input formats, IEEE
+round-to-nearest-even encoders);
 this module only builds it with gcc, loads it with ctypes and marshals numpy
 arrays.  The tolerance rules are in ``oracle.tolerance``.
 
@@ -24,8 +25,8 @@ import threading
 
 import numpy as np
 
-F32, F16, BF16 = 0, 1, 2
-_NAMES = {"f32": F32, "f16": F16, "bf16": BF16}
+F32, F16, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
+_NAMES = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": FP8_E4M3, "e5m2": FP8_E5M2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_ref.c")
@@ -77,7 +78,10 @@ def dtype_code(d) -> int:
 
 
 def _u16(x: np.ndarray) -> np.ndarray:
+    """Input bits as uint16 words: 16-bit codes as they are, 8-bit codes widened."""
     x = np.ascontiguousarray(x)
+    if x.dtype == np.uint8:
+        return x.astype(np.uint16)
     if x.dtype != np.uint16:
         x = x.view(np.uint16)
     return x
@@ -92,7 +96,7 @@ def max_threads() -> int:
 
 
 def decode(bits: np.ndarray, in_dtype) -> np.ndarray:
-    """Exact value of each bf16/f16 bit pattern, as float64."""
+    """Exact value of each bf16/f16/e4m3/e5m2 bit pattern, as float64."""
     b = _u16(bits)
     out = np.empty(b.shape, dtype=np.float64)
     _load().orc_decode(_ptr(b), b.size, dtype_code(in_dtype), _ptr(out))

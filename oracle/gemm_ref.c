@@ -17,10 +17,17 @@
  *     section 4.1' compares a bf16 kernel against float64 arithmetic on the
  *     same bf16 inputs, which is exactly what this file does.
  *
- * Arithmetic: each 16-bit input is decoded exactly to double; every product
- * of two bf16 or two f16 values is exact in double (at most 22 significant
- * bits); the sum runs in increasing k with plain double additions (built with
- * -ffp-contract=off, no fast-math), so the only error is the fp64 summation.
+ * Arithmetic: each input is decoded exactly to double; every product of two
+ * bf16, two f16 or two 8-bit float values is exact in double (at most 22
+ * significant bits); the sum runs in increasing k with plain double additions
+ * (built with -ffp-contract=off, no fast-math), so the only error is the fp64
+ * summation.
+ *
+ * 8-bit inputs (OCP 8-bit floating point formats; the inputs are passed as
+ * 16-bit words holding the code in the low byte): E4M3 has 1 sign, 4 exponent
+ * (bias 7) and 3 fraction bits, no infinities, and S.1111.111 is NaN; E5M2 has
+ * 1 sign, 5 exponent (bias 15) and 2 fraction bits with IEEE-style infinities
+ * and NaNs.  Both have subnormals at the minimum exponent.
  *
  * Output rounding (used by the bit-exact tests): IEEE round-to-nearest-even
  * from the double value straight to the output format, overflow to +-Inf.
@@ -33,7 +40,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_FP8_E4M3 = 3, ORC_FP8_E5M2 = 4 };
 
 /* ---- exact decoders: 16-bit storage -> double ---------------------------- */
 
@@ -69,8 +76,53 @@ static double decode_f16(uint16_t h) {
     return sign ? -v : v;
 }
 
+/* OCP E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits; exponent 15 with
+   fraction 7 is NaN, there is no infinity (largest finite: 448). */
+static double decode_e4m3(uint16_t h) {
+    if (h > 0xFF) return NAN;
+    const int sign = h >> 7;
+    const int e = (h >> 3) & 0xF;
+    const int f = h & 0x7;
+    double v;
+    if (e == 0xF && f == 0x7) {
+        v = NAN;
+    } else if (e == 0) {
+        v = ldexp((double)f, -6 - 3);              /* subnormal: f * 2^-9 */
+    } else {
+        v = ldexp((double)(8 + f), e - 7 - 3);     /* (1.f) * 2^(e-7) */
+    }
+    return sign ? -v : v;
+}
+
+/* OCP E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits; exponent 31 is
+   infinity (fraction 0) or NaN. */
+static double decode_e5m2(uint16_t h) {
+    if (h > 0xFF) return NAN;
+    const int sign = h >> 7;
+    const int e = (h >> 2) & 0x1F;
+    const int f = h & 0x3;
+    double v;
+    if (e == 0x1F) {
+        v = f ? NAN : INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)f, -14 - 2);             /* subnormal: f * 2^-16 */
+    } else {
+        v = ldexp((double)(4 + f), e - 15 - 2);    /* (1.f) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+static int valid_in(int dtype) {
+    return dtype == ORC_BF16 || dtype == ORC_F16 || dtype == ORC_FP8_E4M3 || dtype == ORC_FP8_E5M2;
+}
+
 static double decode(uint16_t h, int dtype) {
-    return dtype == ORC_BF16 ? decode_bf16(h) : decode_f16(h);
+    switch (dtype) {
+        case ORC_BF16: return decode_bf16(h);
+        case ORC_FP8_E4M3: return decode_e4m3(h);
+        case ORC_FP8_E5M2: return decode_e5m2(h);
+        default: return decode_f16(h);
+    }
 }
 
 /* ---- round-to-nearest-even from double ----------------------------------- */
@@ -171,11 +223,11 @@ void orc_round(const double* x, int64_t n, int out_dtype, void* out) {
 
 /* Exact value of every 16-bit pattern, filled once from the decoders above so
    the loops below index a table instead of re-decoding each operand. */
-static double g_table[2][65536];
-static int g_table_ready[2];
+static double g_table[4][65536];
+static int g_table_ready[4];
 
 static const double* table_for(int dtype) {
-    const int t = dtype == ORC_BF16 ? 1 : 0;
+    const int t = dtype == ORC_BF16 ? 1 : (dtype == ORC_FP8_E4M3 ? 2 : (dtype == ORC_FP8_E5M2 ? 3 : 0));
     if (!g_table_ready[t]) {
 #pragma omp critical(orc_table)
         {
@@ -212,7 +264,7 @@ static double norm_row(const uint16_t* a, int64_t K, const double* tab) {
 int orc_gemm_bt(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
                 int in_dtype, double* C, double* nA, double* nB, int nthreads) {
     if (M < 0 || N < 0 || K < 0) return -1;
-    if (in_dtype != ORC_BF16 && in_dtype != ORC_F16) return -1;
+    if (!valid_in(in_dtype)) return -1;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -241,7 +293,7 @@ int orc_gemm_bt_entries(const uint16_t* A, const uint16_t* B, int64_t M, int64_t
                         int in_dtype, const int64_t* I, const int64_t* J, int64_t n,
                         double* out, int nthreads) {
     if (M < 0 || N < 0 || K < 0 || n < 0) return -1;
-    if (in_dtype != ORC_BF16 && in_dtype != ORC_F16) return -1;
+    if (!valid_in(in_dtype)) return -1;
     for (int64_t t = 0; t < n; ++t)
         if (I[t] < 0 || I[t] >= M || J[t] < 0 || J[t] >= N) return -1;
 #ifdef _OPENMP
@@ -260,7 +312,7 @@ int orc_gemm_bt_entries(const uint16_t* A, const uint16_t* B, int64_t M, int64_t
 int orc_row_norms(const uint16_t* X, int64_t R, int64_t K, int in_dtype, double* out,
                   int nthreads) {
     if (R < 0 || K < 0) return -1;
-    if (in_dtype != ORC_BF16 && in_dtype != ORC_F16) return -1;
+    if (!valid_in(in_dtype)) return -1;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else

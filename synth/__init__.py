@@ -1,19 +1,23 @@
 """Seeded synthetic inputs for C = A·Bᵀ, shared by the oracle side and the GPU side.
 
-This module draws random numbers and rounds them to the 16-bit input format.
+This module draws random numbers and rounds them to the input format.
 It holds none of the product's arithmetic: no dot products, no accumulation,
-no output rounding.  Each generator returns raw bit patterns (uint16 arrays),
-so the very same bits feed the GPU kernel and the CPU oracle.
+no output rounding.  Each generator returns raw bit patterns (uint16 arrays for
+the 16-bit formats, uint8 for the 8-bit ones), so the very same bits feed the
+GPU kernel and the CPU oracle.
 
 Recipe (also stated in the design notes):
   * ``numpy.random.default_rng(seed)`` (PCG64); A is drawn first (M×K, row-major
     order), then B (N×K, row-major order — B is stored transposed).
   * distributions: ``normal`` N(0, 1); ``normal_scaled`` N(0, σ=1/√K);
     ``uniform`` U[-1, 1) via ``rng.uniform(-1, 1)``; ``int`` uniform integers in
-    [-4, 4] (exact in bf16 and f16, so fp32 accumulation is exact).
+    [-4, 4] (exact in every input format, so fp32 accumulation is exact).
   * rounding: bf16 values go float64 → float32 (numpy, round-to-nearest-even)
     → bfloat16 (torch CPU conversion, round-to-nearest-even); f16 values go
-    float64 → float16 directly (numpy, round-to-nearest-even).
+    float64 → float16 directly (numpy, round-to-nearest-even); e4m3 / e5m2
+    values go float64 → float32 → torch ``float8_e4m3fn`` / ``float8_e5m2``
+    (torch CPU conversion, round-to-nearest-even; the distributions used stay
+    far inside both formats' range).
 
 The workloads are the matrix products the pages measure: 4096³ square
 ("Optimizing Blackwell matrix multiplication in Mojo (part 2)", section
@@ -28,7 +32,7 @@ import dataclasses
 
 import numpy as np
 
-IN_DTYPES = ("bf16", "f16")
+IN_DTYPES = ("bf16", "f16", "e4m3", "e5m2")
 OUT_DTYPES = ("f32", "f16", "bf16")
 
 
@@ -50,7 +54,8 @@ class Workload:
     @property
     def compulsory_bytes(self) -> int:
         osz = 4 if self.out_dtype == "f32" else 2
-        return (self.M * self.K + self.N * self.K) * 2 + self.M * self.N * osz
+        isz = 1 if self.in_dtype in ("e4m3", "e5m2") else 2
+        return (self.M * self.K + self.N * self.K) * isz + self.M * self.N * osz
 
     def integer_twin(self) -> "Workload":
         return dataclasses.replace(self, name=self.name + "_int", dist="int", seed=self.seed + 100)
@@ -81,13 +86,23 @@ def _to_f16_bits(x64: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x64).astype(np.float16).view(np.uint16)
 
 
+def _to_fp8_bits(x64: np.ndarray, in_dtype: str) -> np.ndarray:
+    import torch  # CPU conversion only
+
+    f32 = np.ascontiguousarray(x64, dtype=np.float32)
+    t = torch.from_numpy(f32).to(torch.float8_e4m3fn if in_dtype == "e4m3" else torch.float8_e5m2)
+    return t.view(torch.uint8).numpy().copy()
+
+
 def round_bits(x64: np.ndarray, in_dtype: str) -> np.ndarray:
-    """Round float64 values to the 16-bit input format, returning raw bits."""
+    """Round float64 values to the input format, returning raw bits."""
     if in_dtype == "bf16":
         return _to_bf16_bits(x64)
     if in_dtype == "f16":
         return _to_f16_bits(x64)
-    raise ValueError("in_dtype must be bf16 or f16")
+    if in_dtype in ("e4m3", "e5m2"):
+        return _to_fp8_bits(x64, in_dtype)
+    raise ValueError("in_dtype must be bf16, f16, e4m3 or e5m2")
 
 
 def _draw(rng: np.random.Generator, shape, dist: str, K: int) -> np.ndarray:
@@ -103,7 +118,7 @@ def _draw(rng: np.random.Generator, shape, dist: str, K: int) -> np.ndarray:
 
 
 def make(M: int, N: int, K: int, in_dtype: str, dist: str, seed: int):
-    """Return (a_bits (M,K) uint16, b_bits (N,K) uint16)."""
+    """Return (a_bits (M,K), b_bits (N,K)): uint16 for 16-bit inputs, uint8 for 8-bit ones."""
     rng = np.random.default_rng(seed)
     a = _draw(rng, (M, K), dist, K)
     b = _draw(rng, (N, K), dist, K)

@@ -4,7 +4,9 @@ The oracle is checked against things other than itself:
   * hand-computed products (tests/golden/hand_products.txt);
   * the IEEE-754 definitions of the 16-bit formats (tests/golden/*.txt) and the
     library conversions of numpy (float16) and torch-CPU (bfloat16), exhaustively
-    over all 65536 bit patterns for decoding;
+    over all 65536 bit patterns for decoding; the OCP 8-bit formats against
+    torch-CPU float8_e4m3fn / float8_e5m2 over all 256 codes, and their special
+    values;
   * exact rational brute force (fractions.Fraction) on tiny shapes, within the
     fp64 summation bound, and equal on integer inputs;
   * closed forms: identity, all-ones, zero and permutation operands;
@@ -51,8 +53,14 @@ def parse_products():
     return cases
 
 
+FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
 def indep_decode(bits, in_dtype):
-    """Library decode (numpy float16 / torch bfloat16), independent of the oracle's C decoders."""
+    """Library decode (numpy float16 / torch bfloat16 / torch float8), independent of the oracle's C decoders."""
+    if in_dtype in FP8:
+        b8 = np.ascontiguousarray(bits).astype(np.uint8)
+        return torch.from_numpy(b8.copy()).view(FP8[in_dtype]).to(torch.float64).numpy()
     b = np.ascontiguousarray(bits).view(np.uint16)
     if in_dtype == "f16":
         return b.view(np.float16).astype(np.float64)
@@ -62,7 +70,7 @@ def indep_decode(bits, in_dtype):
 
 # ---------------------------------------------------------------- golden fixtures
 
-@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "e4m3"])  # the fixture's inputs are not all exact in e5m2
 def test_hand_products(in_dtype):
     for name, A, B, C in parse_products():
         a = synth.round_bits(A, in_dtype)
@@ -111,13 +119,34 @@ def test_golden_rne_cases():
 
 def test_decode_exhaustive_vs_libraries():
     allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    for d in ("bf16", "f16"):
-        got = oracle.decode(allbits, d)
-        want = indep_decode(allbits, d)
+    codes = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    for d, bits in (("bf16", allbits), ("f16", allbits), ("e4m3", codes), ("e5m2", codes)):
+        got = oracle.decode(bits, d)
+        want = indep_decode(bits, d)
         nan = np.isnan(want)
-        assert np.array_equal(np.isnan(got), nan)
-        assert np.array_equal(got[~nan], want[~nan])
-        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+        assert np.array_equal(np.isnan(got), nan), d
+        assert np.array_equal(got[~nan], want[~nan]), d
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), d
+
+
+def test_fp8_special_values():
+    # OCP 8-bit formats: E4M3 has no infinity, S.1111.111 is NaN and 448 is the
+    # largest finite value; E5M2 follows IEEE (infinity at exponent 31,
+    # fraction 0).  Smallest subnormals 2^-9 and 2^-16, smallest normals
+    # 2^-6 and 2^-14.
+    e4 = {0x00: 0.0, 0x80: -0.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5, 0x7E: 448.0,
+          0xFE: -448.0, 0x7F: math.nan, 0xFF: math.nan, 0x77: 240.0, 0x48: 4.0}
+    e5 = {0x00: 0.0, 0x01: 2.0 ** -16, 0x04: 2.0 ** -14, 0x3C: 1.0, 0x3E: 1.5, 0x7B: 57344.0,
+          0x7C: math.inf, 0xFC: -math.inf, 0x7D: math.nan, 0x7F: math.nan, 0x44: 4.0}
+    for d, table in (("e4m3", e4), ("e5m2", e5)):
+        codes = np.array(list(table), dtype=np.uint8)
+        got = oracle.decode(codes, d)
+        for c, g in zip(table, got):
+            want = table[c]
+            if math.isnan(want):
+                assert math.isnan(g), (d, hex(c))
+            else:
+                assert g == want and math.copysign(1, g) == math.copysign(1, want), (d, hex(c), g, want)
 
 
 def test_round_f16_vs_numpy():
@@ -195,7 +224,7 @@ def _exact_products(a_val, b_val):
     return C, S
 
 
-@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "e4m3", "e5m2"])
 def test_brute_force_random_tiny(in_dtype):
     rng = np.random.default_rng(21)
     for trial in range(25):
@@ -209,7 +238,7 @@ def test_brute_force_random_tiny(in_dtype):
                 assert abs(Fraction(c[i, j]) - C[i][j]) <= Fraction(gamma(K) * S[i, j]), (trial, i, j)
 
 
-@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "e4m3", "e5m2"])
 def test_brute_force_integer_exact(in_dtype):
     for trial in range(10):
         M, N, K = 3 + trial % 4, 2 + trial % 5, 1 + 3 * trial
@@ -231,7 +260,7 @@ def test_brute_force_cancellation():
 
 # ---------------------------------------------------------------- closed forms
 
-@pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "e4m3", "e5m2"])
 def test_identity_B(in_dtype):
     M, K = 37, 45
     a, _ = synth.make(M, 1, K, in_dtype, "normal", seed=5)
@@ -294,7 +323,8 @@ def test_empty_shapes():
 # ---------------------------------------------------------------- library cross-check
 
 @pytest.mark.parametrize("in_dtype,shape", [("bf16", (64, 80, 96)), ("f16", (33, 65, 127)),
-                                            ("bf16", (512, 512, 512))])
+                                            ("bf16", (512, 512, 512)), ("e4m3", (70, 90, 160)),
+                                            ("e5m2", (65, 33, 256))])
 def test_vs_numpy_matmul(in_dtype, shape):
     M, N, K = shape
     a, b = synth.make(M, N, K, in_dtype, "normal", seed=8)
