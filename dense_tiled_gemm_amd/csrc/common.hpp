@@ -14,6 +14,8 @@ typedef unsigned short u16;
 typedef unsigned int u32;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef u32 u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -98,6 +100,34 @@ struct Mfma<GEMM_BT_F16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
+};
+
+// OCP 8-bit float inputs: v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales
+// (exponent 127, i.e. 2^0) on both operands.  Each lane supplies 32 bytes of
+// one row (the same k bytes of A and of B, so any lane order of k gives the
+// full sum); the accumulator layout is that of the 16-bit 32x32 MFMAs.
+template <int FMT>
+struct MfmaF8 {
+    __device__ static inline f32x16 m32x32x64(u32x8 a, u32x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
+                                                               c, FMT, FMT, 0, 127, 0, 127);
+    }
+};
+template <>
+struct Mfma<GEMM_BT_FP8_E4M3> : MfmaF8<0> {};  // operand format 0: E4M3
+template <>
+struct Mfma<GEMM_BT_FP8_E5M2> : MfmaF8<1> {};  // operand format 1: E5M2
+
+// Bytes per input element, and the per-lane MFMA operand fragment: 8 elements
+// (16 bytes) of 16-bit data, 32 elements (32 bytes) of 8-bit data.
+constexpr int in_size(int in) { return in == GEMM_BT_FP8_E4M3 || in == GEMM_BT_FP8_E5M2 ? 1 : 2; }
+template <int ESZ>
+struct FragT {
+    typedef u32x4 type;
+};
+template <>
+struct FragT<1> {
+    typedef u32x8 type;
 };
 
 // 8 consecutive 16-bit elements of one row, starting at byte offset `off`

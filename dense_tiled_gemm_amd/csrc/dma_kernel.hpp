@@ -155,18 +155,24 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
                                                           int tiles_m, int tiles_n, int group_m,
                                                           int vec_store) {
     constexpr int W = WM * WN;
-    constexpr int CPR = BK / 8;          // 16-byte chunks per tile row
-    constexpr int ROWB = BK * 2;         // bytes per tile row
+    constexpr int ESZ = in_size(IN);     // bytes per input element (2, or 1 for 8-bit floats)
+    constexpr int EPC = 16 / ESZ;        // elements per 16-byte chunk
+    constexpr int ROWB = BK * ESZ;       // bytes per tile row
+    constexpr int CPR = ROWB / 16;       // 16-byte chunks per tile row
     constexpr int RPI = 1024 / ROWB;     // tile rows per wave load instruction
     constexpr int LA = BM / (RPI * W);   // A load instructions per wave per stage
     constexpr int LB = BN / (RPI * W);
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / MF, FN = TN / MF;
-    constexpr int KSUB = 512 / MF;       // K per MFMA: 16 (32x32x16) or 32 (16x16x32)
+    // K per MFMA: 16-bit inputs 16 (32x32x16) or 32 (16x16x32); 8-bit inputs 64 (32x32x64)
+    constexpr int KSUB = (512 / MF) * (ESZ == 2 ? 1 : 4);
+    typedef typename FragT<ESZ>::type Frag;
     constexpr int STAGE_BYTES = (BM + BN) * ROWB;
     constexpr int PFI = PF > 0 ? (BM + BN) / (64 * W) : 0;  // prefetch instructions per wave per step
     constexpr int PEND = (STAGES - 2) * (LA + LB + PFI) + PFI;
-    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static_assert(ROWB == 64 || ROWB == 128, "tile rows of 64 or 128 bytes");
+    static_assert(ESZ == 2 || MF == 32, "8-bit inputs use the 32x32x64 MFMA");
+    static_assert((64 / MF) * (2 / ESZ) * 16 == KSUB * ESZ, "the lanes' fragments cover one substep's bytes once");
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert(LA * RPI * W == BM && LB * RPI * W == BN, "tile rows must split evenly over waves");
     static_assert(MF == 32 || MF == 16, "MFMA 32x32x16 or 16x16x32");
@@ -190,13 +196,13 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
     const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
-    const i32x4 ra = rsrc_words(A + (size_t)m0 * K, (u32)rows_a * (u32)K * 2u);
-    const i32x4 rb = rsrc_words(B + (size_t)n0 * K, (u32)rows_b * (u32)K * 2u);
-    const u32 row_bytes = (u32)K * 2u;
+    const u32 row_bytes = (u32)K * (u32)ESZ;
+    const i32x4 ra = rsrc_words((const unsigned char*)A + (size_t)m0 * row_bytes, (u32)rows_a * row_bytes);
+    const i32x4 rb = rsrc_words((const unsigned char*)B + (size_t)n0 * row_bytes, (u32)rows_b * row_bytes);
     // Only whole 16-byte chunks go through the LDS DMA: k < Kf.  When rows are
     // 4-byte aligned but K % 8 != 0, the last K - Kf (2, 4 or 6) elements of
     // every row are added after the loop (see the tail below).
-    const int Kf = K & ~7;
+    const int Kf = K & ~(EPC - 1);
 
     // Loader geometry.  Wave instruction i of this wave fills row block
     // j = wave + i*W (rows j*RPI .. j*RPI+RPI-1 of the tile); lane L writes
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     // rather than held in registers (they are one add each).
     static_assert((W * RPI) % 16 == 0, "a wave's row blocks share one swizzle");
     const int lchunk = lphys ^ swz_row<CPR, SWZ>(wave * RPI + lrow);
-    const int l_kc = lchunk * 8;  // first K index (within a tile) of the lane's chunk
+    const int l_kc = lchunk * EPC;  // first K index (within a tile) of the lane's chunk
     u32 l_off = (u32)(wave * RPI + lrow) * row_bytes + (u32)lchunk * 16u;
     const u32 i_stride = (u32)(W * RPI) * row_bytes;
     auto ld_off = [&](int i) { return l_off + (u32)i * i_stride; };
@@ -277,18 +283,32 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     // Operand fragments are double-buffered in registers: the LDS reads for
     // k-substep ks+1 are issued before the MFMAs of substep ks, so their
     // latency hides behind 8 MFMAs instead of stalling the wave.
-    auto read_frags = [&](const unsigned char* s, int ks, u32x4 (&fb)[FN], u32x4 (&fa)[FM]) {
-        const int ch = (((KSUB / 8) * ks + fhi) ^ fsw) * 16;
-#pragma unroll
-        for (int i = 0; i < FN; ++i) fb[i] = *(const u32x4*)(s + b_base + MF * ROWB * i + ch);
-#pragma unroll
-        for (int j = 0; j < FM; ++j) fa[j] = *(const u32x4*)(s + a_base + MF * ROWB * j + ch);
+    // The lane's fragment of k-substep ks from the row at `rowp`: one 16-byte
+    // chunk (16-bit inputs) or two consecutive ones (8-bit inputs), logical
+    // chunks (KSUB*ESZ/16)*ks + fhi*CPL + j, stored at chunk ^ fsw.
+    auto ld_frag = [&](const unsigned char* rowp, int ks) -> Frag {
+        constexpr int CPL = 2 / ESZ;  // chunks per lane per fragment
+        const int c0 = (KSUB * ESZ / 16) * ks + fhi * CPL;
+        if constexpr (CPL == 1) {
+            return *(const u32x4*)(rowp + ((c0 ^ fsw) * 16));
+        } else {
+            const u32x4 lo = *(const u32x4*)(rowp + ((c0 ^ fsw) * 16));
+            const u32x4 hi = *(const u32x4*)(rowp + (((c0 + 1) ^ fsw) * 16));
+            return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
     };
-    auto mfma1 = [&](const u32x4& b, const u32x4& a, typename AB::type& c) {
-        if constexpr (MF == 32) c = Mfma<IN>::m32x32x16(b, a, c);
+    auto read_frags = [&](const unsigned char* s, int ks, Frag (&fb)[FN], Frag (&fa)[FM]) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) fb[i] = ld_frag(s + b_base + MF * ROWB * i, ks);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) fa[j] = ld_frag(s + a_base + MF * ROWB * j, ks);
+    };
+    auto mfma1 = [&](const Frag& b, const Frag& a, typename AB::type& c) {
+        if constexpr (ESZ == 1) c = Mfma<IN>::m32x32x64(b, a, c);
+        else if constexpr (MF == 32) c = Mfma<IN>::m32x32x16(b, a, c);
         else c = Mfma<IN>::m16x16x32(b, a, c);
     };
-    auto mma = [&](const u32x4 (&fb)[FN], const u32x4 (&fa)[FM]) {
+    auto mma = [&](const Frag (&fb)[FN], const Frag (&fa)[FM]) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -297,7 +317,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     auto compute = [&](int stage) {
         const unsigned char* s = lds + stage * STAGE_BYTES;
         constexpr int KS = BK / KSUB;
-        u32x4 fb0[FN], fa0[FM], fb1[FN], fa1[FM];
+        Frag fb0[FN], fa0[FM], fb1[FN], fa1[FM];
         read_frags(s, 0, fb0, fa0);
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2) {
@@ -350,7 +370,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         constexpr int HEADC = FD < SPREAD ? FD : SPREAD;  // chunks issued after the barrier
         static_assert(KS % NSLOT == 0 && KS > FD && PF == 0, "fragment buffers rotate per substep");
         static_assert(L % SPREAD == 0 && SPREAD <= KS, "refill chunks");
-        u32x4 fb[NSLOT][FN], fa[NSLOT][FM];
+        Frag fb[NSLOT][FN], fa[NSLOT][FM];
         // load d of this wave's share of tile kt into stage `stage` (A rows
         // first), k >= K masked as in issue()
         auto load_one = [&](int stage, int kt, int d) {
@@ -367,21 +387,20 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         };
         // fragment r of substep ks in consumption order: b0, a0 .. a[FM-1], b1 ..
         // (sta, stb: the A and B tiles)
-        auto read_one = [&](const unsigned char* sta, const unsigned char* stb, int ks, auto rc, u32x4 (&fb)[FN],
-                            u32x4 (&fa)[FM]) {
+        auto read_one = [&](const unsigned char* sta, const unsigned char* stb, int ks, auto rc, Frag (&fb)[FN],
+                            Frag (&fa)[FM]) {
             constexpr int r = decltype(rc)::value;
-            const int ch = (((KSUB / 8) * ks + fhi) ^ fsw) * 16;
             if constexpr (r == 0)
-                fb[0] = *(const u32x4*)(stb + b_base0 + ch);
+                fb[0] = ld_frag(stb + b_base0, ks);
             else if constexpr (r <= FM)
-                fa[r - 1] = *(const u32x4*)(sta + a_base + MF * ROWB * (r - 1) + ch);
+                fa[r - 1] = ld_frag(sta + a_base + MF * ROWB * (r - 1), ks);
             else
-                fb[r - FM] = *(const u32x4*)(stb + b_base0 + MF * ROWB * (r - FM) + ch);
+                fb[r - FM] = ld_frag(stb + b_base0 + MF * ROWB * (r - FM), ks);
         };
         // the NMMA MFMAs of one substep; after MFMA t it issues load d of the
         // refill if d * NMMA / CH == t (when do_load), and with ILR fragment
         // read r of the next substep if r * RS == t
-        auto mma_step = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], bool do_load, auto&& load_d, auto&& read_r) {
+        auto mma_step = [&](const Frag (&b)[FN], const Frag (&a)[FM], bool do_load, auto&& load_d, auto&& read_r) {
             static_for<0, NMMA>([&](auto tc) {
                 constexpr int t = decltype(tc)::value;
                 mfma1(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
@@ -400,8 +419,8 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         };
         // chunk c of the refill of stage `stage` with tile kt, and with ILR
         // the reads of substep rks of stage rst into rfb/rfa
-        auto mma_refill = [&](const u32x4 (&b)[FN], const u32x4 (&a)[FM], int stage, int kt, int c,
-                              const unsigned char* rst, int rks, u32x4 (&rfb)[FN], u32x4 (&rfa)[FM]) {
+        auto mma_refill = [&](const Frag (&b)[FN], const Frag (&a)[FM], int stage, int kt, int c,
+                              const unsigned char* rst, int rks, Frag (&rfb)[FN], Frag (&rfa)[FM]) {
             mma_step(b, a, c >= 0, [&](int d) { load_one(stage, kt, c * CH + d); },
                      [&](auto rc) { read_one(rst, rst + BM * ROWB, rks, rc, rfb, rfa); });
         };
@@ -546,7 +565,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         // 2t+1, when both groups are done reading tile t-1; wm = 0 waits for
         // tile t+1 (allowing STAGES-2 younger tiles in flight) before barrier
         // 2t+3, after which it reads tile t+1.
-        u32x4 fb[KS][FN], fa[KS][FM];
+        Frag fb[KS][FN], fa[KS][FM];
         if (grp == 0) {
 #pragma unroll
             for (int t = 0; t < STAGES - 1; ++t) issue_g0(t, t);
@@ -596,7 +615,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     }
     wait_vmcnt<0>();  // the ring's last (out-of-range) loads still write LDS
 
-    if (Kf != K) {
+    if (ESZ == 2 && Kf != K) {
         // K tail: the last K - Kf (2, 4 or 6) elements of every row form one
         // more K tile, zero-padded, written into LDS stage 0 in the same
         // swizzled layout and multiplied like the others.  It comes after all
@@ -621,7 +640,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             *(u32x4*)(lds + r * ROWB + ((c ^ swz_row<CPR, SWZ>(r)) * 16)) = u32x4{v[0], v[1], v[2], v[3]};
         }
         __syncthreads();
-        u32x4 tb[FN], ta[FM];
+        Frag tb[FN], ta[FM];
 #pragma unroll
         for (int ks = 0; ks < BK / KSUB; ++ks) {
             read_frags(lds, ks, tb, ta);

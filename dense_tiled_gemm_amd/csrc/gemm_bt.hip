@@ -44,37 +44,56 @@ struct DmaVariant {
     const char* name;
     int bm, bn, bk, stages, wm, wn, swz;
     int lds_bytes;  // the ring: `stages` A+B stages, or five operand-tile slots
-    const void* fn[2][3];
+    const void* fn[4][3];  // [bf16, f16, e4m3, e5m2][f32, bf16, f16]
 };
 
-static int in_index(int in_dtype) { return in_dtype == GEMM_BT_BF16 ? 0 : 1; }
+static bool is_fp8(int in_dtype) { return in_dtype == GEMM_BT_FP8_E4M3 || in_dtype == GEMM_BT_FP8_E5M2; }
+static int in_index(int in_dtype) {
+    return in_dtype == GEMM_BT_BF16 ? 0 : (in_dtype == GEMM_BT_F16 ? 1 : (in_dtype == GEMM_BT_FP8_E4M3 ? 2 : 3));
+}
 static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out_dtype == GEMM_BT_BF16 ? 1 : 2); }
 
 template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32,
-          bool ALL = false, int LDW = 0, int RING5 = 0>
+          bool ALL = false, int LDW = 0, int RING5 = 0, bool F8 = false>
 static DmaVariant dma_variant(const char* name) {
-    DmaVariant v = {name, BM, BN, BK, RING5 ? 5 : S, WM, WN, SWZ, RING5 ? 5 * BM * BK * 2 : S * (BM + BN) * BK * 2,
-                    {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
-    v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-    v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-    if constexpr (ALL) {
-        v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-        v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-        v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-        v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+    DmaVariant v = {name, BM, BN, BK, RING5 ? 5 : S, WM, WN, SWZ, 0, {}};
+    // LDS: BK elements of 1 (8-bit inputs) or 2 bytes per tile row
+    const int rowb = BK * (F8 ? 1 : 2);
+    v.lds_bytes = RING5 ? 5 * BM * rowb : S * (BM + BN) * rowb;
+    if constexpr (F8) {
+        v.fn[2][0] = (const void*)&dma_kernel<GEMM_BT_FP8_E4M3, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[2][1] = (const void*)&dma_kernel<GEMM_BT_FP8_E4M3, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[2][2] = (const void*)&dma_kernel<GEMM_BT_FP8_E4M3, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[3][0] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[3][1] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[3][2] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+    } else {
+        v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        if constexpr (ALL) {
+            v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        }
     }
     return v;
 }
 
 // Index 0 is the default for large grids, 1 for smaller ones, 2 for the
-// smallest (see plan_impl); the
-// rest exist for tuning (GEMM_BT_FORCE_TILE=<name>) and are built for the
+// smallest (see plan_impl), 3..5 the same for 8-bit float inputs (128-element
+// K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32x64 MFMAs);
+// the rest exist for tuning (GEMM_BT_FORCE_TILE=<name>) and are built for the
 // bf16->bf16 and f16->f16 combinations only.
+constexpr int kFp8Variants = 3;
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 8, 0, 16, true>("M64E4s4i"),
         dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true>("Q64E4m16"),
+        dma_variant<256, 256, 128, 2, 2, 4, 2, 6, 0, 32, false, 0, 2, true>("L128F8R5s"),
+        dma_variant<128, 128, 128, 4, 2, 2, 2, 8, 0, 32, false, 0, 0, true>("M128F8s4i"),
+        dma_variant<64, 64, 128, 4, 2, 2, 2, 4, 0, 32, false, 0, 0, true>("Q128F8"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16>("L64E16i"),
@@ -185,13 +204,14 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
     if (!p) return GEMM_BT_ERR_INVALID_VALUE;
     std::memset(p, 0, sizeof(*p));
     if (M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
-    if (in_dtype != GEMM_BT_BF16 && in_dtype != GEMM_BT_F16) return GEMM_BT_ERR_UNSUPPORTED;
+    if (in_dtype != GEMM_BT_BF16 && in_dtype != GEMM_BT_F16 && !is_fp8(in_dtype)) return GEMM_BT_ERR_UNSUPPORTED;
     if (out_dtype != GEMM_BT_F32 && out_dtype != GEMM_BT_BF16 && out_dtype != GEMM_BT_F16)
         return GEMM_BT_ERR_UNSUPPORTED;
     const int osz = out_dtype == GEMM_BT_F32 ? 4 : 2;
     // 32-bit buffer offsets inside one 256-row panel of A, B and C.
     if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
-    if (256 * K * 2 >= 0x7FFFFFFFLL || 256 * N * (int64_t)osz >= 0x7FFFFFFFLL) return GEMM_BT_ERR_UNSUPPORTED;
+    const int isz = is_fp8(in_dtype) ? 1 : 2;
+    if (256 * K * isz >= 0x7FFFFFFFLL || 256 * N * (int64_t)osz >= 0x7FFFFFFFLL) return GEMM_BT_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) {
         p->kernel = KIND_NONE;
         return GEMM_BT_OK;
@@ -202,6 +222,32 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         const int64_t n16 = M * N * osz / 2;
         int64_t g = (n16 + 255) / 256;
         p->grid = g < 4096 ? g : 4096;
+        return GEMM_BT_OK;
+    }
+    if (is_fp8(in_dtype)) {
+        // 8-bit inputs: whole 16-byte chunks only (K a multiple of 16, A and B
+        // 16-byte aligned), always the LDS-DMA kernel
+        if (K % 16 != 0 || a_align % 16 != 0 || b_align % 16 != 0) return GEMM_BT_ERR_UNSUPPORTED;
+        int n = 0;
+        const DmaVariant* vs = dma_variants(&n);
+        const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256);
+        const int64_t tiles_m128 = ((M + 127) / 128) * ((N + 127) / 128);
+        const int use = kFp8Variants + (tiles_l >= num_cu ? 0 : (tiles_m128 * 4 >= num_cu ? 1 : 2));
+        const DmaVariant& v = vs[use];
+        p->kernel = KIND_DMA;
+        p->variant = use;
+        p->vec = 16;
+        p->bm = v.bm;
+        p->bn = v.bn;
+        p->bk = v.bk;
+        p->stages = v.stages;
+        p->threads = 64 * v.wm * v.wn;
+        p->lds_bytes = v.lds_bytes;
+        p->group_m = kGroupM;
+        p->ksplit = 1;
+        p->tiles_m = (M + p->bm - 1) / p->bm;
+        p->tiles_n = (N + p->bn - 1) / p->bn;
+        p->grid = p->tiles_m * p->tiles_n;
         return GEMM_BT_OK;
     }
     p->vec = pick_vec(K, a_align, b_align);
@@ -399,7 +445,8 @@ int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
     const int osz = out_dtype == GEMM_BT_F32 ? 4 : 2;
     if (!C) return GEMM_BT_ERR_INVALID_VALUE;
     if (p.kernel != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
-    if ((uintptr_t)A % 2 || (uintptr_t)B % 2 || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
+    const int isz = is_fp8(in_dtype) ? 1 : 2;
+    if ((uintptr_t)A % isz || (uintptr_t)B % isz || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
 
     int num_cu = 256;
     st = check_device(&num_cu);

@@ -39,9 +39,11 @@ extern "C" {
 
 /* Element types. */
 typedef enum {
-    GEMM_BT_F32 = 0,  /* IEEE binary32 (output only) */
-    GEMM_BT_F16 = 1,  /* IEEE binary16 */
-    GEMM_BT_BF16 = 2  /* bfloat16: the upper 16 bits of a binary32 */
+    GEMM_BT_F32 = 0,      /* IEEE binary32 (output only) */
+    GEMM_BT_F16 = 1,      /* IEEE binary16 */
+    GEMM_BT_BF16 = 2,     /* bfloat16: the upper 16 bits of a binary32 */
+    GEMM_BT_FP8_E4M3 = 3, /* OCP 8-bit E4M3 (input only): bias 7, no infinities, max 448 */
+    GEMM_BT_FP8_E5M2 = 4  /* OCP 8-bit E5M2 (input only): bias 15, IEEE-style infinities */
 } gemm_bt_dtype;
 
 /* Status codes returned by every entry point. */

@@ -61,7 +61,8 @@ class Workload:
         return dataclasses.replace(self, name=self.name + "_int", dist="int", seed=self.seed + 100)
 
 
-# The five measured shapes, seeds 0..4 in this order.
+# The five measured shapes, seeds 0..4 in this order, and the 4096³ product
+# with 8-bit E4M3 inputs (seed 5).
 WORKLOADS = {
     "sq512_bf16_f32": Workload("sq512_bf16_f32", 512, 512, 512, "bf16", "f32", "normal", 0),
     "m1024_n4096_k4096_f16_f16": Workload("m1024_n4096_k4096_f16_f16", 1024, 4096, 4096, "f16", "f16",
@@ -71,6 +72,7 @@ WORKLOADS = {
                                                   "bf16", "f32", "uniform", 3),
     "skinny_m16_n8192_k8192_bf16_bf16": Workload("skinny_m16_n8192_k8192_bf16_bf16", 16, 8192, 8192,
                                                  "bf16", "bf16", "normal_scaled", 4),
+    "sq4096_e4m3_bf16": Workload("sq4096_e4m3_bf16", 4096, 4096, 4096, "e4m3", "bf16", "normal", 5),
 }
 
 

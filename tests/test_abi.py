@@ -79,6 +79,16 @@ def test_plan_choices():
     # several streaming workgroups fit on one CU
     assert 4 * p.lds_bytes <= 160 * 1024 and p.stages >= 3
     assert gb.gemm_bt_plan(16, 8192, 8190, gb.BF16, gb.BF16).variant == 0  # narrow loads: register streaming
+    # 8-bit float inputs: the LDS-DMA kernel with 128-element K steps, also for M <= 16
+    for code in (gb.FP8_E4M3, gb.FP8_E5M2):
+        p = gb.gemm_bt_plan(4096, 4096, 4096, code, gb.BF16)
+        assert (p.kernel, p.bm, p.bn, p.bk, p.vec, p.stages, p.lds_bytes) == (4, 256, 256, 128, 16, 5, 160 * 1024)
+        assert gb.gemm_bt_plan(1024, 4096, 4096, code, gb.F16).bm == 128
+        assert gb.gemm_bt_plan(16, 8192, 8192, code, gb.BF16).kernel == 4
+        for args in ((64, 64, 40, code, gb.F32, 256, 256, 256), (64, 64, 48, code, gb.F32, 8, 256, 256),
+                     (64, 64, 48, code, code, 256, 256, 256)):
+            with pytest.raises(gb.GemmBtError):
+                gb.gemm_bt_plan(*args)
     p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)  # 16 tiles of 128: 64x64 tiles fill more CUs
     assert (p.kernel, p.bm, p.grid) == (4, 64, 64)
     assert gb.gemm_bt_plan(1024, 1024, 200, gb.BF16, gb.F32).bm == 128

@@ -17,7 +17,8 @@ from oracle import tolerance
 
 pytestmark = pytest.mark.gpu
 
-TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
+            "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 
 
 def say(*a):
@@ -26,7 +27,8 @@ def say(*a):
 
 
 def to_dev(bits, in_dtype):
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    raw = np.uint8 if in_dtype in ("e4m3", "e5m2") else np.int16
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(raw))
     return t.to("cuda").view(TORCH_DT[in_dtype])
 
 
@@ -99,6 +101,53 @@ def test_integer_bit_exact_sweep(gpu, in_dtype, out_dtype):
         a, b = synth.make(M, N, K, in_dtype, "int", seed)
         c = run_gpu(gpu, a, b, in_dtype, out_dtype)
         check_bits_full(c, a, b, in_dtype, out_dtype, (M, N, K))
+
+
+# 8-bit float inputs (K a multiple of 16): one K step of 128, a partial last
+# step, the 64x64, 128x128 and 256x256 tiles (the last with ragged edges and
+# several steps of its five-slot ring), and M <= 16 (no streaming kernel for
+# 8-bit inputs: the 64x64 tiles take it).
+FP8_SHAPES = [(1, 1, 16), (16, 16, 16), (17, 33, 64), (8, 1000, 64), (64, 64, 128), (130, 260, 160),
+              (257, 513, 144), (300, 700, 1024), (1024, 1024, 256), (4096, 4096, 128), (4100, 4100, 272),
+              (4096, 4096, 400)]
+
+
+@pytest.mark.parametrize("in_dtype", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_fp8_sweep(gpu, in_dtype, out_dtype):
+    for i, (M, N, K) in enumerate(FP8_SHAPES):
+        seed = 900 + i
+        say("fp8 sweep", in_dtype, out_dtype, M, N, K, "seed", seed)
+        a, b = synth.make(M, N, K, in_dtype, "normal", seed)
+        c = run_gpu(gpu, a, b, in_dtype, out_dtype)
+        check_full(c, a, b, in_dtype, out_dtype, (M, N, K))
+
+
+@pytest.mark.parametrize("in_dtype", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_fp8_integer_bit_exact(gpu, in_dtype, out_dtype):
+    for i, (M, N, K) in enumerate(FP8_SHAPES):
+        seed = 950 + i
+        say("fp8 int sweep", in_dtype, out_dtype, M, N, K, "seed", seed)
+        a, b = synth.make(M, N, K, in_dtype, "int", seed)
+        c = run_gpu(gpu, a, b, in_dtype, out_dtype)
+        check_bits_full(c, a, b, in_dtype, out_dtype, (M, N, K))
+
+
+def test_fp8_unsupported_layouts(gpu):
+    """8-bit inputs need K % 16 == 0 and 16-byte aligned A and B; anything else is refused before any launch."""
+    s = torch.cuda.current_stream().cuda_stream
+    a = torch.zeros(64 * 48 + 64, dtype=torch.uint8, device="cuda")
+    b = torch.zeros(64 * 48 + 64, dtype=torch.uint8, device="cuda")
+    c = torch.full((64, 64), float("nan"), dtype=torch.float32, device="cuda")
+    for code in (gpu.FP8_E4M3, gpu.FP8_E5M2):
+        say("fp8 unsupported", code)
+        assert gpu.gemm_bt(a.data_ptr(), b.data_ptr(), c.data_ptr(), 64, 64, 40, code, gpu.F32, s) == gpu.ERR_UNSUPPORTED
+        assert gpu.gemm_bt(a.data_ptr() + 8, b.data_ptr(), c.data_ptr(), 64, 64, 48, code, gpu.F32, s) == \
+            gpu.ERR_UNSUPPORTED
+        assert gpu.gemm_bt(a.data_ptr(), b.data_ptr(), c.data_ptr(), 64, 64, 48, code, code, s) == gpu.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.isnan(c).all()
 
 
 def sample_entries(M, N, rng, tile=256):
