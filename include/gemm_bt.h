@@ -6,17 +6,20 @@
  * transposed so both operands are read along K ("Optimizing Blackwell matrix
  * multiplication in Mojo (part 2)", sections "Starting from the 4-line kernel"
  * and "Kernel 2: TMA and Tensor Core", where B is laid out row_major(N, K) so
- * its loads coalesce).  Inputs are bf16 or f16 (both operands the same type,
- * as the MMA contract of "Writing Mosaic GPU kernels with Pallas", section
- * "MMA (TensorCore)", requires); products are accumulated in fp32 and the
+ * its loads coalesce).  Inputs are bf16, f16 or one of the OCP 8-bit float
+ * formats E4M3 / E5M2 (both operands the same type, as the MMA contract of
+ * "Writing Mosaic GPU kernels with Pallas", section "MMA (TensorCore)",
+ * requires; the pages list 8-bit floats among the supported MMA element
+ * types); products are accumulated in fp32 and the
  * result is rounded once, to nearest even, into the output type ("Chapter 7:
  * Writing custom kernels with Pallas", section 4.1': fp32 accumulator, cast
  * only after the last K step).  C is overwritten: there is no alpha/beta.
  *
  * Layout.  Dense and contiguous: lda = ldb = K elements, ldc = N elements.
- * Pointers need only element alignment (2 bytes for 16-bit data, 4 bytes for
+ * For 16-bit inputs pointers need only element alignment (2 bytes, 4 bytes for
  * fp32 output); 16-byte alignment together with K % 8 == 0 selects the
- * widest loads and is a performance matter only.
+ * widest loads and is a performance matter only.  8-bit inputs need whole
+ * 16-byte rows: K % 16 == 0 and A, B 16-byte aligned (else UNSUPPORTED).
  *
  * Ownership.  The caller owns A, B and C (device memory, e.g. from PyTorch).
  * The library allocates nothing per call, keeps no pointer after it returns
@@ -61,8 +64,9 @@ typedef enum {
  *   B          device pointer, N x K elements of in_dtype, row-major (B^T stored)
  *   C          device pointer, M x N elements of out_dtype, row-major; overwritten
  *   M, N, K    sizes, each in [0, 2^31 - 1]; M*K, N*K and M*N elements must each
- *              fit below 2^31 bytes per 256-row panel (checked: UNSUPPORTED)
- *   in_dtype   GEMM_BT_BF16 or GEMM_BT_F16
+ *              fit below 2^31 bytes per 256-row panel (checked: UNSUPPORTED);
+ *              8-bit inputs: K % 16 == 0 and A, B 16-byte aligned (UNSUPPORTED)
+ *   in_dtype   GEMM_BT_BF16, GEMM_BT_F16, GEMM_BT_FP8_E4M3 or GEMM_BT_FP8_E5M2
  *   out_dtype  GEMM_BT_F32, GEMM_BT_BF16 or GEMM_BT_F16
  *   stream     hipStream_t to enqueue on; NULL means the default stream
  * M == 0 or N == 0: nothing is enqueued, returns GEMM_BT_OK.
@@ -91,7 +95,7 @@ typedef struct {
     int variant;      /* tile-shape variant index within the kernel family */
     int bm, bn, bk;   /* workgroup tile (rows of C, columns of C, K step) */
     int threads;      /* threads per workgroup */
-    int vec;          /* elements per global load: 8 (16 bytes), 2 or 1 */
+    int vec;          /* elements per global load: 16 (16 bytes of 8-bit data), 8 (16 bytes), 2 or 1 */
     int group_m;      /* tile-rows per group in the grouped tile order */
     int ksplit;       /* waves that split K inside a workgroup (skinny kernel) */
     int stages;       /* LDS pipeline depth: A+B stages (tiled kernels), or for the 256x256 tile the 5 slots of
