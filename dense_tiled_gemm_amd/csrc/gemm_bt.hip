@@ -61,12 +61,15 @@ static DmaVariant dma_variant(const char* name) {
     const int rowb = BK * (F8 ? 1 : 2);
     v.lds_bytes = RING5 ? 5 * BM * rowb : S * (BM + BN) * rowb;
     if constexpr (F8) {
-        v.fn[2][0] = (const void*)&dma_kernel<GEMM_BT_FP8_E4M3, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        // tuning forms: E4M3 -> bf16 only
         v.fn[2][1] = (const void*)&dma_kernel<GEMM_BT_FP8_E4M3, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-        v.fn[2][2] = (const void*)&dma_kernel<GEMM_BT_FP8_E4M3, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-        v.fn[3][0] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-        v.fn[3][1] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-        v.fn[3][2] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        if constexpr (ALL) {
+            v.fn[2][0] = (const void*)&dma_kernel<GEMM_BT_FP8_E4M3, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[2][2] = (const void*)&dma_kernel<GEMM_BT_FP8_E4M3, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[3][0] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[3][1] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[3][2] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        }
     } else {
         v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
         v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
@@ -91,9 +94,9 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 8, 0, 16, true>("M64E4s4i"),
         dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true>("Q64E4m16"),
-        dma_variant<256, 256, 128, 2, 2, 4, 2, 6, 0, 32, false, 0, 2, true>("L128F8R5s"),
-        dma_variant<128, 128, 128, 4, 2, 2, 2, 8, 0, 32, false, 0, 0, true>("M128F8s4i"),
-        dma_variant<64, 64, 128, 4, 2, 2, 2, 4, 0, 32, false, 0, 0, true>("Q128F8"),
+        dma_variant<256, 256, 128, 2, 2, 4, 2, 6, 0, 32, true, 0, 2, true>("L128F8R5s"),
+        dma_variant<128, 128, 128, 4, 2, 2, 2, 8, 0, 32, true, 0, 0, true>("M128F8s4i"),
+        dma_variant<64, 64, 128, 4, 2, 2, 2, 4, 0, 32, true, 0, 0, true>("Q128F8"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16>("L64E16i"),
@@ -232,7 +235,9 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         const DmaVariant* vs = dma_variants(&n);
         const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t tiles_m128 = ((M + 127) / 128) * ((N + 127) / 128);
-        const int use = kFp8Variants + (tiles_l >= num_cu ? 0 : (tiles_m128 * 4 >= num_cu ? 1 : 2));
+        int use = kFp8Variants + (tiles_l >= num_cu ? 0 : (tiles_m128 * 4 >= num_cu ? 1 : 2));
+        const int f = forced_variant();
+        if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];
         p->kernel = KIND_DMA;
         p->variant = use;
