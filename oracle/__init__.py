@@ -6,8 +6,8 @@ links or calls it, and the two share no code.
 
 The arithmetic lives in ``gemm_ref.c`` (plain C, fp64 accumulation in
 increasing k, exact decoders for the 16-bit and OCP 8-bit input formats, IEEE
-round-to-nearest-even encoders);
-this module only builds it with gcc, loads it with ctypes and marshals numpy
+round-to-nearest-even encoders, and an exact int64 path for 8-bit integer
+inputs); this module only builds it with gcc, loads it with ctypes and marshals numpy
 arrays.  The tolerance rules are in ``oracle.tolerance``.
 
 Definition followed ("Optimizing Blackwell matrix multiplication in Mojo
@@ -67,6 +67,10 @@ def _load():
             lib.orc_round.argtypes = [p, i64, ci, p]
             lib.orc_round.restype = None
             lib.orc_max_threads.restype = ci
+            lib.orc_gemm_bt_i8.argtypes = [p, p, i64, i64, i64, p, ci]
+            lib.orc_gemm_bt_i8.restype = ci
+            lib.orc_gemm_bt_i8_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ci]
+            lib.orc_gemm_bt_i8_entries.restype = ci
             _lib = lib
     return _lib
 
@@ -161,5 +165,46 @@ def row_norms(x_bits: np.ndarray, in_dtype, nthreads: int = 0) -> np.ndarray:
     out = np.empty(R, dtype=np.float64)
     rc = _load().orc_row_norms(_ptr(x), R, K, dtype_code(in_dtype), _ptr(out), int(nthreads))
     if rc != 0:
+        raise ValueError("oracle rejected arguments")
+    return out
+
+
+def _i8(x: np.ndarray) -> np.ndarray:
+    """Two's-complement bytes as an int8 array (int8 or uint8 input)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype not in (np.int8, np.uint8):
+        raise ValueError("8-bit integer inputs must be int8 or uint8 arrays")
+    return x.view(np.int8)
+
+
+def gemm_bt_i8(a: np.ndarray, b: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """Exact product of int8 operands: C (M,N) int64 = sum_k A[i,k]*B[j,k]."""
+    a = _i8(a)
+    b = _i8(b)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise ValueError("A is %dx%d but B is %dx%d" % (M, K, N, K2))
+    C = np.empty((M, N), dtype=np.int64)
+    if _load().orc_gemm_bt_i8(_ptr(a), _ptr(b), M, N, K, _ptr(C), int(nthreads)) != 0:
+        raise ValueError("oracle rejected arguments")
+    return C
+
+
+def gemm_bt_i8_entries(a: np.ndarray, b: np.ndarray, I, J, nthreads: int = 0) -> np.ndarray:
+    """C[I[t], J[t]] (int64) for each t, for int8 operands."""
+    a = _i8(a)
+    b = _i8(b)
+    M, K = a.shape
+    N, K2 = b.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    I = np.ascontiguousarray(I, dtype=np.int64)
+    J = np.ascontiguousarray(J, dtype=np.int64)
+    if I.shape != J.shape:
+        raise ValueError("I and J differ in shape")
+    out = np.empty(I.shape, dtype=np.int64)
+    if _load().orc_gemm_bt_i8_entries(_ptr(a), _ptr(b), M, N, K, _ptr(I), _ptr(J), I.size, _ptr(out),
+                                      int(nthreads)) != 0:
         raise ValueError("oracle rejected arguments")
     return out

@@ -31,6 +31,12 @@
  *
  * Output rounding (used by the bit-exact tests): IEEE round-to-nearest-even
  * from the double value straight to the output format, overflow to +-Inf.
+ *
+ * 8-bit integer inputs ("Writing Mosaic GPU kernels with Pallas", section
+ * "MMA (TensorCore)": int8 is the integer operand type, with an int32
+ * accumulator) have their own entry points below: two's-complement bytes,
+ * products and sums in int64, which is exact for every K below 2^49 (each
+ * product is at most 2^14 in magnitude).  No rounding is involved.
  */
 #include <math.h>
 #include <stdint.h>
@@ -322,5 +328,49 @@ int orc_row_norms(const uint16_t* X, int64_t R, int64_t K, int in_dtype, double*
     int64_t r;
 #pragma omp parallel for schedule(static)
     for (r = 0; r < R; ++r) out[r] = norm_row(X + r * K, K, tab);
+    return 0;
+}
+
+/* ---- 8-bit integer inputs -------------------------------------------------- */
+
+/* One output entry: the exact integer dot product of row i of A and row j of
+   stored B. */
+static int64_t dot_row_i8(const int8_t* a, const int8_t* b, int64_t K) {
+    int64_t s = 0;
+    for (int64_t k = 0; k < K; ++k) s += (int64_t)a[k] * (int64_t)b[k];
+    return s;
+}
+
+/* Full product of int8 operands: C (M x N int64) is caller-owned.  Returns 0,
+   or -1 on bad args. */
+int orc_gemm_bt_i8(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K, int64_t* C,
+                   int nthreads) {
+    if (M < 0 || N < 0 || K < 0 || K >= ((int64_t)1 << 49)) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) C[i * N + j] = dot_row_i8(A + i * K, B + j * K, K);
+    return 0;
+}
+
+/* Selected entries of an int8 product: out[t] = C[I[t]][J[t]] for t < n. */
+int orc_gemm_bt_i8_entries(const int8_t* A, const int8_t* B, int64_t M, int64_t N, int64_t K,
+                           const int64_t* I, const int64_t* J, int64_t n, int64_t* out, int nthreads) {
+    if (M < 0 || N < 0 || K < 0 || n < 0 || K >= ((int64_t)1 << 49)) return -1;
+    for (int64_t t = 0; t < n; ++t)
+        if (I[t] < 0 || I[t] >= M || J[t] < 0 || J[t] >= N) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int64_t t;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (t = 0; t < n; ++t) out[t] = dot_row_i8(A + I[t] * K, B + J[t] * K, K);
     return 0;
 }

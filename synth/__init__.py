@@ -3,21 +3,23 @@
 This module draws random numbers and rounds them to the input format.
 It holds none of the product's arithmetic: no dot products, no accumulation,
 no output rounding.  Each generator returns raw bit patterns (uint16 arrays for
-the 16-bit formats, uint8 for the 8-bit ones), so the very same bits feed the
-GPU kernel and the CPU oracle.
+the 16-bit formats, uint8 for the 8-bit ones, two's-complement bytes for int8),
+so the very same bits feed the GPU kernel and the CPU oracle.
 
 Recipe (also stated in the design notes):
   * ``numpy.random.default_rng(seed)`` (PCG64); A is drawn first (M×K, row-major
     order), then B (N×K, row-major order — B is stored transposed).
   * distributions: ``normal`` N(0, 1); ``normal_scaled`` N(0, σ=1/√K);
     ``uniform`` U[-1, 1) via ``rng.uniform(-1, 1)``; ``int`` uniform integers in
-    [-4, 4] (exact in every input format, so fp32 accumulation is exact).
+    [-4, 4] (exact in every input format, so fp32 accumulation is exact);
+    ``int8`` uniform integers over the whole int8 range [-128, 127].
   * rounding: bf16 values go float64 → float32 (numpy, round-to-nearest-even)
     → bfloat16 (torch CPU conversion, round-to-nearest-even); f16 values go
     float64 → float16 directly (numpy, round-to-nearest-even); e4m3 / e5m2
     values go float64 → float32 → torch ``float8_e4m3fn`` / ``float8_e5m2``
     (torch CPU conversion, round-to-nearest-even; the distributions used stay
-    far inside both formats' range).
+    far inside both formats' range); i8 takes integer draws only (anything
+    else is an error) and stores them as two's-complement bytes.
 
 The workloads are the matrix products the pages measure: 4096³ square
 ("Optimizing Blackwell matrix multiplication in Mojo (part 2)", section
@@ -32,8 +34,8 @@ import dataclasses
 
 import numpy as np
 
-IN_DTYPES = ("bf16", "f16", "e4m3", "e5m2")
-OUT_DTYPES = ("f32", "f16", "bf16")
+IN_DTYPES = ("bf16", "f16", "e4m3", "e5m2", "i8")
+OUT_DTYPES = ("f32", "f16", "bf16", "i32")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -53,16 +55,16 @@ class Workload:
 
     @property
     def compulsory_bytes(self) -> int:
-        osz = 4 if self.out_dtype == "f32" else 2
-        isz = 1 if self.in_dtype in ("e4m3", "e5m2") else 2
+        osz = 4 if self.out_dtype in ("f32", "i32") else 2
+        isz = 1 if self.in_dtype in ("e4m3", "e5m2", "i8") else 2
         return (self.M * self.K + self.N * self.K) * isz + self.M * self.N * osz
 
     def integer_twin(self) -> "Workload":
         return dataclasses.replace(self, name=self.name + "_int", dist="int", seed=self.seed + 100)
 
 
-# The five measured shapes, seeds 0..4 in this order, and the 4096³ product
-# with 8-bit E4M3 inputs (seed 5).
+# The five measured shapes, seeds 0..4 in this order, the 4096³ product
+# with 8-bit E4M3 inputs (seed 5) and with int8 inputs and int32 output (seed 6).
 WORKLOADS = {
     "sq512_bf16_f32": Workload("sq512_bf16_f32", 512, 512, 512, "bf16", "f32", "normal", 0),
     "m1024_n4096_k4096_f16_f16": Workload("m1024_n4096_k4096_f16_f16", 1024, 4096, 4096, "f16", "f16",
@@ -73,6 +75,7 @@ WORKLOADS = {
     "skinny_m16_n8192_k8192_bf16_bf16": Workload("skinny_m16_n8192_k8192_bf16_bf16", 16, 8192, 8192,
                                                  "bf16", "bf16", "normal_scaled", 4),
     "sq4096_e4m3_bf16": Workload("sq4096_e4m3_bf16", 4096, 4096, 4096, "e4m3", "bf16", "normal", 5),
+    "sq4096_i8_i32": Workload("sq4096_i8_i32", 4096, 4096, 4096, "i8", "i32", "int8", 6),
 }
 
 
@@ -96,6 +99,13 @@ def _to_fp8_bits(x64: np.ndarray, in_dtype: str) -> np.ndarray:
     return t.view(torch.uint8).numpy().copy()
 
 
+def _to_i8_bits(x64: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x64, dtype=np.float64)
+    if x.size and (not np.all(x == np.rint(x)) or x.min() < -128 or x.max() > 127):
+        raise ValueError("int8 inputs must be integers in [-128, 127]")
+    return x.astype(np.int8).view(np.uint8)
+
+
 def round_bits(x64: np.ndarray, in_dtype: str) -> np.ndarray:
     """Round float64 values to the input format, returning raw bits."""
     if in_dtype == "bf16":
@@ -104,7 +114,9 @@ def round_bits(x64: np.ndarray, in_dtype: str) -> np.ndarray:
         return _to_f16_bits(x64)
     if in_dtype in ("e4m3", "e5m2"):
         return _to_fp8_bits(x64, in_dtype)
-    raise ValueError("in_dtype must be bf16, f16, e4m3 or e5m2")
+    if in_dtype == "i8":
+        return _to_i8_bits(x64)
+    raise ValueError("in_dtype must be bf16, f16, e4m3, e5m2 or i8")
 
 
 def _draw(rng: np.random.Generator, shape, dist: str, K: int) -> np.ndarray:
@@ -116,6 +128,8 @@ def _draw(rng: np.random.Generator, shape, dist: str, K: int) -> np.ndarray:
         return rng.uniform(-1.0, 1.0, shape)
     if dist == "int":
         return rng.integers(-4, 5, shape).astype(np.float64)
+    if dist == "int8":
+        return rng.integers(-128, 128, shape).astype(np.float64)
     raise ValueError("unknown distribution %r" % dist)
 
 

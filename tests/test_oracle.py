@@ -11,6 +11,9 @@ The oracle is checked against things other than itself:
     fp64 summation bound, and equal on integer inputs;
   * closed forms: identity, all-ones, zero and permutation operands;
   * a library routine: numpy float64 matmul on independently decoded inputs.
+The exact int8 path is pinned by its own hand-computed products
+(tests/golden/int8_products.txt), Python-integer brute force over the whole
+int8 range, numpy int64 matmul, and closed forms at the range ends.
 A mistake planted in a copy of the oracle's result (transposed operand, dropped
 last term, wrong sign) must fail these pins.
 """
@@ -442,9 +445,106 @@ def test_synth_recipe():
     a, _ = synth.make(50, 4, wu.K, "bf16", wu.dist, wu.seed)
     v = indep_decode(a, "bf16")
     assert v.min() >= -1 and v.max() <= 1 and abs(v.std() - 1 / math.sqrt(3)) < 0.01
-    assert [x.seed for x in synth.WORKLOADS.values()] == [0, 1, 2, 3, 4, 5]
+    assert [x.seed for x in synth.WORKLOADS.values()] == [0, 1, 2, 3, 4, 5, 6]
     w8 = synth.WORKLOADS["sq4096_e4m3_bf16"]
     a8, _ = synth.make(64, 4, w8.K, w8.in_dtype, w8.dist, w8.seed)
     assert a8.dtype == np.uint8 and w8.compulsory_bytes == 2 * 4096 * 4096 + 4096 * 4096 * 2
     v8 = indep_decode(a8, "e4m3")
     assert abs(v8.std() - 1) < 0.02  # N(0,1) rounded to 3 fraction bits
+
+
+# ---------------------------------------------------------------- 8-bit integer inputs
+
+def parse_int_products():
+    cases = []
+    lines = [l.strip() for l in open(os.path.join(GOLDEN, "int8_products.txt"))]
+    lines = [l for l in lines if l and not l.startswith("#")]
+    i = 0
+    while i < len(lines):
+        tag, name, M, N, K = lines[i].split()
+        assert tag == "case"
+        M, N, K = int(M), int(N), int(K)
+        rows = [[int(v) for v in l.split()] for l in lines[i + 1:i + 1 + M + N + M]]
+        A = np.array(rows[:M], dtype=np.int64)
+        B = np.array(rows[M:M + N], dtype=np.int64)
+        C = np.array(rows[M + N:], dtype=np.int64)
+        assert A.shape == (M, K) and B.shape == (N, K) and C.shape == (M, N)
+        cases.append((name, A, B, C))
+        i += 1 + M + N + M
+    assert len(cases) == 3
+    return cases
+
+
+def test_i8_hand_products():
+    for name, A, B, C in parse_int_products():
+        a = synth.round_bits(A.astype(np.float64), "i8")
+        b = synth.round_bits(B.astype(np.float64), "i8")
+        assert a.dtype == np.uint8 and np.array_equal(a.view(np.int8), A)  # two's-complement bytes
+        assert np.array_equal(oracle.gemm_bt_i8(a, b), C), name
+
+
+def test_i8_brute_force_full_range():
+    rng = np.random.default_rng(61)
+    for M, N, K in [(1, 1, 1), (3, 5, 7), (4, 4, 16), (6, 3, 33)]:
+        a = rng.integers(-128, 128, (M, K)).astype(np.int8)
+        b = rng.integers(-128, 128, (N, K)).astype(np.int8)
+        c = oracle.gemm_bt_i8(a, b)
+        for i in range(M):
+            for j in range(N):
+                assert int(c[i, j]) == sum(int(a[i, k]) * int(b[j, k]) for k in range(K))
+
+
+def test_i8_vs_numpy_int64():
+    for (M, N, K), seed in [((70, 90, 160), 62), ((33, 65, 4096), 63), ((128, 1, 1000), 64)]:
+        a, b = synth.make(M, N, K, "i8", "int8", seed)
+        ref = a.view(np.int8).astype(np.int64) @ b.view(np.int8).astype(np.int64).T
+        assert np.array_equal(oracle.gemm_bt_i8(a, b), ref)
+
+
+def test_i8_closed_forms():
+    K = 131071  # the largest K whose every sum fits int32
+    lo = np.full((1, K), -128, np.int8)
+    hi = np.full((1, K), 127, np.int8)
+    c = oracle.gemm_bt_i8(lo, np.concatenate([lo, hi]))
+    assert c[0, 0] == 16384 * K and c[0, 1] == -16256 * K
+    assert c[0, 0] < 2 ** 31 and 16384 * (K + 1) == 2 ** 31
+    rng = np.random.default_rng(65)
+    a = rng.integers(-128, 128, (9, 12)).astype(np.int8)
+    eye = np.eye(12, dtype=np.int8)
+    assert np.array_equal(oracle.gemm_bt_i8(a, eye), a.astype(np.int64))  # identity B
+    perm = rng.permutation(12)
+    assert np.array_equal(oracle.gemm_bt_i8(a, eye[perm]), a[:, perm].astype(np.int64))  # permutation B
+    assert np.all(oracle.gemm_bt_i8(a, np.zeros((5, 12), np.int8)) == 0)
+    assert oracle.gemm_bt_i8(np.zeros((4, 0), np.int8), np.zeros((3, 0), np.int8)).tolist() == [[0] * 3] * 4
+
+
+def test_i8_entries_match_full_and_planted_mistakes():
+    a, b = synth.make(40, 50, 96, "i8", "int8", 66)
+    c = oracle.gemm_bt_i8(a, b)
+    rng = np.random.default_rng(67)
+    I = rng.integers(0, 40, 300)
+    J = rng.integers(0, 50, 300)
+    assert np.array_equal(oracle.gemm_bt_i8_entries(a, b, I, J), c[I, J])
+    with pytest.raises(ValueError):
+        oracle.gemm_bt_i8_entries(a, b, np.array([40]), np.array([0]))
+    # each plausible slip gives a different product
+    av, bv = a.view(np.int8).astype(np.int64), b.view(np.int8).astype(np.int64)
+    bad = {"unsigned bytes": a.astype(np.int64) @ b.astype(np.int64).T,
+           "dropped last term": av[:, :-1] @ bv[:, :-1].T,
+           "off-by-one k": av[:, 1:] @ bv[:, :-1].T,
+           "int8 wrap of each product": (((av[:, None, :] * bv[None, :, :] + 128) % 256) - 128).sum(-1)}
+    for name, v in bad.items():
+        assert not np.array_equal(v, c), name
+
+
+def test_i8_recipe():
+    w = synth.WORKLOADS["sq4096_i8_i32"]
+    a, b = synth.make(64, 8, w.K, w.in_dtype, w.dist, w.seed)
+    v = a.view(np.int8)
+    assert a.dtype == np.uint8 and v.min() == -128 and v.max() == 127
+    assert abs(v.astype(np.float64).mean() + 0.5) < 0.2  # uniform on [-128, 127]
+    assert w.compulsory_bytes == 2 * 4096 * 4096 + 4 * 4096 * 4096
+    with pytest.raises(ValueError):
+        synth.round_bits(np.array([0.5]), "i8")
+    with pytest.raises(ValueError):
+        synth.round_bits(np.array([128.0]), "i8")
