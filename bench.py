@@ -8,8 +8,9 @@ Prints ONE JSON line on stdout:
   roofline     the tiled MFMA kernel against the MI355X dense bf16 peak
   cpu_baseline the CPU oracle timed on a bounded sample of the same product
   secondary    µs / TFLOP/s / GB/s of the other workloads (1024×4096×4096
-               f16, 16×8192×8192 skinny, 512³, 1000×3000×2050, and 4096³ with
-               E4M3 inputs against the fp8 peak), same timing
+               f16, 16×8192×8192 skinny, 512³, 1000×3000×2050, 4096³ with
+               E4M3 inputs against the fp8 peak, and 4096³ int8 -> int32
+               against the int8 peak), same timing
   copy_GBps    a plain 1 GiB device copy, as context for achievable HBM
 Diagnostics go to stderr.  The default 400 untimed warm-up launches matter:
 from idle, an MI355X needs about 25 ms of sustained GEMM launches before its
@@ -33,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s and % of MI355X bf16 MFMA peak (4096³); µs @1024×4096×4096"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU × 4096 dense bf16 FLOP/clk/CU × 2.4 GHz (published 2.5 PFLOP/s)
 PEAK_FP8_TFLOPS = 5033.2   # twice the bf16 rate (published dense fp8: 5.0 PFLOP/s)
+PEAK_I8_TOPS = 5033.2      # the same rate in integer operations (published dense int8: 5.0 POP/s)
 PEAK_HBM_GBS = 8000.0      # published HBM3E bandwidth
 MALL_BYTES = 256 << 20     # rotate inputs over more than the 256 MiB Infinity Cache
 
@@ -77,7 +79,7 @@ class Case:
         self.torch = torch
         self.gb = gb
         dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
-              "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+              "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2, "i8": torch.int8, "i32": torch.int32}
         a_bits, b_bits = synth.make_workload(w)
         raw = np.uint8 if a_bits.dtype == np.uint8 else np.int16
         a = torch.from_numpy(a_bits.view(raw)).to("cuda").view(dt[w.in_dtype])
@@ -93,8 +95,9 @@ class Case:
             br = b if r == 0 else b.clone()
             c = torch.empty((w.M, w.N), dtype=dt[w.out_dtype], device="cuda")
             self.sets.append((ar, br, c))
-        self.in_code = {"bf16": gb.BF16, "f16": gb.F16, "e4m3": gb.FP8_E4M3, "e5m2": gb.FP8_E5M2}[w.in_dtype]
-        self.out_code = {"f32": gb.F32, "bf16": gb.BF16, "f16": gb.F16}[w.out_dtype]
+        self.in_code = {"bf16": gb.BF16, "f16": gb.F16, "e4m3": gb.FP8_E4M3, "e5m2": gb.FP8_E5M2,
+                        "i8": gb.INT8}[w.in_dtype]
+        self.out_code = {"f32": gb.F32, "bf16": gb.BF16, "f16": gb.F16, "i32": gb.INT32}[w.out_dtype]
         self.ptrs = [(x.data_ptr(), y.data_ptr(), z.data_ptr()) for x, y, z in self.sets]
         torch.cuda.synchronize()
 
@@ -253,7 +256,7 @@ def main():
     if not args.no_secondary:
         sec = {}
         for name in ("m1024_n4096_k4096_f16_f16", "skinny_m16_n8192_k8192_bf16_bf16", "sq512_bf16_f32",
-                     "ragged_m1000_n3000_k2050_bf16_f32", "sq4096_e4m3_bf16"):
+                     "ragged_m1000_n3000_k2050_bf16_f32", "sq4096_e4m3_bf16", "sq4096_i8_i32"):
             w2 = synth.WORKLOADS[name]
             c2 = Case(w2, torch, gb)
             _, ms2 = c2.time(max(50, args.steps // 2), args.warmup)
@@ -264,6 +267,9 @@ def main():
                 ent["frac_hbm"] = round(ent["GB/s"] / PEAK_HBM_GBS, 4)
             elif w2.in_dtype in ("e4m3", "e5m2"):
                 ent["frac_mfma_fp8"] = round(ent["TFLOP/s"] / PEAK_FP8_TFLOPS, 4)
+            elif w2.in_dtype == "i8":  # integer operations: TOP/s
+                ent["TOP/s"] = ent.pop("TFLOP/s")
+                ent["frac_mfma_i8"] = round(ent["TOP/s"] / PEAK_I8_TOPS, 4)
             else:
                 ent["frac_mfma"] = round(ent["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
             sec[name] = ent

@@ -17,7 +17,7 @@ import ctypes
 import os
 import threading
 
-F32, F16, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
+F32, F16, BF16, FP8_E4M3, FP8_E5M2, INT8, INT32 = 0, 1, 2, 3, 4, 5, 6
 OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_LAUNCH = 0, 1, 2, 3, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -117,21 +117,26 @@ def _torch_code(dt):
         return FP8_E4M3
     if dt == torch.float8_e5m2:
         return FP8_E5M2
+    if dt == torch.int8:
+        return INT8
+    if dt == torch.int32:
+        return INT32
     raise TypeError("unsupported dtype %s" % dt)
 
 
 def _torch_dtype(code):
     import torch
 
-    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[code]
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, INT32: torch.int32}[code]
 
 
 def mm_bt(a, b, out_dtype=None, out=None, stream=None):
     """C = a @ b.T for CUDA/HIP tensors a (M×K) and b (N×K) of one input dtype.
 
-    Inputs: bfloat16, float16, float8_e4m3fn or float8_e5m2 (8-bit inputs need
-    K % 16 == 0).  ``out_dtype`` defaults to a's dtype (bfloat16 for 8-bit
-    inputs, which are not an output format); ``out`` may be a preallocated
+    Inputs: bfloat16, float16, float8_e4m3fn, float8_e5m2 or int8 (8-bit
+    inputs need K % 16 == 0; int8 also K <= 131071).  ``out_dtype`` defaults
+    to a's dtype (bfloat16 for 8-bit float inputs, which are not an output
+    format; int32, the only one allowed, for int8); ``out`` may be a preallocated
     contiguous M×N tensor.  The call is asynchronous on ``stream`` (default:
     torch's current stream of a's device).
     """
@@ -144,7 +149,7 @@ def mm_bt(a, b, out_dtype=None, out=None, stream=None):
     if not a.is_cuda or not b.is_cuda or a.device != b.device:
         raise ValueError("a and b must be on the same GPU")
     in_code = _torch_code(a.dtype)
-    default_out = BF16 if in_code in (FP8_E4M3, FP8_E5M2) else in_code
+    default_out = BF16 if in_code in (FP8_E4M3, FP8_E5M2) else (INT32 if in_code == INT8 else in_code)
     out_code = default_out if out_dtype is None else (_torch_code(out_dtype) if not isinstance(out_dtype, int)
                                                       else out_dtype)
     a = a.contiguous()

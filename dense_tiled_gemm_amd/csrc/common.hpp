@@ -16,6 +16,8 @@ typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef u32 u32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -118,9 +120,33 @@ struct Mfma<GEMM_BT_FP8_E4M3> : MfmaF8<0> {};  // operand format 0: E4M3
 template <>
 struct Mfma<GEMM_BT_FP8_E5M2> : MfmaF8<1> {};  // operand format 1: E5M2
 
+// 8-bit integer inputs: v_mfma_i32_32x32x32_i8 takes 16 bytes of one row per
+// lane, so the 32-byte fragment of a 64-element substep is two instructions,
+// one per 16-byte half, each pairing the same half of A and of B (the same k
+// bytes, so the sum over both is the full one).  The int32 sums are exact and
+// live in the fp32 accumulator registers as raw bits; the int32 output path
+// copies those bits unchanged.
+template <>
+struct Mfma<GEMM_BT_INT8> {
+    // half H (0 or 1) of the fragment pair: bytes 16*H .. 16*H+15 of each lane
+    template <int H>
+    __device__ static inline f32x16 half(u32x8 a, u32x8 b, f32x16 c) {
+        const i32x8 ai = __builtin_bit_cast(i32x8, a), bi = __builtin_bit_cast(i32x8, b);
+        return __builtin_bit_cast(
+            f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{ai[4 * H], ai[4 * H + 1], ai[4 * H + 2], ai[4 * H + 3]},
+                                                          i32x4{bi[4 * H], bi[4 * H + 1], bi[4 * H + 2], bi[4 * H + 3]},
+                                                          __builtin_bit_cast(i32x16, c), 0, 0, 0));
+    }
+    __device__ static inline f32x16 m32x32x64(u32x8 a, u32x8 b, f32x16 c) { return half<1>(a, b, half<0>(a, b, c)); }
+};
+
 // Bytes per input element, and the per-lane MFMA operand fragment: 8 elements
 // (16 bytes) of 16-bit data, 32 elements (32 bytes) of 8-bit data.
-constexpr int in_size(int in) { return in == GEMM_BT_FP8_E4M3 || in == GEMM_BT_FP8_E5M2 ? 1 : 2; }
+constexpr int in_size(int in) {
+    return in == GEMM_BT_FP8_E4M3 || in == GEMM_BT_FP8_E5M2 || in == GEMM_BT_INT8 ? 1 : 2;
+}
+// int32 results are stored exactly as fp32 ones: 4 bytes of accumulator bits.
+constexpr int store_type(int out) { return out == GEMM_BT_INT32 ? GEMM_BT_F32 : out; }
 template <int ESZ>
 struct FragT {
     typedef u32x4 type;

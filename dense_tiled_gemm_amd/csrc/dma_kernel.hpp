@@ -399,21 +399,33 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         };
         // the NMMA MFMAs of one substep; after MFMA t it issues load d of the
         // refill if d * NMMA / CH == t (when do_load), and with ILR fragment
-        // read r of the next substep if r * RS == t
+        // read r of the next substep if r * RS == t.  An int8 fragment pair
+        // takes NH = 2 MFMAs of half the length (one per 16-byte half): the
+        // first halves of all NMMA pairs go before the second halves, so no
+        // MFMA waits for the accumulator of the one just before it, and the
+        // reads and loads follow every second one, at the same points in time.
+        constexpr int NH = IN == GEMM_BT_INT8 ? 2 : 1;
         auto mma_step = [&](const Frag (&b)[FN], const Frag (&a)[FM], bool do_load, auto&& load_d, auto&& read_r) {
-            static_for<0, NMMA>([&](auto tc) {
-                constexpr int t = decltype(tc)::value;
-                mfma1(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
+            static_for<0, NMMA * NH>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                constexpr int t = u % NMMA;
+                if constexpr (NH == 1)
+                    mfma1(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
+                else
+                    acc[t / FM][t % FM] = Mfma<IN>::template half<u / NMMA>(b[t / FM], a[t % FM], acc[t / FM][t % FM]);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (ILR)
-                    static_for<0, NRD>([&](auto rc) {
-                        if constexpr (decltype(rc)::value * RS == t) read_r(rc);
+                if constexpr (u % NH == NH - 1) {
+                    constexpr int p = u / NH;  // issue point, in units of full fragment pairs
+                    if constexpr (ILR)
+                        static_for<0, NRD>([&](auto rc) {
+                            if constexpr (decltype(rc)::value * RS == p) read_r(rc);
+                        });
+                    static_for<0, CH>([&](auto dc) {
+                        constexpr int d = decltype(dc)::value;
+                        if constexpr (d * NMMA / CH == p)
+                            if (do_load) load_d(d);
                     });
-                static_for<0, CH>([&](auto dc) {
-                    constexpr int d = decltype(dc)::value;
-                    if constexpr (d * NMMA / CH == t)
-                        if (do_load) load_d(d);
-                });
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
@@ -651,10 +663,10 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     if (vec_store == 2) {
         // every wave is past its last LDS read and its loads have landed
         barrier_no_fence();
-        store_tile_lds<OUT, FN, FM, BM, BN, WM, 64 * W, STAGES * STAGE_BYTES, MF>(acc, lds, C, M, N, m0, n0, wm * TM,
+        store_tile_lds<store_type(OUT), FN, FM, BM, BN, WM, 64 * W, STAGES * STAGE_BYTES, MF>(acc, lds, C, M, N, m0, n0, wm * TM,
                                                                              wn * TN, wm, threadIdx.x);
     } else {
-        store_tile<OUT, FN, FM, MF>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+        store_tile<store_type(OUT), FN, FM, MF>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
     }
 }
 

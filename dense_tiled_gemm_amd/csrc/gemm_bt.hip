@@ -39,19 +39,35 @@ constexpr int kSkinnyNB = 2, kSkinnyKS = 4;
 constexpr int kSwz = 2;
 constexpr int kGroupM = 4;
 
-// DMA-kernel variants: [in: bf16, f16][out: f32, bf16, f16] entry points.
+// DMA-kernel variants: [in][out] entry points.
 struct DmaVariant {
     const char* name;
     int bm, bn, bk, stages, wm, wn, swz;
     int lds_bytes;  // the ring: `stages` A+B stages, or five operand-tile slots
-    const void* fn[4][3];  // [bf16, f16, e4m3, e5m2][f32, bf16, f16]
+    const void* fn[5][4];  // [bf16, f16, e4m3, e5m2, int8][f32, bf16, f16, int32]
 };
 
 static bool is_fp8(int in_dtype) { return in_dtype == GEMM_BT_FP8_E4M3 || in_dtype == GEMM_BT_FP8_E5M2; }
+// 8-bit inputs of either kind: 128-element K steps, whole 16-byte rows
+static bool is_8bit(int in_dtype) { return is_fp8(in_dtype) || in_dtype == GEMM_BT_INT8; }
 static int in_index(int in_dtype) {
-    return in_dtype == GEMM_BT_BF16 ? 0 : (in_dtype == GEMM_BT_F16 ? 1 : (in_dtype == GEMM_BT_FP8_E4M3 ? 2 : 3));
+    switch (in_dtype) {
+        case GEMM_BT_BF16: return 0;
+        case GEMM_BT_F16: return 1;
+        case GEMM_BT_FP8_E4M3: return 2;
+        case GEMM_BT_FP8_E5M2: return 3;
+        default: return 4;
+    }
 }
-static int out_index(int out_dtype) { return out_dtype == GEMM_BT_F32 ? 0 : (out_dtype == GEMM_BT_BF16 ? 1 : 2); }
+static int out_index(int out_dtype) {
+    switch (out_dtype) {
+        case GEMM_BT_F32: return 0;
+        case GEMM_BT_BF16: return 1;
+        case GEMM_BT_F16: return 2;
+        default: return 3;
+    }
+}
+static int out_size(int out_dtype) { return out_dtype == GEMM_BT_F32 || out_dtype == GEMM_BT_INT32 ? 4 : 2; }
 
 template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32,
           bool ALL = false, int LDW = 0, int RING5 = 0, bool F8 = false>
@@ -69,6 +85,7 @@ static DmaVariant dma_variant(const char* name) {
             v.fn[3][0] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
             v.fn[3][1] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
             v.fn[3][2] = (const void*)&dma_kernel<GEMM_BT_FP8_E5M2, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[4][3] = (const void*)&dma_kernel<GEMM_BT_INT8, GEMM_BT_INT32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
         }
     } else {
         v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
@@ -84,8 +101,9 @@ static DmaVariant dma_variant(const char* name) {
 }
 
 // Index 0 is the default for large grids, 1 for smaller ones, 2 for the
-// smallest (see plan_impl), 3..5 the same for 8-bit float inputs (128-element
-// K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32x64 MFMAs);
+// smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
+// (128-element K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32
+// MFMAs over 64-element substeps);
 // the rest exist for tuning (GEMM_BT_FORCE_TILE=<name>) and are built for the
 // bf16->bf16 and f16->f16 combinations only.
 constexpr int kFp8Variants = 3;
@@ -120,12 +138,12 @@ static const DmaVariant* dma_variants(int* count) {
 struct SkinnyVariant {
     const char* name;
     int bn, kb, stages, waves;
-    const void* fn[2][3];
+    const void* fn[5][4];  // 16-bit inputs only: [bf16, f16][f32, bf16, f16]
 };
 
 template <int BN, int KB, int S, int W, bool ALL = false, int ROT = 0>
 static SkinnyVariant skinny_variant(const char* name) {
-    SkinnyVariant v = {name, BN, KB, S, W, {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}}};
+    SkinnyVariant v = {name, BN, KB, S, W, {}};
     v.fn[0][1] = (const void*)&skinny_dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BN, KB, S, W, ROT>;
     v.fn[1][2] = (const void*)&skinny_dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BN, KB, S, W, ROT>;
     if constexpr (ALL) {
@@ -207,13 +225,17 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
     if (!p) return GEMM_BT_ERR_INVALID_VALUE;
     std::memset(p, 0, sizeof(*p));
     if (M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
-    if (in_dtype != GEMM_BT_BF16 && in_dtype != GEMM_BT_F16 && !is_fp8(in_dtype)) return GEMM_BT_ERR_UNSUPPORTED;
-    if (out_dtype != GEMM_BT_F32 && out_dtype != GEMM_BT_BF16 && out_dtype != GEMM_BT_F16)
+    if (in_dtype != GEMM_BT_BF16 && in_dtype != GEMM_BT_F16 && !is_8bit(in_dtype)) return GEMM_BT_ERR_UNSUPPORTED;
+    if (out_dtype != GEMM_BT_F32 && out_dtype != GEMM_BT_BF16 && out_dtype != GEMM_BT_F16 && out_dtype != GEMM_BT_INT32)
         return GEMM_BT_ERR_UNSUPPORTED;
-    const int osz = out_dtype == GEMM_BT_F32 ? 4 : 2;
+    // integer inputs give integer outputs, float inputs float outputs
+    if ((in_dtype == GEMM_BT_INT8) != (out_dtype == GEMM_BT_INT32)) return GEMM_BT_ERR_UNSUPPORTED;
+    // int8: every partial sum within int32 (|product| <= 2^14, K * 2^14 < 2^31)
+    if (in_dtype == GEMM_BT_INT8 && K > 131071) return GEMM_BT_ERR_UNSUPPORTED;
+    const int osz = out_size(out_dtype);
     // 32-bit buffer offsets inside one 256-row panel of A, B and C.
     if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
-    const int isz = is_fp8(in_dtype) ? 1 : 2;
+    const int isz = is_8bit(in_dtype) ? 1 : 2;
     if (256 * K * isz >= 0x7FFFFFFFLL || 256 * N * (int64_t)osz >= 0x7FFFFFFFLL) return GEMM_BT_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) {
         p->kernel = KIND_NONE;
@@ -227,7 +249,7 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         p->grid = g < 4096 ? g : 4096;
         return GEMM_BT_OK;
     }
-    if (is_fp8(in_dtype)) {
+    if (is_8bit(in_dtype)) {
         // 8-bit inputs: whole 16-byte chunks only (K a multiple of 16, A and B
         // 16-byte aligned), always the LDS-DMA kernel
         if (K % 16 != 0 || a_align % 16 != 0 || b_align % 16 != 0) return GEMM_BT_ERR_UNSUPPORTED;
@@ -447,10 +469,10 @@ int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
     int st = plan_impl(M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
     if (st != GEMM_BT_OK) return st;
     if (p.kernel == KIND_NONE) return GEMM_BT_OK;
-    const int osz = out_dtype == GEMM_BT_F32 ? 4 : 2;
+    const int osz = out_size(out_dtype);
     if (!C) return GEMM_BT_ERR_INVALID_VALUE;
     if (p.kernel != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
-    const int isz = is_fp8(in_dtype) ? 1 : 2;
+    const int isz = is_8bit(in_dtype) ? 1 : 2;
     if ((uintptr_t)A % isz || (uintptr_t)B % isz || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
 
     int num_cu = 256;

@@ -13,13 +13,19 @@
  * types); products are accumulated in fp32 and the
  * result is rounded once, to nearest even, into the output type ("Chapter 7:
  * Writing custom kernels with Pallas", section 4.1': fp32 accumulator, cast
- * only after the last K step).  C is overwritten: there is no alpha/beta.
+ * only after the last K step).  8-bit integer inputs (two's complement) are
+ * the integer MMA operand type of the same Mosaic GPU section, with an int32
+ * accumulator: there C is the exact int32 sum, and int8 in requires int32
+ * out (and int32 out requires int8 in).  C is overwritten: there is no
+ * alpha/beta.
  *
  * Layout.  Dense and contiguous: lda = ldb = K elements, ldc = N elements.
  * For 16-bit inputs pointers need only element alignment (2 bytes, 4 bytes for
  * fp32 output); 16-byte alignment together with K % 8 == 0 selects the
- * widest loads and is a performance matter only.  8-bit inputs need whole
- * 16-byte rows: K % 16 == 0 and A, B 16-byte aligned (else UNSUPPORTED).
+ * widest loads and is a performance matter only.  8-bit inputs (float or
+ * integer) need whole 16-byte rows: K % 16 == 0 and A, B 16-byte aligned
+ * (else UNSUPPORTED).  int8 inputs also need K <= 131071, so that no sum can
+ * leave the int32 range (|A[i][k] * B[j][k]| <= 2^14).
  *
  * Ownership.  The caller owns A, B and C (device memory, e.g. from PyTorch).
  * The library allocates nothing per call, keeps no pointer after it returns
@@ -46,7 +52,9 @@ typedef enum {
     GEMM_BT_F16 = 1,      /* IEEE binary16 */
     GEMM_BT_BF16 = 2,     /* bfloat16: the upper 16 bits of a binary32 */
     GEMM_BT_FP8_E4M3 = 3, /* OCP 8-bit E4M3 (input only): bias 7, no infinities, max 448 */
-    GEMM_BT_FP8_E5M2 = 4  /* OCP 8-bit E5M2 (input only): bias 15, IEEE-style infinities */
+    GEMM_BT_FP8_E5M2 = 4, /* OCP 8-bit E5M2 (input only): bias 15, IEEE-style infinities */
+    GEMM_BT_INT8 = 5,     /* two's-complement 8-bit integer (input only; output GEMM_BT_INT32) */
+    GEMM_BT_INT32 = 6     /* two's-complement 32-bit integer (output only; input GEMM_BT_INT8) */
 } gemm_bt_dtype;
 
 /* Status codes returned by every entry point. */
@@ -65,9 +73,11 @@ typedef enum {
  *   C          device pointer, M x N elements of out_dtype, row-major; overwritten
  *   M, N, K    sizes, each in [0, 2^31 - 1]; M*K, N*K and M*N elements must each
  *              fit below 2^31 bytes per 256-row panel (checked: UNSUPPORTED);
- *              8-bit inputs: K % 16 == 0 and A, B 16-byte aligned (UNSUPPORTED)
- *   in_dtype   GEMM_BT_BF16, GEMM_BT_F16, GEMM_BT_FP8_E4M3 or GEMM_BT_FP8_E5M2
- *   out_dtype  GEMM_BT_F32, GEMM_BT_BF16 or GEMM_BT_F16
+ *              8-bit inputs: K % 16 == 0 and A, B 16-byte aligned (UNSUPPORTED);
+ *              int8 inputs: K <= 131071 (UNSUPPORTED)
+ *   in_dtype   GEMM_BT_BF16, GEMM_BT_F16, GEMM_BT_FP8_E4M3, GEMM_BT_FP8_E5M2 or GEMM_BT_INT8
+ *   out_dtype  GEMM_BT_F32, GEMM_BT_BF16 or GEMM_BT_F16 for float inputs; GEMM_BT_INT32
+ *              for GEMM_BT_INT8 inputs (any other pairing: UNSUPPORTED)
  *   stream     hipStream_t to enqueue on; NULL means the default stream
  * M == 0 or N == 0: nothing is enqueued, returns GEMM_BT_OK.
  * K == 0: C is filled with zeros (the empty sum) on `stream`.

@@ -89,6 +89,20 @@ def test_plan_choices():
                      (64, 64, 48, code, code, 256, 256, 256)):
             with pytest.raises(gb.GemmBtError):
                 gb.gemm_bt_plan(*args)
+    # 8-bit integer inputs: the same kernels and tiles, int32 out only, K <= 131071
+    p = gb.gemm_bt_plan(4096, 4096, 4096, gb.INT8, gb.INT32)
+    assert (p.kernel, p.bm, p.bn, p.bk, p.vec, p.stages, p.lds_bytes) == (4, 256, 256, 128, 16, 5, 160 * 1024)
+    assert gb.gemm_bt_plan(1024, 4096, 4096, gb.INT8, gb.INT32).bm == 128
+    assert gb.gemm_bt_plan(512, 512, 512, gb.INT8, gb.INT32).bm == 64
+    assert gb.gemm_bt_plan(64, 64, 131056, gb.INT8, gb.INT32).kernel == 4
+    assert gb.gemm_bt_plan(7, 9, 0, gb.INT8, gb.INT32).kernel == 1
+    for args in ((64, 64, 48, gb.INT8, gb.F32), (64, 64, 48, gb.INT8, gb.BF16), (64, 64, 48, gb.BF16, gb.INT32),
+                 (64, 64, 48, gb.FP8_E5M2, gb.INT32), (64, 64, 48, gb.INT32, gb.INT32), (64, 64, 48, gb.INT8, gb.INT8),
+                 (64, 64, 40, gb.INT8, gb.INT32), (64, 64, 131072, gb.INT8, gb.INT32)):
+        with pytest.raises(gb.GemmBtError):
+            gb.gemm_bt_plan(*args)
+    with pytest.raises(gb.GemmBtError):
+        gb.gemm_bt_plan(64, 64, 48, gb.INT8, gb.INT32, a_align=8)
     p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)  # 16 tiles of 128: 64x64 tiles fill more CUs
     assert (p.kernel, p.bm, p.grid) == (4, 64, 64)
     assert gb.gemm_bt_plan(1024, 1024, 200, gb.BF16, gb.F32).bm == 128

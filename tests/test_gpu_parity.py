@@ -3,7 +3,8 @@
 Every case prints its name, shape and seed before it touches the GPU.  Outputs
 are poisoned with NaN before each call so a missed store cannot pass.  The
 rules (oracle.tolerance): fp32 out |err| <= 1e-3·‖A_i‖‖B_j‖; 16-bit out adds one
-ulp of the oracle value; integer-valued inputs must match bit for bit.
+ulp of the oracle value; integer-valued inputs must match bit for bit, and so
+must every int32 result of int8 inputs (against the oracle's exact int64 sums).
 """
 import sys
 
@@ -18,7 +19,9 @@ from oracle import tolerance
 pytestmark = pytest.mark.gpu
 
 TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
-            "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+            "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2, "i8": torch.int8, "i32": torch.int32}
+# int32 poison: no sum of K <= 131071 products of int8 values reaches -2^31
+I32_POISON = -2 ** 31
 
 
 def say(*a):
@@ -27,7 +30,7 @@ def say(*a):
 
 
 def to_dev(bits, in_dtype):
-    raw = np.uint8 if in_dtype in ("e4m3", "e5m2") else np.int16
+    raw = np.uint8 if in_dtype in ("e4m3", "e5m2", "i8") else np.int16
     t = torch.from_numpy(np.ascontiguousarray(bits).view(raw))
     return t.to("cuda").view(TORCH_DT[in_dtype])
 
@@ -36,10 +39,23 @@ def run_gpu(gb, a_bits, b_bits, in_dtype, out_dtype):
     a = to_dev(a_bits, in_dtype)
     b = to_dev(b_bits, in_dtype)
     M, N = a.shape[0], b.shape[0]
-    c = torch.full((M, N), float("nan"), dtype=TORCH_DT[out_dtype], device="cuda")
+    poison = I32_POISON if out_dtype == "i32" else float("nan")
+    c = torch.full((M, N), poison, dtype=TORCH_DT[out_dtype], device="cuda")
     gb.mm_bt(a, b, out_dtype=TORCH_DT[out_dtype], out=c)
     torch.cuda.synchronize()
     return c.cpu()
+
+
+def check_i8(c, a_bits, b_bits, what, I=None, J=None):
+    """int32 results of int8 inputs: equal to the oracle's exact sums, entry for entry."""
+    got = c.numpy().astype(np.int64)
+    if I is None:
+        ref = oracle.gemm_bt_i8(a_bits, b_bits)
+    else:
+        ref = oracle.gemm_bt_i8_entries(a_bits, b_bits, I, J)
+        got = got[I, J]
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, (what, len(bad), [(tuple(x), int(got[tuple(x)]), int(ref[tuple(x)])) for x in bad[:5]])
 
 
 def f64(c):
@@ -150,6 +166,53 @@ def test_fp8_unsupported_layouts(gpu):
     assert torch.isnan(c).all()
 
 
+# 8-bit integer inputs: the same shapes over the whole int8 range, the range
+# ends at the largest K whose sums all fit int32, and the refused layouts.
+@pytest.mark.parametrize("dist", ["int8", "int"])
+def test_i8_sweep(gpu, dist):
+    for i, (M, N, K) in enumerate(FP8_SHAPES):
+        seed = (1100 if dist == "int8" else 1150) + i
+        say("i8 sweep", dist, M, N, K, "seed", seed)
+        a, b = synth.make(M, N, K, "i8", dist, seed)
+        c = run_gpu(gpu, a, b, "i8", "i32")
+        check_i8(c, a, b, (M, N, K))
+
+
+def test_i8_range_ends(gpu):
+    """Rows of all -128 or all 127 at K = 131056: the sums 16384·K, -16256·K and 16129·K, next to 2^31."""
+    M, N, K = 64, 96, 131056
+    say("i8 range ends", M, N, K)
+    ra = np.where(np.arange(M)[:, None] % 2 == 0, -128, 127) * np.ones((1, K))
+    rb = np.where(np.arange(N)[:, None] % 3 == 0, -128, 127) * np.ones((1, K))
+    a, b = synth.round_bits(ra, "i8"), synth.round_bits(rb, "i8")
+    c = run_gpu(gpu, a, b, "i8", "i32")
+    want = ra[:, :1] * rb[:, :1].T * K
+    assert np.array_equal(c.numpy().astype(np.int64), want.astype(np.int64))
+    assert int(c.max()) == 16384 * K and int(c.min()) == -16256 * K
+    check_i8(c, a, b, "range ends")
+
+
+def test_i8_unsupported(gpu):
+    """int8 needs int32 out (and the reverse), K % 16 == 0, 16-byte aligned A and B, K <= 131071."""
+    s = torch.cuda.current_stream().cuda_stream
+    a = torch.zeros(64 * 131072 + 64, dtype=torch.int8, device="cuda")
+    b = torch.zeros(64 * 131072 + 64, dtype=torch.int8, device="cuda")
+    c = torch.full((64, 64), I32_POISON, dtype=torch.int32, device="cuda")
+    A, B, C = a.data_ptr(), b.data_ptr(), c.data_ptr()
+    I8, I32 = gpu.INT8, gpu.INT32
+    cases = [(A, B, 48, I8, gpu.F32), (A, B, 48, I8, gpu.BF16), (A, B, 48, gpu.BF16, I32), (A, B, 48, gpu.FP8_E4M3, I32),
+             (A, B, 40, I8, I32), (A + 8, B, 48, I8, I32), (A, B + 4, 48, I8, I32), (A, B, 131072, I8, I32)]
+    for A_, B_, K, ind, outd in cases:
+        say("i8 unsupported", K, ind, outd, A_ - A, B_ - B)
+        assert gpu.gemm_bt(A_, B_, C, 64, 64, K, ind, outd, s) == gpu.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert (c == I32_POISON).all()
+    say("i8 K = 0")
+    assert gpu.gemm_bt(A, B, C, 64, 64, 0, I8, I32, s) == gpu.OK  # the empty sum
+    torch.cuda.synchronize()
+    assert (c == 0).all()
+
+
 def sample_entries(M, N, rng, tile=256):
     """Rows and columns at every tile edge plus random ones; returns (I, J)."""
     edge_r = sorted({0, M - 1} | {min(M - 1, t + d) for t in range(0, M, tile) for d in (-1, 0)} - {-1})
@@ -172,6 +235,10 @@ def test_workload_full_size(gpu, name):
     say("workload", name, w.M, w.N, w.K, w.in_dtype, w.out_dtype, "seed", w.seed)
     a, b = synth.make_workload(w)
     c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
+    if w.in_dtype == "i8":
+        I, J = sample_entries(w.M, w.N, np.random.default_rng(w.seed))
+        check_i8(c, a, b, name, I, J)
+        return
     cf = f64(c)
     assert np.isfinite(cf).all(), name
     if w.M * w.N * w.K <= 8e9:
@@ -192,7 +259,10 @@ def test_workload_integer_twin_bit_exact(gpu, name):
     say("workload int twin", w.name, w.M, w.N, w.K, "seed", w.seed)
     a, b = synth.make_workload(w)
     c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
-    if w.M * w.N * w.K <= 8e9:
+    if w.in_dtype == "i8":
+        I, J = sample_entries(w.M, w.N, np.random.default_rng(w.seed))
+        check_i8(c, a, b, w.name, I, J)
+    elif w.M * w.N * w.K <= 8e9:
         check_bits_full(c, a, b, w.in_dtype, w.out_dtype, w.name)
     else:
         rng = np.random.default_rng(w.seed)
