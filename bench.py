@@ -9,8 +9,9 @@ Prints ONE JSON line on stdout:
   cpu_baseline the CPU oracle timed on a bounded sample of the same product
   secondary    µs / TFLOP/s / GB/s of the other workloads (1024×4096×4096
                f16, 16×8192×8192 skinny, 512³, 1000×3000×2050, 4096³ with
-               E4M3 inputs against the fp8 peak, and 4096³ int8 -> int32
-               against the int8 peak), same timing
+               E4M3 inputs against the fp8 peak, 4096³ int8 -> int32
+               against the int8 peak, and a batch of 64 products of 512³ in
+               one gemm_bt_batched call), same timing
   copy_GBps    a plain 1 GiB device copy, as context for achievable HBM
 Diagnostics go to stderr.  The default 400 untimed warm-up launches matter:
 from idle, an MI355X needs about 25 ms of sustained GEMM launches before its
@@ -93,7 +94,7 @@ class Case:
         for r in range(rotate):
             ar = a if r == 0 else a.clone()
             br = b if r == 0 else b.clone()
-            c = torch.empty((w.M, w.N), dtype=dt[w.out_dtype], device="cuda")
+            c = torch.empty(((w.batch,) if w.batch > 1 else ()) + (w.M, w.N), dtype=dt[w.out_dtype], device="cuda")
             self.sets.append((ar, br, c))
         self.in_code = {"bf16": gb.BF16, "f16": gb.F16, "e4m3": gb.FP8_E4M3, "e5m2": gb.FP8_E5M2,
                         "i8": gb.INT8}[w.in_dtype]
@@ -103,7 +104,12 @@ class Case:
 
     def step(self, i, stream):
         pa, pb, pc = self.ptrs[i % self.rotate]
-        st = self.gb.gemm_bt(pa, pb, pc, self.w.M, self.w.N, self.w.K, self.in_code, self.out_code, stream)
+        w = self.w
+        if w.batch > 1:
+            st = self.gb.gemm_bt_batched(pa, pb, pc, w.batch, w.M, w.N, w.K, w.M * w.K, w.N * w.K, w.M * w.N,
+                                         self.in_code, self.out_code, stream)
+        else:
+            st = self.gb.gemm_bt(pa, pb, pc, w.M, w.N, w.K, self.in_code, self.out_code, stream)
         if st != self.gb.OK:
             raise self.gb.GemmBtError(st)
 
@@ -256,7 +262,8 @@ def main():
     if not args.no_secondary:
         sec = {}
         for name in ("m1024_n4096_k4096_f16_f16", "skinny_m16_n8192_k8192_bf16_bf16", "sq512_bf16_f32",
-                     "ragged_m1000_n3000_k2050_bf16_f32", "sq4096_e4m3_bf16", "sq4096_i8_i32"):
+                     "ragged_m1000_n3000_k2050_bf16_f32", "sq4096_e4m3_bf16", "sq4096_i8_i32",
+                     "batch64_sq512_bf16_bf16"):
             w2 = synth.WORKLOADS[name]
             c2 = Case(w2, torch, gb)
             _, ms2 = c2.time(max(50, args.steps // 2), args.warmup)

@@ -6,10 +6,12 @@ PyTorch fallback: if the shared library is missing, every call raises.
 
 Entry points (same names as the C-ABI in ``include/gemm_bt.h``):
   gemm_bt(A, B, C, M, N, K, in_dtype, out_dtype, stream)   raw device pointers
+  gemm_bt_batched(A, B, C, batch, M, N, K, stride_a, stride_b, stride_c, in_dtype, out_dtype, stream)
   gemm_bt_status_string(status), gemm_bt_version()
   gemm_bt_plan(M, N, K, in_dtype, out_dtype, a_align, b_align, c_align)
+  gemm_bt_plan_batched(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align)
   gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m)
-and a torch convenience wrapper ``mm_bt(a, b, out_dtype)``.
+and a torch convenience wrapper ``mm_bt(a, b, out_dtype)`` (2-D or batched 3-D operands).
 """
 from __future__ import annotations
 
@@ -22,7 +24,8 @@ OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_LAUNCH = 0, 1, 2, 3, 
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemm_bt.so")
-EXPORTS = ("gemm_bt", "gemm_bt_status_string", "gemm_bt_version", "gemm_bt_plan", "gemm_bt_tile_coord")
+EXPORTS = ("gemm_bt", "gemm_bt_batched", "gemm_bt_status_string", "gemm_bt_version", "gemm_bt_plan",
+           "gemm_bt_plan_batched", "gemm_bt_tile_coord")
 
 _lock = threading.Lock()
 _lib = None
@@ -39,7 +42,7 @@ class Plan(ctypes.Structure):
                 ("bk", ctypes.c_int), ("threads", ctypes.c_int), ("vec", ctypes.c_int), ("group_m", ctypes.c_int),
                 ("ksplit", ctypes.c_int), ("stages", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("tiles_m", ctypes.c_int64),
-                ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64)]
+                ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64), ("batch", ctypes.c_int64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -57,6 +60,10 @@ def load():
             vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
             lib.gemm_bt.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
             lib.gemm_bt.restype = ci
+            lib.gemm_bt_batched.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
+            lib.gemm_bt_batched.restype = ci
+            lib.gemm_bt_plan_batched.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
+            lib.gemm_bt_plan_batched.restype = ci
             lib.gemm_bt_status_string.argtypes = [ci]
             lib.gemm_bt_status_string.restype = ctypes.c_char_p
             lib.gemm_bt_version.argtypes = []
@@ -84,6 +91,21 @@ def gemm_bt(A: int, B: int, C: int, M: int, N: int, K: int, in_dtype: int, out_d
             stream: int | None) -> int:
     """Raw call: device pointers as integers, returns the status code."""
     return int(load().gemm_bt(A or None, B or None, C or None, M, N, K, in_dtype, out_dtype, stream or None))
+
+
+def gemm_bt_batched(A: int, B: int, C: int, batch: int, M: int, N: int, K: int, stride_a: int, stride_b: int,
+                    stride_c: int, in_dtype: int, out_dtype: int, stream: int | None) -> int:
+    """Raw batched call: item z uses A + z*stride_a etc. (strides in elements); returns the status code."""
+    return int(load().gemm_bt_batched(A or None, B or None, C or None, batch, M, N, K, stride_a, stride_b, stride_c,
+                                      in_dtype, out_dtype, stream or None))
+
+
+def gemm_bt_plan_batched(batch, M, N, K, in_dtype, out_dtype, a_align=256, b_align=256, c_align=256):
+    p = Plan()
+    st = load().gemm_bt_plan_batched(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, ctypes.byref(p))
+    if st != OK:
+        raise GemmBtError(st, "gemm_bt_plan_batched")
+    return p
 
 
 def gemm_bt_plan(M, N, K, in_dtype, out_dtype, a_align=256, b_align=256, c_align=256):
@@ -130,20 +152,36 @@ def _torch_dtype(code):
     return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, INT32: torch.int32}[code]
 
 
+def _batch_operand(x):
+    """(tensor, item stride in elements) of a 2-D or 3-D operand: a 2-D operand, or a 3-D one whose batch
+    stride is 0 over contiguous items (``expand``), is shared by every item; others are made contiguous."""
+    if x.dim() == 2:
+        return x.contiguous(), 0
+    if x.shape[0] > 0 and x.stride(0) == 0 and x[0].is_contiguous():
+        return x[0], 0
+    x = x.contiguous()
+    return x, x.shape[1] * x.shape[2]
+
+
 def mm_bt(a, b, out_dtype=None, out=None, stream=None):
     """C = a @ b.T for CUDA/HIP tensors a (M×K) and b (N×K) of one input dtype.
 
+    Batched: a (Z×M×K) and/or b (Z×N×K) give C (Z×M×N), C[z] = a[z] @ b[z].T;
+    a 2-D operand (or one expanded along the batch) is shared by every item.
     Inputs: bfloat16, float16, float8_e4m3fn, float8_e5m2 or int8 (8-bit
     inputs need K % 16 == 0; int8 also K <= 131071).  ``out_dtype`` defaults
     to a's dtype (bfloat16 for 8-bit float inputs, which are not an output
     format; int32, the only one allowed, for int8); ``out`` may be a preallocated
-    contiguous M×N tensor.  The call is asynchronous on ``stream`` (default:
-    torch's current stream of a's device).
+    contiguous M×N (Z×M×N) tensor.  The call is asynchronous on ``stream``
+    (default: torch's current stream of a's device).
     """
     import torch
 
-    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
-        raise ValueError("expected a (M,K) and b (N,K), got %s and %s" % (tuple(a.shape), tuple(b.shape)))
+    if a.dim() not in (2, 3) or b.dim() not in (2, 3) or a.shape[-1] != b.shape[-1]:
+        raise ValueError("expected a (M,K) or (Z,M,K) and b (N,K) or (Z,N,K), got %s and %s"
+                         % (tuple(a.shape), tuple(b.shape)))
+    if a.dim() == 3 and b.dim() == 3 and a.shape[0] != b.shape[0]:
+        raise ValueError("batch sizes differ: %d and %d" % (a.shape[0], b.shape[0]))
     if a.dtype != b.dtype:
         raise TypeError("a and b must share one dtype")
     if not a.is_cuda or not b.is_cuda or a.device != b.device:
@@ -152,18 +190,25 @@ def mm_bt(a, b, out_dtype=None, out=None, stream=None):
     default_out = BF16 if in_code in (FP8_E4M3, FP8_E5M2) else (INT32 if in_code == INT8 else in_code)
     out_code = default_out if out_dtype is None else (_torch_code(out_dtype) if not isinstance(out_dtype, int)
                                                       else out_dtype)
-    a = a.contiguous()
-    b = b.contiguous()
-    M, K = a.shape
-    N = b.shape[0]
+    batched = a.dim() == 3 or b.dim() == 3
+    Z = a.shape[0] if a.dim() == 3 else (b.shape[0] if b.dim() == 3 else 1)
+    M, K = a.shape[-2], a.shape[-1]
+    N = b.shape[-2]
+    a, sa = _batch_operand(a)
+    b, sb = _batch_operand(b)
+    shape = (Z, M, N) if batched else (M, N)
     if out is None:
-        out = torch.empty((M, N), dtype=_torch_dtype(out_code), device=a.device)
-    elif out.shape != (M, N) or not out.is_contiguous() or out.dtype != _torch_dtype(out_code):
-        raise ValueError("out must be a contiguous %dx%d %s tensor" % (M, N, _torch_dtype(out_code)))
+        out = torch.empty(shape, dtype=_torch_dtype(out_code), device=a.device)
+    elif tuple(out.shape) != shape or not out.is_contiguous() or out.dtype != _torch_dtype(out_code):
+        raise ValueError("out must be a contiguous %s %s tensor" % ("x".join(map(str, shape)), _torch_dtype(out_code)))
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream
     with torch.cuda.device(a.device):
-        st = gemm_bt(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, in_code, out_code, stream)
+        if batched:
+            st = gemm_bt_batched(a.data_ptr(), b.data_ptr(), out.data_ptr(), Z, M, N, K, sa, sb, M * N, in_code,
+                                 out_code, stream)
+        else:
+            st = gemm_bt(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, in_code, out_code, stream)
     if st != OK:
         raise GemmBtError(st)
     return out

@@ -78,6 +78,16 @@ __device__ inline u32 pack2<GEMM_BT_F16>(float a, float b) {
     return __builtin_bit_cast(u32, p);
 }
 
+// Batch item z of a batched product: its A, B and C start z byte strides
+// after the base pointers.  A stride of 0 shares the operand between all
+// items; a single product is item 0 with zero strides.
+template <class PA, class PB, class PC>
+__device__ inline void batch_item(long long z, PA& A, PB& B, PC& C, long long sa, long long sb, long long sc) {
+    A = (PA)((const char*)A + z * sa);
+    B = (PB)((const char*)B + z * sb);
+    C = (PC)((char*)C + z * sc);
+}
+
 // MFMA wrappers over raw 16-byte operands (8 elements of the input type).
 template <int IN>
 struct Mfma;

@@ -153,7 +153,8 @@ template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, i
 __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                           void* __restrict__ C, int M, int N, int K,
                                                           int tiles_m, int tiles_n, int group_m,
-                                                          int vec_store) {
+                                                          int vec_store, int item_tiles_m, long long sa, long long sb,
+                                                          long long sc) {
     constexpr int W = WM * WN;
     constexpr int ESZ = in_size(IN);     // bytes per input element (2, or 1 for 8-bit floats)
     constexpr int EPC = 16 / ESZ;        // elements per 16-byte chunk
@@ -194,6 +195,13 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
 
     int64_t tm64, tn64;
     tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
+    {
+        // batch items are stacked along the tile rows (tiles_m counts all of
+        // them), so the XCD regrouping gives each die whole items
+        const int z = (int)tm64 / item_tiles_m;
+        tm64 -= (int64_t)z * item_tiles_m;
+        batch_item(z, A, B, C, sa, sb, sc);
+    }
     const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
     const u32 row_bytes = (u32)K * (u32)ESZ;

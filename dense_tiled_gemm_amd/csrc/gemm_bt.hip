@@ -14,8 +14,10 @@
 
 namespace gbt {
 
-// Zero fill of C for K == 0 (every entry is an empty sum).
-__global__ void zero_fill_kernel(u16* __restrict__ c, size_t n16) {
+// Zero fill of C for K == 0 (every entry is an empty sum); batch item
+// blockIdx.y starts `sc` bytes after the previous one.
+__global__ void zero_fill_kernel(u16* __restrict__ c, size_t n16, long long sc) {
+    c = (u16*)((char*)c + (long long)blockIdx.y * sc);
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) c[i] = 0;
 }
@@ -220,11 +222,16 @@ static int pick_vec(int64_t K, int a_align, int b_align) {
     return 1;
 }
 
-static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
+// Largest batch: the batch index is the grid's y dimension.
+constexpr int64_t kMaxBatch = 65535;
+
+static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
                      int b_align, int c_align, int num_cu, gemm_bt_plan_t* p) {
     if (!p) return GEMM_BT_ERR_INVALID_VALUE;
     std::memset(p, 0, sizeof(*p));
-    if (M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
+    if (batch > kMaxBatch) return GEMM_BT_ERR_UNSUPPORTED;
+    p->batch = batch;
     if (in_dtype != GEMM_BT_BF16 && in_dtype != GEMM_BT_F16 && !is_8bit(in_dtype)) return GEMM_BT_ERR_UNSUPPORTED;
     if (out_dtype != GEMM_BT_F32 && out_dtype != GEMM_BT_BF16 && out_dtype != GEMM_BT_F16 && out_dtype != GEMM_BT_INT32)
         return GEMM_BT_ERR_UNSUPPORTED;
@@ -237,10 +244,13 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
     if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
     const int isz = is_8bit(in_dtype) ? 1 : 2;
     if (256 * K * isz >= 0x7FFFFFFFLL || 256 * N * (int64_t)osz >= 0x7FFFFFFFLL) return GEMM_BT_ERR_UNSUPPORTED;
-    if (M == 0 || N == 0) {
+    if (batch == 0 || M == 0 || N == 0) {
         p->kernel = KIND_NONE;
         return GEMM_BT_OK;
     }
+    // the tile tiers count the workgroups of all batch items
+    const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256) * batch;
+    const int64_t tiles_m128 = ((M + 127) / 128) * ((N + 127) / 128) * batch;
     if (K == 0) {
         p->kernel = KIND_FILL;
         p->threads = 256;
@@ -255,8 +265,6 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         if (K % 16 != 0 || a_align % 16 != 0 || b_align % 16 != 0) return GEMM_BT_ERR_UNSUPPORTED;
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
-        const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256);
-        const int64_t tiles_m128 = ((M + 127) / 128) * ((N + 127) / 128);
         int use = kFp8Variants + (tiles_l >= num_cu ? 0 : (tiles_m128 * 4 >= num_cu ? 1 : 2));
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
@@ -275,6 +283,7 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         p->tiles_m = (M + p->bm - 1) / p->bm;
         p->tiles_n = (N + p->bn - 1) / p->bn;
         p->grid = p->tiles_m * p->tiles_n;
+        if (p->grid * batch > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
         return GEMM_BT_OK;
     }
     p->vec = pick_vec(K, a_align, b_align);
@@ -311,7 +320,6 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         p->grid = p->tiles_n;
         return GEMM_BT_OK;
     }
-    const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256);
     const bool big = tiles_l >= num_cu;
     p->group_m = kGroupM;
     p->ksplit = 1;
@@ -322,7 +330,6 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
         const DmaVariant* vs = dma_variants(&n);
         // 256x256 when that fills every CU; else 128x128 unless it leaves
         // three quarters of the CUs idle, then 64x64
-        const int64_t tiles_m128 = ((M + 127) / 128) * ((N + 127) / 128);
         int use = big ? 0 : (tiles_m128 * 4 >= num_cu ? 1 : 2);
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
@@ -348,6 +355,8 @@ static int plan_impl(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtyp
     p->tiles_m = (M + p->bm - 1) / p->bm;
     p->tiles_n = (N + p->bn - 1) / p->bn;
     p->grid = p->tiles_m * p->tiles_n;
+    // the tiled kernels launch all items' tiles in one grid row
+    if (p->grid * batch > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
     (void)c_align;
     return GEMM_BT_OK;
 }
@@ -450,7 +459,12 @@ const char* gemm_bt_status_string(int status) {
 
 int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align, int b_align,
                  int c_align, gemm_bt_plan_t* plan) {
-    return plan_impl(M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
+    return plan_impl(1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
+}
+
+int gemm_bt_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
+                         int b_align, int c_align, gemm_bt_plan_t* plan) {
+    return plan_impl(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
 }
 
 int gemm_bt_tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m, int64_t* tm, int64_t* tn) {
@@ -462,35 +476,57 @@ int gemm_bt_tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_
 
 int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
             void* stream) {
+    return gemm_bt_batched(A, B, C, 1, M, N, K, 0, 0, 0, in_dtype, out_dtype, stream);
+}
+
+int gemm_bt_batched(const void* A, const void* B, void* C, int64_t batch, int64_t M, int64_t N, int64_t K,
+                    int64_t stride_a, int64_t stride_b, int64_t stride_c, int in_dtype, int out_dtype, void* stream) {
     gemm_bt_plan_t p;
-    const int a_al = align_of(A), b_al = align_of(B), c_al = align_of(C);
+    if (stride_a < 0 || stride_b < 0 || stride_c < 0) return GEMM_BT_ERR_INVALID_VALUE;
+    const bool multi = batch > 1;
+    const int isz = is_8bit(in_dtype) ? 1 : 2;
+    const int osz = out_size(out_dtype);
+    // every item's pointers: the base alignment, lowered by that of the byte stride
+    auto item_align = [&](const void* base, int64_t stride, int esz) {
+        const int a = align_of(base);
+        if (!multi || stride == 0) return a;
+        const int s = align_of((const void*)(uintptr_t)((uint64_t)stride * (uint64_t)esz));
+        return a < s ? a : s;
+    };
+    const int a_al = item_align(A, stride_a, isz), b_al = item_align(B, stride_b, isz),
+              c_al = item_align(C, stride_c, osz);
     // Plan against the default CU count first: it validates the arguments
     // without touching the device.
-    int st = plan_impl(M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
+    int st = plan_impl(batch, M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
     if (st != GEMM_BT_OK) return st;
     if (p.kernel == KIND_NONE) return GEMM_BT_OK;
-    const int osz = out_size(out_dtype);
+    // items of C must not overlap; byte strides must fit 63 bits
+    if (multi && stride_c < M * N) return GEMM_BT_ERR_INVALID_VALUE;
+    if (stride_a > (INT64_MAX >> 2) || stride_b > (INT64_MAX >> 2) || stride_c > (INT64_MAX >> 3))
+        return GEMM_BT_ERR_INVALID_VALUE;
     if (!C) return GEMM_BT_ERR_INVALID_VALUE;
     if (p.kernel != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
-    const int isz = is_8bit(in_dtype) ? 1 : 2;
     if ((uintptr_t)A % isz || (uintptr_t)B % isz || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
 
     int num_cu = 256;
     st = check_device(&num_cu);
     if (st != GEMM_BT_OK) return st;
     if (num_cu != 256) {
-        st = plan_impl(M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, num_cu, &p);
+        st = plan_impl(batch, M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, num_cu, &p);
         if (st != GEMM_BT_OK) return st;
     }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+    long long sa = multi ? (long long)stride_a * isz : 0, sb = multi ? (long long)stride_b * isz : 0,
+              sc = multi ? (long long)stride_c * osz : 0;
+    const unsigned gy = (unsigned)batch;
 
     if (p.kernel == KIND_FILL) {
         u16* c16 = (u16*)C;
         size_t n16 = (size_t)M * (size_t)N * osz / 2;
-        void* args[] = {&c16, &n16};
-        e = hipLaunchKernel((const void*)&zero_fill_kernel, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+        void* args[] = {&c16, &n16, &sc};
+        e = hipLaunchKernel((const void*)&zero_fill_kernel, dim3((unsigned)p.grid, gy), dim3(p.threads), args, 0, s);
     } else {
         const u16* a = (const u16*)A;
         const u16* b = (const u16*)B;
@@ -508,9 +544,10 @@ int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
                 fn = in_dtype == GEMM_BT_BF16 ? tiled_fn_out<GEMM_BT_BF16>(out_dtype, p.variant, p.vec)
                                               : tiled_fn_out<GEMM_BT_F16>(out_dtype, p.variant, p.vec);
             }
-            int tm = (int)p.tiles_m, tn = (int)p.tiles_n, gm = p.group_m;
-            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store};
-            e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+            // one grid row: the items stacked along the tile rows
+            int tm = (int)(p.tiles_m * batch), tn = (int)p.tiles_n, gm = p.group_m, itm = (int)p.tiles_m;
+            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store, &itm, &sa, &sb, &sc};
+            e = hipLaunchKernel(fn, dim3((unsigned)(p.grid * batch)), dim3(p.threads), args, 0, s);
         } else {
             const void* fn;
             if (p.variant >= 1) {
@@ -520,8 +557,8 @@ int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t
                 fn = in_dtype == GEMM_BT_BF16 ? skinny_fn_out<GEMM_BT_BF16>(out_dtype, p.vec)
                                               : skinny_fn_out<GEMM_BT_F16>(out_dtype, p.vec);
             }
-            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &vec_store};
-            e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &vec_store, &sa, &sb, &sc};
+            e = hipLaunchKernel(fn, dim3((unsigned)p.grid, gy), dim3(p.threads), args, 0, s);
         }
     }
     if (e != hipSuccess) {

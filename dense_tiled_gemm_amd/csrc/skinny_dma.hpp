@@ -38,7 +38,8 @@ namespace gbt {
 template <int IN, int OUT, int BN, int KB, int STAGES, int W, int ROT = 0>
 __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                            void* __restrict__ C, int M, int N, int K,
-                                                           int vec_store) {
+                                                           int vec_store, long long sa, long long sb, long long sc) {
+    batch_item(blockIdx.y, A, B, C, sa, sb, sc);  // one grid row per batch item
     constexpr int AR = 16;                 // rows of A held (M <= 16)
     constexpr int CPR = KB / 8;            // 16-byte chunks per row per stage
     constexpr int ROWB = KB * 2;           // bytes per row per stage

@@ -28,7 +28,8 @@ template <int IN, int OUT, int NB, int KS, int VEC>
 __global__ __launch_bounds__(64 * KS) void skinny_kernel(const u16* __restrict__ A,
                                                          const u16* __restrict__ B,
                                                          void* __restrict__ C, int M, int N, int K,
-                                                         int vec_store) {
+                                                         int vec_store, long long sa, long long sb, long long sc) {
+    batch_item(blockIdx.y, A, B, C, sa, sb, sc);  // one grid row per batch item
     constexpr int U = 4;  // k-blocks of 32 per batch
     constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
     __shared__ f32x4 red[KS][NB][64];

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(64 * WM * WN) void staged_kernel(const u16* __restr
                                                             const u16* __restrict__ B,
                                                             void* __restrict__ C, int M, int N, int K,
                                                             int tiles_m, int tiles_n, int group_m,
-                                                            int vec_store) {
+                                                            int vec_store, int item_tiles_m, long long sa, long long sb,
+                                                          long long sc) {
     constexpr int T = 64 * WM * WN;  // threads
     constexpr int BK = 64;           // K elements per step = 128 bytes = 8 chunks
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -79,6 +80,13 @@ __global__ __launch_bounds__(64 * WM * WN) void staged_kernel(const u16* __restr
 
     int64_t tm64, tn64;
     tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
+    {
+        // batch items are stacked along the tile rows (tiles_m counts all of
+        // them), so the XCD regrouping gives each die whole items
+        const int z = (int)tm64 / item_tiles_m;
+        tm64 -= (int64_t)z * item_tiles_m;
+        batch_item(z, A, B, C, sa, sb, sc);
+    }
     const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
 

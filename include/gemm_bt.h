@@ -86,6 +86,27 @@ typedef enum {
 int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
             int in_dtype, int out_dtype, void* stream);
 
+/*
+ * Batched product: C_z = A_z * B_z^T for z = 0 .. batch-1, every item with
+ * the same sizes and types ("Chapter 7: Writing custom kernels with Pallas",
+ * section 5.2: batching a kernel adds a leading grid dimension and runs the
+ * unchanged kernel once per item; an operand mapped with in_axes=None is
+ * shared by all items rather than copied).  One launch covers all items.
+ *   A, B, C    base device pointers; item z uses A + z*stride_a, B + z*stride_b
+ *              and C + z*stride_c (strides in elements of the operand's type)
+ *   batch      number of items, 0 .. 65535 (0: nothing enqueued; more: UNSUPPORTED)
+ *   stride_a   >= 0; 0 shares one A between all items (likewise stride_b for B)
+ *   stride_c   >= M*N when batch > 1, so items of C never overlap (INVALID_VALUE)
+ * Strides are ignored when batch == 1.  Alignment rules apply to every item's
+ * pointers (the base pointers and the strides in bytes): e.g. 8-bit inputs
+ * need 16-byte aligned A and B items.  Everything else is as for gemm_bt,
+ * which is the batch == 1 case of this call.  Negative sizes or strides:
+ * INVALID_VALUE.
+ */
+int gemm_bt_batched(const void* A, const void* B, void* C, int64_t batch, int64_t M, int64_t N, int64_t K,
+                    int64_t stride_a, int64_t stride_b, int64_t stride_c, int in_dtype, int out_dtype,
+                    void* stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* gemm_bt_status_string(int status);
 
@@ -112,11 +133,17 @@ typedef struct {
                          its ring of single-operand tiles */
     int lds_bytes;    /* LDS per workgroup */
     int64_t tiles_m, tiles_n;
-    int64_t grid;     /* workgroups launched */
+    int64_t grid;     /* workgroups per batch item (grid * batch are launched) */
+    int64_t batch;    /* batch items (1 for gemm_bt) */
 } gemm_bt_plan_t;
 
 int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
                  int b_align, int c_align, gemm_bt_plan_t* plan);
+
+/* The plan of gemm_bt_batched: the tile tier counts the workgroups of all
+   items; the alignments are those of every item's pointers. */
+int gemm_bt_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
+                         int a_align, int b_align, int c_align, gemm_bt_plan_t* plan);
 
 /*
  * Tile order used by the tiled kernel: workgroup `pid` (0 <= pid < tiles_m *
@@ -127,7 +154,9 @@ int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, i
  * tile-rows, column by column inside a band, so that tiles running at the
  * same time share A-row and B-row panels in L2 ("Writing Mosaic GPU kernels
  * with Pallas", section "Using the L2 cache": reorder the grid into bands of
- * mt rows so that concurrently scheduled blocks touch less data).
+ * mt rows so that concurrently scheduled blocks touch less data).  A batched
+ * call stacks its items along the tile rows (tiles_m = batch * tile rows per
+ * item), so each die receives whole items and their panels stay in its L2.
  * Host-callable copy of the device function; returns INVALID_VALUE for a pid
  * outside the grid.
  */

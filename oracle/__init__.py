@@ -208,3 +208,29 @@ def gemm_bt_i8_entries(a: np.ndarray, b: np.ndarray, I, J, nthreads: int = 0) ->
                                       int(nthreads)) != 0:
         raise ValueError("oracle rejected arguments")
     return out
+
+
+def gemm_bt_batched_ref(a_bits: np.ndarray, b_bits: np.ndarray, in_dtype, nthreads: int = 0):
+    """Batched product: C[z] = A[z]·B[z]ᵀ in fp64 for each item z ("Chapter 7: Writing custom kernels
+    with Pallas", section 5.2: a batch runs the unchanged product once per item; an operand given
+    as 2-D is shared by every item).  Returns (C (Z,M,N), ‖A_z,i‖ (Z,M), ‖B_z,j‖ (Z,N)); int8 inputs
+    return (C int64, None, None)."""
+    a = np.asarray(a_bits)
+    b = np.asarray(b_bits)
+    Z = a.shape[0] if a.ndim == 3 else b.shape[0]
+    if a.ndim == 3 and b.ndim == 3 and a.shape[0] != b.shape[0]:
+        raise ValueError("batch sizes differ")
+    Cs, nAs, nBs = [], [], []
+    for z in range(Z):
+        az = a[z] if a.ndim == 3 else a
+        bz = b[z] if b.ndim == 3 else b
+        if in_dtype == "i8":
+            Cs.append(gemm_bt_i8(az, bz, nthreads))
+        else:
+            c, nA, nB = gemm_bt_ref(az, bz, in_dtype, nthreads)
+            Cs.append(c)
+            nAs.append(nA)
+            nBs.append(nB)
+    if in_dtype == "i8":
+        return np.stack(Cs), None, None
+    return np.stack(Cs), np.stack(nAs), np.stack(nBs)

@@ -8,7 +8,8 @@ so the very same bits feed the GPU kernel and the CPU oracle.
 
 Recipe (also stated in the design notes):
   * ``numpy.random.default_rng(seed)`` (PCG64); A is drawn first (M×K, row-major
-    order), then B (N×K, row-major order — B is stored transposed).
+    order), then B (N×K, row-major order — B is stored transposed).  A batch of
+    Z products draws all of A (Z×M×K) and then all of B (Z×N×K), row-major.
   * distributions: ``normal`` N(0, 1); ``normal_scaled`` N(0, σ=1/√K);
     ``uniform`` U[-1, 1) via ``rng.uniform(-1, 1)``; ``int`` uniform integers in
     [-4, 4] (exact in every input format, so fp32 accumulation is exact);
@@ -48,23 +49,25 @@ class Workload:
     out_dtype: str
     dist: str
     seed: int
+    batch: int = 1
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.batch * self.M * self.N * self.K
 
     @property
     def compulsory_bytes(self) -> int:
         osz = 4 if self.out_dtype in ("f32", "i32") else 2
         isz = 1 if self.in_dtype in ("e4m3", "e5m2", "i8") else 2
-        return (self.M * self.K + self.N * self.K) * isz + self.M * self.N * osz
+        return self.batch * ((self.M * self.K + self.N * self.K) * isz + self.M * self.N * osz)
 
     def integer_twin(self) -> "Workload":
         return dataclasses.replace(self, name=self.name + "_int", dist="int", seed=self.seed + 100)
 
 
 # The five measured shapes, seeds 0..4 in this order, the 4096³ product
-# with 8-bit E4M3 inputs (seed 5) and with int8 inputs and int32 output (seed 6).
+# with 8-bit E4M3 inputs (seed 5) and with int8 inputs and int32 output (seed 6),
+# and a batch of 64 products of 512³ (seed 7).
 WORKLOADS = {
     "sq512_bf16_f32": Workload("sq512_bf16_f32", 512, 512, 512, "bf16", "f32", "normal", 0),
     "m1024_n4096_k4096_f16_f16": Workload("m1024_n4096_k4096_f16_f16", 1024, 4096, 4096, "f16", "f16",
@@ -76,6 +79,7 @@ WORKLOADS = {
                                                  "bf16", "bf16", "normal_scaled", 4),
     "sq4096_e4m3_bf16": Workload("sq4096_e4m3_bf16", 4096, 4096, 4096, "e4m3", "bf16", "normal", 5),
     "sq4096_i8_i32": Workload("sq4096_i8_i32", 4096, 4096, 4096, "i8", "i32", "int8", 6),
+    "batch64_sq512_bf16_bf16": Workload("batch64_sq512_bf16_bf16", 512, 512, 512, "bf16", "bf16", "normal", 7, 64),
 }
 
 
@@ -141,5 +145,14 @@ def make(M: int, N: int, K: int, in_dtype: str, dist: str, seed: int):
     return round_bits(a, in_dtype), round_bits(b, in_dtype)
 
 
+def make_batched(Z: int, M: int, N: int, K: int, in_dtype: str, dist: str, seed: int):
+    """Return (a_bits (Z,M,K), b_bits (Z,N,K)): all of A drawn first, then all of B."""
+    a, b = make(Z * M, Z * N, K, in_dtype, dist, seed)
+    return a.reshape(Z, M, K), b.reshape(Z, N, K)
+
+
 def make_workload(w: Workload):
+    """(a_bits, b_bits) of a workload: 2-D for one product, 3-D (Z, rows, K) for a batch."""
+    if w.batch > 1:
+        return make_batched(w.batch, w.M, w.N, w.K, w.in_dtype, w.dist, w.seed)
     return make(w.M, w.N, w.K, w.in_dtype, w.dist, w.seed)

@@ -53,6 +53,42 @@ def test_argument_validation_before_any_device_call(args, want):
     assert gb.gemm_bt(A, B, C, M, N, K, i, o, None) == want
 
 
+@pytest.mark.parametrize("args,want", [
+    ((16, 16, 16, -1, 4, 4, 4, 16, 16, 16), gb.ERR_INVALID_VALUE),       # negative batch
+    ((16, 16, 16, 2, 4, 4, 4, -16, 16, 16), gb.ERR_INVALID_VALUE),       # negative stride
+    ((16, 16, 16, 2, 4, 4, 4, 16, 16, 15), gb.ERR_INVALID_VALUE),        # items of C overlap
+    ((16, 16, 16, 70000, 4, 4, 4, 16, 16, 16), gb.ERR_UNSUPPORTED),      # beyond the grid's y range
+    ((0, 0, 0, 0, 4, 4, 4, 16, 16, 16), gb.OK),                          # no items: nothing enqueued
+    ((0, 0, 0, 3, 0, 4, 4, 16, 16, 16), gb.OK),
+    ((16, 0, 16, 2, 4, 4, 4, 16, 16, 16), gb.ERR_INVALID_VALUE),         # null B
+])
+def test_batched_argument_validation(args, want):
+    A, B, C, Z, M, N, K, sa, sb, sc = args
+    assert gb.gemm_bt_batched(A, B, C, Z, M, N, K, sa, sb, sc, gb.BF16, gb.F32, None) == want
+    # the stride of C is checked only when there is more than one item
+    assert gb.gemm_bt_batched(16, 16, 16, 1, 4, 4, 4, 0, 0, 0, gb.BF16, gb.F32, None) in (gb.ERR_NO_DEVICE, gb.OK)
+
+
+def test_batched_plan():
+    # the tile tier counts all items: 64 items of 512^2 fill 256 CUs with 256x256 tiles
+    p = gb.gemm_bt_plan_batched(64, 512, 512, 512, gb.BF16, gb.BF16)
+    assert (p.kernel, p.bm, p.grid, p.batch) == (4, 256, 4, 64)
+    p = gb.gemm_bt_plan_batched(8, 512, 512, 512, gb.BF16, gb.BF16)   # 8 x 16 tiles of 128
+    assert (p.bm, p.grid, p.batch) == (128, 16, 8)
+    p = gb.gemm_bt_plan_batched(1, 512, 512, 512, gb.BF16, gb.BF16)
+    assert (p.bm, p.batch) == (64, 1) and p.as_dict() == gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.BF16).as_dict()
+    p = gb.gemm_bt_plan_batched(5, 16, 8192, 8192, gb.BF16, gb.BF16)  # streaming kernel per item
+    assert (p.kernel, p.grid, p.batch) == (3, 1024, 5)
+    assert gb.gemm_bt_plan_batched(0, 64, 64, 64, gb.BF16, gb.BF16).kernel == 0
+    assert gb.gemm_bt_plan_batched(4, 64, 64, 0, gb.BF16, gb.BF16).kernel == 1
+    with pytest.raises(gb.GemmBtError):
+        gb.gemm_bt_plan_batched(65536, 64, 64, 64, gb.BF16, gb.BF16)
+    # an item stride that breaks 16-byte alignment narrows the loads, or is refused for 8-bit inputs
+    assert gb.gemm_bt_plan_batched(2, 64, 64, 64, gb.BF16, gb.F32, a_align=2).kernel == 2
+    with pytest.raises(gb.GemmBtError):
+        gb.gemm_bt_plan_batched(2, 64, 64, 64, gb.FP8_E4M3, gb.F32, b_align=8)
+
+
 def test_no_device_status_without_gpu():
     import torch
 

@@ -234,6 +234,14 @@ def test_workload_full_size(gpu, name):
     w = synth.WORKLOADS[name]
     say("workload", name, w.M, w.N, w.K, w.in_dtype, w.out_dtype, "seed", w.seed)
     a, b = synth.make_workload(w)
+    if w.batch > 1:
+        c = gpu.mm_bt(to_dev(a, w.in_dtype), to_dev(b, w.in_dtype), out_dtype=TORCH_DT[w.out_dtype])
+        torch.cuda.synchronize()
+        cref, nA, nB = oracle.gemm_bt_batched_ref(a, b, w.in_dtype)
+        for z in range(w.batch):
+            rep = tolerance.check(f64(c[z].cpu()), cref[z], np.outer(nA[z], nB[z]), w.out_dtype)
+            assert rep.ok, (name, z, rep)
+        return
     c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
     if w.in_dtype == "i8":
         I, J = sample_entries(w.M, w.N, np.random.default_rng(w.seed))
@@ -258,6 +266,14 @@ def test_workload_integer_twin_bit_exact(gpu, name):
     w = synth.WORKLOADS[name].integer_twin()
     say("workload int twin", w.name, w.M, w.N, w.K, "seed", w.seed)
     a, b = synth.make_workload(w)
+    if w.batch > 1:
+        c = gpu.mm_bt(to_dev(a, w.in_dtype), to_dev(b, w.in_dtype), out_dtype=TORCH_DT[w.out_dtype])
+        torch.cuda.synchronize()
+        cref, _, _ = oracle.gemm_bt_batched_ref(a, b, w.in_dtype)
+        for z in range(w.batch):
+            rep = tolerance.bit_exact(out_bits(c[z].cpu()), oracle.round_to(cref[z], w.out_dtype), w.out_dtype)
+            assert rep.ok, (w.name, z, rep)
+        return
     c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
     if w.in_dtype == "i8":
         I, J = sample_entries(w.M, w.N, np.random.default_rng(w.seed))
@@ -374,3 +390,129 @@ def test_deterministic_and_stream(gpu):
     s.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
+
+
+# ---------------------------------------------------------------- batched products
+
+RAW = {"bf16": torch.int16, "f16": torch.int16, "e4m3": torch.uint8, "e5m2": torch.uint8, "i8": torch.uint8}
+
+
+def _flat_items(items, rows, K, pad, in_dtype):
+    """Device buffer holding the items (z, rows, K) at a stride of rows*K + pad elements."""
+    stride = rows * K + pad
+    raw = RAW[in_dtype]
+    nbytes_el = 1 if raw == torch.uint8 else 2
+    buf = torch.zeros((items.shape[0] - 1) * stride + rows * K + 64, dtype=raw, device="cuda")
+    for z in range(items.shape[0]):
+        src = torch.from_numpy(np.ascontiguousarray(items[z]).view(np.uint8 if nbytes_el == 1 else np.int16))
+        buf[z * stride:z * stride + rows * K] = src.reshape(-1).to("cuda")
+    return buf, stride
+
+
+def run_batched(gb, Z, M, N, K, in_dtype, out_dtype, share=None, pad=(0, 0, 0), dist="normal", seed=0):
+    """One gemm_bt_batched call; returns (C items (Z,M,N) on the CPU, a_bits, b_bits) after checking
+    that the padding between items of C was not written."""
+    a3, b3 = synth.make_batched(Z, M, N, K, in_dtype, dist, seed)
+    a_bits = a3[0] if share == "a" else a3
+    b_bits = b3[0] if share == "b" else b3
+    abuf, sa = _flat_items(a_bits[None] if share == "a" else a_bits, M, K, pad[0], in_dtype)
+    bbuf, sb = _flat_items(b_bits[None] if share == "b" else b_bits, N, K, pad[1], in_dtype)
+    sc = M * N + pad[2]
+    poison = I32_POISON if out_dtype == "i32" else float("nan")
+    cbuf = torch.full(((Z - 1) * sc + M * N,), poison, dtype=TORCH_DT[out_dtype], device="cuda")
+    st = gb.gemm_bt_batched(abuf.data_ptr(), bbuf.data_ptr(), cbuf.data_ptr(), Z, M, N, K,
+                            0 if share == "a" else sa, 0 if share == "b" else sb, sc,
+                            getattr(gb, {"bf16": "BF16", "f16": "F16", "e4m3": "FP8_E4M3", "e5m2": "FP8_E5M2",
+                                         "i8": "INT8"}[in_dtype]),
+                            getattr(gb, {"f32": "F32", "bf16": "BF16", "f16": "F16", "i32": "INT32"}[out_dtype]),
+                            torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK, gb.status_string(st)
+    torch.cuda.synchronize()
+    c = cbuf.cpu()
+    items = torch.stack([c[z * sc:z * sc + M * N].reshape(M, N) for z in range(Z)])
+    for z in range(Z - 1):
+        gap = c[z * sc + M * N:(z + 1) * sc]
+        assert (gap == I32_POISON).all() if out_dtype == "i32" else torch.isnan(gap).all(), ("pad written", z)
+    return items, a_bits, b_bits
+
+
+# (Z, M, N, K, in, out, shared operand, element padding of A, B, C items): the 64x64, 128x128 and
+# 256x256 tiers, the register-staged kernel (odd K, or an odd item stride), both streaming kernels,
+# 8-bit inputs, shared A and shared B
+BATCHED = [
+    (3, 130, 260, 72, "bf16", "f32", None, (0, 0, 0)),
+    (5, 300, 200, 520, "f16", "f16", "b", (8, 0, 40)),
+    (4, 257, 513, 129, "bf16", "bf16", "a", (0, 8, 16)),
+    (2, 1024, 1024, 200, "bf16", "f32", None, (0, 0, 0)),
+    (2, 4096, 4096, 136, "bf16", "bf16", None, (0, 0, 8)),
+    (3, 16, 1000, 520, "bf16", "bf16", None, (0, 0, 0)),
+    (2, 5, 33, 35, "f16", "f32", "b", (0, 0, 3)),
+    (3, 100, 130, 200, "bf16", "f32", None, (1, 0, 0)),
+    (3, 130, 260, 160, "e4m3", "bf16", None, (16, 32, 0)),
+    (3, 300, 200, 256, "i8", "i32", "b", (0, 0, 5)),
+    (7, 64, 96, 48, "e5m2", "f32", "a", (0, 0, 0)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BATCHED)))
+def test_batched(gpu, case):
+    Z, M, N, K, ind, outd, share, pad = BATCHED[case]
+    seed = 1200 + case
+    say("batched", Z, M, N, K, ind, outd, "share", share, "pad", pad, "seed", seed)
+    items, a_bits, b_bits = run_batched(gpu, Z, M, N, K, ind, outd, share, pad, seed=seed if ind != "i8" else seed,
+                                        dist="int8" if ind == "i8" else "normal")
+    cref, nA, nB = oracle.gemm_bt_batched_ref(a_bits, b_bits, ind)
+    for z in range(Z):
+        if ind == "i8":
+            assert np.array_equal(items[z].numpy().astype(np.int64), cref[z]), z
+        else:
+            rep = tolerance.check(f64(items[z]), cref[z], np.outer(nA[z], nB[z]), outd)
+            assert rep.ok, (z, rep)
+
+
+def test_batched_integer_bit_exact(gpu):
+    Z, M, N, K = 4, 257, 300, 136
+    say("batched int", Z, M, N, K)
+    items, a_bits, b_bits = run_batched(gpu, Z, M, N, K, "bf16", "bf16", None, (0, 8, 4), dist="int", seed=1250)
+    cref, _, _ = oracle.gemm_bt_batched_ref(a_bits, b_bits, "bf16")
+    for z in range(Z):
+        rep = tolerance.bit_exact(out_bits(items[z]), oracle.round_to(cref[z], "bf16"), "bf16")
+        assert rep.ok, (z, rep)
+
+
+def test_batched_k_zero_and_refused_strides(gpu):
+    s = torch.cuda.current_stream().cuda_stream
+    c = torch.full((3 * 40 + 8,), float("nan"), dtype=torch.float32, device="cuda")
+    a = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    say("batched K = 0")
+    assert gpu.gemm_bt_batched(a.data_ptr(), a.data_ptr(), c.data_ptr(), 3, 4, 8, 0, 0, 0, 40, gpu.BF16, gpu.F32, s) == gpu.OK
+    torch.cuda.synchronize()
+    cc = c.cpu()
+    for z in range(3):
+        assert (cc[z * 40:z * 40 + 32] == 0).all() and torch.isnan(cc[z * 40 + 32:z * 40 + 40]).all()
+    say("batched refused")
+    # 8-bit items 8 bytes apart are not 16-byte aligned; C items overlapping
+    assert gpu.gemm_bt_batched(a.data_ptr(), a.data_ptr(), c.data_ptr(), 2, 4, 4, 16, 72, 0, 16, gpu.FP8_E4M3, gpu.F32,
+                               s) == gpu.ERR_UNSUPPORTED
+    assert gpu.gemm_bt_batched(a.data_ptr(), a.data_ptr(), c.data_ptr(), 2, 4, 4, 16, 64, 0, 15, gpu.FP8_E4M3, gpu.F32,
+                               s) == gpu.ERR_INVALID_VALUE
+    torch.cuda.synchronize()
+
+
+def test_mm_bt_batched_wrapper(gpu):
+    """The torch wrapper: 3-D operands, a 2-D (shared) operand, an expanded one, int8."""
+    say("mm_bt batched")
+    a3, b3 = synth.make_batched(3, 70, 90, 64, "bf16", "normal", 1260)
+    A, B = to_dev(a3, "bf16"), to_dev(b3, "bf16")
+    cref, nA, nB = oracle.gemm_bt_batched_ref(a3, b3, "bf16")
+    for got, bb in ((gpu.mm_bt(A, B, out_dtype=torch.float32), b3), (gpu.mm_bt(A, B[0], out_dtype=torch.float32), b3[0]),
+                    (gpu.mm_bt(A, B[0].expand(3, 90, 64), out_dtype=torch.float32), b3[0])):
+        torch.cuda.synchronize()
+        ref, nA2, nB2 = oracle.gemm_bt_batched_ref(a3, bb, "bf16")
+        for z in range(3):
+            assert tolerance.check(f64(got[z].cpu()), ref[z], np.outer(nA2[z], nB2[z]), "f32").ok
+    a8, b8 = synth.make_batched(2, 33, 17, 48, "i8", "int8", 1261)
+    got = gpu.mm_bt(to_dev(a8, "i8"), to_dev(b8, "i8"))
+    torch.cuda.synchronize()
+    assert got.dtype == torch.int32 and got.shape == (2, 33, 17)
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), oracle.gemm_bt_batched_ref(a8, b8, "i8")[0])

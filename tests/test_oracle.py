@@ -445,7 +445,7 @@ def test_synth_recipe():
     a, _ = synth.make(50, 4, wu.K, "bf16", wu.dist, wu.seed)
     v = indep_decode(a, "bf16")
     assert v.min() >= -1 and v.max() <= 1 and abs(v.std() - 1 / math.sqrt(3)) < 0.01
-    assert [x.seed for x in synth.WORKLOADS.values()] == [0, 1, 2, 3, 4, 5, 6]
+    assert [x.seed for x in synth.WORKLOADS.values()] == [0, 1, 2, 3, 4, 5, 6, 7]
     w8 = synth.WORKLOADS["sq4096_e4m3_bf16"]
     a8, _ = synth.make(64, 4, w8.K, w8.in_dtype, w8.dist, w8.seed)
     assert a8.dtype == np.uint8 and w8.compulsory_bytes == 2 * 4096 * 4096 + 4096 * 4096 * 2
@@ -548,3 +548,52 @@ def test_i8_recipe():
         synth.round_bits(np.array([0.5]), "i8")
     with pytest.raises(ValueError):
         synth.round_bits(np.array([128.0]), "i8")
+
+
+# ---------------------------------------------------------------- batched products
+
+def test_batched_items_brute_force():
+    """Each item of a batch is its own product: exact rationals per item, no item mixed with another."""
+    Z, M, N, K = 3, 3, 4, 5
+    a, b = synth.make_batched(Z, M, N, K, "bf16", "normal", 71)
+    c, nA, nB = oracle.gemm_bt_batched_ref(a, b, "bf16")
+    assert c.shape == (Z, M, N) and nA.shape == (Z, M) and nB.shape == (Z, N)
+    for z in range(Z):
+        av, bv = indep_decode(a[z], "bf16"), indep_decode(b[z], "bf16")
+        C, S = _exact_products(av, bv)
+        for i in range(M):
+            for j in range(N):
+                assert abs(Fraction(float(c[z, i, j])) - C[i][j]) <= Fraction(gamma(K) * S[i, j])
+    # the items differ, so a swapped or repeated item would show
+    assert not np.array_equal(c[0], c[1]) and not np.array_equal(c[1], c[2])
+
+
+def test_batched_shared_operand_closed_forms():
+    """A shared B: stacking the A items gives one product of (Z·M)×K with B.  A shared A with
+    identity-then-permutation B items gives A and its column permutation."""
+    Z, M, N, K = 4, 5, 6, 7
+    a, b = synth.make_batched(Z, M, N, K, "f16", "normal", 72)
+    c, _, _ = oracle.gemm_bt_batched_ref(a, b[0], "f16")
+    av, bv = indep_decode(a.reshape(Z * M, K), "f16"), indep_decode(b[0], "f16")
+    ref = av @ bv.T
+    S = np.abs(av) @ np.abs(bv).T
+    assert np.all(np.abs(c.reshape(Z * M, N) - ref) <= 2 * gamma(K) * S)
+    a2, _ = synth.make(M, 1, K, "bf16", "normal", 73)
+    eye = np.eye(K)
+    perm = np.random.default_rng(74).permutation(K)
+    bi = np.stack([synth.round_bits(eye, "bf16"), synth.round_bits(eye[perm], "bf16")])
+    c2, _, _ = oracle.gemm_bt_batched_ref(a2, bi, "bf16")
+    A2 = indep_decode(a2, "bf16")
+    assert np.array_equal(c2[0], A2) and np.array_equal(c2[1], A2[:, perm])
+
+
+def test_batched_int8_and_recipe():
+    a, b = synth.make_batched(3, 4, 5, 32, "i8", "int8", 75)
+    c, _, _ = oracle.gemm_bt_batched_ref(a, b, "i8")
+    ref = np.einsum("zmk,znk->zmn", a.view(np.int8).astype(np.int64), b.view(np.int8).astype(np.int64))
+    assert c.dtype == np.int64 and np.array_equal(c, ref)
+    w = synth.WORKLOADS["batch64_sq512_bf16_bf16"]
+    assert w.batch == 64 and w.flops == 64 * 2 * 512 ** 3 and w.compulsory_bytes == 64 * 3 * 512 * 512 * 2
+    wa, wb = synth.make_batched(2, 3, 4, 8, "bf16", "normal", 9)
+    fa, fb = synth.make(6, 8, 8, "bf16", "normal", 9)  # the same draws: all of A, then all of B
+    assert np.array_equal(wa.reshape(6, 8), fa) and np.array_equal(wb.reshape(8, 8), fb)
