@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
 
     int64_t tm64, tn64;
     tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
-    {
+    if (tiles_m != item_tiles_m) {
         // batch items are stacked along the tile rows (tiles_m counts all of
         // them), so the XCD regrouping gives each die whole items
         const int z = (int)tm64 / item_tiles_m;
