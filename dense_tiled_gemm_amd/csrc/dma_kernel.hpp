@@ -211,6 +211,25 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     // 4-byte aligned but K % 8 != 0, the last K - Kf (2, 4 or 6) elements of
     // every row are added after the loop (see the tail below).
     const int Kf = K & ~(EPC - 1);
+    // K tail (see after the loop): thread t fetches the last K - Kf elements
+    // (1 to 3 dwords; rows and K are 4-byte aligned here) of tile row t (A
+    // rows first, then B rows) now, so that their latency hides behind the
+    // main loop.  Being older than every ring load, they are also covered by
+    // each of the ring's vmcnt waits.
+    static_assert(64 * W >= BM + BN, "one thread per tile row of the K tail");
+    u32 tail_v[3] = {0u, 0u, 0u};
+    if (ESZ == 2 && Kf != K) {
+        const int r = threadIdx.x;
+        const bool in_a = r < BM;
+        const bool valid = in_a ? r < rows_a : (r < BM + BN && r - BM < rows_b);
+        if (valid) {
+            const u32* src = (const u32*)(in_a ? A + (size_t)(m0 + r) * K + Kf : B + (size_t)(n0 + r - BM) * K + Kf);
+            const int nd = (K - Kf) >> 1;
+#pragma unroll
+            for (int d = 0; d < 3; ++d)
+                if (d < nd) tail_v[d] = __builtin_nontemporal_load(src + d);
+        }
+    }
 
     // Loader geometry.  Wave instruction i of this wave fills row block
     // j = wave + i*W (rows j*RPI .. j*RPI+RPI-1 of the tile); lane L writes
@@ -641,23 +660,14 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         // swizzled layout and multiplied like the others.  It comes after all
         // whole chunks, so each sum still runs over k in order.
         barrier_no_fence();  // every wave is past its last read of the ring
-        for (int q = threadIdx.x; q < (BM + BN) * CPR; q += 64 * W) {
-            const int r = q / CPR, c = q % CPR;
-            u32 v[4] = {0u, 0u, 0u, 0u};
-            if (c == 0) {
-                const u16* src = nullptr;
-                if (r < BM) {
-                    if (r < rows_a) src = A + (size_t)(m0 + r) * K;
-                } else if (r - BM < rows_b) {
-                    src = B + (size_t)(n0 + r - BM) * K;
-                }
-                if (src) {
+        const int r = threadIdx.x;  // tile row r: A rows 0 .. BM-1, then B rows
+        if (r < BM + BN) {
+            // chunk 0 holds elements Kf .. Kf+7 (the fetched dwords, zeros
+            // past K and for rows past M or N); the other chunks are zero
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (Kf + e < K) v[e >> 1] |= (u32)src[Kf + e] << (16 * (e & 1));
-                }
-            }
-            *(u32x4*)(lds + r * ROWB + ((c ^ swz_row<CPR, SWZ>(r)) * 16)) = u32x4{v[0], v[1], v[2], v[3]};
+            for (int c = 0; c < CPR; ++c)
+                *(u32x4*)(lds + r * ROWB + ((c ^ swz_row<CPR, SWZ>(r)) * 16)) =
+                    c == 0 ? u32x4{tail_v[0], tail_v[1], tail_v[2], 0u} : u32x4{0u, 0u, 0u, 0u};
         }
         __syncthreads();
         Frag tb[FN], ta[FM];
