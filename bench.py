@@ -10,8 +10,9 @@ Prints ONE JSON line on stdout:
   secondary    µs / TFLOP/s / GB/s of the other workloads (1024×4096×4096
                f16, 16×8192×8192 skinny, 512³, 1000×3000×2050, 4096³ with
                E4M3 inputs against the fp8 peak, 4096³ int8 -> int32
-               against the int8 peak, and a batch of 64 products of 512³ in
-               one gemm_bt_batched call), same timing
+               against the int8 peak, a batch of 64 products of 512³ in one
+               gemm_bt_batched call, and 4096³ with B stored K×N through
+               gemm_bt_layout), same timing
   copy_GBps    a plain 1 GiB device copy, as context for achievable HBM
 Diagnostics go to stderr.  The default 400 untimed warm-up launches matter:
 from idle, an MI355X needs about 25 ms of sustained GEMM launches before its
@@ -82,6 +83,8 @@ class Case:
         dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
               "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2, "i8": torch.int8, "i32": torch.int32}
         a_bits, b_bits = synth.make_workload(w)
+        if w.b_layout:
+            b_bits = np.ascontiguousarray(b_bits.T)  # B stored K x N
         raw = np.uint8 if a_bits.dtype == np.uint8 else np.int16
         a = torch.from_numpy(a_bits.view(raw)).to("cuda").view(dt[w.in_dtype])
         b = torch.from_numpy(b_bits.view(raw)).to("cuda").view(dt[w.in_dtype])
@@ -105,7 +108,10 @@ class Case:
     def step(self, i, stream):
         pa, pb, pc = self.ptrs[i % self.rotate]
         w = self.w
-        if w.batch > 1:
+        if w.b_layout:
+            st = self.gb.gemm_bt_layout(pa, pb, pc, w.M, w.N, w.K, self.gb.K_INNER, w.b_layout, self.in_code,
+                                        self.out_code, stream)
+        elif w.batch > 1:
             st = self.gb.gemm_bt_batched(pa, pb, pc, w.batch, w.M, w.N, w.K, w.M * w.K, w.N * w.K, w.M * w.N,
                                          self.in_code, self.out_code, stream)
         else:
@@ -263,7 +269,7 @@ def main():
         sec = {}
         for name in ("m1024_n4096_k4096_f16_f16", "skinny_m16_n8192_k8192_bf16_bf16", "sq512_bf16_f32",
                      "ragged_m1000_n3000_k2050_bf16_f32", "sq4096_e4m3_bf16", "sq4096_i8_i32",
-                     "batch64_sq512_bf16_bf16"):
+                     "batch64_sq512_bf16_bf16", "sq4096_nn_bf16_bf16"):
             w2 = synth.WORKLOADS[name]
             c2 = Case(w2, torch, gb)
             _, ms2 = c2.time(max(50, args.steps // 2), args.warmup)

@@ -7,11 +7,14 @@ PyTorch fallback: if the shared library is missing, every call raises.
 Entry points (same names as the C-ABI in ``include/gemm_bt.h``):
   gemm_bt(A, B, C, M, N, K, in_dtype, out_dtype, stream)   raw device pointers
   gemm_bt_batched(A, B, C, batch, M, N, K, stride_a, stride_b, stride_c, in_dtype, out_dtype, stream)
+  gemm_bt_layout(A, B, C, M, N, K, a_layout, b_layout, in_dtype, out_dtype, stream)
   gemm_bt_status_string(status), gemm_bt_version()
   gemm_bt_plan(M, N, K, in_dtype, out_dtype, a_align, b_align, c_align)
   gemm_bt_plan_batched(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align)
+  gemm_bt_plan_layout(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align)
   gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m)
-and a torch convenience wrapper ``mm_bt(a, b, out_dtype)`` (2-D or batched 3-D operands).
+and torch convenience wrappers ``mm_bt(a, b, out_dtype)`` (2-D or batched 3-D operands),
+``mm_layout(a, b, a_layout, b_layout, out_dtype)`` and ``mm(a, b, out_dtype)`` (= a @ b).
 """
 from __future__ import annotations
 
@@ -21,11 +24,12 @@ import threading
 
 F32, F16, BF16, FP8_E4M3, FP8_E5M2, INT8, INT32 = 0, 1, 2, 3, 4, 5, 6
 OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_LAUNCH = 0, 1, 2, 3, 4
+K_INNER, K_OUTER = 0, 1  # operand layouts of gemm_bt_layout
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemm_bt.so")
-EXPORTS = ("gemm_bt", "gemm_bt_batched", "gemm_bt_status_string", "gemm_bt_version", "gemm_bt_plan",
-           "gemm_bt_plan_batched", "gemm_bt_tile_coord")
+EXPORTS = ("gemm_bt", "gemm_bt_batched", "gemm_bt_layout", "gemm_bt_status_string", "gemm_bt_version",
+           "gemm_bt_plan", "gemm_bt_plan_batched", "gemm_bt_plan_layout", "gemm_bt_tile_coord")
 
 _lock = threading.Lock()
 _lib = None
@@ -64,6 +68,10 @@ def load():
             lib.gemm_bt_batched.restype = ci
             lib.gemm_bt_plan_batched.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             lib.gemm_bt_plan_batched.restype = ci
+            lib.gemm_bt_layout.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, ci, vp]
+            lib.gemm_bt_layout.restype = ci
+            lib.gemm_bt_plan_layout.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
+            lib.gemm_bt_plan_layout.restype = ci
             lib.gemm_bt_status_string.argtypes = [ci]
             lib.gemm_bt_status_string.restype = ctypes.c_char_p
             lib.gemm_bt_version.argtypes = []
@@ -98,6 +106,22 @@ def gemm_bt_batched(A: int, B: int, C: int, batch: int, M: int, N: int, K: int, 
     """Raw batched call: item z uses A + z*stride_a etc. (strides in elements); returns the status code."""
     return int(load().gemm_bt_batched(A or None, B or None, C or None, batch, M, N, K, stride_a, stride_b, stride_c,
                                       in_dtype, out_dtype, stream or None))
+
+
+def gemm_bt_layout(A: int, B: int, C: int, M: int, N: int, K: int, a_layout: int, b_layout: int, in_dtype: int,
+                   out_dtype: int, stream: int | None) -> int:
+    """Raw call with operand layouts (K_INNER / K_OUTER); returns the status code."""
+    return int(load().gemm_bt_layout(A or None, B or None, C or None, M, N, K, a_layout, b_layout, in_dtype, out_dtype,
+                                     stream or None))
+
+
+def gemm_bt_plan_layout(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align=256, b_align=256, c_align=256):
+    p = Plan()
+    st = load().gemm_bt_plan_layout(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align,
+                                    ctypes.byref(p))
+    if st != OK:
+        raise GemmBtError(st, "gemm_bt_plan_layout")
+    return p
 
 
 def gemm_bt_plan_batched(batch, M, N, K, in_dtype, out_dtype, a_align=256, b_align=256, c_align=256):
@@ -212,3 +236,42 @@ def mm_bt(a, b, out_dtype=None, out=None, stream=None):
     if st != OK:
         raise GemmBtError(st)
     return out
+
+
+def mm_layout(a, b, a_layout=K_INNER, b_layout=K_INNER, out_dtype=None, out=None, stream=None):
+    """C = op(a) @ op(b).T for 2-D 16-bit tensors: a is (M,K) for K_INNER or (K,M) for K_OUTER, b is (N,K)
+    for K_INNER or (K,N) for K_OUTER.  Operands stored K-outer are transposed inside the kernel."""
+    import torch
+
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("expected 2-D operands")
+    M, K = (a.shape[1], a.shape[0]) if a_layout == K_OUTER else (a.shape[0], a.shape[1])
+    N, Kb = (b.shape[1], b.shape[0]) if b_layout == K_OUTER else (b.shape[0], b.shape[1])
+    if K != Kb:
+        raise ValueError("inner dimensions differ: %d and %d" % (K, Kb))
+    if a.dtype != b.dtype:
+        raise TypeError("a and b must share one dtype")
+    if not a.is_cuda or not b.is_cuda or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    in_code = _torch_code(a.dtype)
+    out_code = in_code if out_dtype is None else (_torch_code(out_dtype) if not isinstance(out_dtype, int)
+                                                  else out_dtype)
+    a = a.contiguous()
+    b = b.contiguous()
+    if out is None:
+        out = torch.empty((M, N), dtype=_torch_dtype(out_code), device=a.device)
+    elif tuple(out.shape) != (M, N) or not out.is_contiguous() or out.dtype != _torch_dtype(out_code):
+        raise ValueError("out must be a contiguous %dx%d %s tensor" % (M, N, _torch_dtype(out_code)))
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    with torch.cuda.device(a.device):
+        st = gemm_bt_layout(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, a_layout, b_layout, in_code,
+                            out_code, stream)
+    if st != OK:
+        raise GemmBtError(st)
+    return out
+
+
+def mm(a, b, out_dtype=None, out=None, stream=None):
+    """C = a @ b for 2-D 16-bit tensors a (M,K) and b (K,N): B is read K-outer, as it lies in memory."""
+    return mm_layout(a, b, K_INNER, K_OUTER, out_dtype, out, stream)

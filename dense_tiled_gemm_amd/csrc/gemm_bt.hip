@@ -11,6 +11,7 @@
 #include "skinny_dma.hpp"
 #include "skinny_kernel.hpp"
 #include "tiled_kernel.hpp"
+#include "trans_kernel.hpp"
 
 namespace gbt {
 
@@ -22,7 +23,7 @@ __global__ void zero_fill_kernel(u16* __restrict__ c, size_t n16, long long sc) 
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) c[i] = 0;
 }
 
-enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3, KIND_DMA = 4 };
+enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3, KIND_DMA = 4, KIND_TRANS = 5 };
 
 // Tile shapes.  The aligned path (16-byte loads) uses dma_kernel; rows that
 // are not 16-byte aligned use the register-staged kernel with narrower loads.
@@ -361,6 +362,82 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
     return GEMM_BT_OK;
 }
 
+// Plan for operands stored K-outer (A as K x M and/or B as K x N): the
+// 128 x 128 transpose-read kernel; 16-bit inputs with every operand row in
+// whole, aligned 16-byte chunks.
+static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
+                            int a_align, int b_align, int c_align, gemm_bt_plan_t* p) {
+    if (!p) return GEMM_BT_ERR_INVALID_VALUE;
+    if ((a_layout != GEMM_BT_K_INNER && a_layout != GEMM_BT_K_OUTER) ||
+        (b_layout != GEMM_BT_K_INNER && b_layout != GEMM_BT_K_OUTER)) {
+        std::memset(p, 0, sizeof(*p));
+        return GEMM_BT_ERR_INVALID_VALUE;
+    }
+    if (a_layout == GEMM_BT_K_INNER && b_layout == GEMM_BT_K_INNER)
+        return plan_impl(1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, p);
+    std::memset(p, 0, sizeof(*p));
+    if (M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
+    p->batch = 1;
+    if (in_dtype != GEMM_BT_BF16 && in_dtype != GEMM_BT_F16) return GEMM_BT_ERR_UNSUPPORTED;
+    if (out_dtype != GEMM_BT_F32 && out_dtype != GEMM_BT_BF16 && out_dtype != GEMM_BT_F16)
+        return GEMM_BT_ERR_UNSUPPORTED;
+    if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
+    const int osz = out_size(out_dtype);
+    // 32-bit buffer offsets: a K-outer operand as a whole, a K-inner one per
+    // 128-row panel, C per 128-row panel
+    auto fits = [&](int layout, int64_t ext) {
+        return layout == GEMM_BT_K_OUTER ? K * ext * 2 < 0x7FFFFFFFLL : 128 * K * 2 < 0x7FFFFFFFLL;
+    };
+    if (!fits(a_layout, M) || !fits(b_layout, N) || 128 * N * (int64_t)osz >= 0x7FFFFFFFLL)
+        return GEMM_BT_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) {
+        p->kernel = KIND_NONE;
+        return GEMM_BT_OK;
+    }
+    if (K == 0) {
+        p->kernel = KIND_FILL;
+        p->threads = 256;
+        const int64_t g = (M * N * osz / 2 + 255) / 256;
+        p->grid = g < 4096 ? g : 4096;
+        return GEMM_BT_OK;
+    }
+    // whole 16-byte chunks along every operand row, 16-byte aligned operands
+    auto rows_ok = [&](int layout, int64_t ext, int align) {
+        return align % 16 == 0 && (layout == GEMM_BT_K_OUTER ? ext % 8 == 0 : K % 8 == 0);
+    };
+    if (!rows_ok(a_layout, M, a_align) || !rows_ok(b_layout, N, b_align)) return GEMM_BT_ERR_UNSUPPORTED;
+    p->kernel = KIND_TRANS;
+    p->variant = (a_layout == GEMM_BT_K_OUTER ? 1 : 0) + (b_layout == GEMM_BT_K_OUTER ? 2 : 0) - 1;
+    p->bm = p->bn = 128;
+    p->bk = 64;
+    p->threads = 256;
+    p->vec = 8;
+    p->group_m = kGroupM;
+    p->ksplit = 1;
+    p->stages = 2;
+    p->lds_bytes = 2 * 2 * 128 * 64 * 2;
+    p->tiles_m = (M + 127) / 128;
+    p->tiles_n = (N + 127) / 128;
+    p->grid = p->tiles_m * p->tiles_n;
+    if (p->grid > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
+    (void)c_align;
+    return GEMM_BT_OK;
+}
+
+// transpose-read kernels [in: bf16, f16][out: f32, bf16, f16][variant: A K-outer, B K-outer, both]
+template <int IN, int OUT>
+static const void* trans_fn_v(int variant) {
+    if (variant == 0) return (const void*)&trans_kernel<IN, OUT, true, false>;
+    if (variant == 1) return (const void*)&trans_kernel<IN, OUT, false, true>;
+    return (const void*)&trans_kernel<IN, OUT, true, true>;
+}
+template <int IN>
+static const void* trans_fn_out(int out, int variant) {
+    if (out == GEMM_BT_F32) return trans_fn_v<IN, GEMM_BT_F32>(variant);
+    if (out == GEMM_BT_BF16) return trans_fn_v<IN, GEMM_BT_BF16>(variant);
+    return trans_fn_v<IN, GEMM_BT_F16>(variant);
+}
+
 // ---- kernel selection --------------------------------------------------------
 
 typedef void (*TiledFn)(const u16*, const u16*, void*, int, int, int, int, int, int, int);
@@ -465,6 +542,53 @@ int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, i
 int gemm_bt_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
                          int b_align, int c_align, gemm_bt_plan_t* plan) {
     return plan_impl(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
+}
+
+int gemm_bt_plan_layout(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
+                        int a_align, int b_align, int c_align, gemm_bt_plan_t* plan) {
+    return plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align, plan);
+}
+
+int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int a_layout, int b_layout,
+                   int in_dtype, int out_dtype, void* stream) {
+    if (a_layout == GEMM_BT_K_INNER && b_layout == GEMM_BT_K_INNER)
+        return gemm_bt(A, B, C, M, N, K, in_dtype, out_dtype, stream);
+    gemm_bt_plan_t p;
+    const int a_al = align_of(A), b_al = align_of(B), c_al = align_of(C);
+    int st = plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, &p);
+    if (st != GEMM_BT_OK) return st;
+    if (p.kernel == KIND_NONE) return GEMM_BT_OK;
+    const int osz = out_size(out_dtype);
+    if (!C) return GEMM_BT_ERR_INVALID_VALUE;
+    if (p.kernel != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
+    if ((uintptr_t)A % 2 || (uintptr_t)B % 2 || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
+    int num_cu = 256;
+    st = check_device(&num_cu);
+    if (st != GEMM_BT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (p.kernel == KIND_FILL) {
+        u16* c16 = (u16*)C;
+        size_t n16 = (size_t)M * (size_t)N * osz / 2;
+        long long sc = 0;
+        void* args[] = {&c16, &n16, &sc};
+        e = hipLaunchKernel((const void*)&zero_fill_kernel, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+    } else {
+        const u16* a = (const u16*)A;
+        const u16* b = (const u16*)B;
+        int vec_store = (N % 4 == 0) && c_al >= 4 * osz ? 1 : 0;
+        if (vec_store && (N * osz) % 16 == 0 && c_al >= 16) vec_store = 2;
+        const void* fn = in_dtype == GEMM_BT_BF16 ? trans_fn_out<GEMM_BT_BF16>(out_dtype, p.variant)
+                                                  : trans_fn_out<GEMM_BT_F16>(out_dtype, p.variant);
+        int Mi = (int)M, Ni = (int)N, Ki = (int)K, tm = (int)p.tiles_m, tn = (int)p.tiles_n, gm = p.group_m;
+        void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store};
+        e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_BT_ERR_LAUNCH;
+    }
+    return GEMM_BT_OK;
 }
 
 int gemm_bt_tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m, int64_t* tm, int64_t* tn) {

@@ -57,6 +57,12 @@ typedef enum {
     GEMM_BT_INT32 = 6     /* two's-complement 32-bit integer (output only; input GEMM_BT_INT8) */
 } gemm_bt_dtype;
 
+/* Operand layouts for gemm_bt_layout. */
+typedef enum {
+    GEMM_BT_K_INNER = 0, /* A stored M x K, B stored N x K (K contiguous): the gemm_bt layout */
+    GEMM_BT_K_OUTER = 1  /* A stored K x M (M contiguous), B stored K x N (N contiguous) */
+} gemm_bt_layout_t;
+
 /* Status codes returned by every entry point. */
 typedef enum {
     GEMM_BT_OK = 0,
@@ -107,6 +113,24 @@ int gemm_bt_batched(const void* A, const void* B, void* C, int64_t batch, int64_
                     int64_t stride_a, int64_t stride_b, int64_t stride_c, int in_dtype, int out_dtype,
                     void* stream);
 
+/*
+ * C = op(A) * op(B)^T with either operand stored K-outer ("Writing Mosaic GPU
+ * kernels with Pallas", section "MMA (TensorCore)", transposed operands: for
+ * 16-bit operands an A of shape (K, M), and likewise a B of shape (K, N), is
+ * accepted and transposed by the hardware).  a_layout = GEMM_BT_K_OUTER: A is
+ * K x M row-major; b_layout = GEMM_BT_K_OUTER: B is K x N row-major, so
+ * (K_INNER, K_OUTER) is the plain C = A * B.  Both K_INNER is exactly gemm_bt.
+ * Operands stored K-outer are transposed inside the kernel (LDS transpose
+ * reads); nothing is copied.  Requirements (else UNSUPPORTED): bf16 or f16
+ * inputs; every operand row in whole 16-byte chunks (M % 8 == 0 for a K-outer
+ * A, N % 8 == 0 for a K-outer B, K % 8 == 0 for a K-inner operand) and A, B
+ * 16-byte aligned; a K-outer operand below 2 GiB.  An unknown layout value is
+ * INVALID_VALUE.  Everything else (C, sizes, K == 0, streams, errors) is as
+ * for gemm_bt.
+ */
+int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int a_layout,
+                   int b_layout, int in_dtype, int out_dtype, void* stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* gemm_bt_status_string(int status);
 
@@ -122,7 +146,8 @@ int gemm_bt_version(void);
 typedef struct {
     int kernel;       /* 0 = none (empty), 1 = zero fill (K == 0), 2 = LDS-tiled MFMA with register-staged
                          loads (rows not 16-byte aligned), 3 = skinny streaming (M <= 16), 4 = LDS-tiled
-                         MFMA with direct global->LDS loads (16-byte aligned rows) */
+                         MFMA with direct global->LDS loads (16-byte aligned rows), 5 = LDS-tiled MFMA
+                         with LDS transpose reads (an operand stored K-outer) */
     int variant;      /* tile-shape variant index within the kernel family */
     int bm, bn, bk;   /* workgroup tile (rows of C, columns of C, K step) */
     int threads;      /* threads per workgroup */
@@ -139,6 +164,11 @@ typedef struct {
 
 int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
                  int b_align, int c_align, gemm_bt_plan_t* plan);
+
+/* The plan of gemm_bt_layout (for kernel 5 the variant is 0: A K-outer, 1: B
+   K-outer, 2: both). */
+int gemm_bt_plan_layout(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
+                        int a_align, int b_align, int c_align, gemm_bt_plan_t* plan);
 
 /* The plan of gemm_bt_batched: the tile tier counts the workgroups of all
    items; the alignments are those of every item's pointers. */

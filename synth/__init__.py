@@ -50,6 +50,7 @@ class Workload:
     dist: str
     seed: int
     batch: int = 1
+    b_layout: int = 0  # 1: B is stored K x N (the plain product A·B), read through gemm_bt_layout
 
     @property
     def flops(self) -> int:
@@ -67,7 +68,7 @@ class Workload:
 
 # The five measured shapes, seeds 0..4 in this order, the 4096³ product
 # with 8-bit E4M3 inputs (seed 5) and with int8 inputs and int32 output (seed 6),
-# and a batch of 64 products of 512³ (seed 7).
+# a batch of 64 products of 512³ (seed 7), and 4096³ with B stored K×N (seed 8).
 WORKLOADS = {
     "sq512_bf16_f32": Workload("sq512_bf16_f32", 512, 512, 512, "bf16", "f32", "normal", 0),
     "m1024_n4096_k4096_f16_f16": Workload("m1024_n4096_k4096_f16_f16", 1024, 4096, 4096, "f16", "f16",
@@ -80,6 +81,7 @@ WORKLOADS = {
     "sq4096_e4m3_bf16": Workload("sq4096_e4m3_bf16", 4096, 4096, 4096, "e4m3", "bf16", "normal", 5),
     "sq4096_i8_i32": Workload("sq4096_i8_i32", 4096, 4096, 4096, "i8", "i32", "int8", 6),
     "batch64_sq512_bf16_bf16": Workload("batch64_sq512_bf16_bf16", 512, 512, 512, "bf16", "bf16", "normal", 7, 64),
+    "sq4096_nn_bf16_bf16": Workload("sq4096_nn_bf16_bf16", 4096, 4096, 4096, "bf16", "bf16", "normal", 8, 1, 1),
 }
 
 

@@ -89,6 +89,35 @@ def test_batched_plan():
         gb.gemm_bt_plan_batched(2, 64, 64, 64, gb.FP8_E4M3, gb.F32, b_align=8)
 
 
+def test_layout_plan_and_validation():
+    KI, KO = gb.K_INNER, gb.K_OUTER
+    # both K-inner is the gemm_bt plan
+    assert gb.gemm_bt_plan_layout(4096, 4096, 4096, KI, KI, gb.BF16, gb.BF16).as_dict() == \
+        gb.gemm_bt_plan(4096, 4096, 4096, gb.BF16, gb.BF16).as_dict()
+    for la, lb, var in ((KO, KI, 0), (KI, KO, 1), (KO, KO, 2)):
+        p = gb.gemm_bt_plan_layout(1000, 3000, 2048, la, lb, gb.BF16, gb.F32)
+        assert (p.kernel, p.variant, p.bm, p.bn, p.tiles_m, p.tiles_n, p.grid) == (5, var, 128, 128, 8, 24, 192)
+    assert gb.gemm_bt_plan_layout(200, 104, 301, KO, KO, gb.F16, gb.F16).kernel == 5  # any K when both are K-outer
+    assert gb.gemm_bt_plan_layout(8, 8, 0, KO, KO, gb.BF16, gb.F32).kernel == 1
+    assert gb.gemm_bt_plan_layout(0, 8, 8, KO, KO, gb.BF16, gb.F32).kernel == 0
+    refused = [(100, 64, 64, KO, KI, gb.BF16, gb.F32),    # K-outer A needs M % 8 == 0
+               (64, 100, 64, KI, KO, gb.BF16, gb.F32),    # K-outer B needs N % 8 == 0
+               (64, 64, 60, KO, KI, gb.BF16, gb.F32),     # a K-inner operand needs K % 8 == 0
+               (64, 64, 64, KO, KI, gb.FP8_E4M3, gb.F32),  # 16-bit inputs only
+               (64, 64, 64, KO, KI, gb.INT8, gb.INT32),
+               (1 << 16, 64, 1 << 15, KO, KI, gb.BF16, gb.F32)]  # K-outer operand of 4 GiB
+    for args in refused:
+        with pytest.raises(gb.GemmBtError) as ei:
+            gb.gemm_bt_plan_layout(*args)
+        assert ei.value.status == gb.ERR_UNSUPPORTED, args
+    with pytest.raises(gb.GemmBtError) as ei:
+        gb.gemm_bt_plan_layout(64, 64, 64, 2, KI, gb.BF16, gb.F32)
+    assert ei.value.status == gb.ERR_INVALID_VALUE
+    with pytest.raises(gb.GemmBtError):
+        gb.gemm_bt_plan_layout(64, 64, 64, KO, KI, gb.BF16, gb.F32, a_align=8)
+    assert gb.gemm_bt_layout(16, 16, 16, 4, 4, 4, 3, 0, gb.BF16, gb.F32, None) == gb.ERR_INVALID_VALUE
+
+
 def test_no_device_status_without_gpu():
     import torch
 

@@ -242,7 +242,10 @@ def test_workload_full_size(gpu, name):
             rep = tolerance.check(f64(c[z].cpu()), cref[z], np.outer(nA[z], nB[z]), w.out_dtype)
             assert rep.ok, (name, z, rep)
         return
-    c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
+    if w.b_layout:
+        c = run_layout(gpu, a, b, 0, w.b_layout, w.in_dtype, w.out_dtype)
+    else:
+        c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
     if w.in_dtype == "i8":
         I, J = sample_entries(w.M, w.N, np.random.default_rng(w.seed))
         check_i8(c, a, b, name, I, J)
@@ -274,7 +277,10 @@ def test_workload_integer_twin_bit_exact(gpu, name):
             rep = tolerance.bit_exact(out_bits(c[z].cpu()), oracle.round_to(cref[z], w.out_dtype), w.out_dtype)
             assert rep.ok, (w.name, z, rep)
         return
-    c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
+    if w.b_layout:
+        c = run_layout(gpu, a, b, 0, w.b_layout, w.in_dtype, w.out_dtype)
+    else:
+        c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
     if w.in_dtype == "i8":
         I, J = sample_entries(w.M, w.N, np.random.default_rng(w.seed))
         check_i8(c, a, b, w.name, I, J)
@@ -516,3 +522,76 @@ def test_mm_bt_batched_wrapper(gpu):
     torch.cuda.synchronize()
     assert got.dtype == torch.int32 and got.shape == (2, 33, 17)
     assert np.array_equal(got.cpu().numpy().astype(np.int64), oracle.gemm_bt_batched_ref(a8, b8, "i8")[0])
+
+
+# ---------------------------------------------------------------- operands stored K-outer
+
+def run_layout(gb, a_bits, b_bits, a_layout, b_layout, in_dtype, out_dtype):
+    """Upload A (M,K) and B (N,K) bits in the requested storage (K-outer = transposed) and call gemm_bt_layout."""
+    KO = gb.K_OUTER
+    a_st = np.ascontiguousarray(a_bits.T) if a_layout == KO else a_bits
+    b_st = np.ascontiguousarray(b_bits.T) if b_layout == KO else b_bits
+    a, b = to_dev(a_st, in_dtype), to_dev(b_st, in_dtype)
+    M, N = a_bits.shape[0], b_bits.shape[0]
+    c = torch.full((M, N), float("nan"), dtype=TORCH_DT[out_dtype], device="cuda")
+    out = gb.mm_layout(a, b, a_layout, b_layout, out_dtype=TORCH_DT[out_dtype], out=c)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+# (M, N, K, A K-outer, B K-outer, in, out): one tile, ragged tiles, K tails of one step, odd K with both
+# operands K-outer, the plain product A·B at several sizes, and 16-bit edges of M and N
+LAYOUTS = [
+    (16, 16, 16, 1, 1, "bf16", "f32"), (64, 64, 64, 0, 1, "bf16", "bf16"), (136, 264, 72, 1, 0, "f16", "f32"),
+    (136, 256, 200, 0, 1, "bf16", "f32"), (200, 104, 301, 1, 1, "f16", "f16"), (1000, 3000, 2048, 0, 1, "bf16", "f32"),
+    (520, 1032, 264, 1, 1, "bf16", "bf16"), (257, 512, 136, 0, 1, "f16", "f16"), (512, 264, 136, 1, 0, "bf16", "bf16"),
+    (4096, 4096, 200, 0, 1, "bf16", "bf16"), (64, 4104, 64, 1, 1, "bf16", "f32"), (8, 8, 5, 1, 1, "bf16", "f32"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LAYOUTS)))
+def test_layouts(gpu, case):
+    M, N, K, la, lb, ind, outd = LAYOUTS[case]
+    seed = 1300 + case
+    say("layout", M, N, K, "A K-outer" if la else "A K-inner", "B K-outer" if lb else "B K-inner", ind, outd, "seed", seed)
+    a, b = synth.make(M, N, K, ind, "normal", seed)
+    c = run_layout(gpu, a, b, la, lb, ind, outd)
+    check_full(c, a, b, ind, outd, LAYOUTS[case])
+
+
+@pytest.mark.parametrize("case", [0, 3, 4, 6, 9])
+def test_layouts_integer_bit_exact(gpu, case):
+    M, N, K, la, lb, ind, outd = LAYOUTS[case]
+    seed = 1350 + case
+    say("layout int", M, N, K, la, lb, ind, outd, "seed", seed)
+    a, b = synth.make(M, N, K, ind, "int", seed)
+    c = run_layout(gpu, a, b, la, lb, ind, outd)
+    check_bits_full(c, a, b, ind, outd, LAYOUTS[case])
+
+
+def test_layouts_refused_and_inner_equals_gemm_bt(gpu):
+    s = torch.cuda.current_stream().cuda_stream
+    buf = torch.zeros(1 << 16, dtype=torch.int16, device="cuda")
+    c = torch.full((100, 64), float("nan"), dtype=torch.float32, device="cuda")
+    p = buf.data_ptr()
+    say("layout refused")
+    assert gpu.gemm_bt_layout(p, p, c.data_ptr(), 100, 64, 64, 1, 0, gpu.BF16, gpu.F32, s) == gpu.ERR_UNSUPPORTED
+    assert gpu.gemm_bt_layout(p + 8, p, c.data_ptr(), 64, 64, 64, 1, 0, gpu.BF16, gpu.F32, s) == gpu.ERR_UNSUPPORTED
+    assert gpu.gemm_bt_layout(p, p, c.data_ptr(), 64, 64, 64, 1, 7, gpu.BF16, gpu.F32, s) == gpu.ERR_INVALID_VALUE
+    torch.cuda.synchronize()
+    assert torch.isnan(c).all()
+    say("layout K-inner = gemm_bt")
+    a, b = synth.make(300, 200, 136, "bf16", "normal", 1399)
+    c1 = run_layout(gpu, a, b, 0, 0, "bf16", "bf16")
+    c2 = run_gpu(gpu, a, b, "bf16", "bf16")
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+
+
+def test_mm_wrapper_is_a_times_b(gpu):
+    say("mm wrapper")
+    a, bt = synth.make(96, 80, 64, "bf16", "normal", 1398)  # bt is B^T (N x K)
+    A = to_dev(a, "bf16")
+    Bkn = to_dev(np.ascontiguousarray(bt.T), "bf16")  # B stored K x N
+    got = gpu.mm(A, Bkn, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_full(got.cpu(), a, bt, "bf16", "f32", "mm")
