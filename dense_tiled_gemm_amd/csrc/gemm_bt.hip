@@ -366,7 +366,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
 // 128 x 128 transpose-read kernel; 16-bit inputs with every operand row in
 // whole, aligned 16-byte chunks.
 static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
-                            int a_align, int b_align, int c_align, gemm_bt_plan_t* p) {
+                            int a_align, int b_align, int c_align, int num_cu, gemm_bt_plan_t* p) {
     if (!p) return GEMM_BT_ERR_INVALID_VALUE;
     if ((a_layout != GEMM_BT_K_INNER && a_layout != GEMM_BT_K_OUTER) ||
         (b_layout != GEMM_BT_K_INNER && b_layout != GEMM_BT_K_OUTER)) {
@@ -374,7 +374,7 @@ static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b
         return GEMM_BT_ERR_INVALID_VALUE;
     }
     if (a_layout == GEMM_BT_K_INNER && b_layout == GEMM_BT_K_INNER)
-        return plan_impl(1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, p);
+        return plan_impl(1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, p);
     std::memset(p, 0, sizeof(*p));
     if (M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
     p->batch = 1;
@@ -406,30 +406,38 @@ static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b
         return align % 16 == 0 && (layout == GEMM_BT_K_OUTER ? ext % 8 == 0 : K % 8 == 0);
     };
     if (!rows_ok(a_layout, M, a_align) || !rows_ok(b_layout, N, b_align)) return GEMM_BT_ERR_UNSUPPORTED;
+    // 256 x 256 tiles (8 waves) when that fills every CU, else 128 x 128 (4 waves)
+    const bool big = ((M + 255) / 256) * ((N + 255) / 256) >= num_cu;
+    const int bt = big ? 256 : 128;
     p->kernel = KIND_TRANS;
-    p->variant = (a_layout == GEMM_BT_K_OUTER ? 1 : 0) + (b_layout == GEMM_BT_K_OUTER ? 2 : 0) - 1;
-    p->bm = p->bn = 128;
+    p->variant = (a_layout == GEMM_BT_K_OUTER ? 1 : 0) + (b_layout == GEMM_BT_K_OUTER ? 2 : 0) - 1 + (big ? 3 : 0);
+    p->bm = p->bn = bt;
     p->bk = 64;
-    p->threads = 256;
+    p->threads = big ? 512 : 256;
     p->vec = 8;
     p->group_m = kGroupM;
     p->ksplit = 1;
     p->stages = 2;
-    p->lds_bytes = 2 * 2 * 128 * 64 * 2;
-    p->tiles_m = (M + 127) / 128;
-    p->tiles_n = (N + 127) / 128;
+    p->lds_bytes = 2 * 2 * bt * 64 * 2;
+    p->tiles_m = (M + bt - 1) / bt;
+    p->tiles_n = (N + bt - 1) / bt;
     p->grid = p->tiles_m * p->tiles_n;
     if (p->grid > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
     (void)c_align;
     return GEMM_BT_OK;
 }
 
-// transpose-read kernels [in: bf16, f16][out: f32, bf16, f16][variant: A K-outer, B K-outer, both]
+// transpose-read kernels [in: bf16, f16][out: f32, bf16, f16][variant: A K-outer, B K-outer, both; + 3 for the
+// 256 x 256 tile]
+template <int IN, int OUT, int BT, int W2>
+static const void* trans_fn_t(int layouts) {
+    if (layouts == 0) return (const void*)&trans_kernel<IN, OUT, true, false, BT, BT, 2, W2>;
+    if (layouts == 1) return (const void*)&trans_kernel<IN, OUT, false, true, BT, BT, 2, W2>;
+    return (const void*)&trans_kernel<IN, OUT, true, true, BT, BT, 2, W2>;
+}
 template <int IN, int OUT>
 static const void* trans_fn_v(int variant) {
-    if (variant == 0) return (const void*)&trans_kernel<IN, OUT, true, false>;
-    if (variant == 1) return (const void*)&trans_kernel<IN, OUT, false, true>;
-    return (const void*)&trans_kernel<IN, OUT, true, true>;
+    return variant >= 3 ? trans_fn_t<IN, OUT, 256, 4>(variant - 3) : trans_fn_t<IN, OUT, 128, 2>(variant);
 }
 template <int IN>
 static const void* trans_fn_out(int out, int variant) {
@@ -546,7 +554,7 @@ int gemm_bt_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int in_
 
 int gemm_bt_plan_layout(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
                         int a_align, int b_align, int c_align, gemm_bt_plan_t* plan) {
-    return plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align, plan);
+    return plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
 }
 
 int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int a_layout, int b_layout,
@@ -555,7 +563,7 @@ int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, 
         return gemm_bt(A, B, C, M, N, K, in_dtype, out_dtype, stream);
     gemm_bt_plan_t p;
     const int a_al = align_of(A), b_al = align_of(B), c_al = align_of(C);
-    int st = plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, &p);
+    int st = plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
     if (st != GEMM_BT_OK) return st;
     if (p.kernel == KIND_NONE) return GEMM_BT_OK;
     const int osz = out_size(out_dtype);
@@ -565,6 +573,10 @@ int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, 
     int num_cu = 256;
     st = check_device(&num_cu);
     if (st != GEMM_BT_OK) return st;
+    if (num_cu != 256) {
+        st = plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, num_cu, &p);
+        if (st != GEMM_BT_OK) return st;
+    }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (p.kernel == KIND_FILL) {

@@ -98,6 +98,9 @@ def test_layout_plan_and_validation():
         p = gb.gemm_bt_plan_layout(1000, 3000, 2048, la, lb, gb.BF16, gb.F32)
         assert (p.kernel, p.variant, p.bm, p.bn, p.tiles_m, p.tiles_n, p.grid) == (5, var, 128, 128, 8, 24, 192)
     assert gb.gemm_bt_plan_layout(200, 104, 301, KO, KO, gb.F16, gb.F16).kernel == 5  # any K when both are K-outer
+    for la, lb, var in ((KO, KI, 3), (KI, KO, 4), (KO, KO, 5)):  # 256 x 256 tiles when they fill every CU
+        p = gb.gemm_bt_plan_layout(4096, 4096, 4096, la, lb, gb.BF16, gb.BF16)
+        assert (p.kernel, p.variant, p.bm, p.threads, p.grid, p.lds_bytes) == (5, var, 256, 512, 256, 128 * 1024)
     assert gb.gemm_bt_plan_layout(8, 8, 0, KO, KO, gb.BF16, gb.F32).kernel == 1
     assert gb.gemm_bt_plan_layout(0, 8, 8, KO, KO, gb.BF16, gb.F32).kernel == 0
     refused = [(100, 64, 64, KO, KI, gb.BF16, gb.F32),    # K-outer A needs M % 8 == 0
