@@ -15,17 +15,17 @@
 // One workgroup computes one BM x BN tile of C (256 x 256 with 8 waves as
 // 2 x 4, or 128 x 128 with 4 waves as 2 x 2), each wave (BM/WM) x (BN/WN) as
 // 16 x 16 blocks of v_mfma_f32_16x16x32.  Per K step of 64:
-//   * loader: every thread moves 16-byte chunks of each operand through
-//     registers (buffer loads; rows past M or N, k >= K, and chunks past the
-//     edge of a K-outer row read as zero);
+//   * loader: LDS DMA (buffer_load ... lds), one 1 KiB block of tile rows
+//     per wave instruction, the swizzle applied by choosing which global
+//     chunk each lane fetches; rows past M or N, k >= K, and chunks past the
+//     edge of a K-outer row land as zeros;
 //   * LDS, per operand and stage BX x 64 x 2 bytes (BX = BM or BN):
 //       K-inner: BX rows x 128 bytes, chunk c of row r at c ^ ((r >> 1) & 7);
 //       K-outer: 64 rows x 2*BX bytes, chunk c of row r at c ^ 2 s(r) with
 //       s(r) = (r & 3) | ((r >> 3) & 1) << 2, so the 16 rows x 32 bytes that
 //       one transpose read touches fall in distinct bank ranges;
-//   * pipeline: two stages; the loads for step k+1 are issued before the
-//     MFMAs of step k and written to the other stage after them, one barrier
-//     per step (the register-staged scheme of tiled_kernel.hpp);
+//   * pipeline: two stages; the transfers for step k+1 go out before the
+//     MFMAs of step k, one s_waitcnt vmcnt(0) and one barrier per step;
 //   * epilogue: the shared store_tile / store_tile_lds.
 // Requirements checked by the host: bf16 or f16 inputs, every operand row in
 // 16-byte chunks (K % 8 == 0 for a K-inner operand, M % 8 == 0 for a K-outer
@@ -33,6 +33,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "dma_kernel.hpp"  // dma16, rsrc_words, wait_vmcnt, barrier_no_fence
 
 namespace gbt {
 
@@ -50,17 +51,12 @@ __device__ inline int kouter_swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) 
 // Geometry of one operand tile of BX rows/columns by 64 k in LDS.
 //   K-inner: BX rows of 128 bytes (8 chunks), chunk c of row r at c ^ ((r >> 1) & 7);
 //   K-outer: 64 rows of 2*BX bytes (BX/8 chunks), chunk c of row r at c ^ kouter_swz(r).
-// Loader: T threads, 16-byte chunks; thread t takes chunk column t % CR of rows
-// t / CR + (T / CR) * i, so its swizzle term is the same for all its rows.
 template <int BX, bool KOUTER, int T>
 struct OpGeom {
     static constexpr int ROWB = KOUTER ? 2 * BX : 128;  // bytes per LDS row
     static constexpr int CR = ROWB / 16;                 // chunks per row
     static constexpr int ROWS = KOUTER ? 64 : BX;
-    static constexpr int STEP = T / CR;                  // rows between a thread's chunks
-    static constexpr int NCH = ROWS * CR / T;            // chunks per thread per K step
     static constexpr int BYTES = ROWS * ROWB;
-    static_assert(STEP % 16 == 0 && NCH * T == ROWS * CR, "loader rows must keep the swizzle phase");
 };
 
 template <int IN, int OUT, bool TA, bool TB, int BM, int BN, int WM, int WN>
@@ -76,64 +72,63 @@ __global__ __launch_bounds__(64 * WM * WN) void trans_kernel(const u16* __restri
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (LDS-DMA base)
     const int wm = wave / WN, wn = wave % WN;
 
     int64_t tm64, tn64;
     tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
     const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
 
-    // Global view of one operand: rows past the extent (K-inner) or k >= K
-    // (K-outer: the range ends at the matrix end) read as zero.
-    struct Src {
-        __amdgpu_buffer_rsrc_t r;
-        u32 ld_bytes;  // bytes between consecutive k (K-outer) or rows (K-inner)
-        int lim;       // elements of a k-row from x0 (K-outer)
-    };
+    // Global view of one operand as four buffer-resource words: rows past the
+    // extent (K-inner) or the matrix end (K-outer) read as zero.
     auto make_src = [&](const u16* X, int x0, int ext, bool kouter, int bx) {
-        Src s;
-        if (kouter) {
-            s.r = make_rsrc(X + x0, (u32)min(((size_t)K * ext - x0) * 2, (size_t)0x7FFFFFFF));
-            s.ld_bytes = (u32)ext * 2u;
-        } else {
-            s.r = make_rsrc(X + (size_t)x0 * K, (u32)min(bx, ext - x0) * (u32)K * 2u);
-            s.ld_bytes = (u32)K * 2u;
-        }
-        s.lim = ext - x0;
-        return s;
+        if (kouter)
+            return rsrc_words(X + x0, (u32)min(((size_t)K * ext - x0) * 2, (size_t)0x7FFFFFFF));
+        return rsrc_words(X + (size_t)x0 * K, (u32)min(bx, ext - x0) * (u32)K * 2u);
     };
-    const Src sa = make_src(A, m0, M, TA, BM);
-    const Src sb = make_src(B, n0, N, TB, BN);
+    const i32x4 ra = make_src(A, m0, M, TA, BM);
+    const i32x4 rb = make_src(B, n0, N, TB, BN);
+    const int lim_a = M - m0, lim_b = N - n0;
 
-    u32x4 ga[GA::NCH], gb[GB::NCH];
-    auto gload_op = [&](const Src& s, auto geom, auto kouter_c, int kt, auto& g) {
+    // Loader: LDS-DMA, one 1 KiB block (RPI = 1024 / ROWB rows) per wave
+    // instruction; this wave fills blocks wave + W*i.  Lane L writes row
+    // (block * RPI + L / CR) at physical chunk L % CR, so it fetches the
+    // logical chunk (L % CR) ^ swizzle(row); chunks at k >= K (K-inner: whole
+    // chunks, K % 8 == 0) or past the edge of a K-outer row are sent out of
+    // range and land as zeros.
+    constexpr int W = WM * WN;
+    auto issue_op = [&](const i32x4& r, unsigned char* dst, auto geom, auto kouter_c, int kt, int lim, u32 ld_bytes) {
         typedef decltype(geom) G;
         constexpr bool KO = decltype(kouter_c)::value;
-        const int c = tid % G::CR, r = tid / G::CR;
-        if constexpr (KO) {
-            const bool col_ok = c * 8 < s.lim;
+        constexpr int RPI = 1024 / G::ROWB, NI = G::BYTES / 1024 / W;
+        static_assert(NI * W * 1024 == G::BYTES, "blocks split evenly over waves");
+        const int lc = lane % G::CR;
 #pragma unroll
-            for (int i = 0; i < G::NCH; ++i) {
-                const int k = kt * BK + r + G::STEP * i;
-                g[i] = load8<8>(s.r, (u32)k * s.ld_bytes + (u32)c * 16u, col_ok && k < K ? 8 : 0);
+        for (int i = 0; i < NI; ++i) {
+            const int blk = wave + W * i;
+            const int row = blk * RPI + lane / G::CR;
+            u32 off;
+            if constexpr (KO) {
+                // row = k within the step; ld_bytes = the operand's row pitch (2 * M or 2 * N)
+                const int c = lc ^ kouter_swz(row);
+                const int k = kt * BK + row;
+                off = (k < K && c * 8 < lim) ? (u32)k * ld_bytes + (u32)c * 16u : kOutOfRange;
+            } else {
+                // row = tile row; ld_bytes = 2 * K
+                const int c = lc ^ ((row >> 1) & 7);
+                const int kc = kt * BK + c * 8;
+                off = kc < K ? (u32)row * ld_bytes + (u32)kc * 2u : kOutOfRange;
             }
-        } else {
-            const int kc = kt * BK + c * 8;
-#pragma unroll
-            for (int i = 0; i < G::NCH; ++i)
-                g[i] = load8<8>(s.r, (u32)(r + G::STEP * i) * s.ld_bytes + (u32)kc * 2u, kc < K ? 8 : 0);
+            dma16(r, dst + blk * 1024, off, 0u);
         }
-    };
-    auto swrite_op = [&](unsigned char* dst, auto geom, auto kouter_c, const auto& g) {
-        typedef decltype(geom) G;
-        constexpr bool KO = decltype(kouter_c)::value;
-        const int c = tid % G::CR, r = tid / G::CR;
-        const int phys = c ^ (KO ? kouter_swz(r) : ((r >> 1) & 7));
-#pragma unroll
-        for (int i = 0; i < G::NCH; ++i) *(u32x4*)(dst + (r + G::STEP * i) * G::ROWB + phys * 16) = g[i];
     };
     typedef std::integral_constant<bool, TA> KA;
     typedef std::integral_constant<bool, TB> KB;
+    auto issue = [&](int stage, int kt) {
+        unsigned char* base = lds + stage * STAGE;
+        issue_op(ra, base, GA(), KA(), kt, lim_a, TA ? (u32)M * 2u : (u32)K * 2u);
+        issue_op(rb, base + GA::BYTES, GB(), KB(), kt, lim_b, TB ? (u32)N * 2u : (u32)K * 2u);
+    };
 
     // Fragment reads for k-substep ks (32 k) of the 16-row/column block at x
     // (a multiple of 16) within an operand tile.
@@ -165,41 +160,40 @@ __global__ __launch_bounds__(64 * WM * WN) void trans_kernel(const u16* __restri
 #pragma unroll
             for (int r = 0; r < AB::regs; ++r) acc[i][j][r] = 0.0f;
 
+    // Both k-substeps' fragments are read before their MFMAs, so the second
+    // substep's reads run under the first substep's MFMAs.
     auto compute = [&](int stage) {
         const unsigned char* sA = lds + stage * STAGE;
         const unsigned char* sB = sA + GA::BYTES;
+        u32x4 fb[BK / 32][FN], fa[BK / 32][FM];
         static_for<0, BK / 32>([&](auto ksc) {
             constexpr int ks = decltype(ksc)::value;
-            u32x4 fb[FN], fa[FM];
-            static_for<0, FN>([&](auto ic) { fb[ic] = frag(sB, GB(), KB(), wn * TN + 16 * ic, ks); });
-            static_for<0, FM>([&](auto jc) { fa[jc] = frag(sA, GA(), KA(), wm * TM + 16 * jc, ks); });
+            static_for<0, FN>([&](auto ic) { fb[ks][ic] = frag(sB, GB(), KB(), wn * TN + 16 * ic, ks); });
+            static_for<0, FM>([&](auto jc) { fa[ks][jc] = frag(sA, GA(), KA(), wm * TM + 16 * jc, ks); });
+        });
+        static_for<0, BK / 32>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
             static_for<0, FN * FM>([&](auto tc) {
                 constexpr int t = decltype(tc)::value;
-                acc[t / FM][t % FM] = Mfma<IN>::m16x16x32(fb[t / FM], fa[t % FM], acc[t / FM][t % FM]);
+                acc[t / FM][t % FM] = Mfma<IN>::m16x16x32(fb[ks][t / FM], fa[ks][t % FM], acc[t / FM][t % FM]);
             });
         });
     };
 
+    // Two LDS stages: the transfers of tile kt+1 go out into the other stage
+    // (free since the last barrier) before tile kt is multiplied; each wave
+    // then waits for its own transfers and the barrier makes all of them,
+    // and the end of every wave's reads of stage kt, visible.
     const int nk = (K + BK - 1) / BK;
-    gload_op(sa, GA(), KA(), 0, ga);
-    gload_op(sb, GB(), KB(), 0, gb);
-    swrite_op(lds, GA(), KA(), ga);
-    swrite_op(lds + GA::BYTES, GB(), KB(), gb);
-    __syncthreads();
+    issue(0, 0);
+    wait_vmcnt<0>();
+    barrier_no_fence();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            gload_op(sa, GA(), KA(), kt + 1, ga);
-            gload_op(sb, GB(), KB(), kt + 1, gb);
-        }
+        if (kt + 1 < nk) issue(cur ^ 1, kt + 1);
         compute(cur);
-        if (more) {
-            unsigned char* nxt = lds + (cur ^ 1) * STAGE;
-            swrite_op(nxt, GA(), KA(), ga);
-            swrite_op(nxt + GA::BYTES, GB(), KB(), gb);
-        }
-        __syncthreads();
+        wait_vmcnt<0>();
+        barrier_no_fence();
     }
 
     // the loop ended on a barrier: LDS is free for the whole-row epilogue
