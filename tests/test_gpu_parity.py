@@ -597,3 +597,57 @@ def test_mm_wrapper_is_a_times_b(gpu):
     got = gpu.mm(A, Bkn, out_dtype=torch.float32)
     torch.cuda.synchronize()
     check_full(got.cpu(), a, bt, "bf16", "f32", "mm")
+
+
+# ---------------------------------------------------------------- graph capture
+
+def test_graph_capture_replays_match_eager(gpu):
+    """Calls captured into a HIP graph (plain, batched, K-outer, int8, K = 0) replay bit for bit like eager
+    calls, several times, with eager work and synchronisation between the replays.  The library allocates
+    nothing and clears memory with a kernel, never a memset node."""
+    say("graph capture")
+    a, b = synth.make(300, 520, 136, "bf16", "normal", 1400)
+    a3, b3 = synth.make_batched(3, 64, 96, 64, "f16", "normal", 1401)
+    a8, b8 = synth.make(130, 260, 160, "i8", "int8", 1402)
+    A, B = to_dev(a, "bf16"), to_dev(b, "bf16")
+    Bko = to_dev(np.ascontiguousarray(b.T), "bf16")
+    A3, B3 = to_dev(a3, "f16"), to_dev(b3, "f16")
+    A8, B8 = to_dev(a8, "i8"), to_dev(b8, "i8")
+    outs = [torch.empty(300, 520, dtype=torch.bfloat16, device="cuda"),
+            torch.empty(300, 520, dtype=torch.float32, device="cuda"),
+            torch.empty(3, 64, 96, dtype=torch.float16, device="cuda"),
+            torch.empty(130, 260, dtype=torch.int32, device="cuda"),
+            torch.full((40, 24), float("nan"), dtype=torch.float32, device="cuda")]
+
+    def work(stream):
+        s = stream.cuda_stream
+        assert gpu.gemm_bt(A.data_ptr(), B.data_ptr(), outs[0].data_ptr(), 300, 520, 136, gpu.BF16, gpu.BF16, s) == 0
+        assert gpu.gemm_bt_layout(A.data_ptr(), Bko.data_ptr(), outs[1].data_ptr(), 300, 520, 136, gpu.K_INNER,
+                                  gpu.K_OUTER, gpu.BF16, gpu.F32, s) == 0
+        assert gpu.gemm_bt_batched(A3.data_ptr(), B3.data_ptr(), outs[2].data_ptr(), 3, 64, 96, 64, 64 * 64, 96 * 64,
+                                   64 * 96, gpu.F16, gpu.F16, s) == 0
+        assert gpu.gemm_bt(A8.data_ptr(), B8.data_ptr(), outs[3].data_ptr(), 130, 260, 160, gpu.INT8, gpu.INT32, s) == 0
+        assert gpu.gemm_bt(A.data_ptr(), B.data_ptr(), outs[4].data_ptr(), 40, 24, 0, gpu.BF16, gpu.F32, s) == 0
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        work(side)
+    side.synchronize()
+    eager = [o.clone() for o in outs]
+    bits = lambda t: t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        work(side)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(7)  # eager work between replays; the replay must overwrite all of it
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(bits(o), bits(e)), ("replay", rep, "output", i)
+    # and the eager results are right
+    check_full(eager[0].cpu(), a, b, "bf16", "bf16", "graph plain")
+    check_full(eager[1].cpu(), a, b, "bf16", "f32", "graph K-outer")
+    assert np.array_equal(eager[3].cpu().numpy().astype(np.int64), oracle.gemm_bt_i8(a8, b8))
+    assert (eager[4] == 0).all()
