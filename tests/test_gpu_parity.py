@@ -651,3 +651,25 @@ def test_graph_capture_replays_match_eager(gpu):
     check_full(eager[1].cpu(), a, b, "bf16", "f32", "graph K-outer")
     assert np.array_equal(eager[3].cpu().numpy().astype(np.int64), oracle.gemm_bt_i8(a8, b8))
     assert (eager[4] == 0).all()
+
+
+# ---------------------------------------------------------------- the largest supported K
+
+@pytest.mark.parametrize("M,N,K,ind,outd", [
+    (32, 40, 4194296, "bf16", "f32"),    # tiled kernel: 256 rows of K at the 32-bit panel limit (K % 8 == 0)
+    (33, 24, 4194298, "f16", "f16"),     # tiled kernel with a K tail of 2
+    (16, 24, 4194296, "bf16", "bf16"),   # streaming kernel (M <= 16)
+    (32, 32, 8388592, "e4m3", "bf16"),   # 8-bit inputs: the largest K % 16 == 0 below the limit
+])
+def test_largest_k(gpu, M, N, K, ind, outd):
+    """The largest K that the 32-bit buffer offsets allow (256 * K * element size < 2^31), and the first refused."""
+    say("largest K", M, N, K, ind, outd)
+    a, b = synth.make(M, N, K, ind, "normal_scaled", 1450)
+    c = run_gpu(gpu, a, b, ind, outd)
+    check_full(c, a, b, ind, outd, (M, N, K))
+    isz = 1 if ind == "e4m3" else 2
+    code = {"bf16": gpu.BF16, "f16": gpu.F16, "e4m3": gpu.FP8_E4M3}[ind]
+    too_big = (0x7FFFFFFF // (256 * isz)) + 16
+    with pytest.raises(gpu.GemmBtError) as ei:
+        gpu.gemm_bt_plan(M, N, too_big, code, gpu.F32)
+    assert ei.value.status == gpu.ERR_UNSUPPORTED
