@@ -511,12 +511,18 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading A(kt), B(kt)
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);
+            // the post-barrier substep (MFMAs with the refill loads and the next
+            // tile's first reads among them) runs at raised wave priority, so
+            // the SIMD's arbiter favours it over the other wave's pre-barrier
+            // substep (4096^3: 97.8 -> 96.3 us)
+            __builtin_amdgcn_s_setprio(1);
             mma_step(fb[1], fa[1], true,
                      [&](int d) {
                          if (d < LBW) load_b(sa, kt + 2, d);
                          else if (!SPLIT) load_a(sb, kt + 3, d - LBW);
                      },
                      [&](auto rc) { read_one(slot(na), slot(nb), 0, rc, fb[0], fa[0]); });
+            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_s_waitcnt(0xC07F);
             sa = na;
         }
