@@ -8,10 +8,13 @@ Entry points (same names as the C-ABI in ``include/gemm_bt.h``):
   gemm_bt(A, B, C, M, N, K, in_dtype, out_dtype, stream)   raw device pointers
   gemm_bt_batched(A, B, C, batch, M, N, K, stride_a, stride_b, stride_c, in_dtype, out_dtype, stream)
   gemm_bt_layout(A, B, C, M, N, K, a_layout, b_layout, in_dtype, out_dtype, stream)
+  gemm_bt_batched_layout(A, B, C, batch, M, N, K, stride_a, stride_b, stride_c, a_layout, b_layout, in_dtype,
+                         out_dtype, stream)
   gemm_bt_status_string(status), gemm_bt_version()
   gemm_bt_plan(M, N, K, in_dtype, out_dtype, a_align, b_align, c_align)
   gemm_bt_plan_batched(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align)
   gemm_bt_plan_layout(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align)
+  gemm_bt_plan_batched_layout(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align)
   gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m)
 and torch convenience wrappers ``mm_bt(a, b, out_dtype)`` (2-D or batched 3-D operands),
 ``mm_layout(a, b, a_layout, b_layout, out_dtype)`` and ``mm(a, b, out_dtype)`` (= a @ b).
@@ -28,8 +31,9 @@ K_INNER, K_OUTER = 0, 1  # operand layouts of gemm_bt_layout
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemm_bt.so")
-EXPORTS = ("gemm_bt", "gemm_bt_batched", "gemm_bt_layout", "gemm_bt_status_string", "gemm_bt_version",
-           "gemm_bt_plan", "gemm_bt_plan_batched", "gemm_bt_plan_layout", "gemm_bt_tile_coord")
+EXPORTS = ("gemm_bt", "gemm_bt_batched", "gemm_bt_layout", "gemm_bt_batched_layout", "gemm_bt_status_string",
+           "gemm_bt_version", "gemm_bt_plan", "gemm_bt_plan_batched", "gemm_bt_plan_layout",
+           "gemm_bt_plan_batched_layout", "gemm_bt_tile_coord")
 
 _lock = threading.Lock()
 _lib = None
@@ -72,6 +76,11 @@ def load():
             lib.gemm_bt_layout.restype = ci
             lib.gemm_bt_plan_layout.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             lib.gemm_bt_plan_layout.restype = ci
+            lib.gemm_bt_batched_layout.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, ci, ci, vp]
+            lib.gemm_bt_batched_layout.restype = ci
+            lib.gemm_bt_plan_batched_layout.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ci, ci, ci,
+                                                        ctypes.POINTER(Plan)]
+            lib.gemm_bt_plan_batched_layout.restype = ci
             lib.gemm_bt_status_string.argtypes = [ci]
             lib.gemm_bt_status_string.restype = ctypes.c_char_p
             lib.gemm_bt_version.argtypes = []
@@ -121,6 +130,24 @@ def gemm_bt_plan_layout(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_alig
                                     ctypes.byref(p))
     if st != OK:
         raise GemmBtError(st, "gemm_bt_plan_layout")
+    return p
+
+
+def gemm_bt_batched_layout(A: int, B: int, C: int, batch: int, M: int, N: int, K: int, stride_a: int, stride_b: int,
+                           stride_c: int, a_layout: int, b_layout: int, in_dtype: int, out_dtype: int,
+                           stream: int | None) -> int:
+    """Raw batched call with operand layouts; returns the status code."""
+    return int(load().gemm_bt_batched_layout(A or None, B or None, C or None, batch, M, N, K, stride_a, stride_b,
+                                             stride_c, a_layout, b_layout, in_dtype, out_dtype, stream or None))
+
+
+def gemm_bt_plan_batched_layout(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align=256, b_align=256,
+                                c_align=256):
+    p = Plan()
+    st = load().gemm_bt_plan_batched_layout(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align,
+                                            c_align, ctypes.byref(p))
+    if st != OK:
+        raise GemmBtError(st, "gemm_bt_plan_batched_layout")
     return p
 
 
@@ -239,14 +266,18 @@ def mm_bt(a, b, out_dtype=None, out=None, stream=None):
 
 
 def mm_layout(a, b, a_layout=K_INNER, b_layout=K_INNER, out_dtype=None, out=None, stream=None):
-    """C = op(a) @ op(b).T for 2-D 16-bit tensors: a is (M,K) for K_INNER or (K,M) for K_OUTER, b is (N,K)
-    for K_INNER or (K,N) for K_OUTER.  Operands stored K-outer are transposed inside the kernel."""
+    """C = op(a) @ op(b).T for 16-bit tensors: a is (M,K) for K_INNER or (K,M) for K_OUTER, b is (N,K) for
+    K_INNER or (K,N) for K_OUTER.  Either may carry a leading batch dimension Z (then C is (Z,M,N)); a 2-D
+    operand, or one expanded along the batch, is shared by every item.  Operands stored K-outer are
+    transposed inside the kernel."""
     import torch
 
-    if a.dim() != 2 or b.dim() != 2:
-        raise ValueError("expected 2-D operands")
-    M, K = (a.shape[1], a.shape[0]) if a_layout == K_OUTER else (a.shape[0], a.shape[1])
-    N, Kb = (b.shape[1], b.shape[0]) if b_layout == K_OUTER else (b.shape[0], b.shape[1])
+    if a.dim() not in (2, 3) or b.dim() not in (2, 3):
+        raise ValueError("expected 2-D or 3-D operands")
+    if a.dim() == 3 and b.dim() == 3 and a.shape[0] != b.shape[0]:
+        raise ValueError("batch sizes differ: %d and %d" % (a.shape[0], b.shape[0]))
+    M, K = (a.shape[-1], a.shape[-2]) if a_layout == K_OUTER else (a.shape[-2], a.shape[-1])
+    N, Kb = (b.shape[-1], b.shape[-2]) if b_layout == K_OUTER else (b.shape[-2], b.shape[-1])
     if K != Kb:
         raise ValueError("inner dimensions differ: %d and %d" % (K, Kb))
     if a.dtype != b.dtype:
@@ -256,22 +287,26 @@ def mm_layout(a, b, a_layout=K_INNER, b_layout=K_INNER, out_dtype=None, out=None
     in_code = _torch_code(a.dtype)
     out_code = in_code if out_dtype is None else (_torch_code(out_dtype) if not isinstance(out_dtype, int)
                                                   else out_dtype)
-    a = a.contiguous()
-    b = b.contiguous()
+    batched = a.dim() == 3 or b.dim() == 3
+    Z = a.shape[0] if a.dim() == 3 else (b.shape[0] if b.dim() == 3 else 1)
+    a, sa = _batch_operand(a)
+    b, sb = _batch_operand(b)
+    shape = (Z, M, N) if batched else (M, N)
     if out is None:
-        out = torch.empty((M, N), dtype=_torch_dtype(out_code), device=a.device)
-    elif tuple(out.shape) != (M, N) or not out.is_contiguous() or out.dtype != _torch_dtype(out_code):
-        raise ValueError("out must be a contiguous %dx%d %s tensor" % (M, N, _torch_dtype(out_code)))
+        out = torch.empty(shape, dtype=_torch_dtype(out_code), device=a.device)
+    elif tuple(out.shape) != shape or not out.is_contiguous() or out.dtype != _torch_dtype(out_code):
+        raise ValueError("out must be a contiguous %s %s tensor" % ("x".join(map(str, shape)), _torch_dtype(out_code)))
     if stream is None:
         stream = torch.cuda.current_stream(a.device).cuda_stream
     with torch.cuda.device(a.device):
-        st = gemm_bt_layout(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, a_layout, b_layout, in_code,
-                            out_code, stream)
+        st = gemm_bt_batched_layout(a.data_ptr(), b.data_ptr(), out.data_ptr(), Z, M, N, K, sa, sb, M * N, a_layout,
+                                    b_layout, in_code, out_code, stream)
     if st != OK:
         raise GemmBtError(st)
     return out
 
 
 def mm(a, b, out_dtype=None, out=None, stream=None):
-    """C = a @ b for 2-D 16-bit tensors a (M,K) and b (K,N): B is read K-outer, as it lies in memory."""
+    """C = a @ b for 16-bit tensors a (M,K) and b (K,N), or batches of them (Z,M,K) and (Z,K,N): B is read
+    K-outer, as it lies in memory."""
     return mm_layout(a, b, K_INNER, K_OUTER, out_dtype, out, stream)

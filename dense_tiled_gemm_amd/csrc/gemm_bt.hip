@@ -365,8 +365,8 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
 // Plan for operands stored K-outer (A as K x M and/or B as K x N): the
 // 128 x 128 transpose-read kernel; 16-bit inputs with every operand row in
 // whole, aligned 16-byte chunks.
-static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
-                            int a_align, int b_align, int c_align, int num_cu, gemm_bt_plan_t* p) {
+static int plan_layout_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype,
+                            int out_dtype, int a_align, int b_align, int c_align, int num_cu, gemm_bt_plan_t* p) {
     if (!p) return GEMM_BT_ERR_INVALID_VALUE;
     if ((a_layout != GEMM_BT_K_INNER && a_layout != GEMM_BT_K_OUTER) ||
         (b_layout != GEMM_BT_K_INNER && b_layout != GEMM_BT_K_OUTER)) {
@@ -374,10 +374,11 @@ static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b
         return GEMM_BT_ERR_INVALID_VALUE;
     }
     if (a_layout == GEMM_BT_K_INNER && b_layout == GEMM_BT_K_INNER)
-        return plan_impl(1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, p);
+        return plan_impl(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, p);
     std::memset(p, 0, sizeof(*p));
-    if (M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
-    p->batch = 1;
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
+    if (batch > kMaxBatch) return GEMM_BT_ERR_UNSUPPORTED;
+    p->batch = batch;
     if (in_dtype != GEMM_BT_BF16 && in_dtype != GEMM_BT_F16) return GEMM_BT_ERR_UNSUPPORTED;
     if (out_dtype != GEMM_BT_F32 && out_dtype != GEMM_BT_BF16 && out_dtype != GEMM_BT_F16)
         return GEMM_BT_ERR_UNSUPPORTED;
@@ -390,7 +391,7 @@ static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b
     };
     if (!fits(a_layout, M) || !fits(b_layout, N) || 128 * N * (int64_t)osz >= 0x7FFFFFFFLL)
         return GEMM_BT_ERR_UNSUPPORTED;
-    if (M == 0 || N == 0) {
+    if (batch == 0 || M == 0 || N == 0) {
         p->kernel = KIND_NONE;
         return GEMM_BT_OK;
     }
@@ -406,8 +407,8 @@ static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b
         return align % 16 == 0 && (layout == GEMM_BT_K_OUTER ? ext % 8 == 0 : K % 8 == 0);
     };
     if (!rows_ok(a_layout, M, a_align) || !rows_ok(b_layout, N, b_align)) return GEMM_BT_ERR_UNSUPPORTED;
-    // 256 x 256 tiles (8 waves) when that fills every CU, else 128 x 128 (4 waves)
-    const bool big = ((M + 255) / 256) * ((N + 255) / 256) >= num_cu;
+    // 256 x 256 tiles (8 waves) when the tiles of all items fill every CU, else 128 x 128 (4 waves)
+    const bool big = ((M + 255) / 256) * ((N + 255) / 256) * batch >= num_cu;
     const int bt = big ? 256 : 128;
     p->kernel = KIND_TRANS;
     p->variant = (a_layout == GEMM_BT_K_OUTER ? 1 : 0) + (b_layout == GEMM_BT_K_OUTER ? 2 : 0) - 1 + (big ? 3 : 0);
@@ -422,7 +423,7 @@ static int plan_layout_impl(int64_t M, int64_t N, int64_t K, int a_layout, int b
     p->tiles_m = (M + bt - 1) / bt;
     p->tiles_n = (N + bt - 1) / bt;
     p->grid = p->tiles_m * p->tiles_n;
-    if (p->grid > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
+    if (p->grid * batch > 0x7FFFFFFF) return GEMM_BT_ERR_UNSUPPORTED;
     (void)c_align;
     return GEMM_BT_OK;
 }
@@ -554,19 +555,37 @@ int gemm_bt_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int in_
 
 int gemm_bt_plan_layout(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
                         int a_align, int b_align, int c_align, gemm_bt_plan_t* plan) {
-    return plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
+    return plan_layout_impl(1, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
 }
 
 int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int a_layout, int b_layout,
                    int in_dtype, int out_dtype, void* stream) {
+    return gemm_bt_batched_layout(A, B, C, 1, M, N, K, 0, 0, 0, a_layout, b_layout, in_dtype, out_dtype, stream);
+}
+
+int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch, int64_t M, int64_t N, int64_t K,
+                           int64_t stride_a, int64_t stride_b, int64_t stride_c, int a_layout, int b_layout,
+                           int in_dtype, int out_dtype, void* stream) {
     if (a_layout == GEMM_BT_K_INNER && b_layout == GEMM_BT_K_INNER)
-        return gemm_bt(A, B, C, M, N, K, in_dtype, out_dtype, stream);
+        return gemm_bt_batched(A, B, C, batch, M, N, K, stride_a, stride_b, stride_c, in_dtype, out_dtype, stream);
     gemm_bt_plan_t p;
-    const int a_al = align_of(A), b_al = align_of(B), c_al = align_of(C);
-    int st = plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
+    if (stride_a < 0 || stride_b < 0 || stride_c < 0) return GEMM_BT_ERR_INVALID_VALUE;
+    const bool multi = batch > 1;
+    const int osz = out_size(out_dtype);
+    // every item's pointers: the base alignment, lowered by that of the byte stride
+    auto item_align = [&](const void* base, int64_t stride, int esz) {
+        const int a = align_of(base);
+        if (!multi || stride == 0) return a;
+        const int s = align_of((const void*)(uintptr_t)((uint64_t)stride * (uint64_t)esz));
+        return a < s ? a : s;
+    };
+    const int a_al = item_align(A, stride_a, 2), b_al = item_align(B, stride_b, 2), c_al = item_align(C, stride_c, osz);
+    int st = plan_layout_impl(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
     if (st != GEMM_BT_OK) return st;
     if (p.kernel == KIND_NONE) return GEMM_BT_OK;
-    const int osz = out_size(out_dtype);
+    if (multi && stride_c < M * N) return GEMM_BT_ERR_INVALID_VALUE;
+    if (stride_a > (INT64_MAX >> 2) || stride_b > (INT64_MAX >> 2) || stride_c > (INT64_MAX >> 3))
+        return GEMM_BT_ERR_INVALID_VALUE;
     if (!C) return GEMM_BT_ERR_INVALID_VALUE;
     if (p.kernel != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
     if ((uintptr_t)A % 2 || (uintptr_t)B % 2 || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
@@ -574,17 +593,19 @@ int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, 
     st = check_device(&num_cu);
     if (st != GEMM_BT_OK) return st;
     if (num_cu != 256) {
-        st = plan_layout_impl(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, num_cu, &p);
+        st = plan_layout_impl(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, num_cu, &p);
         if (st != GEMM_BT_OK) return st;
     }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    long long sa = multi ? (long long)stride_a * 2 : 0, sb = multi ? (long long)stride_b * 2 : 0,
+              sc = multi ? (long long)stride_c * osz : 0;
     if (p.kernel == KIND_FILL) {
         u16* c16 = (u16*)C;
         size_t n16 = (size_t)M * (size_t)N * osz / 2;
-        long long sc = 0;
         void* args[] = {&c16, &n16, &sc};
-        e = hipLaunchKernel((const void*)&zero_fill_kernel, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+        e = hipLaunchKernel((const void*)&zero_fill_kernel, dim3((unsigned)p.grid, (unsigned)batch), dim3(p.threads),
+                            args, 0, s);
     } else {
         const u16* a = (const u16*)A;
         const u16* b = (const u16*)B;
@@ -592,15 +613,24 @@ int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, 
         if (vec_store && (N * osz) % 16 == 0 && c_al >= 16) vec_store = 2;
         const void* fn = in_dtype == GEMM_BT_BF16 ? trans_fn_out<GEMM_BT_BF16>(out_dtype, p.variant)
                                                   : trans_fn_out<GEMM_BT_F16>(out_dtype, p.variant);
-        int Mi = (int)M, Ni = (int)N, Ki = (int)K, tm = (int)p.tiles_m, tn = (int)p.tiles_n, gm = p.group_m;
-        void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store};
-        e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, s);
+        // one grid row: the items stacked along the tile rows
+        int Mi = (int)M, Ni = (int)N, Ki = (int)K, tm = (int)(p.tiles_m * batch), tn = (int)p.tiles_n, gm = p.group_m,
+            itm = (int)p.tiles_m;
+        void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store, &itm, &sa, &sb, &sc};
+        e = hipLaunchKernel(fn, dim3((unsigned)(p.grid * batch)), dim3(p.threads), args, 0, s);
     }
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return GEMM_BT_ERR_LAUNCH;
     }
     return GEMM_BT_OK;
+}
+
+int gemm_bt_plan_batched_layout(int64_t batch, int64_t M, int64_t N, int64_t K, int a_layout, int b_layout,
+                                int in_dtype, int out_dtype, int a_align, int b_align, int c_align,
+                                gemm_bt_plan_t* plan) {
+    return plan_layout_impl(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align, 256,
+                            plan);
 }
 
 int gemm_bt_tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m, int64_t* tm, int64_t* tn) {

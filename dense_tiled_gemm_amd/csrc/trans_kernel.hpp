@@ -62,7 +62,8 @@ struct OpGeom {
 template <int IN, int OUT, bool TA, bool TB, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void trans_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                              void* __restrict__ C, int M, int N, int K, int tiles_m,
-                                                             int tiles_n, int group_m, int vec_store) {
+                                                             int tiles_n, int group_m, int vec_store, int item_tiles_m,
+                                                             long long sa, long long sb, long long sc) {
     constexpr int T = 64 * WM * WN, BK = 64;
     constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
     typedef OpGeom<BM, TA, T> GA;
@@ -77,6 +78,12 @@ __global__ __launch_bounds__(64 * WM * WN) void trans_kernel(const u16* __restri
 
     int64_t tm64, tn64;
     tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
+    if (tiles_m != item_tiles_m) {
+        // batch items are stacked along the tile rows, as in dma_kernel
+        const int z = (int)tm64 / item_tiles_m;
+        tm64 -= (int64_t)z * item_tiles_m;
+        batch_item(z, A, B, C, sa, sb, sc);
+    }
     const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
 
     // Global view of one operand as four buffer-resource words: rows past the

@@ -131,6 +131,19 @@ int gemm_bt_batched(const void* A, const void* B, void* C, int64_t batch, int64_
 int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int a_layout,
                    int b_layout, int in_dtype, int out_dtype, void* stream);
 
+/*
+ * Batched products with operand layouts: gemm_bt_batched's items (item z at
+ * A + z*stride_a, B + z*stride_b, C + z*stride_c elements; a stride of 0
+ * shares an operand; stride_c >= M*N when batch > 1) with each operand stored
+ * as gemm_bt_layout's a_layout / b_layout say.  An item of a K-outer A is a
+ * K x M matrix, of a K-outer B a K x N one.  The rules of both calls apply, to
+ * every item's pointers; gemm_bt_layout is the batch == 1 case and
+ * gemm_bt_batched the (K_INNER, K_INNER) one.
+ */
+int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch, int64_t M, int64_t N, int64_t K,
+                           int64_t stride_a, int64_t stride_b, int64_t stride_c, int a_layout, int b_layout,
+                           int in_dtype, int out_dtype, void* stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* gemm_bt_status_string(int status);
 
@@ -169,6 +182,11 @@ int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, i
    K-outer, 2: both). */
 int gemm_bt_plan_layout(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
                         int a_align, int b_align, int c_align, gemm_bt_plan_t* plan);
+
+/* The plan of gemm_bt_batched_layout. */
+int gemm_bt_plan_batched_layout(int64_t batch, int64_t M, int64_t N, int64_t K, int a_layout, int b_layout,
+                                int in_dtype, int out_dtype, int a_align, int b_align, int c_align,
+                                gemm_bt_plan_t* plan);
 
 /* The plan of gemm_bt_batched: the tile tier counts the workgroups of all
    items; the alignments are those of every item's pointers. */

@@ -119,6 +119,17 @@ def test_layout_plan_and_validation():
     with pytest.raises(gb.GemmBtError):
         gb.gemm_bt_plan_layout(64, 64, 64, KO, KI, gb.BF16, gb.F32, a_align=8)
     assert gb.gemm_bt_layout(16, 16, 16, 4, 4, 4, 3, 0, gb.BF16, gb.F32, None) == gb.ERR_INVALID_VALUE
+    # batched layouts: the tier counts the tiles of all items; strides as for gemm_bt_batched
+    p = gb.gemm_bt_plan_batched_layout(64, 512, 512, 512, KI, KO, gb.BF16, gb.BF16)
+    assert (p.kernel, p.bm, p.grid, p.batch) == (5, 256, 4, 64)
+    p = gb.gemm_bt_plan_batched_layout(8, 512, 512, 512, KO, KO, gb.BF16, gb.BF16)
+    assert (p.kernel, p.bm, p.grid, p.batch) == (5, 128, 16, 8)
+    assert gb.gemm_bt_plan_batched_layout(3, 64, 64, 64, KI, KI, gb.BF16, gb.F32).kernel == 4
+    assert gb.gemm_bt_plan_batched_layout(0, 64, 64, 64, KO, KI, gb.BF16, gb.F32).kernel == 0
+    with pytest.raises(gb.GemmBtError):
+        gb.gemm_bt_plan_batched_layout(2, 64, 64, 64, KO, KI, gb.BF16, gb.F32, a_align=4)  # item stride breaks 16 B
+    assert gb.gemm_bt_batched_layout(16, 16, 16, 2, 8, 8, 8, 64, 64, 63, KO, KO, gb.BF16, gb.F32, None) == \
+        gb.ERR_INVALID_VALUE  # items of C overlap
 
 
 def test_no_device_status_without_gpu():

@@ -673,3 +673,30 @@ def test_largest_k(gpu, M, N, K, ind, outd):
     with pytest.raises(gpu.GemmBtError) as ei:
         gpu.gemm_bt_plan(M, N, too_big, code, gpu.F32)
     assert ei.value.status == gpu.ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- batched products with operands stored K-outer
+
+BATCHED_LAYOUTS = [  # (Z, M, N, K, A K-outer, B K-outer, shared operand)
+    (3, 136, 264, 72, 1, 0, None), (4, 200, 104, 301, 1, 1, "b"), (64, 512, 512, 512, 0, 1, None),
+    (2, 520, 1032, 264, 1, 1, "a"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BATCHED_LAYOUTS)))
+def test_batched_layouts(gpu, case):
+    Z, M, N, K, la, lb, share = BATCHED_LAYOUTS[case]
+    seed = 1500 + case
+    say("batched layout", Z, M, N, K, la, lb, "share", share, "seed", seed)
+    a3, b3 = synth.make_batched(Z, M, N, K, "bf16", "normal", seed)
+    a_bits = a3[0] if share == "a" else a3
+    b_bits = b3[0] if share == "b" else b3
+    tr = lambda x, lay: np.ascontiguousarray(np.swapaxes(x, -1, -2)) if lay else x
+    A = to_dev(tr(a_bits, la), "bf16")
+    B = to_dev(tr(b_bits, lb), "bf16")
+    c = gpu.mm_layout(A, B, la, lb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cref, nA, nB = oracle.gemm_bt_batched_ref(a_bits, b_bits, "bf16")
+    for z in range(Z):
+        rep = tolerance.check(f64(c[z].cpu()), cref[z], np.outer(nA[z], nB[z]), "f32")
+        assert rep.ok, (z, rep)
