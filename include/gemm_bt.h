@@ -179,7 +179,7 @@ int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, i
                  int b_align, int c_align, gemm_bt_plan_t* plan);
 
 /* The plan of gemm_bt_layout (for kernel 5 the variant is 0: A K-outer, 1: B
-   K-outer, 2: both). */
+   K-outer, 2: both, on 128 x 128 tiles; 3, 4, 5 the same on 256 x 256 tiles). */
 int gemm_bt_plan_layout(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
                         int a_align, int b_align, int c_align, gemm_bt_plan_t* plan);
 
