@@ -4,7 +4,7 @@
 // The MMA contract of "Writing Mosaic GPU kernels with Pallas", section "MMA
 // (TensorCore)", lets 16-bit operands arrive transposed (an A reference of
 // shape (K, M), likewise for B).  Here a K-outer operand is copied to LDS as
-// it lies in memory, one 256-byte row per k, and transposed on the way out of
+// it lies in memory, one row of its tile's columns per k, and transposed on the way out of
 // LDS by ds_read_b64_tr_b16: inside each group of 16 lanes, lane i's element
 // e is the i-th of the 16 values that lanes 4e .. 4e+3 address (measured on
 // the device).  Lanes 4e+a of group g pointing at T[8g + 4h + e][x + 4a]
@@ -51,7 +51,7 @@ __device__ inline int kouter_swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) 
 // Geometry of one operand tile of BX rows/columns by 64 k in LDS.
 //   K-inner: BX rows of 128 bytes (8 chunks), chunk c of row r at c ^ ((r >> 1) & 7);
 //   K-outer: 64 rows of 2*BX bytes (BX/8 chunks), chunk c of row r at c ^ kouter_swz(r).
-template <int BX, bool KOUTER, int T>
+template <int BX, bool KOUTER>
 struct OpGeom {
     static constexpr int ROWB = KOUTER ? 2 * BX : 128;  // bytes per LDS row
     static constexpr int CR = ROWB / 16;                 // chunks per row
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(64 * WM * WN) void trans_kernel(const u16* __restri
                                                              long long sa, long long sb, long long sc) {
     constexpr int T = 64 * WM * WN, BK = 64;
     constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
-    typedef OpGeom<BM, TA, T> GA;
-    typedef OpGeom<BN, TB, T> GB;
+    typedef OpGeom<BM, TA> GA;
+    typedef OpGeom<BN, TB> GB;
     constexpr int STAGE = GA::BYTES + GB::BYTES;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
 
