@@ -524,6 +524,29 @@ static int align_of(const void* p) {
     return 1;
 }
 
+// Alignment of every item's pointer in a batched call: the base pointer's,
+// lowered by that of the byte stride between items.
+static int item_align(const void* base, int64_t batch, int64_t stride, int esz) {
+    const int a = align_of(base);
+    if (batch <= 1 || stride == 0) return a;
+    const int s = align_of((const void*)(uintptr_t)((uint64_t)stride * (uint64_t)esz));
+    return a < s ? a : s;
+}
+
+// Checks shared by the batched entry points once the plan is known: items of
+// C must not overlap, byte strides must fit 63 bits, pointers must be present
+// and hold whole elements.
+static int check_items(const void* A, const void* B, const void* C, int kind, int64_t batch, int64_t M, int64_t N,
+                       int64_t stride_a, int64_t stride_b, int64_t stride_c, int isz, int osz) {
+    if (batch > 1 && stride_c < M * N) return GEMM_BT_ERR_INVALID_VALUE;
+    if (stride_a > (INT64_MAX >> 2) || stride_b > (INT64_MAX >> 2) || stride_c > (INT64_MAX >> 3))
+        return GEMM_BT_ERR_INVALID_VALUE;
+    if (!C) return GEMM_BT_ERR_INVALID_VALUE;
+    if (kind != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
+    if ((uintptr_t)A % isz || (uintptr_t)B % isz || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
+    return GEMM_BT_OK;
+}
+
 }  // namespace gbt
 
 using namespace gbt;
@@ -572,23 +595,13 @@ int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch,
     if (stride_a < 0 || stride_b < 0 || stride_c < 0) return GEMM_BT_ERR_INVALID_VALUE;
     const bool multi = batch > 1;
     const int osz = out_size(out_dtype);
-    // every item's pointers: the base alignment, lowered by that of the byte stride
-    auto item_align = [&](const void* base, int64_t stride, int esz) {
-        const int a = align_of(base);
-        if (!multi || stride == 0) return a;
-        const int s = align_of((const void*)(uintptr_t)((uint64_t)stride * (uint64_t)esz));
-        return a < s ? a : s;
-    };
-    const int a_al = item_align(A, stride_a, 2), b_al = item_align(B, stride_b, 2), c_al = item_align(C, stride_c, osz);
+    const int a_al = item_align(A, batch, stride_a, 2), b_al = item_align(B, batch, stride_b, 2),
+              c_al = item_align(C, batch, stride_c, osz);
     int st = plan_layout_impl(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
     if (st != GEMM_BT_OK) return st;
     if (p.kernel == KIND_NONE) return GEMM_BT_OK;
-    if (multi && stride_c < M * N) return GEMM_BT_ERR_INVALID_VALUE;
-    if (stride_a > (INT64_MAX >> 2) || stride_b > (INT64_MAX >> 2) || stride_c > (INT64_MAX >> 3))
-        return GEMM_BT_ERR_INVALID_VALUE;
-    if (!C) return GEMM_BT_ERR_INVALID_VALUE;
-    if (p.kernel != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
-    if ((uintptr_t)A % 2 || (uintptr_t)B % 2 || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
+    st = check_items(A, B, C, p.kernel, batch, M, N, stride_a, stride_b, stride_c, 2, osz);
+    if (st != GEMM_BT_OK) return st;
     int num_cu = 256;
     st = check_device(&num_cu);
     if (st != GEMM_BT_OK) return st;
@@ -652,27 +665,15 @@ int gemm_bt_batched(const void* A, const void* B, void* C, int64_t batch, int64_
     const bool multi = batch > 1;
     const int isz = is_8bit(in_dtype) ? 1 : 2;
     const int osz = out_size(out_dtype);
-    // every item's pointers: the base alignment, lowered by that of the byte stride
-    auto item_align = [&](const void* base, int64_t stride, int esz) {
-        const int a = align_of(base);
-        if (!multi || stride == 0) return a;
-        const int s = align_of((const void*)(uintptr_t)((uint64_t)stride * (uint64_t)esz));
-        return a < s ? a : s;
-    };
-    const int a_al = item_align(A, stride_a, isz), b_al = item_align(B, stride_b, isz),
-              c_al = item_align(C, stride_c, osz);
+    const int a_al = item_align(A, batch, stride_a, isz), b_al = item_align(B, batch, stride_b, isz),
+              c_al = item_align(C, batch, stride_c, osz);
     // Plan against the default CU count first: it validates the arguments
     // without touching the device.
     int st = plan_impl(batch, M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
     if (st != GEMM_BT_OK) return st;
     if (p.kernel == KIND_NONE) return GEMM_BT_OK;
-    // items of C must not overlap; byte strides must fit 63 bits
-    if (multi && stride_c < M * N) return GEMM_BT_ERR_INVALID_VALUE;
-    if (stride_a > (INT64_MAX >> 2) || stride_b > (INT64_MAX >> 2) || stride_c > (INT64_MAX >> 3))
-        return GEMM_BT_ERR_INVALID_VALUE;
-    if (!C) return GEMM_BT_ERR_INVALID_VALUE;
-    if (p.kernel != KIND_FILL && (!A || !B)) return GEMM_BT_ERR_INVALID_VALUE;
-    if ((uintptr_t)A % isz || (uintptr_t)B % isz || (uintptr_t)C % osz) return GEMM_BT_ERR_INVALID_VALUE;
+    st = check_items(A, B, C, p.kernel, batch, M, N, stride_a, stride_b, stride_c, isz, osz);
+    if (st != GEMM_BT_OK) return st;
 
     int num_cu = 256;
     st = check_device(&num_cu);
