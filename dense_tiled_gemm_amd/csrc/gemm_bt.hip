@@ -266,7 +266,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         if (K % 16 != 0 || a_align % 16 != 0 || b_align % 16 != 0) return GEMM_BT_ERR_UNSUPPORTED;
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
-        int use = kFp8Variants + (tiles_l >= num_cu ? 0 : (tiles_m128 * 4 >= num_cu ? 1 : 2));
+        int use = kFp8Variants + (tiles_l >= num_cu ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2));
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];
@@ -329,9 +329,10 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
     if (p->vec >= 2 && !forced_staged()) {
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
-        // 256x256 when that fills every CU; else 128x128 unless it leaves
-        // three quarters of the CUs idle, then 64x64
-        int use = big ? 0 : (tiles_m128 * 4 >= num_cu ? 1 : 2);
+        // 256x256 when that fills every CU; else 128x128 when its tiles
+        // fill more than half the CUs, else 64x64 (more workgroups for what
+        // is then a thin or small, memory-bound product)
+        int use = big ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2);
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];

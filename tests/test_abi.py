@@ -73,8 +73,10 @@ def test_batched_plan():
     # the tile tier counts all items: 64 items of 512^2 fill 256 CUs with 256x256 tiles
     p = gb.gemm_bt_plan_batched(64, 512, 512, 512, gb.BF16, gb.BF16)
     assert (p.kernel, p.bm, p.grid, p.batch) == (4, 256, 4, 64)
-    p = gb.gemm_bt_plan_batched(8, 512, 512, 512, gb.BF16, gb.BF16)   # 8 x 16 tiles of 128
-    assert (p.bm, p.grid, p.batch) == (128, 16, 8)
+    p = gb.gemm_bt_plan_batched(8, 512, 512, 512, gb.BF16, gb.BF16)   # 8 x 16 tiles of 128: half the CUs
+    assert (p.bm, p.grid, p.batch) == (64, 64, 8)
+    p = gb.gemm_bt_plan_batched(12, 512, 512, 512, gb.BF16, gb.BF16)  # 12 x 16 tiles of 128
+    assert (p.bm, p.grid, p.batch) == (128, 16, 12)
     p = gb.gemm_bt_plan_batched(1, 512, 512, 512, gb.BF16, gb.BF16)
     assert (p.bm, p.batch) == (64, 1) and p.as_dict() == gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.BF16).as_dict()
     p = gb.gemm_bt_plan_batched(5, 16, 8192, 8192, gb.BF16, gb.BF16)  # streaming kernel per item
@@ -146,7 +148,7 @@ def test_plan_choices():
     assert (p.kernel, p.bm, p.bn, p.vec, p.grid) == (4, 256, 256, 8, 256)
     # five-slot ring: one A or B tile (256 rows x 64 K) per slot, all of LDS
     assert (p.stages, p.lds_bytes) == (5, 5 * p.bm * p.bk * 2) and p.lds_bytes == 160 * 1024
-    p = gb.gemm_bt_plan(1024, 1024, 4096, gb.BF16, gb.BF16)  # 128x128 tiles: A+B stages
+    p = gb.gemm_bt_plan(2048, 1536, 4096, gb.BF16, gb.BF16)  # 128x128 tiles (192 > half the CUs): A+B stages
     assert p.bm == 128 and p.lds_bytes == p.stages * (p.bm + p.bn) * p.bk * 2 <= 160 * 1024
     p = gb.gemm_bt_plan(1024, 4096, 4096, gb.F16, gb.F16)
     assert (p.kernel, p.bm, p.bn, p.grid) == (4, 128, 128, 256)
@@ -184,7 +186,11 @@ def test_plan_choices():
         gb.gemm_bt_plan(64, 64, 48, gb.INT8, gb.INT32, a_align=8)
     p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)  # 16 tiles of 128: 64x64 tiles fill more CUs
     assert (p.kernel, p.bm, p.grid) == (4, 64, 64)
-    assert gb.gemm_bt_plan(1024, 1024, 200, gb.BF16, gb.F32).bm == 128
+    assert gb.gemm_bt_plan(2048, 1536, 200, gb.BF16, gb.F32).bm == 128
+    # at most half the CUs busy with 128x128 tiles: 64x64 (thin products)
+    assert gb.gemm_bt_plan(1024, 2048, 4096, gb.BF16, gb.BF16).bm == 64   # 128 tiles of 128
+    assert gb.gemm_bt_plan(64, 8192, 8192, gb.BF16, gb.BF16).bm == 64
+    assert gb.gemm_bt_plan(1024, 1024, 200, gb.BF16, gb.F32).bm == 64
     assert gb.gemm_bt_plan(7, 9, 0, gb.BF16, gb.F32).kernel == 1   # K == 0: zero fill
     assert gb.gemm_bt_plan(0, 9, 5, gb.BF16, gb.F32).kernel == 0   # empty
     # alignment decides the load width

@@ -90,7 +90,7 @@ SHAPES = [
     # 4-byte rows whose K is not a whole number of 8-element chunks (K tail), and K < 8
     (130, 264, 74), (96, 200, 36), (300, 520, 1006), (64, 64, 6), (257, 300, 2050),
     # shapes that select the 128x128 and 256x256 tiles (the ones above take 64x64)
-    (1024, 1024, 200), (1030, 1030, 202), (4096, 4096, 72),
+    (1024, 1024, 200), (1030, 1030, 202), (2048, 1536, 200), (1540, 2050, 136), (4096, 4096, 72),
     # 256x256 tiles (five-slot ring): one K step, a K tail, ragged edges with three steps, a wrapped ring
     (4096, 4096, 8), (4096, 4096, 130), (4100, 4100, 136), (4096, 4096, 200),
 ]
