@@ -103,13 +103,14 @@ static DmaVariant dma_variant(const char* name) {
     return v;
 }
 
-// Index 0 is the default for large grids, 1 for smaller ones, 2 for the
-// smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
+// Index 0 is the default for large grids, 1 for smaller ones, 2 and 6 for
+// the smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
 // (128-element K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32
 // MFMAs over 64-element substeps);
 // the rest exist for tuning (GEMM_BT_FORCE_TILE=<name>) and are built for the
 // bf16->bf16 and f16->f16 combinations only.
 constexpr int kFp8Variants = 3;
+constexpr int kTiny16 = 6;  // 32 x 64 tiles (16-bit inputs), when even 64 x 64 tiles leave half the CUs idle
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
@@ -118,6 +119,7 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<256, 256, 128, 2, 2, 4, 2, 6, 0, 32, true, 0, 2, true>("L128F8R5s"),
         dma_variant<128, 128, 128, 4, 2, 2, 2, 8, 0, 32, true, 0, 0, true>("M128F8s4i"),
         dma_variant<64, 64, 128, 4, 2, 2, 2, 4, 0, 32, true, 0, 0, true>("Q128F8"),
+        dma_variant<32, 64, 64, 4, 2, 2, 2, 2, 0, 16, true>("T32x64"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16>("L64E16i"),
@@ -331,8 +333,11 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         const DmaVariant* vs = dma_variants(&n);
         // 256x256 when that fills every CU; else 128x128 when its tiles
         // fill more than half the CUs, else 64x64 (more workgroups for what
-        // is then a thin or small, memory-bound product)
+        // is then a thin or small, memory-bound product), and 32x64 when even
+        // 64x64 tiles fill at most half the CUs
         int use = big ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2);
+        const int64_t tiles_q64 = ((M + 63) / 64) * ((N + 63) / 64) * batch;
+        if (use == 2 && tiles_q64 * 2 <= num_cu) use = kTiny16;
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];

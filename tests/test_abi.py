@@ -78,7 +78,7 @@ def test_batched_plan():
     p = gb.gemm_bt_plan_batched(12, 512, 512, 512, gb.BF16, gb.BF16)  # 12 x 16 tiles of 128
     assert (p.bm, p.grid, p.batch) == (128, 16, 12)
     p = gb.gemm_bt_plan_batched(1, 512, 512, 512, gb.BF16, gb.BF16)
-    assert (p.bm, p.batch) == (64, 1) and p.as_dict() == gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.BF16).as_dict()
+    assert (p.bm, p.batch) == (32, 1) and p.as_dict() == gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.BF16).as_dict()
     p = gb.gemm_bt_plan_batched(5, 16, 8192, 8192, gb.BF16, gb.BF16)  # streaming kernel per item
     assert (p.kernel, p.grid, p.batch) == (3, 1024, 5)
     assert gb.gemm_bt_plan_batched(0, 64, 64, 64, gb.BF16, gb.BF16).kernel == 0
@@ -184,12 +184,16 @@ def test_plan_choices():
             gb.gemm_bt_plan(*args)
     with pytest.raises(gb.GemmBtError):
         gb.gemm_bt_plan(64, 64, 48, gb.INT8, gb.INT32, a_align=8)
-    p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)  # 16 tiles of 128: 64x64 tiles fill more CUs
-    assert (p.kernel, p.bm, p.grid) == (4, 64, 64)
+    p = gb.gemm_bt_plan(512, 512, 512, gb.BF16, gb.F32)  # 16 tiles of 128, 64 of 64: 32x64 tiles fill more CUs
+    assert (p.kernel, p.bm, p.bn, p.grid) == (4, 32, 64, 128)
+    p = gb.gemm_bt_plan(1024, 1024, 512, gb.BF16, gb.F32)  # 256 tiles of 64x64: all CUs
+    assert (p.kernel, p.bm, p.bn, p.grid) == (4, 64, 64, 256)
+    assert gb.gemm_bt_plan(512, 512, 512, gb.FP8_E4M3, gb.F32).bm == 64  # no 32x64 tier for 8-bit inputs
     assert gb.gemm_bt_plan(2048, 1536, 200, gb.BF16, gb.F32).bm == 128
     # at most half the CUs busy with 128x128 tiles: 64x64 (thin products)
     assert gb.gemm_bt_plan(1024, 2048, 4096, gb.BF16, gb.BF16).bm == 64   # 128 tiles of 128
-    assert gb.gemm_bt_plan(64, 8192, 8192, gb.BF16, gb.BF16).bm == 64
+    assert gb.gemm_bt_plan(128, 8192, 8192, gb.BF16, gb.BF16).bm == 64
+    assert (gb.gemm_bt_plan(64, 8192, 8192, gb.BF16, gb.BF16).bm, gb.gemm_bt_plan(64, 8192, 8192, gb.BF16, gb.BF16).bn) == (32, 64)
     assert gb.gemm_bt_plan(1024, 1024, 200, gb.BF16, gb.F32).bm == 64
     assert gb.gemm_bt_plan(7, 9, 0, gb.BF16, gb.F32).kernel == 1   # K == 0: zero fill
     assert gb.gemm_bt_plan(0, 9, 5, gb.BF16, gb.F32).kernel == 0   # empty

@@ -89,8 +89,9 @@ SHAPES = [
     (130, 264, 72), (520, 1032, 264), (256, 256, 4096),
     # 4-byte rows whose K is not a whole number of 8-element chunks (K tail), and K < 8
     (130, 264, 74), (96, 200, 36), (300, 520, 1006), (64, 64, 6), (257, 300, 2050),
-    # shapes that select the 128x128 and 256x256 tiles (the ones above take 64x64)
+    # shapes that select the 64x64, 128x128 and 256x256 tiles (most above take 32x64)
     (1024, 1024, 200), (1030, 1030, 202), (2048, 1536, 200), (1540, 2050, 136), (4096, 4096, 72),
+    (64, 4104, 200), (100, 2050, 134),
     # 256x256 tiles (five-slot ring): one K step, a K tail, ragged edges with three steps, a wrapped ring
     (4096, 4096, 8), (4096, 4096, 130), (4100, 4100, 136), (4096, 4096, 200),
 ]
