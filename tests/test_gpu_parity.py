@@ -701,3 +701,47 @@ def test_batched_layouts(gpu, case):
     for z in range(Z):
         rep = tolerance.check(f64(c[z].cpu()), cref[z], np.outer(nA[z], nB[z]), "f32")
         assert rep.ok, (z, rep)
+
+
+# ---------------------------------------------------------------- non-finite inputs and output overflow
+
+@pytest.mark.parametrize("M,N,K", [(100, 130, 72), (16, 600, 256)])  # tiled and streaming kernels
+def test_non_finite_inputs(gpu, M, N, K):
+    """Inf and NaN inputs give the IEEE classes the fp64 oracle gives, entry for entry: ±Inf where one infinite
+    product dominates, NaN for Inf·0, NaN inputs, or +Inf and -Inf in one sum; finite entries stay within the rule."""
+    say("non-finite", M, N, K)
+    a = np.random.default_rng(1700).standard_normal((M, K))
+    b = np.random.default_rng(1701).standard_normal((N, K))
+    a[3, 5] = np.inf            # row 3: ±Inf against columns with b[:, 5] != 0
+    b[:, 5][::7] = 0.0          # ... and NaN where b[j, 5] == 0 (Inf * 0)
+    a[7, 9] = np.nan            # row 7: NaN everywhere
+    b[11, 20] = -np.inf         # column 11: ±Inf ...
+    a[2, 21] = np.inf           # ... and +Inf + -Inf = NaN at (2, 11) with b[11, 21] < 0
+    b[11, 21] = -1.0
+    a[2, 20] = 1.0
+    a_bits, b_bits = synth.round_bits(a, "bf16"), synth.round_bits(b, "bf16")
+    for out in ("f32", "bf16"):
+        c = run_gpu(gpu, a_bits, b_bits, "bf16", out)
+        cref, nA, nB = oracle.gemm_bt_ref(a_bits, b_bits, "bf16")
+        assert np.isnan(cref).any() and np.isinf(cref).any() and np.isfinite(cref).any()
+        got = f64(c)
+        assert np.array_equal(np.isnan(got), np.isnan(cref)), out
+        assert np.array_equal(np.isinf(got), np.isinf(cref)), out
+        inf = np.isinf(cref)
+        assert np.array_equal(np.sign(got[inf]), np.sign(cref[inf])), out
+        fin = np.isfinite(cref) & np.isfinite(nA)[:, None] & np.isfinite(nB)[None, :]
+        rep = tolerance.check(got[fin], cref[fin], np.outer(nA, nB)[fin], out)
+        assert rep.ok, (out, rep)
+
+
+def test_f16_overflow_boundary(gpu):
+    """All-4 operands: every entry is 16 K exactly.  K = 4094 gives 65504, the largest finite f16; K = 4095 gives
+    65520, the midpoint to 65536, which rounds to nearest even into +Inf; bit-exact against the oracle's rounding."""
+    for K in (4094, 4095):
+        say("f16 overflow", K)
+        a = synth.round_bits(np.full((40, K), 4.0), "f16")
+        b = synth.round_bits(np.full((72, K), 4.0), "f16")
+        c = run_gpu(gpu, a, b, "f16", "f16")
+        want = 65504.0 if K == 4094 else np.inf
+        assert (f64(c) == want).all(), (K, f64(c)[0, 0])
+        check_bits_full(c, a, b, "f16", "f16", ("overflow", K))
