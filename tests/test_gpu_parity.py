@@ -745,3 +745,31 @@ def test_f16_overflow_boundary(gpu):
         want = 65504.0 if K == 4094 else np.inf
         assert (f64(c) == want).all(), (K, f64(c)[0, 0])
         check_bits_full(c, a, b, "f16", "f16", ("overflow", K))
+
+
+@pytest.mark.parametrize("fmt", ["e5m2", "e4m3"])
+def test_non_finite_8bit_inputs(gpu, fmt):
+    """8-bit float codes for Inf (E5M2 only) and NaN (both formats) give the oracle's IEEE classes entry for entry."""
+    M, N, K = 100, 130, 128
+    say("non-finite 8-bit", fmt, M, N, K)
+    a_bits = synth.round_bits(np.random.default_rng(1710).standard_normal((M, K)), fmt)
+    b_bits = synth.round_bits(np.random.default_rng(1711).standard_normal((N, K)), fmt)
+    one, neg = synth.round_bits(np.array([1.0, -1.0]), fmt)
+    if fmt == "e5m2":
+        a_bits[3, 5] = 0x7C                       # +Inf
+        b_bits[::7, 5] = 0                        # Inf * 0 = NaN in row 3
+        b_bits[11, 20] = 0xFC                     # -Inf
+        a_bits[2, 21], b_bits[11, 21], a_bits[2, 20] = 0x7C, neg, one  # +Inf + -Inf = NaN at (2, 11)
+        a_bits[7, 9] = 0x7F                       # NaN
+    else:
+        a_bits[7, 9], b_bits[13, 2] = 0x7F, 0xFF  # NaN codes (S.1111.111); E4M3 has no infinity
+    c = run_gpu(gpu, a_bits, b_bits, fmt, "f32")
+    cref, nA, nB = oracle.gemm_bt_ref(a_bits, b_bits, fmt)
+    got = f64(c)
+    assert np.isnan(cref).any()
+    assert np.array_equal(np.isnan(got), np.isnan(cref)) and np.array_equal(np.isinf(got), np.isinf(cref))
+    inf = np.isinf(cref)
+    assert np.array_equal(np.sign(got[inf]), np.sign(cref[inf]))
+    fin = np.isfinite(cref) & np.isfinite(nA)[:, None] & np.isfinite(nB)[None, :]
+    rep = tolerance.check(got[fin], cref[fin], np.outer(nA, nB)[fin], "f32")
+    assert rep.ok, rep
