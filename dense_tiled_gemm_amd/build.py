@@ -45,5 +45,23 @@ def build(extra=None, out=SO, verbose=False) -> str:
     return out
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi_check.cpp")
+C_CHECK = os.path.join(ROOT, "tests", "c_abi_check")
+
+
+def build_c_check(verbose=False) -> str:
+    """The C++ program that calls the library through include/gemm_bt.h alone (host code, linked to the in-tree
+    libgemm_bt.so by an rpath relative to itself)."""
+    tmp = C_CHECK + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), C_CHECK_SRC, "-L", HERE, "-lgemm_bt",
+           "-Wl,-rpath,$ORIGIN/../dense_tiled_gemm_amd", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, C_CHECK)
+    return C_CHECK
+
+
 if __name__ == "__main__":
     print(build(extra=sys.argv[1:], verbose=True))

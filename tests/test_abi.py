@@ -228,3 +228,18 @@ def test_tile_order_keeps_each_die_on_a_compact_block():
     # the first 8 workgroups (one per die, dispatched together) start 8 different blocks
     firsts = [gb.gemm_bt_tile_coord(pid, 16, 16, 4) for pid in range(8)]
     assert len(set(firsts)) == 8
+
+
+def test_c_program_without_a_device():
+    """The C++ program built against include/gemm_bt.h alone: on a machine without a GPU it must see the
+    library's argument errors and GEMM_BT_ERR_NO_DEVICE."""
+    import subprocess
+    import torch
+
+    exe = os.path.join(ROOT, "tests", "c_abi_check")
+    if not os.path.exists(exe):
+        pytest.skip("tests/c_abi_check is not built (run the build entry point)")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; the GPU tests run this program against the device")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip().endswith("no-device ok"), (r.returncode, r.stdout, r.stderr)

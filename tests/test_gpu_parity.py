@@ -773,3 +773,18 @@ def test_non_finite_8bit_inputs(gpu, fmt):
     fin = np.isfinite(cref) & np.isfinite(nA)[:, None] & np.isfinite(nB)[None, :]
     rep = tolerance.check(got[fin], cref[fin], np.outer(nA, nB)[fin], "f32")
     assert rep.ok, rep
+
+
+
+def test_c_program_through_the_header(gpu):
+    """A C++ program that uses only include/gemm_bt.h and hipMalloc (no Python, no PyTorch) gets the closed-form
+    results: all-ones operands give K in every entry (plain and batched with a shared B), an identity B gives A."""
+    import os
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_check")
+    if not os.path.exists(exe):
+        pytest.skip("tests/c_abi_check is not built (run the build entry point)")
+    say("C program", exe)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("c_abi_check ok"), (r.returncode, r.stdout, r.stderr)
