@@ -215,7 +215,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        log("bench.py runs on exactly one GPU: this build is a single-GPU kernel library "
+        log("bench.py runs on exactly one GPU: the library is a single-GPU kernel library "
             "(no collectives); --gpus %d is not supported." % args.gpus)
         sys.exit(2)
 
