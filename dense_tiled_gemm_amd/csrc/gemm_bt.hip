@@ -421,8 +421,14 @@ static int plan_layout_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int 
         return align % 16 == 0 && (layout == GEMM_BT_K_OUTER ? ext % 8 == 0 : K % 8 == 0);
     };
     if (!rows_ok(a_layout, M, a_align) || !rows_ok(b_layout, N, b_align)) return GEMM_BT_ERR_UNSUPPORTED;
-    // 256 x 256 tiles (8 waves) when the tiles of all items fill every CU, else 128 x 128 (4 waves)
-    const bool big = ((M + 255) / 256) * ((N + 255) / 256) * batch >= num_cu;
+    // 256 x 256 tiles (8 waves) when the tiles of all items make exactly one
+    // wave over the CUs or more than 1.375 waves, else 128 x 128 (4 waves):
+    // just above one wave the nearly empty last wave costs more than the
+    // smaller tiles' lower reuse (B stored K x N, 4096 x 4096 per item x M rows:
+    // 128 x 128 tiles 8-17 % faster at 272-320 such tiles on 256 CUs, even at
+    // 352, 4 % slower at 384)
+    const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256) * batch;
+    const bool big = tiles_l == num_cu || tiles_l * 8 > (int64_t)num_cu * 11;
     const int bt = big ? 256 : 128;
     p->kernel = KIND_TRANS;
     p->variant = (a_layout == GEMM_BT_K_OUTER ? 1 : 0) + (b_layout == GEMM_BT_K_OUTER ? 2 : 0) - 1 + (big ? 3 : 0);

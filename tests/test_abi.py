@@ -156,6 +156,15 @@ def test_tier_band_above_one_wave():
     assert bm(5120, 4096, ind=gb.FP8_E4M3) == 256
 
 
+def test_layout_tier_band():
+    """K-outer operands: 256x256 tiles at exactly one wave of them on 256 CUs and above 1.375 waves."""
+    def bm(M, N, K=4096):
+        return gb.gemm_bt_plan_layout(M, N, K, gb.K_INNER, gb.K_OUTER, gb.BF16, gb.BF16).bm
+    assert bm(4096, 4096) == 256                                       # 256 tiles
+    assert bm(4352, 4096) == bm(4864, 4096) == bm(5632, 4096) == 128   # 272, 304, 352 tiles
+    assert bm(6144, 4096) == bm(8192, 8192) == 256                     # 384, 1024 tiles
+
+
 def test_plan_choices():
     p = gb.gemm_bt_plan(4096, 4096, 4096, gb.BF16, gb.BF16)
     assert (p.kernel, p.bm, p.bn, p.vec, p.grid) == (4, 256, 256, 8, 256)

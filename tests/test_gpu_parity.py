@@ -551,7 +551,9 @@ LAYOUTS = [
     (520, 1032, 264, 1, 1, "bf16", "bf16"), (257, 512, 136, 0, 1, "f16", "f16"), (512, 264, 136, 1, 0, "bf16", "bf16"),
     (4096, 4096, 200, 0, 1, "bf16", "bf16"), (64, 4104, 64, 1, 1, "bf16", "f32"), (8, 8, 5, 1, 1, "bf16", "f32"),
     # the 256 x 256 tier: each layout, ragged edges, a K tail
-    (4104, 4096, 136, 1, 1, "bf16", "bf16"), (4096, 4104, 72, 1, 0, "f16", "f32"), (4096, 4096, 100, 1, 1, "bf16", "f16"),
+    (6152, 4096, 136, 1, 1, "bf16", "bf16"), (4096, 6152, 72, 1, 0, "f16", "f32"), (4096, 4096, 100, 1, 1, "bf16", "f16"),
+    # just above one wave of 256 x 256 tiles (272 of them): 128 x 128 tiles, ragged edges
+    (4104, 4096, 136, 1, 1, "bf16", "bf16"), (4096, 4104, 72, 1, 0, "f16", "f32"),
 ]
 
 
