@@ -229,11 +229,13 @@ static int pick_vec(int64_t K, int a_align, int b_align) {
 constexpr int64_t kMaxBatch = 65535;
 
 // 256x256 tiles for the LDS-DMA kernels: once they fill every CU, except
-// just above one wave of them (up to 1.2 waves), where the last, nearly
-// empty wave costs more than the 128x128 tiles' smaller per-tile reuse
-// (measured at 272-304 such tiles on 256 CUs, 16-bit and 8-bit inputs).
-static bool dma_large_tier(int64_t tiles_l, int num_cu) {
-    return tiles_l == num_cu || tiles_l * 5 > (int64_t)num_cu * 6;
+// just above one wave of them, where the last, nearly empty wave costs more
+// than the 128x128 tiles' smaller per-tile reuse: up to 1.2 waves for 16-bit
+// inputs (128x128 faster at 272-304 such tiles on 256 CUs), up to 17/16 waves
+// for 8-bit ones (faster at 272 tiles, slower from 288 on).
+static bool dma_large_tier(int64_t tiles_l, int num_cu, bool eight_bit) {
+    if (tiles_l == num_cu) return true;
+    return eight_bit ? tiles_l * 16 > (int64_t)num_cu * 17 : tiles_l * 5 > (int64_t)num_cu * 6;
 }
 
 static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
@@ -276,7 +278,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         if (K % 16 != 0 || a_align % 16 != 0 || b_align % 16 != 0) return GEMM_BT_ERR_UNSUPPORTED;
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
-        int use = kFp8Variants + (dma_large_tier(tiles_l, num_cu) ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2));
+        int use = kFp8Variants + (dma_large_tier(tiles_l, num_cu, true) ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2));
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];
@@ -343,7 +345,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         // when its tiles fill more than half the CUs, else 64x64 (more
         // workgroups for what is then a thin or small, memory-bound product),
         // and 32x64 when even 64x64 tiles fill at most half the CUs
-        int use = dma_large_tier(tiles_l, num_cu) ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2);
+        int use = dma_large_tier(tiles_l, num_cu, false) ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2);
         const int64_t tiles_q64 = ((M + 63) / 64) * ((N + 63) / 64) * batch;
         if (use == 2 && tiles_q64 * 2 <= num_cu) use = kTiny16;
         const int f = forced_variant();

@@ -124,12 +124,12 @@ def test_integer_bit_exact_sweep(gpu, in_dtype, out_dtype):
 
 # 8-bit float inputs (K a multiple of 16): one K step of 128, a partial last
 # step, the 64x64, 128x128 and 256x256 tiles (the last with ragged edges and
-# several steps of its five-slot ring; 4100 x 4100, just above one wave of
-# 256x256 tiles, takes 128x128 ones), and M <= 16 (no streaming kernel for
+# several steps of its five-slot ring; 4350 x 4090, 272 256x256 tiles just
+# above one wave, takes 128x128 ones), and M <= 16 (no streaming kernel for
 # 8-bit inputs: the 64x64 tiles take it).
 FP8_SHAPES = [(1, 1, 16), (16, 16, 16), (17, 33, 64), (8, 1000, 64), (64, 64, 128), (130, 260, 160),
               (257, 513, 144), (300, 700, 1024), (1024, 1024, 256), (4096, 4096, 128), (4900, 4100, 272),
-              (4096, 4096, 400), (4100, 4100, 272)]
+              (4096, 4096, 400), (4350, 4090, 272)]
 
 
 @pytest.mark.parametrize("in_dtype", ["e4m3", "e5m2"])
