@@ -16,6 +16,8 @@ Entry points (same names as the C-ABI in ``include/gemm_bt.h``):
   gemm_bt_plan_layout(M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align)
   gemm_bt_plan_batched_layout(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align)
   gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m)
+  gemm_bt_ws(A, B, C, M, N, K, in_dtype, out_dtype, workspace, workspace_bytes, stream)   stream-K
+  gemm_bt_workspace_size(M, N, K, in_dtype, out_dtype), gemm_bt_plan_ws(M, N, K, in_dtype, out_dtype, ...)
 and torch convenience wrappers ``mm_bt(a, b, out_dtype)`` (2-D or batched 3-D operands),
 ``mm_layout(a, b, a_layout, b_layout, out_dtype)`` and ``mm(a, b, out_dtype)`` (= a @ b).
 """
@@ -33,7 +35,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemm_bt.so")
 EXPORTS = ("gemm_bt", "gemm_bt_batched", "gemm_bt_layout", "gemm_bt_batched_layout", "gemm_bt_status_string",
            "gemm_bt_version", "gemm_bt_plan", "gemm_bt_plan_batched", "gemm_bt_plan_layout",
-           "gemm_bt_plan_batched_layout", "gemm_bt_tile_coord")
+           "gemm_bt_plan_batched_layout", "gemm_bt_tile_coord", "gemm_bt_ws", "gemm_bt_workspace_size",
+           "gemm_bt_plan_ws")
+SK_COUNTER_BYTES = 16384  # leading counter area of a gemm_bt_ws workspace (zero between calls)
 
 _lock = threading.Lock()
 _lib = None
@@ -50,7 +54,8 @@ class Plan(ctypes.Structure):
                 ("bk", ctypes.c_int), ("threads", ctypes.c_int), ("vec", ctypes.c_int), ("group_m", ctypes.c_int),
                 ("ksplit", ctypes.c_int), ("stages", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("tiles_m", ctypes.c_int64),
-                ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64), ("batch", ctypes.c_int64)]
+                ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64), ("batch", ctypes.c_int64),
+                ("split_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -89,6 +94,12 @@ def load():
             lib.gemm_bt_plan.restype = ci
             lib.gemm_bt_tile_coord.argtypes = [i64, i64, i64, ci, ctypes.POINTER(i64), ctypes.POINTER(i64)]
             lib.gemm_bt_tile_coord.restype = ci
+            lib.gemm_bt_ws.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp, ctypes.c_size_t, vp]
+            lib.gemm_bt_ws.restype = ci
+            lib.gemm_bt_workspace_size.argtypes = [i64, i64, i64, ci, ci, ctypes.POINTER(ctypes.c_size_t)]
+            lib.gemm_bt_workspace_size.restype = ci
+            lib.gemm_bt_plan_ws.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
+            lib.gemm_bt_plan_ws.restype = ci
             _lib = lib
     return _lib
 
@@ -167,6 +178,29 @@ def gemm_bt_plan(M, N, K, in_dtype, out_dtype, a_align=256, b_align=256, c_align
     return p
 
 
+def gemm_bt_ws(A: int, B: int, C: int, M: int, N: int, K: int, in_dtype: int, out_dtype: int, workspace: int,
+               workspace_bytes: int, stream: int | None) -> int:
+    """Raw stream-K call with a caller workspace (device pointer, bytes); returns the status code."""
+    return int(load().gemm_bt_ws(A or None, B or None, C or None, M, N, K, in_dtype, out_dtype, workspace or None,
+                                 workspace_bytes, stream or None))
+
+
+def gemm_bt_workspace_size(M, N, K, in_dtype, out_dtype) -> int:
+    n = ctypes.c_size_t()
+    st = load().gemm_bt_workspace_size(M, N, K, in_dtype, out_dtype, ctypes.byref(n))
+    if st != OK:
+        raise GemmBtError(st, "gemm_bt_workspace_size")
+    return n.value
+
+
+def gemm_bt_plan_ws(M, N, K, in_dtype, out_dtype, a_align=256, b_align=256, c_align=256):
+    p = Plan()
+    st = load().gemm_bt_plan_ws(M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, ctypes.byref(p))
+    if st != OK:
+        raise GemmBtError(st, "gemm_bt_plan_ws")
+    return p
+
+
 def gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m):
     tm, tn = ctypes.c_int64(), ctypes.c_int64()
     st = load().gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m, ctypes.byref(tm), ctypes.byref(tn))
@@ -214,7 +248,27 @@ def _batch_operand(x):
     return x, x.shape[1] * x.shape[2]
 
 
-def mm_bt(a, b, out_dtype=None, out=None, stream=None):
+_ws_lock = threading.Lock()
+_ws_cache = {}
+
+
+def workspace_for(device, stream: int, nbytes: int):
+    """A zero-initialised uint8 device tensor of at least `nbytes` for gemm_bt_ws calls on `stream`, kept per
+    (device, stream) and reused: calls on one stream run in order, and each call leaves the counter area zero
+    again.  Grows (a new zeroed tensor) when a larger size is asked for."""
+    import torch
+
+    key = (torch.device(device).index, int(stream))
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None or ws.numel() < nbytes:
+            with torch.cuda.device(device):
+                ws = torch.zeros(max(nbytes, SK_COUNTER_BYTES), dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
+        return ws
+
+
+def mm_bt(a, b, out_dtype=None, out=None, stream=None, split_k=True):
     """C = a @ b.T for CUDA/HIP tensors a (M×K) and b (N×K) of one input dtype.
 
     Batched: a (Z×M×K) and/or b (Z×N×K) give C (Z×M×N), C[z] = a[z] @ b[z].T;
@@ -224,7 +278,10 @@ def mm_bt(a, b, out_dtype=None, out=None, stream=None):
     to a's dtype (bfloat16 for 8-bit float inputs, which are not an output
     format; int32, the only one allowed, for int8); ``out`` may be a preallocated
     contiguous M×N (Z×M×N) tensor.  The call is asynchronous on ``stream``
-    (default: torch's current stream of a's device).
+    (default: torch's current stream of a's device).  With ``split_k`` (the
+    default) a single product goes through gemm_bt_ws with a workspace kept
+    per stream (``workspace_for``), so shapes whose tiles leave compute units
+    idle are split along K (stream-K); ``split_k=False`` calls gemm_bt.
     """
     import torch
 
@@ -259,7 +316,13 @@ def mm_bt(a, b, out_dtype=None, out=None, stream=None):
             st = gemm_bt_batched(a.data_ptr(), b.data_ptr(), out.data_ptr(), Z, M, N, K, sa, sb, M * N, in_code,
                                  out_code, stream)
         else:
-            st = gemm_bt(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, in_code, out_code, stream)
+            nbytes = gemm_bt_workspace_size(M, N, K, in_code, out_code) if split_k else 0
+            if nbytes:
+                ws = workspace_for(a.device, stream, nbytes)
+                st = gemm_bt_ws(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, in_code, out_code,
+                                ws.data_ptr(), ws.numel(), stream)
+            else:
+                st = gemm_bt(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, in_code, out_code, stream)
     if st != OK:
         raise GemmBtError(st)
     return out

@@ -207,19 +207,21 @@ __device__ inline float decode16(u32 v) {
     else return (float)__builtin_bit_cast(_Float16, (u16)v);
 }
 
-// Tile order: XCD regrouping followed by banded (grouped) order.  Identical
-// on host and device so the host can verify it is a bijection.
-__host__ __device__ inline void tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m,
-                                           int64_t* tm, int64_t* tn) {
-    const int64_t total = tiles_m * tiles_n;
-    // Workgroup pid is dispatched to die pid % 8.  Give die x the contiguous
-    // run [start_x, start_x + count_x) of the tile sequence.
+// Workgroup pid of a grid of `total` is dispatched to die (XCD) pid % 8.
+// xcd_seq renumbers the grid so that die x holds the contiguous run
+// [start_x, start_x + count_x) of the result: a bijection of [0, total).
+__host__ __device__ inline int64_t xcd_seq(int64_t pid, int64_t total) {
     constexpr int64_t kXcd = 8;
     const int64_t q = total / kXcd, rem = total % kXcd;
     const int64_t x = pid % kXcd, i = pid / kXcd;
-    const int64_t seq = x * q + (x < rem ? x : rem) + i;
-    // Banded order over the tile grid: bands of group_m tile-rows, walked
-    // column by column, rows fastest inside a band.
+    return x * q + (x < rem ? x : rem) + i;
+}
+
+// Banded order over the tile grid: position seq of the sequence is tile
+// (tm, tn), with bands of group_m tile-rows walked column by column, rows
+// fastest inside a band.
+__host__ __device__ inline void band_coord(int64_t seq, int64_t tiles_m, int64_t tiles_n, int group_m, int64_t* tm,
+                                           int64_t* tn) {
     const int64_t band_tiles = (int64_t)group_m * tiles_n;
     const int64_t band = seq / band_tiles;
     const int64_t first_m = band * group_m;
@@ -227,6 +229,13 @@ __host__ __device__ inline void tile_coord(int64_t pid, int64_t tiles_m, int64_t
     const int64_t in_band = seq - band * band_tiles;
     *tm = first_m + in_band % rows;
     *tn = in_band / rows;
+}
+
+// Tile order: XCD regrouping followed by banded (grouped) order.  Identical
+// on host and device so the host can verify it is a bijection.
+__host__ __device__ inline void tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m,
+                                           int64_t* tm, int64_t* tn) {
+    band_coord(xcd_seq(pid, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 // Accumulator blocks of the tiled kernels.  The MFMA takes the B tile as its

@@ -148,13 +148,46 @@ __device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, 
 // BK = 64) with 4-byte LDS-DMA loads into a scratch corner of LDS, so that the
 // refill PF steps later finds its lines in L2 instead of paying the full
 // HBM / Infinity-Cache latency with only STAGES - 1 steps of cover.
+//
+// SK = 1: stream-K ("Writing Mosaic GPU kernels with Pallas", section
+// "Cluster launch control": the grid walks the work itself, so that no core
+// idles through a partial last wave).  The sk.sk_tiles tiles of the banded
+// order form sk.iters = sk_tiles * nk (tile, K step) iterations, and
+// workgroup g of the G launched takes the contiguous run [v*iters/G,
+// (v+1)*iters/G) of them, v being g renumbered die by die (xcd_seq), so that
+// the workgroups sharing a tile sit on one die.  A run may cover the tail of
+// one tile, whole tiles and the head of another; each piece is one pipeline
+// over its K steps.  (The host plans G = sk_tiles * S, which makes every run
+// exactly one piece of one tile: split-K with S pieces per tile.)  A tile
+// done by several workgroups is finished by the last of them to arrive:
+// every contributor writes its fp32 sums to its own slot of sk.partials with
+// device-scope (write-through) stores, waits until they are written, and
+// counts itself in the tile's counter; the one that sees every other
+// contributor already counted reads the partial sums back with device-scope
+// loads, adds them in K order (contributor 0 + 1 + 2 ..., whatever the
+// arrival order, so the result is the same bits on every run), resets the
+// counter to zero and stores the tile.  No workgroup ever waits for another.
+struct SkArgs {
+    int sk_tiles;        // tiles split along K over the grid
+    int nk;              // K steps of BK per tile (over the whole 16-byte chunks of K)
+    long long iters;     // sk_tiles * nk
+    unsigned* counters;  // one arrival counter per split tile, zero between calls
+    float* partials;     // two slots of BM * BN floats per workgroup
+};
+
+// Owner of stream-K iteration `it`: the (renumbered) workgroup v whose run
+// [v*I/G, (v+1)*I/G) contains it, i.e. the largest v with floor(v*I/G) <= it.
+__host__ __device__ inline int64_t sk_owner(int64_t it, int64_t iters, int64_t grid) {
+    return ((it + 1) * grid - 1) / iters;
+}
+
 template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0,
-          int MF = 32, int LDW = 0, int RING5 = 0>
+          int MF = 32, int LDW = 0, int RING5 = 0, int SK = 0>
 __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                           void* __restrict__ C, int M, int N, int K,
                                                           int tiles_m, int tiles_n, int group_m,
                                                           int vec_store, int item_tiles_m, long long sa, long long sb,
-                                                          long long sc) {
+                                                          long long sc, const SkArgs sk) {
     constexpr int W = WM * WN;
     constexpr int ESZ = in_size(IN);     // bytes per input element (2, or 1 for 8-bit floats)
     constexpr int EPC = 16 / ESZ;        // elements per 16-byte chunk
@@ -192,50 +225,32 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
-
-    int64_t tm64, tn64;
-    tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
-    if (tiles_m != item_tiles_m) {
-        // batch items are stacked along the tile rows (tiles_m counts all of
-        // them), so the XCD regrouping gives each die whole items
-        const int z = (int)tm64 / item_tiles_m;
-        tm64 -= (int64_t)z * item_tiles_m;
-        batch_item(z, A, B, C, sa, sb, sc);
-    }
-    const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
-    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
     const u32 row_bytes = (u32)K * (u32)ESZ;
-    const i32x4 ra = rsrc_words((const unsigned char*)A + (size_t)m0 * row_bytes, (u32)rows_a * row_bytes);
-    const i32x4 rb = rsrc_words((const unsigned char*)B + (size_t)n0 * row_bytes, (u32)rows_b * row_bytes);
     // Only whole 16-byte chunks go through the LDS DMA: k < Kf.  When rows are
     // 4-byte aligned but K % 8 != 0, the last K - Kf (2, 4 or 6) elements of
     // every row are added after the loop (see the tail below).
     const int Kf = K & ~(EPC - 1);
-    // K tail (see after the loop): thread t fetches the last K - Kf elements
-    // (1 to 3 dwords; rows and K are 4-byte aligned here) of tile row t (A
-    // rows first, then B rows) now, so that their latency hides behind the
-    // main loop.  Being older than every ring load, they are also covered by
-    // each of the ring's vmcnt waits.
+    const int nk_all = (Kf + BK - 1) / BK;  // K steps of a whole tile
     static_assert(64 * W >= BM + BN, "one thread per tile row of the K tail");
-    u32 tail_v[3] = {0u, 0u, 0u};
-    if (ESZ == 2 && Kf != K) {
-        const int r = threadIdx.x;
-        const bool in_a = r < BM;
-        const bool valid = in_a ? r < rows_a : (r < BM + BN && r - BM < rows_b);
-        if (valid) {
-            const u32* src = (const u32*)(in_a ? A + (size_t)(m0 + r) * K + Kf : B + (size_t)(n0 + r - BM) * K + Kf);
-            const int nd = (K - Kf) >> 1;
-#pragma unroll
-            for (int d = 0; d < 3; ++d)
-                if (d < nd) tail_v[d] = __builtin_nontemporal_load(src + d);
-        }
-    }
+    typedef AccBlock<MF> AB;
+    typedef typename AB::type Acc[FN][FM];
 
+    // The pipeline over K steps kb .. ke-1 of the tile whose A rows start at
+    // row m0 of Ap and whose B rows start at row n0 of Bp, added into acc.
+    // When ke is the tile's last step and K % 8 != 0, the K tail follows.
+    // Leaves every LDS DMA landed; other waves may still read LDS.
+    auto run = [&](const u16* Ap, const u16* Bp, int m0, int n0, int kb, int ke, Acc& acc) {
+    // The per-lane geometry below is derived from a copy of the lane index
+    // that the compiler must treat as new on every call: in the stream-K form
+    // (one call per piece) it is then recomputed per piece (a few VALU
+    // operations) instead of being kept live, and spilled, across the pieces.
+    int lane_r = lane;
+    asm volatile("" : "+v"(lane_r));
     // Loader geometry.  Wave instruction i of this wave fills row block
     // j = wave + i*W (rows j*RPI .. j*RPI+RPI-1 of the tile); lane L writes
     // row j*RPI + L/CPR at physical chunk L%CPR and so fetches logical chunk
     // (L%CPR) ^ swz(row).
-    const int lrow = lane / CPR, lphys = lane % CPR;
+    const int lrow = lane_r / CPR, lphys = lane_r % CPR;
     // The rows of a wave's instructions are W * RPI apart, a multiple of the
     // swizzle period (16 rows), so all of them fetch the same logical chunk
     // and instruction i only adds i * W * RPI rows to the byte offset.  A and
@@ -248,10 +263,44 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     const u32 i_stride = (u32)(W * RPI) * row_bytes;
     auto ld_off = [&](int i) { return l_off + (u32)i * i_stride; };
 
+    // Operand reads: row (lane % MF) of each MF-row block, logical chunk
+    // (KSUB/8)*ks + lane/MF for k-substep ks; block bases are multiples of MF
+    // (>= 16), so the swizzle term depends on the lane only.
+    const int fr = lane_r % MF, fhi = lane_r / MF;
+    const int fsw = swz_row<CPR, SWZ>(fr);
+    const int a_base = (wm * TM + fr) * ROWB;
+    const int b_base = BM * ROWB + (wn * TN + fr) * ROWB;
+    const int b_base0 = (wn * TN + fr) * ROWB;  // relative to the B tile
+
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const i32x4 ra = rsrc_words((const unsigned char*)Ap + (size_t)m0 * row_bytes, (u32)rows_a * row_bytes);
+    const i32x4 rb = rsrc_words((const unsigned char*)Bp + (size_t)n0 * row_bytes, (u32)rows_b * row_bytes);
+    // k < Ke: the whole chunks of this K range (loads past it come back as zeros)
+    const int Ke = min(Kf, ke * BK);
+    const bool with_tail = ESZ == 2 && Kf != K && ke == nk_all;
+    // K tail (see after the loop): thread t fetches the last K - Kf elements
+    // (1 to 3 dwords; rows and K are 4-byte aligned here) of tile row t (A
+    // rows first, then B rows) now, so that their latency hides behind the
+    // main loop.  Being older than every ring load, they are also covered by
+    // each of the ring's vmcnt waits.
+    u32 tail_v[3] = {0u, 0u, 0u};
+    if (with_tail) {
+        const int r = threadIdx.x;
+        const bool in_a = r < BM;
+        const bool valid = in_a ? r < rows_a : (r < BM + BN && r - BM < rows_b);
+        if (valid) {
+            const u32* src = (const u32*)(in_a ? Ap + (size_t)(m0 + r) * K + Kf : Bp + (size_t)(n0 + r - BM) * K + Kf);
+            const int nd = (K - Kf) >> 1;
+#pragma unroll
+            for (int d = 0; d < 3; ++d)
+                if (d < nd) tail_v[d] = __builtin_nontemporal_load(src + d);
+        }
+    }
+
     auto issue = [&](int stage, int kt) {
         unsigned char* sbase = lds + stage * STAGE_BYTES;
-        const u32 kbytes = (u32)kt * (u32)ROWB;
-        const int kleft = Kf - kt * BK;  // valid K elements in this tile (may be <= 0)
+        const u32 kbytes = (u32)(kb + kt) * (u32)ROWB;
+        const int kleft = Ke - (kb + kt) * BK;  // valid K elements in this tile (may be <= 0)
         if (kleft >= BK) {
 #pragma unroll
             for (int i = 0; i < LA; ++i)
@@ -276,8 +325,8 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     auto prefetch = [&](int kt) {
         if constexpr (PF > 0) {
             unsigned char* pbase = lds + STAGES * STAGE_BYTES + wave * 256;
-            const u32 kbytes = (u32)kt * (u32)ROWB;
-            const bool live = kt * BK < Kf;
+            const u32 kbytes = (u32)(kb + kt) * (u32)ROWB;
+            const bool live = (kb + kt) * BK < Ke;
 #pragma unroll
             for (int p = 0; p < PFI; ++p) {
                 const int row = (wave * PFI + p) * 64 + lane;
@@ -288,24 +337,6 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             }
         }
     };
-
-    // Operand reads: row (lane % MF) of each MF-row block, logical chunk
-    // (KSUB/8)*ks + lane/MF for k-substep ks; block bases are multiples of MF
-    // (>= 16), so the swizzle term depends on the lane only.
-    typedef AccBlock<MF> AB;
-    const int fr = lane % MF, fhi = lane / MF;
-    const int fsw = swz_row<CPR, SWZ>(fr);
-    const int a_base = (wm * TM + fr) * ROWB;
-    const int b_base = BM * ROWB + (wn * TN + fr) * ROWB;
-    const int b_base0 = (wn * TN + fr) * ROWB;  // relative to the B tile
-
-    typename AB::type acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-#pragma unroll
-            for (int r = 0; r < AB::regs; ++r) acc[i][j][r] = 0.0f;
 
     // Operand fragments are double-buffered in registers: the LDS reads for
     // k-substep ks+1 are issued before the MFMAs of substep ks, so their
@@ -355,7 +386,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         }
     };
 
-    const int nk = (Kf + BK - 1) / BK;
+    const int nk = ke - kb;  // K steps of this range
     if constexpr (SCHED >= 2) {
         // Early barrier: each wave reads the fragments of a tile's last FD
         // k-substeps, then waits for the next tile and joins the barrier
@@ -403,8 +434,8 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         auto load_one = [&](int stage, int kt, int d) {
             if (!loader) return;
             unsigned char* sbase = lds + stage * STAGE_BYTES;
-            const u32 kbytes = (u32)kt * (u32)ROWB;
-            const int kleft = Kf - kt * BK;
+            const u32 kbytes = (u32)(kb + kt) * (u32)ROWB;
+            const int kleft = Ke - (kb + kt) * BK;
             if (d < LAW)
                 dma16(ra, sbase + (wave + d * LW) * 1024, l_kc < kleft ? l_off + (u32)d * lw_stride : kOutOfRange,
                       kbytes);
@@ -473,15 +504,15 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         auto slot = [&](int sl) { return lds + sl * SLOT_BYTES; };
         auto load_a = [&](int sl, int kt, int d) {
             if (!loader) return;
-            const int kleft = Kf - kt * BK;
+            const int kleft = Ke - (kb + kt) * BK;
             dma16(ra, slot(sl) + (wave + d * LW) * 1024, l_kc < kleft ? l_off + (u32)d * lw_stride : kOutOfRange,
-                  (u32)kt * (u32)ROWB);
+                  (u32)(kb + kt) * (u32)ROWB);
         };
         auto load_b = [&](int sl, int kt, int d) {
             if (!loader) return;
-            const int kleft = Kf - kt * BK;
+            const int kleft = Ke - (kb + kt) * BK;
             dma16(rb, slot(sl) + (wave + d * LW) * 1024, l_kc < kleft ? l_off + (u32)d * lw_stride : kOutOfRange,
-                  (u32)kt * (u32)ROWB);
+                  (u32)(kb + kt) * (u32)ROWB);
         };
         static_assert(SPREAD == 1 && FD == 1 && CH == LAW + LBW, "one refill burst per step");
         // RING5 == 2: A(kt + 2) goes out during the first substep of step kt
@@ -581,8 +612,8 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         // `wave + 4`); the wm = 1 group never loads from global memory.
         auto issue_g0 = [&](int stage, int kt) {
             unsigned char* sbase = lds + stage * STAGE_BYTES;
-            const u32 kbytes = (u32)kt * (u32)ROWB;
-            const int kleft = Kf - kt * BK;
+            const u32 kbytes = (u32)(kb + kt) * (u32)ROWB;
+            const int kleft = Ke - (kb + kt) * BK;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int blk = wave + 4 * h;
@@ -660,7 +691,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     }
     wait_vmcnt<0>();  // the ring's last (out-of-range) loads still write LDS
 
-    if (ESZ == 2 && Kf != K) {
+    if (with_tail) {
         // K tail: the last K - Kf (2, 4 or 6) elements of every row form one
         // more K tile, zero-padded, written into LDS stage 0 in the same
         // swizzled layout and multiplied like the others.  It comes after all
@@ -683,14 +714,164 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             mma(tb, ta);
         }
     }
+    };  // run
 
-    if (vec_store == 2) {
-        // every wave is past its last LDS read and its loads have landed
-        barrier_no_fence();
-        store_tile_lds<store_type(OUT), FN, FM, BM, BN, WM, 64 * W, STAGES * STAGE_BYTES, MF>(acc, lds, C, M, N, m0, n0, wm * TM,
-                                                                             wn * TN, wm, threadIdx.x);
+    auto zero = [&](Acc& acc) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int r = 0; r < AB::regs; ++r) acc[i][j][r] = 0.0f;
+    };
+    // the finished tile at rows m0.., columns n0.. of Cp
+    // (tid_r: the thread index, recomputed per call for the same reason as
+    // lane_r in run)
+    auto store_c = [&](void* Cp, int m0, int n0, Acc& acc) {
+        int tid_r = threadIdx.x;
+        asm volatile("" : "+v"(tid_r));
+        if (vec_store == 2) {
+            // every wave is past its last LDS read and its loads have landed
+            barrier_no_fence();
+            store_tile_lds<store_type(OUT), FN, FM, BM, BN, WM, 64 * W, STAGES * STAGE_BYTES, MF>(
+                acc, lds, Cp, M, N, m0, n0, wm * TM, wn * TN, wm, tid_r);
+        } else {
+            store_tile<store_type(OUT), FN, FM, MF>(acc, Cp, M, N, m0, n0, wm * TM, wn * TN, tid_r & 63, vec_store);
+        }
+    };
+
+    if constexpr (!SK) {
+        int64_t tm64, tn64;
+        tile_coord(blockIdx.x, tiles_m, tiles_n, group_m, &tm64, &tn64);
+        if (tiles_m != item_tiles_m) {
+            // batch items are stacked along the tile rows (tiles_m counts all of
+            // them), so the XCD regrouping gives each die whole items
+            const int z = (int)tm64 / item_tiles_m;
+            tm64 -= (int64_t)z * item_tiles_m;
+            batch_item(z, A, B, C, sa, sb, sc);
+        }
+        const int m0 = (int)tm64 * BM, n0 = (int)tn64 * BN;
+        Acc acc;
+        zero(acc);
+        run(A, B, m0, n0, 0, nk_all, acc);
+        store_c(C, m0, n0, acc);
     } else {
-        store_tile<store_type(OUT), FN, FM, MF>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+        // Stream-K (one item; the host sends batches to the plain grid).  The
+        // bookkeeping is wave-uniform and 32-bit (the host keeps iters below
+        // 2^31): readfirstlane pins each value to a scalar register, so none of
+        // it competes with the accumulators for vector registers.
+        constexpr int NT = 64 * W;
+        constexpr int Q = AB::regs / 4;  // 16-byte groups per accumulator block
+        static_assert(W * 64 * 4 * FN * FM * AB::regs == BM * BN * 4, "a partial slot holds one fp32 tile");
+        auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+        const int G = gridDim.x, g = blockIdx.x;
+        const int I = (int)sk.iters, nk = sk.nk;
+        // first iteration of rank r, and the rank owning iteration `it`
+        auto start = [&](int r) { return uni((int)((int64_t)r * I / G)); };
+        auto owner = [&](int it) { return uni((int)sk_owner(it, I, G)); };
+        const int v = uni((int)xcd_seq(g, G));  // rank among the workgroups, die by die
+        const int it0 = start(v), it1 = start(v + 1);
+        // the partial sums of contributor vv to split tile s: slot 0 of vv holds
+        // its first piece, slot 1 its last; thread t owns 16-byte group e at
+        // byte (t + e * NT) * 16 of the slot
+        auto slot = [&](int vv, int s) {
+            const int first = uni(start(vv) / nk);
+            return make_rsrc(sk.partials + (int64_t)(2 * vv + (s == first ? 0 : 1)) * (BM * BN), BM * BN * 4);
+        };
+        // Cache policy of the partial sums: sc1, device scope.  Stores are
+        // written through the die's L2 to device memory, and loads miss any
+        // die-local copy, so pieces computed on different dies (each with its
+        // own L2) see each other's sums.  (The agent-scope release/acquire
+        // fences would write back and invalidate the whole L2 instead: 93 us
+        // against 34 us for 1000x3000x2050 split 192 ways.)
+        constexpr int kCoherent = 16;
+        // acc = P (overwrite) or acc += P, in place, elementwise.  The loads go
+        // out in batches of CHUNK 16-byte groups ahead of their adds (the
+        // sched_barrier keeps the compiler from pairing each load with its add
+        // and waiting for it), so a slot costs NE / CHUNK memory latencies;
+        // the batch is smaller when the accumulators already fill half the
+        // registers.
+        constexpr int NE = FN * FM * Q;
+        constexpr int CHUNK = NE <= 16 ? NE : (NE * 4 * 2 > 256 ? 8 : 16);
+        static_assert(NE % CHUNK == 0, "whole load batches");
+        auto add_slot = [&](__amdgpu_buffer_rsrc_t p, bool overwrite, Acc& acc) {
+            int tid_r = threadIdx.x;
+            asm volatile("" : "+v"(tid_r));
+            static_for<0, NE / CHUNK>([&](auto cc) {
+                constexpr int c0 = decltype(cc)::value * CHUNK;
+                u32x4 x[CHUNK];
+                static_for<0, CHUNK>([&](auto ec) {
+                    constexpr int e = c0 + decltype(ec)::value;
+                    x[e - c0] = __builtin_amdgcn_raw_buffer_load_b128(p, (u32)(tid_r + e * NT) * 16u, 0, kCoherent);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<0, CHUNK>([&](auto ec) {
+                    constexpr int e = c0 + decltype(ec)::value;
+                    constexpr int i = e / (FM * Q), j = (e / Q) % FM, q = e % Q;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[i][j][4 * q + r] =
+                            overwrite ? as_f32(x[e - c0][r]) : acc[i][j][4 * q + r] + as_f32(x[e - c0][r]);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        // One pipeline and one store site per piece of this workgroup's run.
+        for (int it = it0; it < it1;) {
+            const int s = uni(it / nk);
+            const int kb = uni(it - s * nk);
+            const int ke = uni(min(nk, kb + (it1 - it)));
+            it += ke - kb;
+            __syncthreads();  // LDS is free again (the previous piece's epilogue is done)
+            int64_t tm, tn;
+            band_coord(s, tiles_m, tiles_n, group_m, &tm, &tn);
+            const int m0 = uni((int)tm * BM), n0 = uni((int)tn * BN);
+            Acc acc;
+            zero(acc);
+            run(A, B, m0, n0, kb, ke, acc);
+            const int vf = owner(s * nk), vl = owner(s * nk + nk - 1);
+            if (vf != vl) {
+            // a piece of a tile shared with other workgroups: publish its
+            // partial sums (written through), count it in
+            const __amdgpu_buffer_rsrc_t mine = slot(v, s);
+            int tid_r = threadIdx.x;
+            asm volatile("" : "+v"(tid_r));
+            static_for<0, FN * FM * Q>([&](auto ec) {
+                constexpr int e = decltype(ec)::value;
+                constexpr int i = e / (FM * Q), j = (e / Q) % FM, q = e % Q;
+                const u32x4 w = {as_u32(acc[i][j][4 * q]), as_u32(acc[i][j][4 * q + 1]), as_u32(acc[i][j][4 * q + 2]),
+                                 as_u32(acc[i][j][4 * q + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(w, mine, (u32)(tid_r + e * NT) * 16u, 0, kCoherent);
+            });
+            wait_vmcnt<0>();  // this wave's sums have reached device memory
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                // every wave of this workgroup is past its wait (the barrier
+                // above), so the count follows all of the piece's stores
+                const unsigned seen = __hip_atomic_fetch_add(sk.counters + s, 1u, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                const int last = seen == (unsigned)(vl - vf);
+                if (last) __hip_atomic_store(sk.counters + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *(volatile int*)lds = last;
+            }
+            __syncthreads();
+            if (!*(volatile int*)lds) continue;
+            // last to arrive: sum contributor 0 + 1 + ... in that order
+            const int jm = v - vf, n = vl - vf + 1;
+            int jn;
+            if (jm == 0) {
+                jn = 1;  // acc is piece 0
+            } else if (jm == 1) {
+                add_slot(slot(vf, s), false, acc);  // piece 1 + piece 0 == piece 0 + piece 1
+                jn = 2;
+            } else {
+                add_slot(slot(vf, s), true, acc);  // piece 0; ours is read back in its turn
+                jn = 1;
+            }
+            for (int jj = jn; jj < n; ++jj) add_slot(slot(vf + jj, s), false, acc);
+            }
+            store_c(C, m0, n0, acc);
+        }
     }
 }
 

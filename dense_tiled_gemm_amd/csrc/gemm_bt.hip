@@ -106,9 +106,10 @@ static DmaVariant dma_variant(const char* name) {
 // Index 0 is the default for large grids, 1 for smaller ones, 2 and 6 for
 // the smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
 // (128-element K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32
-// MFMAs over 64-element substeps);
-// the rest exist for tuning (GEMM_BT_FORCE_TILE=<name>) and are built for the
-// bf16->bf16 and f16->f16 combinations only.
+// MFMAs over 64-element substeps).
+// A build with GEMM_BT_TUNING defined adds the measured alternatives after
+// them (selected with GEMM_BT_FORCE_TILE=<name>, bf16->bf16 and f16->f16
+// only); the default library holds the seven production kernels only.
 constexpr int kFp8Variants = 3;
 constexpr int kTiny16 = 6;  // 32 x 64 tiles (16-bit inputs), when even 64 x 64 tiles leave half the CUs idle
 static const DmaVariant* dma_variants(int* count) {
@@ -120,6 +121,7 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<128, 128, 128, 4, 2, 2, 2, 8, 0, 32, true, 0, 0, true>("M128F8s4i"),
         dma_variant<64, 64, 128, 4, 2, 2, 2, 4, 0, 32, true, 0, 0, true>("Q128F8"),
         dma_variant<32, 64, 64, 4, 2, 2, 2, 2, 0, 16, true>("T32x64"),
+#ifdef GEMM_BT_TUNING
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16>("L64E16i"),
@@ -134,10 +136,35 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 2>("L64P2"),
+#endif
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
 }
+
+// Stream-K form of the 128 x 128 tier (M64E4s4i, dma_variants() index 1):
+// a grid that splits the K range of tiles over workgroups (16-bit inputs,
+// one item).
+constexpr int kSkVariant = 1;
+template <int IN, int OUT>
+static const void* sk_fn_t() {
+    return (const void*)&dma_kernel<IN, OUT, 128, 128, 64, 4, 2, 2, 2, 8, 0, 16, 0, 0, 1>;
+}
+template <int IN>
+static const void* sk_fn_out(int out) {
+    if (out == GEMM_BT_F32) return sk_fn_t<IN, GEMM_BT_F32>();
+    if (out == GEMM_BT_BF16) return sk_fn_t<IN, GEMM_BT_BF16>();
+    return sk_fn_t<IN, GEMM_BT_F16>();
+}
+static const void* sk_fn(int in_dtype, int out_dtype) {
+    return in_dtype == GEMM_BT_BF16 ? sk_fn_out<GEMM_BT_BF16>(out_dtype) : sk_fn_out<GEMM_BT_F16>(out_dtype);
+}
+
+// Workspace of the stream-K kernels: a fixed area of arrival counters (one
+// per split tile; a plan splits fewer than 2 * grid tiles), then two slots of
+// one fp32 tile per workgroup.
+constexpr int64_t kSkCounterBytes = 16384;
+constexpr int64_t kSkMaxTiles = kSkCounterBytes / 4;
 
 // Skinny DMA-kernel variants [in][out]; index 0 is the default.
 struct SkinnyVariant {
@@ -163,17 +190,20 @@ static SkinnyVariant skinny_variant(const char* name) {
 static const SkinnyVariant* skinny_variants(int* count) {
     static const SkinnyVariant v[] = {
         skinny_variant<8, 256, 3, 1, true>("S8K256x3w1"),
+#ifdef GEMM_BT_TUNING
         skinny_variant<16, 256, 4, 4>("S16K256x4"),
         skinny_variant<8, 256, 3, 2>("S8K256x3w2"),
         skinny_variant<8, 128, 4, 1>("S8K128x4w1"),
         skinny_variant<16, 256, 3, 1>("S16K256x3w1"),
         skinny_variant<32, 256, 6, 4>("S32K256x6"),
         skinny_variant<16, 256, 3, 1, false, 1>("S16K256x3w1r1"),
+#endif
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
 }
 
+#ifdef GEMM_BT_TUNING
 static int forced_skinny() {
     // Benchmarking aid: GEMM_BT_FORCE_SKINNY=<variant name>.
     static std::atomic<int> cached{-2};
@@ -218,6 +248,12 @@ static int forced_variant() {
     }
     return v;
 }
+#else
+// The production library takes no tuning overrides.
+static int forced_skinny() { return -1; }
+static bool forced_staged() { return false; }
+static int forced_variant() { return -1; }
+#endif
 
 static int pick_vec(int64_t K, int a_align, int b_align) {
     if (K % 8 == 0 && a_align % 16 == 0 && b_align % 16 == 0) return 8;
@@ -238,8 +274,50 @@ static bool dma_large_tier(int64_t tiles_l, int num_cu, bool eight_bit) {
     return eight_bit ? tiles_l * 16 > (int64_t)num_cu * 17 : tiles_l * 5 > (int64_t)num_cu * 6;
 }
 
+// Split plan (the stream-K kernel with one piece per workgroup) for 16-bit
+// inputs on the LDS-DMA path, one item, 128 x 128 tiles: when those tiles
+// would fill at most half the CUs (the plain plan then falls back to 64 x 64
+// or 32 x 64 tiles), each of the T tiles is split along K into
+// S = floor(CUs / T) pieces of at least kSkMinSteps K steps, and a grid of
+// T * S workgroups computes one piece each.  Every workgroup's run of
+// iterations then lies inside one tile, at the same K offset as the matching
+// pieces of the other tiles, so workgroups sharing an operand panel read it
+// in step, as in the plain grid.  Measured on 256 CUs, against the plain plan
+// (us): 512x1024x32768 61 vs 121, 1024x1024x16384 51 vs 73, 1024x2048x8192
+// 47 vs 62, 512x2048x8192 34 vs 39, 256x4096x8192 35 vs 41, 2048x1024x4096
+// 27 vs 29; with pieces of 16 steps it loses (1024x1024x4096 22 vs 18.5).
+// With more tiles than half the CUs (e.g. 192 tiles of 1000x3000), pieces
+// that straddle tiles and start at different K offsets lose the panel reuse
+// and the split lost everywhere it was measured (1000x3000x2050 33 vs 26.5,
+// 1000x3000x8192 81 vs 65), so no split is planned there.
+// Fills p and returns true, or returns false and leaves p alone.
+constexpr int64_t kSkMinSteps = 32;
+static bool plan_split(int64_t M, int64_t N, int64_t K, int num_cu, gemm_bt_plan_t* p) {
+    const int64_t T = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t nk = ((K & ~7LL) + 63) / 64;
+    if (T * 2 > num_cu) return false;
+    const int64_t S = num_cu / T;
+    if (nk < kSkMinSteps * S || T > kSkMaxTiles || T * nk >= (1LL << 31)) return false;
+    int n = 0;
+    const DmaVariant& v = dma_variants(&n)[kSkVariant];
+    p->kernel = KIND_DMA;
+    p->variant = kSkVariant;
+    p->bm = v.bm;
+    p->bn = v.bn;
+    p->bk = v.bk;
+    p->stages = v.stages;
+    p->threads = 64 * v.wm * v.wn;
+    p->lds_bytes = v.lds_bytes;
+    p->tiles_m = (M + 127) / 128;
+    p->tiles_n = (N + 127) / 128;
+    p->grid = T * S;
+    p->split_tiles = T;
+    p->workspace_bytes = kSkCounterBytes + 2 * p->grid * 128 * 128 * 4;
+    return true;
+}
+
 static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
-                     int b_align, int c_align, int num_cu, gemm_bt_plan_t* p) {
+                     int b_align, int c_align, int num_cu, bool allow_sk, gemm_bt_plan_t* p) {
     if (!p) return GEMM_BT_ERR_INVALID_VALUE;
     std::memset(p, 0, sizeof(*p));
     if (batch < 0 || M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
@@ -359,6 +437,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         p->stages = v.stages;
         p->threads = 64 * v.wm * v.wn;
         p->lds_bytes = v.lds_bytes;
+        if (allow_sk && f < 0 && batch == 1 && plan_split(M, N, K, num_cu, p)) return GEMM_BT_OK;
     } else {
         const TileCfg c = big ? kCfgL : kCfgM;
         p->kernel = KIND_TILED;
@@ -390,7 +469,7 @@ static int plan_layout_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int 
         return GEMM_BT_ERR_INVALID_VALUE;
     }
     if (a_layout == GEMM_BT_K_INNER && b_layout == GEMM_BT_K_INNER)
-        return plan_impl(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, p);
+        return plan_impl(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, false, p);
     std::memset(p, 0, sizeof(*p));
     if (batch < 0 || M < 0 || N < 0 || K < 0) return GEMM_BT_ERR_INVALID_VALUE;
     if (batch > kMaxBatch) return GEMM_BT_ERR_UNSUPPORTED;
@@ -569,13 +648,122 @@ static int check_items(const void* A, const void* B, const void* C, int kind, in
     return GEMM_BT_OK;
 }
 
+// CU count the plans are made for: the current device's when it is a
+// gfx950, else 256 (an MI355X), so that a plan taken on the host describes the
+// launch on the device that is present.
+static int plan_cus() {
+    int n = 256;
+    return check_device(&n) == GEMM_BT_OK ? n : 256;
+}
+
+// Stream-K arguments of a plan: the counters at the start of the workspace,
+// the partial-sum slots after them.  Zero for a data-parallel plan.
+static SkArgs sk_args(const gemm_bt_plan_t& p, int64_t K, void* ws) {
+    SkArgs a = {0, 0, 0, nullptr, nullptr};
+    if (p.split_tiles > 0) {
+        a.sk_tiles = (int)p.split_tiles;
+        a.nk = (int)(((K & ~7LL) + p.bk - 1) / p.bk);
+        a.iters = (long long)a.sk_tiles * a.nk;
+        a.counters = (unsigned*)ws;
+        a.partials = (float*)((char*)ws + kSkCounterBytes);
+    }
+    return a;
+}
+
+// Every K-inner call: argument checks, the plan for the current device and
+// the launch.  `ws` (with `ws_bytes`) enables the stream-K plan; NULL plans
+// the data-parallel grid as gemm_bt does.
+static int launch_inner(const void* A, const void* B, void* C, int64_t batch, int64_t M, int64_t N, int64_t K,
+                        int64_t stride_a, int64_t stride_b, int64_t stride_c, int in_dtype, int out_dtype, void* ws,
+                        size_t ws_bytes, void* stream) {
+    gemm_bt_plan_t p;
+    if (stride_a < 0 || stride_b < 0 || stride_c < 0) return GEMM_BT_ERR_INVALID_VALUE;
+    const bool multi = batch > 1;
+    const int isz = is_8bit(in_dtype) ? 1 : 2;
+    const int osz = out_size(out_dtype);
+    const int a_al = item_align(A, batch, stride_a, isz), b_al = item_align(B, batch, stride_b, isz),
+              c_al = item_align(C, batch, stride_c, osz);
+    const bool allow_sk = ws != nullptr;
+    // Plan against the default CU count first: it validates the arguments
+    // without touching the device.
+    int st = plan_impl(batch, M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, 256, allow_sk, &p);
+    if (st != GEMM_BT_OK) return st;
+    if (p.kernel == KIND_NONE) return GEMM_BT_OK;
+    st = check_items(A, B, C, p.kernel, batch, M, N, stride_a, stride_b, stride_c, isz, osz);
+    if (st != GEMM_BT_OK) return st;
+
+    int num_cu = 256;
+    st = check_device(&num_cu);
+    if (st != GEMM_BT_OK) return st;
+    if (num_cu != 256) {
+        st = plan_impl(batch, M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, num_cu, allow_sk, &p);
+        if (st != GEMM_BT_OK) return st;
+    }
+    if (p.split_tiles > 0 && ((uintptr_t)ws % 16 != 0 || ws_bytes < (size_t)p.workspace_bytes))
+        return GEMM_BT_ERR_INVALID_VALUE;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+    long long sa = multi ? (long long)stride_a * isz : 0, sb = multi ? (long long)stride_b * isz : 0,
+              sc = multi ? (long long)stride_c * osz : 0;
+    const unsigned gy = (unsigned)batch;
+
+    if (p.kernel == KIND_FILL) {
+        u16* c16 = (u16*)C;
+        size_t n16 = (size_t)M * (size_t)N * osz / 2;
+        void* args[] = {&c16, &n16, &sc};
+        e = hipLaunchKernel((const void*)&zero_fill_kernel, dim3((unsigned)p.grid, gy), dim3(p.threads), args, 0, s);
+    } else {
+        const u16* a = (const u16*)A;
+        const u16* b = (const u16*)B;
+        // Vector stores need 4 consecutive outputs inside one row, aligned;
+        // 2 = rows of C are also whole 16-byte chunks (the DMA kernel then
+        // stores through LDS, whole rows per instruction).
+        int vec_store = (N % 4 == 0) && c_al >= 4 * osz ? 1 : 0;
+        if (vec_store && (N * osz) % 16 == 0 && c_al >= 16) vec_store = 2;
+        if (p.kernel == KIND_DMA) {
+            int n = 0;
+            const void* fn = p.split_tiles > 0 ? sk_fn(in_dtype, out_dtype)
+                                               : dma_variants(&n)[p.variant].fn[in_index(in_dtype)][out_index(out_dtype)];
+            SkArgs ska = sk_args(p, K, ws);
+            // one grid row: the items stacked along the tile rows (stream-K: the persistent grid)
+            int tm = (int)(p.tiles_m * batch), tn = (int)p.tiles_n, gm = p.group_m, itm = (int)p.tiles_m;
+            const unsigned gx = (unsigned)(p.split_tiles > 0 ? p.grid : p.grid * batch);
+            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store, &itm, &sa, &sb, &sc, &ska};
+            e = hipLaunchKernel(fn, dim3(gx), dim3(p.threads), args, 0, s);
+        } else if (p.kernel == KIND_TILED) {
+            const void* fn = in_dtype == GEMM_BT_BF16 ? tiled_fn_out<GEMM_BT_BF16>(out_dtype, p.variant, p.vec)
+                                                      : tiled_fn_out<GEMM_BT_F16>(out_dtype, p.variant, p.vec);
+            int tm = (int)(p.tiles_m * batch), tn = (int)p.tiles_n, gm = p.group_m, itm = (int)p.tiles_m;
+            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store, &itm, &sa, &sb, &sc};
+            e = hipLaunchKernel(fn, dim3((unsigned)(p.grid * batch)), dim3(p.threads), args, 0, s);
+        } else {
+            const void* fn;
+            if (p.variant >= 1) {
+                int n = 0;
+                fn = skinny_variants(&n)[p.variant - 1].fn[in_index(in_dtype)][out_index(out_dtype)];
+            } else {
+                fn = in_dtype == GEMM_BT_BF16 ? skinny_fn_out<GEMM_BT_BF16>(out_dtype, p.vec)
+                                              : skinny_fn_out<GEMM_BT_F16>(out_dtype, p.vec);
+            }
+            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &vec_store, &sa, &sb, &sc};
+            e = hipLaunchKernel(fn, dim3((unsigned)p.grid, gy), dim3(p.threads), args, 0, s);
+        }
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_BT_ERR_LAUNCH;
+    }
+    return GEMM_BT_OK;
+}
+
 }  // namespace gbt
 
 using namespace gbt;
 
 extern "C" {
 
-int gemm_bt_version(void) { return 100; }
+int gemm_bt_version(void) { return 20000; }
 
 const char* gemm_bt_status_string(int status) {
     switch (status) {
@@ -590,19 +778,33 @@ const char* gemm_bt_status_string(int status) {
 
 int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align, int b_align,
                  int c_align, gemm_bt_plan_t* plan) {
-    return plan_impl(1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
+    return plan_impl(1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, plan_cus(), false, plan);
+}
+
+int gemm_bt_plan_ws(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align, int b_align,
+                    int c_align, gemm_bt_plan_t* plan) {
+    return plan_impl(1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, plan_cus(), true, plan);
+}
+
+int gemm_bt_workspace_size(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, size_t* bytes) {
+    if (!bytes) return GEMM_BT_ERR_INVALID_VALUE;
+    *bytes = 0;
+    gemm_bt_plan_t p;
+    const int st = plan_impl(1, M, N, K, in_dtype, out_dtype, 256, 256, 256, plan_cus(), true, &p);
+    if (st == GEMM_BT_OK) *bytes = (size_t)p.workspace_bytes;
+    return st;
 }
 
 int gemm_bt_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
                          int b_align, int c_align, gemm_bt_plan_t* plan) {
-    return plan_impl(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
+    return plan_impl(batch, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, plan_cus(), false, plan);
 }
 
 int gemm_bt_plan_layout(int64_t M, int64_t N, int64_t K, int a_layout, int b_layout, int in_dtype, int out_dtype,
                         int a_align, int b_align, int c_align, gemm_bt_plan_t* plan) {
-    return plan_layout_impl(1, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align, 256, plan);
+    return plan_layout_impl(1, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align,
+                            plan_cus(), plan);
 }
-
 int gemm_bt_layout(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int a_layout, int b_layout,
                    int in_dtype, int out_dtype, void* stream) {
     return gemm_bt_batched_layout(A, B, C, 1, M, N, K, 0, 0, 0, a_layout, b_layout, in_dtype, out_dtype, stream);
@@ -664,8 +866,8 @@ int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch,
 int gemm_bt_plan_batched_layout(int64_t batch, int64_t M, int64_t N, int64_t K, int a_layout, int b_layout,
                                 int in_dtype, int out_dtype, int a_align, int b_align, int c_align,
                                 gemm_bt_plan_t* plan) {
-    return plan_layout_impl(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align, 256,
-                            plan);
+    return plan_layout_impl(batch, M, N, K, a_layout, b_layout, in_dtype, out_dtype, a_align, b_align, c_align,
+                            plan_cus(), plan);
 }
 
 int gemm_bt_tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_m, int64_t* tm, int64_t* tn) {
@@ -677,84 +879,17 @@ int gemm_bt_tile_coord(int64_t pid, int64_t tiles_m, int64_t tiles_n, int group_
 
 int gemm_bt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
             void* stream) {
-    return gemm_bt_batched(A, B, C, 1, M, N, K, 0, 0, 0, in_dtype, out_dtype, stream);
+    return launch_inner(A, B, C, 1, M, N, K, 0, 0, 0, in_dtype, out_dtype, nullptr, 0, stream);
 }
 
 int gemm_bt_batched(const void* A, const void* B, void* C, int64_t batch, int64_t M, int64_t N, int64_t K,
                     int64_t stride_a, int64_t stride_b, int64_t stride_c, int in_dtype, int out_dtype, void* stream) {
-    gemm_bt_plan_t p;
-    if (stride_a < 0 || stride_b < 0 || stride_c < 0) return GEMM_BT_ERR_INVALID_VALUE;
-    const bool multi = batch > 1;
-    const int isz = is_8bit(in_dtype) ? 1 : 2;
-    const int osz = out_size(out_dtype);
-    const int a_al = item_align(A, batch, stride_a, isz), b_al = item_align(B, batch, stride_b, isz),
-              c_al = item_align(C, batch, stride_c, osz);
-    // Plan against the default CU count first: it validates the arguments
-    // without touching the device.
-    int st = plan_impl(batch, M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, 256, &p);
-    if (st != GEMM_BT_OK) return st;
-    if (p.kernel == KIND_NONE) return GEMM_BT_OK;
-    st = check_items(A, B, C, p.kernel, batch, M, N, stride_a, stride_b, stride_c, isz, osz);
-    if (st != GEMM_BT_OK) return st;
+    return launch_inner(A, B, C, batch, M, N, K, stride_a, stride_b, stride_c, in_dtype, out_dtype, nullptr, 0, stream);
+}
 
-    int num_cu = 256;
-    st = check_device(&num_cu);
-    if (st != GEMM_BT_OK) return st;
-    if (num_cu != 256) {
-        st = plan_impl(batch, M, N, K, in_dtype, out_dtype, a_al, b_al, c_al, num_cu, &p);
-        if (st != GEMM_BT_OK) return st;
-    }
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = hipSuccess;
-    int Mi = (int)M, Ni = (int)N, Ki = (int)K;
-    long long sa = multi ? (long long)stride_a * isz : 0, sb = multi ? (long long)stride_b * isz : 0,
-              sc = multi ? (long long)stride_c * osz : 0;
-    const unsigned gy = (unsigned)batch;
-
-    if (p.kernel == KIND_FILL) {
-        u16* c16 = (u16*)C;
-        size_t n16 = (size_t)M * (size_t)N * osz / 2;
-        void* args[] = {&c16, &n16, &sc};
-        e = hipLaunchKernel((const void*)&zero_fill_kernel, dim3((unsigned)p.grid, gy), dim3(p.threads), args, 0, s);
-    } else {
-        const u16* a = (const u16*)A;
-        const u16* b = (const u16*)B;
-        // Vector stores need 4 consecutive outputs inside one row, aligned;
-        // 2 = rows of C are also whole 16-byte chunks (the DMA kernel then
-        // stores through LDS, whole rows per instruction).
-        int vec_store = (N % 4 == 0) && c_al >= 4 * osz ? 1 : 0;
-        if (vec_store && (N * osz) % 16 == 0 && c_al >= 16) vec_store = 2;
-        if (p.kernel == KIND_TILED || p.kernel == KIND_DMA) {
-            const void* fn;
-            if (p.kernel == KIND_DMA) {
-                int n = 0;
-                fn = dma_variants(&n)[p.variant].fn[in_index(in_dtype)][out_index(out_dtype)];
-            } else {
-                fn = in_dtype == GEMM_BT_BF16 ? tiled_fn_out<GEMM_BT_BF16>(out_dtype, p.variant, p.vec)
-                                              : tiled_fn_out<GEMM_BT_F16>(out_dtype, p.variant, p.vec);
-            }
-            // one grid row: the items stacked along the tile rows
-            int tm = (int)(p.tiles_m * batch), tn = (int)p.tiles_n, gm = p.group_m, itm = (int)p.tiles_m;
-            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store, &itm, &sa, &sb, &sc};
-            e = hipLaunchKernel(fn, dim3((unsigned)(p.grid * batch)), dim3(p.threads), args, 0, s);
-        } else {
-            const void* fn;
-            if (p.variant >= 1) {
-                int n = 0;
-                fn = skinny_variants(&n)[p.variant - 1].fn[in_index(in_dtype)][out_index(out_dtype)];
-            } else {
-                fn = in_dtype == GEMM_BT_BF16 ? skinny_fn_out<GEMM_BT_BF16>(out_dtype, p.vec)
-                                              : skinny_fn_out<GEMM_BT_F16>(out_dtype, p.vec);
-            }
-            void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &vec_store, &sa, &sb, &sc};
-            e = hipLaunchKernel(fn, dim3((unsigned)p.grid, gy), dim3(p.threads), args, 0, s);
-        }
-    }
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return GEMM_BT_ERR_LAUNCH;
-    }
-    return GEMM_BT_OK;
+int gemm_bt_ws(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+    return launch_inner(A, B, C, 1, M, N, K, 0, 0, 0, in_dtype, out_dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

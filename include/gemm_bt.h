@@ -27,9 +27,10 @@
  * (else UNSUPPORTED).  int8 inputs also need K <= 131071, so that no sum can
  * leave the int32 range (|A[i][k] * B[j][k]| <= 2^14).
  *
- * Ownership.  The caller owns A, B and C (device memory, e.g. from PyTorch).
- * The library allocates nothing per call, keeps no pointer after it returns
- * and holds no state beyond a per-device cache of device attributes.
+ * Ownership.  The caller owns A, B and C (device memory, e.g. from PyTorch),
+ * and the workspace of gemm_bt_ws.  The library allocates nothing per call,
+ * keeps no pointer after it returns and holds no state beyond a per-device
+ * cache of device attributes.
  *
  * Asynchrony and errors.  gemm_bt enqueues its kernel on `stream` and returns
  * without waiting.  Argument errors are reported before anything is
@@ -40,6 +41,7 @@
 #ifndef GEMM_BT_H
 #define GEMM_BT_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -144,6 +146,42 @@ int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch,
                            int64_t stride_a, int64_t stride_b, int64_t stride_c, int a_layout, int b_layout,
                            int in_dtype, int out_dtype, void* stream);
 
+/*
+ * C = A * B^T with a caller-provided workspace that lets the library split
+ * the K range of output tiles over workgroups (stream-K: "Writing Mosaic GPU
+ * kernels with Pallas", section "Cluster launch control", a persistent grid
+ * with one workgroup per core that keeps every core busy to the end).  Where
+ * the plain grid would leave compute units idle in its last wave of tiles
+ * (e.g. 1000 x 3000 outputs in 192 tiles of 128 x 128 for 256 compute
+ * units), a persistent grid of one workgroup per compute unit gives every
+ * workgroup the same number of K steps; a tile computed in pieces by several
+ * workgroups is added up by the last of them to finish, in K order, so the
+ * result is the same bits on every run with the same sizes on the same
+ * device.  The sum of each output is then formed in a different order than
+ * gemm_bt's (pieces summed in fp32, then added), with the same accuracy
+ * bound.  Where splitting does not pay, the call is exactly gemm_bt.
+ *   A, B, C, M, N, K, in_dtype, out_dtype, stream: as for gemm_bt
+ *   workspace        device memory of at least workspace_bytes, 16-byte
+ *                    aligned, owned by the caller, or NULL (then the call is
+ *                    gemm_bt).  Its first 16 KiB must hold zeros before the
+ *                    first call that uses it (e.g. hipMemset once after
+ *                    allocation); every call leaves them zero again, so one
+ *                    workspace serves any number of later calls with no
+ *                    clearing.  Calls that share a workspace must not run
+ *                    concurrently (one stream, or ordered by events).
+ *   workspace_bytes  its size; smaller than gemm_bt_workspace_size reports for
+ *                    these sizes: INVALID_VALUE (nothing enqueued)
+ * Everything else (sizes, dtypes, K == 0, alignment, errors) is as for gemm_bt.
+ */
+int gemm_bt_ws(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype,
+               int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace gemm_bt_ws needs for these sizes and types (0 when it runs the
+   plain grid), for the current device (256 compute units without one).  At
+   most 16 KiB + 2 * 256 * 64 KiB (32.02 MiB) on an MI355X, whatever the
+   sizes.  Returns gemm_bt's status for invalid arguments. */
+int gemm_bt_workspace_size(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, size_t* bytes);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* gemm_bt_status_string(int status);
 
@@ -151,10 +189,12 @@ const char* gemm_bt_status_string(int status);
 int gemm_bt_version(void);
 
 /*
- * Launch plan: which kernel and tile shape gemm_bt would use for a problem.
- * Host-only (no device call); lets callers and tests see the tiling and the
- * grid.  `a_align`, `b_align`, `c_align` are the byte alignments of the
- * pointers that would be passed (e.g. 256 for fresh allocations).
+ * Launch plan: which kernel and tile shape gemm_bt would use for a problem;
+ * lets callers and tests see the tiling and the grid.  No kernel runs.  The
+ * plan is made for the current device's compute-unit count when it is a
+ * gfx950 (one cached device query), else for 256 (an MI355X).  `a_align`,
+ * `b_align`, `c_align` are the byte alignments of the pointers that would be
+ * passed (e.g. 256 for fresh allocations).
  */
 typedef struct {
     int kernel;       /* 0 = none (empty), 1 = zero fill (K == 0), 2 = LDS-tiled MFMA with register-staged
@@ -171,12 +211,21 @@ typedef struct {
                          its ring of single-operand tiles */
     int lds_bytes;    /* LDS per workgroup */
     int64_t tiles_m, tiles_n;
-    int64_t grid;     /* workgroups per batch item (grid * batch are launched) */
+    int64_t grid;     /* workgroups per batch item (grid * batch are launched); for a split plan the
+                         workgroups of the one launch (split_tiles * pieces per tile) */
     int64_t batch;    /* batch items (1 for gemm_bt) */
+    int64_t split_tiles;     /* split plan: tiles whose K range is split over several workgroups (0: one
+                                workgroup per tile) */
+    int64_t workspace_bytes; /* workspace the plan needs (0 unless split_tiles > 0) */
 } gemm_bt_plan_t;
 
 int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
                  int b_align, int c_align, gemm_bt_plan_t* plan);
+
+/* The plan of gemm_bt_ws given a large enough workspace (the plan gemm_bt_ws
+   runs when its workspace is not NULL). */
+int gemm_bt_plan_ws(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
+                    int b_align, int c_align, gemm_bt_plan_t* plan);
 
 /* The plan of gemm_bt_layout (for kernel 5 the variant is 0: A K-outer, 1: B
    K-outer, 2: both, on 128 x 128 tiles; 3, 4, 5 the same on 256 x 256 tiles). */

@@ -35,13 +35,14 @@ def to_dev(bits, in_dtype):
     return t.to("cuda").view(TORCH_DT[in_dtype])
 
 
-def run_gpu(gb, a_bits, b_bits, in_dtype, out_dtype):
+def run_gpu(gb, a_bits, b_bits, in_dtype, out_dtype, split_k=False):
+    """C through gemm_bt (split_k=False) or through mm_bt's default path, gemm_bt_ws where the plan splits K."""
     a = to_dev(a_bits, in_dtype)
     b = to_dev(b_bits, in_dtype)
     M, N = a.shape[0], b.shape[0]
     poison = I32_POISON if out_dtype == "i32" else float("nan")
     c = torch.full((M, N), poison, dtype=TORCH_DT[out_dtype], device="cuda")
-    gb.mm_bt(a, b, out_dtype=TORCH_DT[out_dtype], out=c)
+    gb.mm_bt(a, b, out_dtype=TORCH_DT[out_dtype], out=c, split_k=split_k)
     torch.cuda.synchronize()
     return c.cpu()
 
@@ -249,7 +250,7 @@ def test_workload_full_size(gpu, name):
     if w.b_layout:
         c = run_layout(gpu, a, b, 0, w.b_layout, w.in_dtype, w.out_dtype)
     else:
-        c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
+        c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype, split_k=True)  # the entry point the benchmark times
     if w.in_dtype == "i8":
         I, J = sample_entries(w.M, w.N, np.random.default_rng(w.seed))
         check_i8(c, a, b, name, I, J)
@@ -284,7 +285,7 @@ def test_workload_integer_twin_bit_exact(gpu, name):
     if w.b_layout:
         c = run_layout(gpu, a, b, 0, w.b_layout, w.in_dtype, w.out_dtype)
     else:
-        c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype)
+        c = run_gpu(gpu, a, b, w.in_dtype, w.out_dtype, split_k=True)  # the entry point the benchmark times
     if w.in_dtype == "i8":
         I, J = sample_entries(w.M, w.N, np.random.default_rng(w.seed))
         check_i8(c, a, b, w.name, I, J)
@@ -793,3 +794,102 @@ def test_c_program_through_the_header(gpu):
     say("C program", exe)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("c_abi_check ok"), (r.returncode, r.stdout, r.stderr)
+
+
+# ---------------------------------------------------------------- stream-K (gemm_bt_ws)
+# Shapes the split plan takes on 256 CUs (at most 128 tiles of 128x128, each
+# split along K into S = 256 // tiles pieces of at least 32 K steps): 4-way
+# (1024x1024), 8-way with f16 out, 4-way with ragged tile edges and a partial
+# last K step, 14-way with a K tail (the last to arrive usually reads its own
+# piece back), C rows of 8-byte (direct 8-byte stores) and 2-byte alignment
+# (element stores), one tile row (M = 64), and 2-way.
+SK_CASES = [  # (M, N, K, in, out)
+    (1024, 1024, 16384, "bf16", "bf16"), (512, 1024, 32768, "f16", "f16"), (1000, 1000, 8200, "bf16", "f32"),
+    (300, 700, 30002, "bf16", "f32"), (130, 4100, 8192, "f16", "f16"), (200, 1999, 17000, "bf16", "f32"),
+    (64, 8192, 8192, "bf16", "bf16"), (1024, 2048, 8192, "f16", "f32"),
+]
+
+
+def run_ws(gb, a_bits, b_bits, in_dtype, out_dtype, ws=None):
+    """C through gemm_bt_ws with a zeroed workspace (or `ws`); returns (C on the host, workspace)."""
+    a = to_dev(a_bits, in_dtype)
+    b = to_dev(b_bits, in_dtype)
+    M, K = a.shape
+    N = b.shape[0]
+    ic, oc = gb._torch_code(a.dtype), gb._torch_code(TORCH_DT[out_dtype])
+    nbytes = gb.gemm_bt_workspace_size(M, N, K, ic, oc)
+    if ws is None:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=TORCH_DT[out_dtype], device="cuda")
+    st = gb.gemm_bt_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, ic, oc, ws.data_ptr(), ws.numel(),
+                       torch.cuda.current_stream().cuda_stream)
+    assert st == gb.OK, gb.status_string(st)
+    torch.cuda.synchronize()
+    return c.cpu(), ws
+
+
+@pytest.mark.parametrize("case", range(len(SK_CASES)))
+def test_stream_k(gpu, case):
+    M, N, K, ind, outd = SK_CASES[case]
+    plan = gpu.gemm_bt_plan_ws(M, N, K, gpu._torch_code(TORCH_DT[ind]), gpu._torch_code(TORCH_DT[outd]))
+    say("split-K", M, N, K, ind, outd, "grid", plan.grid, "split tiles", plan.split_tiles)
+    assert plan.split_tiles > 0, "the case must take the split plan"
+    a, b = synth.make(M, N, K, ind, "normal", 1500 + case)
+    c, ws = run_ws(gpu, a, b, ind, outd)
+    check_full(c, a, b, ind, outd, ("split-K", M, N, K))
+    # the counters are back to zero, and a second call through the same
+    # workspace gives the same bits (fixed summation order, any arrival order)
+    assert int(ws[:gpu.SK_COUNTER_BYTES].count_nonzero()) == 0
+    c2, _ = run_ws(gpu, a, b, ind, outd, ws)
+    assert torch.equal(out_bits_t(c), out_bits_t(c2)), "split result differs between runs"
+    ai, bi = synth.make(M, N, K, ind, "int", 1600 + case)
+    ci, _ = run_ws(gpu, ai, bi, ind, outd, ws)
+    check_bits_full(ci, ai, bi, ind, outd, ("split-K int", M, N, K))
+
+
+def out_bits_t(c):
+    return c.view(torch.int32) if c.dtype == torch.float32 else c.view(torch.int16)
+
+
+def test_stream_k_fallback_and_refusals(gpu):
+    """Shapes the plan does not split run gemm_bt exactly; a short workspace is refused before any launch."""
+    for (M, N, K) in [(4096, 4096, 256), (300, 260, 200), (16, 1000, 520), (1000, 3000, 2050), (1024, 1024, 4096)]:
+        say("ws fallback", M, N, K)
+        a, b = synth.make(M, N, K, "bf16", "normal", 77)
+        assert gpu.gemm_bt_workspace_size(M, N, K, gpu.BF16, gpu.BF16) == 0
+        c_ws, _ = run_ws(gpu, a, b, "bf16", "bf16")
+        c = run_gpu(gpu, a, b, "bf16", "bf16")
+        assert torch.equal(out_bits_t(c_ws), out_bits_t(c))
+    M, N, K = 1024, 1024, 16384
+    need = gpu.gemm_bt_workspace_size(M, N, K, gpu.BF16, gpu.F32)
+    assert need > 0
+    a = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
+    c = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert gpu.gemm_bt_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, gpu.BF16, gpu.F32, ws.data_ptr(),
+                          need - 1, s) == gpu.ERR_INVALID_VALUE
+    assert gpu.gemm_bt_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, gpu.BF16, gpu.F32, ws.data_ptr() + 4,
+                          need - 4, s) == gpu.ERR_INVALID_VALUE
+    torch.cuda.synchronize()
+    assert bool((c == 7.0).all()), "a refused call wrote C"
+    # a NULL workspace is gemm_bt
+    assert gpu.gemm_bt_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, gpu.BF16, gpu.F32, 0, 0, s) == gpu.OK
+    torch.cuda.synchronize()
+    assert bool((c == 0).all())
+
+
+def test_mm_bt_split_k_default(gpu):
+    """mm_bt takes the split path by default (per-stream workspace) and matches the oracle."""
+    M, N, K = 512, 1024, 32768
+    assert gpu.gemm_bt_workspace_size(M, N, K, gpu.BF16, gpu.F32) > 0
+    a_bits, b_bits = synth.make(M, N, K, "bf16", "normal", 3)
+    a, b = to_dev(a_bits, "bf16"), to_dev(b_bits, "bf16")
+    c = gpu.mm_bt(a, b, out_dtype=torch.float32)
+    c_plain = gpu.mm_bt(a, b, out_dtype=torch.float32, split_k=False)
+    torch.cuda.synchronize()
+    check_full(c.cpu(), a_bits, b_bits, "bf16", "f32", "mm_bt split")
+    check_full(c_plain.cpu(), a_bits, b_bits, "bf16", "f32", "mm_bt plain")
+    ws = gpu.workspace_for(a.device, torch.cuda.current_stream().cuda_stream, 0)
+    assert int(ws[:gpu.SK_COUNTER_BYTES].count_nonzero()) == 0
