@@ -18,6 +18,7 @@ Entry points (same names as the C-ABI in ``include/gemm_bt.h``):
   gemm_bt_tile_coord(pid, tiles_m, tiles_n, group_m)
   gemm_bt_ws(A, B, C, M, N, K, in_dtype, out_dtype, workspace, workspace_bytes, stream)   stream-K
   gemm_bt_workspace_size(M, N, K, in_dtype, out_dtype), gemm_bt_plan_ws(M, N, K, in_dtype, out_dtype, ...)
+  gemm_bt_noalloc(A, B, C, M, N, K, in_dtype, out_dtype, stream)   gemm_bt_ws with the library's scratch
 and torch convenience wrappers ``mm_bt(a, b, out_dtype)`` (2-D or batched 3-D operands),
 ``mm_layout(a, b, a_layout, b_layout, out_dtype)`` and ``mm(a, b, out_dtype)`` (= a @ b).
 """
@@ -36,7 +37,7 @@ LIB_PATH = os.path.join(_HERE, "libgemm_bt.so")
 EXPORTS = ("gemm_bt", "gemm_bt_batched", "gemm_bt_layout", "gemm_bt_batched_layout", "gemm_bt_status_string",
            "gemm_bt_version", "gemm_bt_plan", "gemm_bt_plan_batched", "gemm_bt_plan_layout",
            "gemm_bt_plan_batched_layout", "gemm_bt_tile_coord", "gemm_bt_ws", "gemm_bt_workspace_size",
-           "gemm_bt_plan_ws")
+           "gemm_bt_plan_ws", "gemm_bt_noalloc")
 SK_COUNTER_BYTES = 16384  # leading counter area of a gemm_bt_ws workspace (zero between calls)
 
 _lock = threading.Lock()
@@ -100,6 +101,8 @@ def load():
             lib.gemm_bt_workspace_size.restype = ci
             lib.gemm_bt_plan_ws.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             lib.gemm_bt_plan_ws.restype = ci
+            lib.gemm_bt_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+            lib.gemm_bt_noalloc.restype = ci
             _lib = lib
     return _lib
 
@@ -183,6 +186,12 @@ def gemm_bt_ws(A: int, B: int, C: int, M: int, N: int, K: int, in_dtype: int, ou
     """Raw stream-K call with a caller workspace (device pointer, bytes); returns the status code."""
     return int(load().gemm_bt_ws(A or None, B or None, C or None, M, N, K, in_dtype, out_dtype, workspace or None,
                                  workspace_bytes, stream or None))
+
+
+def gemm_bt_noalloc(A: int, B: int, C: int, M: int, N: int, K: int, in_dtype: int, out_dtype: int,
+                    stream: int | None) -> int:
+    """Raw call of gemm_bt_ws with the library's own scratch (allocates nothing); returns the status code."""
+    return int(load().gemm_bt_noalloc(A or None, B or None, C or None, M, N, K, in_dtype, out_dtype, stream or None))
 
 
 def gemm_bt_workspace_size(M, N, K, in_dtype, out_dtype) -> int:

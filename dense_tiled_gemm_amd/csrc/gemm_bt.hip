@@ -166,6 +166,17 @@ static const void* sk_fn(int in_dtype, int out_dtype) {
 constexpr int64_t kSkCounterBytes = 16384;
 constexpr int64_t kSkMaxTiles = kSkCounterBytes / 4;
 
+// Scratch of gemm_bt_noalloc: the workspace of the largest split plan on a
+// device of up to 256 CUs (counters, then two 128 x 128 fp32 slots per
+// workgroup of a grid of at most 256), as a device array of the library's own.
+// Every GPU the library runs on holds one copy (32.02 MiB) until the process
+// ends.  It is zero when the code object is loaded, and every call leaves its
+// counter area zero again.  Host code must not pass `scratch` itself to a
+// kernel (on the host it names a stand-in, not device memory): it uses the
+// per-device address from hipGetSymbolAddress (noalloc_scratch below).
+constexpr int64_t kScratchBytes = kSkCounterBytes + 2 * 256 * 128 * 128 * 4;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // Skinny DMA-kernel variants [in][out]; index 0 is the default.
 struct SkinnyVariant {
     const char* name;
@@ -616,6 +627,27 @@ static int check_device(int* num_cu) {
     return GEMM_BT_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU has its own copy at its own
+// address).  NULL when the lookup fails.
+static std::atomic<void*> g_scratch_ptr[kMaxDev];
+static void* noalloc_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
+
 static int align_of(const void* p) {
     const uintptr_t v = (uintptr_t)p;
     if (v % 16 == 0) return 16;
@@ -890,6 +922,24 @@ int gemm_bt_batched(const void* A, const void* B, void* C, int64_t batch, int64_
 int gemm_bt_ws(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
                void* workspace, size_t workspace_bytes, void* stream) {
     return launch_inner(A, B, C, 1, M, N, K, 0, 0, 0, in_dtype, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int gemm_bt_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype,
+                    int out_dtype, void* stream) {
+    gemm_bt_plan_t p;
+    int st = plan_impl(1, M, N, K, in_dtype, out_dtype, 256, 256, 256, plan_cus(), true, &p);
+    if (st != GEMM_BT_OK) return st;
+    if (p.workspace_bytes > kScratchBytes) return GEMM_BT_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    if (p.workspace_bytes > 0) {
+        int num_cu = 0;
+        st = check_device(&num_cu);  // a gfx950 must be current before its scratch is looked up
+        if (st != GEMM_BT_OK) return st;
+        ws = noalloc_scratch();
+        if (!ws) return GEMM_BT_ERR_NO_DEVICE;
+    }
+    return launch_inner(A, B, C, 1, M, N, K, 0, 0, 0, in_dtype, out_dtype, ws, ws ? (size_t)kScratchBytes : 0,
+                        stream);
 }
 
 }  // extern "C"

@@ -176,6 +176,25 @@ int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch,
 int gemm_bt_ws(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype,
                int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gemm_bt_ws without a workspace argument, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the split plan's counters and partial sums live in a scratch
+ * array of the library's own in device memory, 16 KiB + 32 MiB (the largest
+ * split plan on a GPU of up to 256 compute units), one copy per GPU, held
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  Same arguments, plan, kernels and results as
+ * gemm_bt_ws with a large enough workspace (bit for bit); where no split is
+ * planned it is gemm_bt.  A plan that would need more scratch than that
+ * (more than 256 compute units): UNSUPPORTED, nothing enqueued.  All calls on
+ * one GPU share its scratch, whose counters are zero when the library is
+ * loaded and are left zero by every call: calls that overlap in time on one
+ * GPU (different streams, or concurrent host threads without ordering) race
+ * on it and must not be issued.
+ */
+int gemm_bt_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype,
+                    int out_dtype, void* stream);
+
 /* Workspace gemm_bt_ws needs for these sizes and types (0 when it runs the
    plain grid), for the current device (256 compute units without one).  At
    most 16 KiB + 2 * 256 * 64 KiB (32.02 MiB) on an MI355X, whatever the
