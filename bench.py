@@ -4,19 +4,31 @@
 One step = one gemm_bt call on the 4096×4096×4096 bf16 workload (A and B
 i.i.d. N(0,1) rounded to bf16, seed 2, bf16 output), inputs resident in HBM.
 Prints ONE JSON line on stdout:
-  value        TFLOP/s of the whole job (2·M·N·K per step / step time)
-  roofline     the tiled MFMA kernel against the MI355X dense bf16 peak
-  cpu_baseline the CPU oracle timed on a bounded sample of the same product
-  secondary    µs / TFLOP/s / GB/s of the other workloads (1024×4096×4096
-               f16, 16×8192×8192 skinny, 512³, 1000×3000×2050, 4096³ with
-               E4M3 inputs against the fp8 peak, 4096³ int8 -> int32
-               against the int8 peak, a batch of 64 products of 512³ in one
-               gemm_bt_batched call, and 4096³ with B stored K×N through
-               gemm_bt_layout), same timing
+  value        TFLOP/s of the whole job (2·M·N·K per step / wall time of the
+               K timed steps between two synchronisations)
+  timing       per-launch HIP-event times of the timed steps (median, min,
+               max, p10, p90, mean) and the untimed settle phase before them
+  clock        the GPU clock (per-XCD gfxclk) and socket power of the first
+               amdsmi metrics snapshot the firmware takes under continued
+               launches of the workload after the timed steps (the table
+               refreshes about once per second), and % of peak at that clock
+  roofline     the tiled MFMA kernel against the MI355X dense bf16 peak;
+               achieved = 2·M·N·K / the median launch time
+  cpu_baseline the CPU oracle timed on a bounded sample of the same product,
+               with the host's CPU model and core counts
+  secondary    the other workloads (1024×4096×4096 f16, 16×8192×8192
+               skinny, 512³, 1000×3000×2050, 4096³ with E4M3 inputs against
+               the fp8 peak, 4096³ int8 -> int32 against the int8 peak, a
+               batch of 64 products of 512³ in one gemm_bt_batched call,
+               4096³ with B stored K×N through gemm_bt_layout, and
+               1024×1024×16384, which gemm_bt_ws splits along K), timed the
+               same way (median launch)
   copy_GBps    a plain 1 GiB device copy, as context for achievable HBM
-Diagnostics go to stderr.  The default 400 untimed warm-up launches matter:
-from idle, an MI355X needs about 25 ms of sustained GEMM launches before its
-clocks settle, and launches inside that ramp run up to 15% slower.
+Diagnostics go to stderr.  Whatever --warmup is, the timed steps follow an
+untimed settle phase that runs launches until their time stops falling
+(bounded at 0.5 s): from idle an MI355X needs about 25 ms of sustained GEMM
+launches before its clocks settle, and launches inside that ramp run up to
+15% slower.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
   python bench.py --mode copy     # plain device copy of known size (counter calibration)
@@ -27,7 +39,9 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +83,101 @@ def load_traffic(workload: str):
     return ent.get("bytes_per_launch")
 
 
+class ClockSampler:
+    """amdsmi gpu_metrics snapshots on a background thread: (host time, firmware timestamp, per-XCD gfxclk MHz,
+    socket W).  The firmware refreshes the table about once per second (measured on the MI355X boxes: one
+    refresh in 1.5 s of polling), so a snapshot describes the GPU at its own refresh time, not at the time it
+    is read.  Records nothing (and says why) when amdsmi is missing or refuses."""
+
+    def __init__(self, period_s=0.002):
+        self.samples = []
+        self.error = None
+        self.period = period_s
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self.samples.append(self._read())
+        except Exception as e:  # no amdsmi, no permission, no device: the bench still runs
+            self.error = repr(e)
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)]
+        if not clks and isinstance(m.get("current_gfxclk"), int):
+            clks = [m["current_gfxclk"]]
+        pw = m.get("current_socket_power")
+        fw = m.get("firmware_timestamp")
+        return (time.perf_counter(), fw if isinstance(fw, int) else None, clks, pw if isinstance(pw, int) else None)
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:
+                self.error = repr(e)
+                return
+            time.sleep(self.period)
+
+    def start(self):
+        if self.error is None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def fresh_after(self, t):
+        """The first snapshot the firmware took after host time t (its firmware timestamp differs from that
+        of every sample read up to t), or None."""
+        before = {x[1] for x in self.samples if x[0] <= t}
+        for x in list(self.samples):
+            if x[0] > t and x[1] not in before:
+                return x
+        return None
+
+
+def clock_under_load(case, sampler, t_end, tflops, max_s=1.5):
+    """The GPU clock under this workload: launches continue (untimed) after the timed steps until the
+    firmware publishes a metrics snapshot taken after them, at most `max_s`; that snapshot's per-XCD gfxclk
+    and socket power are reported, with the % of peak at the median clock."""
+    if sampler.error is not None and not sampler.samples:
+        return {"source": "amdsmi", "error": sampler.error}
+    torch = case.torch
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    snap, n = None, 0
+    while snap is None and time.perf_counter() - t0 < max_s:
+        for i in range(20):
+            case.step(n + i, stream.cuda_stream)
+        n += 20
+        stream.synchronize()
+        snap = sampler.fresh_after(t_end)
+    if snap is None:
+        return {"source": "amdsmi", "error": "no fresh metrics snapshot within %.1f s of load" % max_s}
+    clks = sorted(snap[2])
+    med = clks[len(clks) // 2]
+    peak_at = PEAK_BF16_TFLOPS * med / 2400.0  # 256 CU x 4096 FLOP/clk x sclk
+    return {"source": "amdsmi gpu_metrics snapshot taken by the firmware under continued launches of the same "
+                      "workload right after the timed steps (the table refreshes about once per second)",
+            "sclk_mhz": med, "sclk_mhz_per_xcd": snap[2], "socket_power_w": snap[3],
+            "snapshot_after_timed_ms": round((snap[0] - t_end) * 1e3, 1), "extra_launches": n,
+            "peak_at_sclk_tflops": round(peak_at, 1), "pct_of_peak_at_sclk": round(100.0 * tflops / peak_at, 2)}
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
+
+
 class Case:
     """Device-resident inputs (rotated copies) for one workload."""
 
@@ -103,6 +212,19 @@ class Case:
                         "i8": gb.INT8}[w.in_dtype]
         self.out_code = {"f32": gb.F32, "bf16": gb.BF16, "f16": gb.F16, "i32": gb.INT32}[w.out_dtype]
         self.ptrs = [(x.data_ptr(), y.data_ptr(), z.data_ptr()) for x, y, z in self.sets]
+        # a single product goes through gemm_bt_ws (the entry point of mm_bt), which splits K where the plan
+        # says so; its workspace is allocated and zeroed here, outside the timed region
+        self.ws_bytes = 0
+        if not w.b_layout and w.batch == 1:
+            self.ws_bytes = gb.gemm_bt_workspace_size(w.M, w.N, w.K, self.in_code, self.out_code)
+        self.ws = torch.zeros(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        if not w.b_layout and w.batch == 1:
+            self.plan = gb.gemm_bt_plan_ws(w.M, w.N, w.K, self.in_code, self.out_code).as_dict()
+        elif w.b_layout:
+            self.plan = gb.gemm_bt_plan_layout(w.M, w.N, w.K, gb.K_INNER, w.b_layout, self.in_code,
+                                               self.out_code).as_dict()
+        else:
+            self.plan = gb.gemm_bt_plan_batched(w.batch, w.M, w.N, w.K, self.in_code, self.out_code).as_dict()
         torch.cuda.synchronize()
 
     def step(self, i, stream):
@@ -114,29 +236,89 @@ class Case:
         elif w.batch > 1:
             st = self.gb.gemm_bt_batched(pa, pb, pc, w.batch, w.M, w.N, w.K, w.M * w.K, w.N * w.K, w.M * w.N,
                                          self.in_code, self.out_code, stream)
+        elif self.ws_bytes:
+            st = self.gb.gemm_bt_ws(pa, pb, pc, w.M, w.N, w.K, self.in_code, self.out_code, self.ws.data_ptr(),
+                                    self.ws_bytes, stream)
         else:
             st = self.gb.gemm_bt(pa, pb, pc, w.M, w.N, w.K, self.in_code, self.out_code, stream)
         if st != self.gb.OK:
             raise self.gb.GemmBtError(st)
 
-    def time(self, steps, warmup):
-        """Returns (wall seconds for `steps` calls, event-measured ms per call)."""
+    def settle(self, stream, batch=25, max_s=0.5, max_launches=4000, patience=3):
+        """Untimed launches until the per-launch time stops falling: batches of `batch` launches, stopping after
+        `patience` batches in a row that are no more than 0.5 % faster than the best so far, or at the bounds.
+        Returns (launches, ms)."""
+        torch = self.torch
+        sh = stream.cuda_stream
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        best, stale, n = float("inf"), 0, 0
+        while True:
+            e0.record(stream)
+            for i in range(batch):
+                self.step(n + i, sh)
+            e1.record(stream)
+            e1.synchronize()
+            n += batch
+            per = e0.elapsed_time(e1) / batch
+            if per < best * 0.995:
+                best, stale = per, 0
+            else:
+                stale += 1
+            if stale >= patience or time.perf_counter() - t0 > max_s or n >= max_launches:
+                break
+        return n, (time.perf_counter() - t0) * 1e3
+
+    def time(self, steps, warmup, sampler=None):
+        """`warmup` untimed steps, the settle phase, then `steps` timed steps, each bracketed by HIP events on
+        the launch stream (torch's current stream).  Returns a dict: wall seconds of the timed steps (between
+        two synchronisations), per-launch ms, the settle phase, and the host-clock window of the timed steps."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         sh = stream.cuda_stream
         for i in range(warmup):
             self.step(i, sh)
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        settle_n, settle_ms = self.settle(stream)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        e0.record(stream)
+        ev[0].record(stream)
         for i in range(steps):
             self.step(i, sh)
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        return t1 - t0, e0.elapsed_time(e1) / steps
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return {"wall_s": t1 - t0, "per_ms": per, "settle_launches": settle_n, "settle_ms": settle_ms,
+                "t0": t0, "t1": t1}
+
+
+def timing_record(r):
+    per_us = [x * 1e3 for x in r["per_ms"]]
+    return {"launches": len(per_us), "median_us": round(percentile(per_us, 0.5), 3),
+            "min_us": round(min(per_us), 3), "max_us": round(max(per_us), 3),
+            "p10_us": round(percentile(per_us, 0.1), 3), "p90_us": round(percentile(per_us, 0.9), 3),
+            "mean_us": round(sum(per_us) / len(per_us), 3), "settle_launches": r["settle_launches"],
+            "settle_ms": round(r["settle_ms"], 1)}
+
+
+def cpu_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity}
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -158,9 +340,11 @@ def cpu_baseline(w, target_s=12.0):
     oracle.gemm_bt_ref(a_bits[:rows], b_bits, w.in_dtype)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "rows 0..%d of the %dx%dx%d %s product (%.3g multiply-adds, fp64 triple loop, %d OpenMP "
-                      "threads), %.2f s" % (rows - 1, w.M, w.N, w.K, w.in_dtype, rows * w.N * w.K, threads, dt)}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": "rows 0..%d of the %dx%dx%d %s product (%.3g multiply-adds, fp64 triple loop, %d OpenMP "
+                     "threads), %.2f s" % (rows - 1, w.M, w.N, w.K, w.in_dtype, rows * w.N * w.K, threads, dt)}
+    rec.update(cpu_info())
+    return rec
 
 
 def copy_rate(torch, n=1 << 30, reps=10):
@@ -235,14 +419,20 @@ def main():
     w = synth.WORKLOADS[args.workload]
     log("workload", w)
     case = Case(w, torch, gb, args.rotate)
-    plan = gb.gemm_bt_plan(w.M, w.N, w.K, case.in_code, case.out_code).as_dict()
-    log("plan", plan, "rotate", case.rotate)
-    wall, ev_ms = case.time(args.steps, args.warmup)
-    ms_per_step = wall / args.steps * 1e3
+    plan = case.plan
+    log("plan", plan, "rotate", case.rotate, "device CUs", torch.cuda.get_device_properties(0).multi_processor_count)
+    sampler = ClockSampler().start()
+    r = case.time(args.steps, args.warmup)
+    ms_per_step = r["wall_s"] / args.steps * 1e3
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (ev_ms * 1e-3) / 1e12
-    log("wall ms/step %.4f  event ms/launch %.4f  TFLOP/s %.1f (event %.1f)" % (ms_per_step, ev_ms, tflops,
-                                                                                achieved))
+    timing = timing_record(r)
+    achieved = w.flops / (timing["median_us"] * 1e-6) / 1e12
+    clock = clock_under_load(case, sampler, r["t1"], achieved)
+    sampler.stop()
+    log("wall ms/step %.4f  median launch %.3f us (min %.3f, p90 %.3f)  TFLOP/s %.1f (median launch %.1f)  settle "
+        "%d launches / %.1f ms  clock %s" % (ms_per_step, timing["median_us"], timing["min_us"], timing["p90_us"],
+                                             tflops, achieved, timing["settle_launches"], timing["settle_ms"],
+                                             clock))
     traffic = load_traffic(w.name)
     out = {
         "metric": METRIC,
@@ -262,6 +452,8 @@ def main():
                    "tile": [plan["bm"], plan["bn"], plan["bk"]], "threads": plan["threads"],
                    "grid": plan["grid"], "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "timing": timing,
+        "clock": clock,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
@@ -269,13 +461,19 @@ def main():
         sec = {}
         for name in ("m1024_n4096_k4096_f16_f16", "skinny_m16_n8192_k8192_bf16_bf16", "sq512_bf16_f32",
                      "ragged_m1000_n3000_k2050_bf16_f32", "sq4096_e4m3_bf16", "sq4096_i8_i32",
-                     "batch64_sq512_bf16_bf16", "sq4096_nn_bf16_bf16"):
+                     "batch64_sq512_bf16_bf16", "sq4096_nn_bf16_bf16", "splitk_m1024_n1024_k16384_bf16_bf16"):
             w2 = synth.WORKLOADS[name]
             c2 = Case(w2, torch, gb)
-            _, ms2 = c2.time(max(50, args.steps // 2), args.warmup)
-            ent = {"us": round(ms2 * 1e3, 3), "TFLOP/s": round(w2.flops / (ms2 * 1e-3) / 1e12, 2),
-                   "GB/s": round(w2.compulsory_bytes / (ms2 * 1e-3) / 1e9, 1),
-                   "rotated_input_sets": c2.rotate}
+            r2 = c2.time(max(50, args.steps // 2), args.warmup)
+            t2 = timing_record(r2)
+            us = t2["median_us"]
+            ent = {"us": us, "min_us": t2["min_us"], "p90_us": t2["p90_us"],
+                   "TFLOP/s": round(w2.flops / (us * 1e-6) / 1e12, 2),
+                   "GB/s": round(w2.compulsory_bytes / (us * 1e-6) / 1e9, 1),
+                   "rotated_input_sets": c2.rotate, "tile": [c2.plan["bm"], c2.plan["bn"], c2.plan["bk"]],
+                   "grid": c2.plan["grid"]}
+            if c2.plan.get("split_tiles"):
+                ent["split_tiles"] = c2.plan["split_tiles"]
             if name.startswith("skinny"):
                 ent["frac_hbm"] = round(ent["GB/s"] / PEAK_HBM_GBS, 4)
             elif w2.in_dtype in ("e4m3", "e5m2"):

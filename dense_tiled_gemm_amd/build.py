@@ -63,5 +63,21 @@ def build_c_check(verbose=False) -> str:
     return C_CHECK
 
 
+SWZ_DUMP_SRC = os.path.join(ROOT, "tests", "swizzle_dump.cpp")
+SWZ_DUMP = os.path.join(ROOT, "tests", "swizzle_dump")
+
+
+def build_swizzle_dump(verbose=False) -> str:
+    """The host program that prints the kernels' LDS swizzle maps (from the kernel headers) for the CPU tests."""
+    tmp = SWZ_DUMP + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, SWZ_DUMP_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, SWZ_DUMP)
+    return SWZ_DUMP
+
+
 if __name__ == "__main__":
     print(build(extra=sys.argv[1:], verbose=True))

@@ -317,6 +317,15 @@ __device__ inline void store_tile(const typename AccBlock<MF>::type (&acc)[FN][F
     }
 }
 
+// Physical 16-byte chunk of logical chunk c in row r of the parked output
+// tile (rows of CPR chunks): c ^ (r mod min(32, CPR)), except for 128-byte
+// rows (CPR 8), where rows r and r + 8 start in the same bank half: there
+// row bits 1..3 are XORed in instead, so the 16 rows of one parking pass
+// (8-byte writes of 16-bit outputs, 32 lanes per pass) fill all 64 banks.
+__host__ __device__ inline int epi_chunk(int c, int r, int cpr) {
+    return cpr == 8 ? c ^ ((r >> 1) & 7) : c ^ (r & ((cpr < 32 ? cpr : 32) - 1));
+}
+
 // Store the workgroup's BM x BN tile through LDS so that each global store
 // instruction writes whole rows: every wave first parks its accumulator
 // blocks (rounded to OUT) in LDS as a row-major tile, then the NT threads of
@@ -336,7 +345,6 @@ __device__ inline void store_tile_lds(const typename AccBlock<MF>::type (&acc)[F
     constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
     constexpr int ROWB = BN * OSZ;  // bytes per tile row
     constexpr int CPR = ROWB / 16;  // 16-byte chunks per tile row
-    constexpr int SWM = (CPR < 32 ? CPR : 32) - 1;
     constexpr int P = BM * ROWB <= LDS_BYTES ? 1 : WM;
     constexpr int RP = BM / P;  // tile rows per pass
     static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "row chunks");
@@ -359,7 +367,7 @@ __device__ inline void store_tile_lds(const typename AccBlock<MF>::type (&acc)[F
                     for (int g = 0; g < AB::regs / 4; ++g) {
                         const int col = nw + MF * i + AB::col(lane, g);
                         const int c = col * OSZ / 16;
-                        unsigned char* dst = lds + r * ROWB + ((c ^ (r & SWM)) * 16) + (OSZ == 2 ? 8 * ((col >> 2) & 1) : 0);
+                        unsigned char* dst = lds + r * ROWB + (epi_chunk(c, r, CPR) * 16) + (OSZ == 2 ? 8 * ((col >> 2) & 1) : 0);
                         const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
                         const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
                         if constexpr (OUT == GEMM_BT_F32)
@@ -374,7 +382,7 @@ __device__ inline void store_tile_lds(const typename AccBlock<MF>::type (&acc)[F
         for (int q0 = 0; q0 < RP * CPR; q0 += NT) {
             const int q = q0 + tid;
             const int r = q / CPR, c = q % CPR;
-            const u32x4 v = *(const u32x4*)(lds + r * ROWB + ((c ^ (r & SWM)) * 16));
+            const u32x4 v = *(const u32x4*)(lds + r * ROWB + (epi_chunk(c, r, CPR) * 16));
             const int row = p * RP + r, col = c * (16 / OSZ);
             if (row < mlim && col < nlim)
                 __builtin_amdgcn_raw_buffer_store_b128(v, rc, ((u32)row * (u32)N + (u32)col) * OSZ, 0, kStoreNT);

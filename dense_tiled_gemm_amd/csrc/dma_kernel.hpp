@@ -45,7 +45,7 @@ namespace gbt {
 // of r into the chunk (SWZ 2) spreads rows r..r+15 over all 16 groups, while
 // bits 0..2 (SWZ 1, the form that suits 32 banks) leaves 2-way conflicts.
 template <int CPR, int SWZ>
-__device__ inline int swz_row(int row) {
+__host__ __device__ inline int swz_row(int row) {
     if constexpr (SWZ == 0) return 0;
     else if constexpr (CPR == 8) return SWZ == 1 ? (row & 7) : ((row >> 1) & 7);
     else return SWZ == 1 ? ((row >> 1) & 3) : ((row >> 2) & 3);

@@ -46,7 +46,7 @@ __device__ inline u32x2 lds_read_tr16(const unsigned char* p) {
 }
 
 // pair swizzle of a K-outer row (in units of 16-byte chunks: always even)
-__device__ inline int kouter_swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+__host__ __device__ inline int kouter_swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
 
 // Geometry of one operand tile of BX rows/columns by 64 k in LDS.
 //   K-inner: BX rows of 128 bytes (8 chunks), chunk c of row r at c ^ ((r >> 1) & 7);

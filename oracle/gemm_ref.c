@@ -227,22 +227,21 @@ void orc_round(const double* x, int64_t n, int out_dtype, void* out) {
     }
 }
 
-/* Exact value of every 16-bit pattern, filled once from the decoders above so
-   the loops below index a table instead of re-decoding each operand. */
+/* Exact value of every 16-bit pattern (f16, bf16, and the 8-bit formats in
+   the low byte), filled from the decoders above once, when the library is
+   loaded and before any call can run, so that the loops below index a table
+   instead of re-decoding each operand and no call ever sees a table being
+   filled. */
 static double g_table[4][65536];
-static int g_table_ready[4];
+static const int g_table_dtype[4] = {ORC_F16, ORC_BF16, ORC_FP8_E4M3, ORC_FP8_E5M2};
+
+__attribute__((constructor)) static void orc_fill_tables(void) {
+    for (int t = 0; t < 4; ++t)
+        for (int h = 0; h < 65536; ++h) g_table[t][h] = decode((uint16_t)h, g_table_dtype[t]);
+}
 
 static const double* table_for(int dtype) {
     const int t = dtype == ORC_BF16 ? 1 : (dtype == ORC_FP8_E4M3 ? 2 : (dtype == ORC_FP8_E5M2 ? 3 : 0));
-    if (!g_table_ready[t]) {
-#pragma omp critical(orc_table)
-        {
-            if (!g_table_ready[t]) {
-                for (int h = 0; h < 65536; ++h) g_table[t][h] = decode((uint16_t)h, dtype);
-                g_table_ready[t] = 1;
-            }
-        }
-    }
     return g_table[t];
 }
 

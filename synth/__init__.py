@@ -68,7 +68,8 @@ class Workload:
 
 # The five measured shapes, seeds 0..4 in this order, the 4096³ product
 # with 8-bit E4M3 inputs (seed 5) and with int8 inputs and int32 output (seed 6),
-# a batch of 64 products of 512³ (seed 7), and 4096³ with B stored K×N (seed 8).
+# a batch of 64 products of 512³ (seed 7), 4096³ with B stored K×N (seed 8),
+# and 1024×1024×16384, whose 64 tiles the split plan divides along K (seed 9).
 WORKLOADS = {
     "sq512_bf16_f32": Workload("sq512_bf16_f32", 512, 512, 512, "bf16", "f32", "normal", 0),
     "m1024_n4096_k4096_f16_f16": Workload("m1024_n4096_k4096_f16_f16", 1024, 4096, 4096, "f16", "f16",
@@ -82,6 +83,8 @@ WORKLOADS = {
     "sq4096_i8_i32": Workload("sq4096_i8_i32", 4096, 4096, 4096, "i8", "i32", "int8", 6),
     "batch64_sq512_bf16_bf16": Workload("batch64_sq512_bf16_bf16", 512, 512, 512, "bf16", "bf16", "normal", 7, 64),
     "sq4096_nn_bf16_bf16": Workload("sq4096_nn_bf16_bf16", 4096, 4096, 4096, "bf16", "bf16", "normal", 8, 1, 1),
+    "splitk_m1024_n1024_k16384_bf16_bf16": Workload("splitk_m1024_n1024_k16384_bf16_bf16", 1024, 1024, 16384,
+                                                    "bf16", "bf16", "normal", 9),
 }
 
 
