@@ -149,37 +149,25 @@ __device__ inline void dma4_touch(const i32x4& r, unsigned char* dst, u32 voff, 
 // refill PF steps later finds its lines in L2 instead of paying the full
 // HBM / Infinity-Cache latency with only STAGES - 1 steps of cover.
 //
-// SK = 1: stream-K ("Writing Mosaic GPU kernels with Pallas", section
-// "Cluster launch control": the grid walks the work itself, so that no core
-// idles through a partial last wave).  The sk.sk_tiles tiles of the banded
-// order form sk.iters = sk_tiles * nk (tile, K step) iterations, and
-// workgroup g of the G launched takes the contiguous run [v*iters/G,
-// (v+1)*iters/G) of them, v being g renumbered die by die (xcd_seq), so that
-// the workgroups sharing a tile sit on one die.  A run may cover the tail of
-// one tile, whole tiles and the head of another; each piece is one pipeline
-// over its K steps.  (The host plans G = sk_tiles * S, which makes every run
-// exactly one piece of one tile: split-K with S pieces per tile.)  A tile
-// done by several workgroups is finished by the last of them to arrive:
-// every contributor writes its fp32 sums to its own slot of sk.partials with
-// device-scope (write-through) stores, waits until they are written, and
-// counts itself in the tile's counter; the one that sees every other
-// contributor already counted reads the partial sums back with device-scope
-// loads, adds them in K order (contributor 0 + 1 + 2 ..., whatever the
-// arrival order, so the result is the same bits on every run), resets the
-// counter to zero and stores the tile.  No workgroup ever waits for another.
+// SK = 1: split-K, the work-splitting step of stream-K ("Writing Mosaic GPU
+// kernels with Pallas", section "Cluster launch control": the grid walks the
+// work itself, so that no core idles while a few tiles finish).  Each of the
+// sk.tiles tiles is split along K into sk.pieces = S pieces, one per
+// workgroup of a grid of tiles * S.  A tile is finished by the last of its S
+// workgroups to arrive: every piece writes its fp32 sums to its own slot of
+// sk.partials with device-scope (write-through) stores, waits until they are
+// written, and counts itself in the tile's counter; the one that sees the
+// other S - 1 already counted reads their sums back with device-scope loads,
+// adds the pieces in K order (piece 0 + 1 + 2 ..., whatever the arrival
+// order, so the result is the same bits on every run), resets the counter to
+// zero and stores the tile.  No workgroup ever waits for another.
 struct SkArgs {
-    int sk_tiles;        // tiles split along K over the grid
+    int tiles;           // tiles, each split along K into `pieces` pieces (grid = tiles * pieces)
+    int pieces;          // S >= 2
     int nk;              // K steps of BK per tile (over the whole 16-byte chunks of K)
-    long long iters;     // sk_tiles * nk
-    unsigned* counters;  // one arrival counter per split tile, zero between calls
-    float* partials;     // two slots of BM * BN floats per workgroup
+    unsigned* counters;  // one arrival counter per tile, zero between calls
+    float* partials;     // one slot of BM * BN floats per workgroup
 };
-
-// Owner of stream-K iteration `it`: the (renumbered) workgroup v whose run
-// [v*I/G, (v+1)*I/G) contains it, i.e. the largest v with floor(v*I/G) <= it.
-__host__ __device__ inline int64_t sk_owner(int64_t it, int64_t iters, int64_t grid) {
-    return ((it + 1) * grid - 1) / iters;
-}
 
 template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0,
           int MF = 32, int LDW = 0, int RING5 = 0, int SK = 0>
@@ -756,27 +744,24 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         run(A, B, m0, n0, 0, nk_all, acc);
         store_c(C, m0, n0, acc);
     } else {
-        // Stream-K (one item; the host sends batches to the plain grid).  The
-        // bookkeeping is wave-uniform and 32-bit (the host keeps iters below
-        // 2^31): readfirstlane pins each value to a scalar register, so none of
-        // it competes with the accumulators for vector registers.
+        // Split-K (one item; the host sends batches to the plain grid): the
+        // workgroups are renumbered die by die (xcd_seq, so that the pieces of
+        // a tile sit on one die); rank v computes piece j = v % S, K steps
+        // [j*nk/S, (j+1)*nk/S), of tile v / S of the banded order.  The
+        // bookkeeping is wave-uniform: readfirstlane pins each value to a
+        // scalar register, so none of it competes with the accumulators.
         constexpr int NT = 64 * W;
         constexpr int Q = AB::regs / 4;  // 16-byte groups per accumulator block
         static_assert(W * 64 * 4 * FN * FM * AB::regs == BM * BN * 4, "a partial slot holds one fp32 tile");
         auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
-        const int G = gridDim.x, g = blockIdx.x;
-        const int I = (int)sk.iters, nk = sk.nk;
-        // first iteration of rank r, and the rank owning iteration `it`
-        auto start = [&](int r) { return uni((int)((int64_t)r * I / G)); };
-        auto owner = [&](int it) { return uni((int)sk_owner(it, I, G)); };
-        const int v = uni((int)xcd_seq(g, G));  // rank among the workgroups, die by die
-        const int it0 = start(v), it1 = start(v + 1);
-        // the partial sums of contributor vv to split tile s: slot 0 of vv holds
-        // its first piece, slot 1 its last; thread t owns 16-byte group e at
-        // byte (t + e * NT) * 16 of the slot
-        auto slot = [&](int vv, int s) {
-            const int first = uni(start(vv) / nk);
-            return make_rsrc(sk.partials + (int64_t)(2 * vv + (s == first ? 0 : 1)) * (BM * BN), BM * BN * 4);
+        const int S = sk.pieces, nk = sk.nk;
+        const int v = uni((int)xcd_seq(blockIdx.x, (int64_t)sk.tiles * S));
+        const int s = uni(v / S), j = uni(v - s * S);
+        const int kb = uni((int)((int64_t)j * nk / S)), ke = uni((int)((int64_t)(j + 1) * nk / S));
+        // slot of piece jj of this tile: the partial sums of rank s * S + jj;
+        // thread t owns 16-byte group e at byte (t + e * NT) * 16 of it
+        auto slot = [&](int jj) {
+            return make_rsrc(sk.partials + (int64_t)(s * S + jj) * (BM * BN), BM * BN * 4);
         };
         // Cache policy of the partial sums: sc1, device scope.  Stores are
         // written through the die's L2 to device memory, and loads miss any
@@ -807,71 +792,59 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
                 __builtin_amdgcn_sched_barrier(0);
                 static_for<0, CHUNK>([&](auto ec) {
                     constexpr int e = c0 + decltype(ec)::value;
-                    constexpr int i = e / (FM * Q), j = (e / Q) % FM, q = e % Q;
+                    constexpr int i = e / (FM * Q), jf = (e / Q) % FM, q = e % Q;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        acc[i][j][4 * q + r] =
-                            overwrite ? as_f32(x[e - c0][r]) : acc[i][j][4 * q + r] + as_f32(x[e - c0][r]);
+                        acc[i][jf][4 * q + r] =
+                            overwrite ? as_f32(x[e - c0][r]) : acc[i][jf][4 * q + r] + as_f32(x[e - c0][r]);
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        // One pipeline and one store site per piece of this workgroup's run.
-        for (int it = it0; it < it1;) {
-            const int s = uni(it / nk);
-            const int kb = uni(it - s * nk);
-            const int ke = uni(min(nk, kb + (it1 - it)));
-            it += ke - kb;
-            __syncthreads();  // LDS is free again (the previous piece's epilogue is done)
-            int64_t tm, tn;
-            band_coord(s, tiles_m, tiles_n, group_m, &tm, &tn);
-            const int m0 = uni((int)tm * BM), n0 = uni((int)tn * BN);
-            Acc acc;
-            zero(acc);
-            run(A, B, m0, n0, kb, ke, acc);
-            const int vf = owner(s * nk), vl = owner(s * nk + nk - 1);
-            if (vf != vl) {
-            // a piece of a tile shared with other workgroups: publish its
-            // partial sums (written through), count it in
-            const __amdgpu_buffer_rsrc_t mine = slot(v, s);
+        int64_t tm, tn;
+        band_coord(s, tiles_m, tiles_n, group_m, &tm, &tn);
+        const int m0 = uni((int)tm * BM), n0 = uni((int)tn * BN);
+        Acc acc;
+        zero(acc);
+        run(A, B, m0, n0, kb, ke, acc);
+        // publish this piece: its partial sums, written through, then counted
+        {
+            const __amdgpu_buffer_rsrc_t mine = slot(j);
             int tid_r = threadIdx.x;
             asm volatile("" : "+v"(tid_r));
             static_for<0, FN * FM * Q>([&](auto ec) {
                 constexpr int e = decltype(ec)::value;
-                constexpr int i = e / (FM * Q), j = (e / Q) % FM, q = e % Q;
-                const u32x4 w = {as_u32(acc[i][j][4 * q]), as_u32(acc[i][j][4 * q + 1]), as_u32(acc[i][j][4 * q + 2]),
-                                 as_u32(acc[i][j][4 * q + 3])};
+                constexpr int i = e / (FM * Q), jf = (e / Q) % FM, q = e % Q;
+                const u32x4 w = {as_u32(acc[i][jf][4 * q]), as_u32(acc[i][jf][4 * q + 1]),
+                                 as_u32(acc[i][jf][4 * q + 2]), as_u32(acc[i][jf][4 * q + 3])};
                 __builtin_amdgcn_raw_buffer_store_b128(w, mine, (u32)(tid_r + e * NT) * 16u, 0, kCoherent);
             });
-            wait_vmcnt<0>();  // this wave's sums have reached device memory
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                // every wave of this workgroup is past its wait (the barrier
-                // above), so the count follows all of the piece's stores
-                const unsigned seen = __hip_atomic_fetch_add(sk.counters + s, 1u, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT);
-                const int last = seen == (unsigned)(vl - vf);
-                if (last) __hip_atomic_store(sk.counters + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                *(volatile int*)lds = last;
-            }
-            __syncthreads();
-            if (!*(volatile int*)lds) continue;
-            // last to arrive: sum contributor 0 + 1 + ... in that order
-            const int jm = v - vf, n = vl - vf + 1;
-            int jn;
-            if (jm == 0) {
-                jn = 1;  // acc is piece 0
-            } else if (jm == 1) {
-                add_slot(slot(vf, s), false, acc);  // piece 1 + piece 0 == piece 0 + piece 1
-                jn = 2;
-            } else {
-                add_slot(slot(vf, s), true, acc);  // piece 0; ours is read back in its turn
-                jn = 1;
-            }
-            for (int jj = jn; jj < n; ++jj) add_slot(slot(vf + jj, s), false, acc);
-            }
-            store_c(C, m0, n0, acc);
         }
+        wait_vmcnt<0>();  // this wave's sums have reached device memory
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            // every wave of this workgroup is past its wait (the barrier
+            // above), so the count follows all of the piece's stores
+            const unsigned seen = __hip_atomic_fetch_add(sk.counters + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int last = seen == (unsigned)(S - 1);
+            if (last) __hip_atomic_store(sk.counters + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *(volatile int*)lds = last;
+        }
+        __syncthreads();
+        if (!*(volatile int*)lds) return;
+        // last to arrive: sum piece 0 + 1 + ... + S-1 in that order
+        int jn;
+        if (j == 0) {
+            jn = 1;  // acc is piece 0
+        } else if (j == 1) {
+            add_slot(slot(0), false, acc);  // piece 1 + piece 0 == piece 0 + piece 1
+            jn = 2;
+        } else {
+            add_slot(slot(0), true, acc);  // piece 0; ours is read back in its turn
+            jn = 1;
+        }
+        for (int jj = jn; jj < S; ++jj) add_slot(slot(jj), false, acc);
+        store_c(C, m0, n0, acc);
     }
 }
 

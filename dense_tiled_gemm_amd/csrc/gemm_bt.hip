@@ -103,8 +103,8 @@ static DmaVariant dma_variant(const char* name) {
     return v;
 }
 
-// Index 0 is the default for large grids, 1 for smaller ones, 2 and 6 for
-// the smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
+// Index 0 is the default for large grids, 7 and 1 for smaller ones, 2 and 6
+// for the smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
 // (128-element K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32
 // MFMAs over 64-element substeps).
 // A build with GEMM_BT_TUNING defined adds the measured alternatives after
@@ -112,6 +112,7 @@ static DmaVariant dma_variant(const char* name) {
 // only); the default library holds the seven production kernels only.
 constexpr int kFp8Variants = 3;
 constexpr int kTiny16 = 6;  // 32 x 64 tiles (16-bit inputs), when even 64 x 64 tiles leave half the CUs idle
+constexpr int kWide16 = 7;  // 128 x 256 tiles (16-bit inputs, 8 waves of 64 x 64), see plan_impl
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
@@ -121,6 +122,7 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<128, 128, 128, 4, 2, 2, 2, 8, 0, 32, true, 0, 0, true>("M128F8s4i"),
         dma_variant<64, 64, 128, 4, 2, 2, 2, 4, 0, 32, true, 0, 0, true>("Q128F8"),
         dma_variant<32, 64, 64, 4, 2, 2, 2, 2, 0, 16, true>("T32x64"),
+        dma_variant<128, 256, 64, 3, 2, 4, 2, 8, 0, 16, true>("H128x256s3"),
 #ifdef GEMM_BT_TUNING
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
@@ -136,45 +138,54 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<256, 256, 32, 4, 2, 4, 2>("L32S4"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 1>("L64PP"),
         dma_variant<256, 256, 64, 2, 2, 4, 2, 0, 2>("L64P2"),
+        dma_variant<256, 128, 64, 3, 4, 2, 2, 8, 0, 16>("H256x128s3"),
+        dma_variant<128, 256, 64, 2, 2, 4, 2, 8, 0, 16>("H128x256s2"),
+        dma_variant<128, 128, 64, 2, 2, 2, 2, 8, 0, 16>("M64s2"),
 #endif
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
     return v;
 }
 
-// Stream-K form of the 128 x 128 tier (M64E4s4i, dma_variants() index 1):
-// a grid that splits the K range of tiles over workgroups (16-bit inputs,
-// one item).
+// Split-K form of the 128 x 128 tier (M64E4s4i, dma_variants() index 1): a
+// grid that splits the K range of every tile over several workgroups (16-bit
+// inputs, one item).  A tuning build also has the split form of the 128 x 256
+// tier (index 7; measured no faster: 1024x4096x4096 f16 43.1 us split 2 ways
+// against 42.9 us unsplit on 128 x 128 tiles).
 constexpr int kSkVariant = 1;
 template <int IN, int OUT>
-static const void* sk_fn_t() {
+static const void* sk_fn_t(int variant) {
+#ifdef GEMM_BT_TUNING
+    if (variant == 7) return (const void*)&dma_kernel<IN, OUT, 128, 256, 64, 3, 2, 4, 2, 8, 0, 16, 0, 0, 1>;
+#endif
+    (void)variant;
     return (const void*)&dma_kernel<IN, OUT, 128, 128, 64, 4, 2, 2, 2, 8, 0, 16, 0, 0, 1>;
 }
 template <int IN>
-static const void* sk_fn_out(int out) {
-    if (out == GEMM_BT_F32) return sk_fn_t<IN, GEMM_BT_F32>();
-    if (out == GEMM_BT_BF16) return sk_fn_t<IN, GEMM_BT_BF16>();
-    return sk_fn_t<IN, GEMM_BT_F16>();
+static const void* sk_fn_out(int out, int variant) {
+    if (out == GEMM_BT_F32) return sk_fn_t<IN, GEMM_BT_F32>(variant);
+    if (out == GEMM_BT_BF16) return sk_fn_t<IN, GEMM_BT_BF16>(variant);
+    return sk_fn_t<IN, GEMM_BT_F16>(variant);
 }
-static const void* sk_fn(int in_dtype, int out_dtype) {
-    return in_dtype == GEMM_BT_BF16 ? sk_fn_out<GEMM_BT_BF16>(out_dtype) : sk_fn_out<GEMM_BT_F16>(out_dtype);
+static const void* sk_fn(int variant, int in_dtype, int out_dtype) {
+    return in_dtype == GEMM_BT_BF16 ? sk_fn_out<GEMM_BT_BF16>(out_dtype, variant)
+                                    : sk_fn_out<GEMM_BT_F16>(out_dtype, variant);
 }
 
-// Workspace of the stream-K kernels: a fixed area of arrival counters (one
-// per split tile; a plan splits fewer than 2 * grid tiles), then two slots of
-// one fp32 tile per workgroup.
+// Workspace of the split kernels: a fixed area of arrival counters (one per
+// split tile), then one slot of one fp32 tile per workgroup.
 constexpr int64_t kSkCounterBytes = 16384;
 constexpr int64_t kSkMaxTiles = kSkCounterBytes / 4;
 
 // Scratch of gemm_bt_noalloc: the workspace of the largest split plan on a
-// device of up to 256 CUs (counters, then two 128 x 128 fp32 slots per
+// device of up to 256 CUs (counters, then one 128 x 128 fp32 slot per
 // workgroup of a grid of at most 256), as a device array of the library's own.
-// Every GPU the library runs on holds one copy (32.02 MiB) until the process
+// Every GPU the library runs on holds one copy (16.02 MiB) until the process
 // ends.  It is zero when the code object is loaded, and every call leaves its
 // counter area zero again.  Host code must not pass `scratch` itself to a
 // kernel (on the host it names a stand-in, not device memory): it uses the
 // per-device address from hipGetSymbolAddress (noalloc_scratch below).
-constexpr int64_t kScratchBytes = kSkCounterBytes + 2 * 256 * 128 * 128 * 4;
+constexpr int64_t kScratchBytes = kSkCounterBytes + 256 * 128 * 128 * 4;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 // Skinny DMA-kernel variants [in][out]; index 0 is the default.
@@ -303,28 +314,36 @@ static bool dma_large_tier(int64_t tiles_l, int num_cu, bool eight_bit) {
 // 1000x3000x8192 81 vs 65), so no split is planned there.
 // Fills p and returns true, or returns false and leaves p alone.
 constexpr int64_t kSkMinSteps = 32;
-static bool plan_split(int64_t M, int64_t N, int64_t K, int num_cu, gemm_bt_plan_t* p) {
-    const int64_t T = ((M + 127) / 128) * ((N + 127) / 128);
+static bool plan_split(int64_t M, int64_t N, int64_t K, int variant, int num_cu, gemm_bt_plan_t* p) {
+    int n = 0;
+    const DmaVariant& v = dma_variants(&n)[variant];
+    const int64_t T = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
     const int64_t nk = ((K & ~7LL) + 63) / 64;
     if (T * 2 > num_cu) return false;
     const int64_t S = num_cu / T;
-    if (nk < kSkMinSteps * S || T > kSkMaxTiles || T * nk >= (1LL << 31)) return false;
-    int n = 0;
-    const DmaVariant& v = dma_variants(&n)[kSkVariant];
+    if (nk < kSkMinSteps * S || T > kSkMaxTiles) return false;
     p->kernel = KIND_DMA;
-    p->variant = kSkVariant;
+    p->variant = variant;
     p->bm = v.bm;
     p->bn = v.bn;
     p->bk = v.bk;
     p->stages = v.stages;
     p->threads = 64 * v.wm * v.wn;
     p->lds_bytes = v.lds_bytes;
-    p->tiles_m = (M + 127) / 128;
-    p->tiles_n = (N + 127) / 128;
+    p->tiles_m = (M + v.bm - 1) / v.bm;
+    p->tiles_n = (N + v.bn - 1) / v.bn;
     p->grid = T * S;
     p->split_tiles = T;
-    p->workspace_bytes = kSkCounterBytes + 2 * p->grid * 128 * 128 * 4;
+    p->workspace_bytes = kSkCounterBytes + p->grid * (int64_t)v.bm * v.bn * 4;
     return true;
+}
+
+// Which split, if any (the measured rule; see plan_split)
+static bool plan_split_rule(int64_t M, int64_t N, int64_t K, int num_cu, gemm_bt_plan_t* p) {
+#ifdef GEMM_BT_TUNING
+    if (const char* e = std::getenv("GEMM_BT_SPLIT_TILE")) return plan_split(M, N, K, std::atoi(e), num_cu, p);
+#endif
+    return plan_split(M, N, K, kSkVariant, num_cu, p);
 }
 
 static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
@@ -437,6 +456,18 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         int use = dma_large_tier(tiles_l, num_cu, false) ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2);
         const int64_t tiles_q64 = ((M + 63) / 64) * ((N + 63) / 64) * batch;
         if (use == 2 && tiles_q64 * 2 <= num_cu) use = kTiny16;
+        // 128 x 256 tiles (8 waves, two per SIMD, each 64 x 64) instead of
+        // 128 x 128 ones (4 waves, one per SIMD) once they make whole waves
+        // or more than 1.375 waves: per FLOP they load 3/4 of the bytes, and
+        // one wave's MFMAs cover the other's loads.  Measured (us, 128 x 128
+        // vs 128 x 256 tiles): 2048x4096x4096 76.4 vs 61.3, 2048x4096x8192 f16
+        // 140 vs 119, 2048x4096x2048 37.6 vs 33.4, 3072x4096x4096 102.6 vs 98.1,
+        // 4608x4096x4096 153.5 vs 148.0, 4352x4096x8192 305 vs 281; just
+        // above one wave no better (3000x3000x4096, 1.125 waves, 95.3 vs 95.2;
+        // 2560x4096x4096, 1.25 waves, 93.9 vs 95.5).
+        const int64_t tiles_h = ((M + 127) / 128) * ((N + 255) / 256) * batch;
+        if (use == 1 && tiles_h >= num_cu && (tiles_h % num_cu == 0 || tiles_h * 8 > (int64_t)num_cu * 11))
+            use = kWide16;
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];
@@ -448,7 +479,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         p->stages = v.stages;
         p->threads = 64 * v.wm * v.wn;
         p->lds_bytes = v.lds_bytes;
-        if (allow_sk && f < 0 && batch == 1 && plan_split(M, N, K, num_cu, p)) return GEMM_BT_OK;
+        if (allow_sk && f < 0 && batch == 1 && plan_split_rule(M, N, K, num_cu, p)) return GEMM_BT_OK;
     } else {
         const TileCfg c = big ? kCfgL : kCfgM;
         p->kernel = KIND_TILED;
@@ -693,9 +724,9 @@ static int plan_cus() {
 static SkArgs sk_args(const gemm_bt_plan_t& p, int64_t K, void* ws) {
     SkArgs a = {0, 0, 0, nullptr, nullptr};
     if (p.split_tiles > 0) {
-        a.sk_tiles = (int)p.split_tiles;
+        a.tiles = (int)p.split_tiles;
+        a.pieces = (int)(p.grid / p.split_tiles);
         a.nk = (int)(((K & ~7LL) + p.bk - 1) / p.bk);
-        a.iters = (long long)a.sk_tiles * a.nk;
         a.counters = (unsigned*)ws;
         a.partials = (float*)((char*)ws + kSkCounterBytes);
     }
@@ -755,7 +786,7 @@ static int launch_inner(const void* A, const void* B, void* C, int64_t batch, in
         if (vec_store && (N * osz) % 16 == 0 && c_al >= 16) vec_store = 2;
         if (p.kernel == KIND_DMA) {
             int n = 0;
-            const void* fn = p.split_tiles > 0 ? sk_fn(in_dtype, out_dtype)
+            const void* fn = p.split_tiles > 0 ? sk_fn(p.variant, in_dtype, out_dtype)
                                                : dma_variants(&n)[p.variant].fn[in_index(in_dtype)][out_index(out_dtype)];
             SkArgs ska = sk_args(p, K, ws);
             // one grid row: the items stacked along the tile rows (stream-K: the persistent grid)

@@ -180,7 +180,7 @@ int gemm_bt_ws(const void* A, const void* B, void* C, int64_t M, int64_t N, int6
  * gemm_bt_ws without a workspace argument, for callers that cannot allocate
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the split plan's counters and partial sums live in a scratch
- * array of the library's own in device memory, 16 KiB + 32 MiB (the largest
+ * array of the library's own in device memory, 16 KiB + 16 MiB (the largest
  * split plan on a GPU of up to 256 compute units), one copy per GPU, held
  * until the process ends.  The call allocates nothing (no hipMalloc, no
  * allocating library routine).  Same arguments, plan, kernels and results as
@@ -197,7 +197,7 @@ int gemm_bt_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N,
 
 /* Workspace gemm_bt_ws needs for these sizes and types (0 when it runs the
    plain grid), for the current device (256 compute units without one).  At
-   most 16 KiB + 2 * 256 * 64 KiB (32.02 MiB) on an MI355X, whatever the
+   most 16 KiB + 256 * 64 KiB (16.02 MiB) on an MI355X, whatever the
    sizes.  Returns gemm_bt's status for invalid arguments. */
 int gemm_bt_workspace_size(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, size_t* bytes);
 

@@ -149,13 +149,43 @@ def test_tier_band_above_one_wave():
     def bm(M, N, K=4096, ind=gb.BF16, outd=gb.BF16, batch=1):
         return gb.gemm_bt_plan_batched(batch, M, N, K, ind, outd).bm
     assert bm(4096, 4096) == 256                                  # 256 tiles: one wave
-    assert bm(4352, 4096) == bm(4096, 4160) == bm(4864, 4096) == 128  # 272, 272, 304 tiles
+    assert bm(4352, 4096) == bm(4096, 4160) == bm(4864, 4096) == 128  # 272, 272, 304 tiles (128x256 ones)
     assert bm(5120, 4096) == bm(4608, 4608) == 256                # 320, 324 tiles
     assert bm(512, 512, 512, batch=68) == 128                     # 68 items x 4 tiles
     # 8-bit inputs: a narrower band, up to 17/16 waves
     assert bm(4352, 4096, ind=gb.FP8_E4M3) == bm(4352, 4096, ind=gb.INT8, outd=gb.INT32) == 128  # 272 tiles
     assert bm(4608, 4096, ind=gb.FP8_E4M3) == bm(4864, 4096, ind=gb.INT8, outd=gb.INT32) == 256  # 288, 304
     assert bm(5120, 4096, ind=gb.FP8_E4M3) == 256
+
+
+def test_wide_tier_and_split_plans():
+    """16-bit inputs: 128x256 tiles once they make whole waves or more than 1.375 waves (where 128x128 tiles
+    would otherwise be taken); the split plan (gemm_bt_ws) only where 128x128 tiles fill at most half the CUs and
+    each piece keeps at least 32 K steps, one piece per workgroup."""
+    def tile(M, N, K=4096, batch=1, ind=gb.BF16):
+        p = gb.gemm_bt_plan_batched(batch, M, N, K, ind, gb.BF16)
+        return p.bm, p.bn
+    assert tile(2048, 4096) == (128, 256)                        # 256 tiles of 128x256: one wave
+    assert tile(3072, 4096) == tile(4352, 4096) == (128, 256)    # 384 (1.5 waves), 544
+    assert tile(2560, 4096) == tile(3000, 3000) == (128, 128)    # 320 (1.25 waves), 288 (1.125)
+    assert tile(2048, 2048) == (128, 128)                        # 128 tiles of 128x256: half the CUs
+    assert tile(4096, 4096) == (256, 256)
+    assert tile(512, 1024, K=72, batch=16) == (128, 256)         # items stacked: 256 tiles
+    assert tile(2048, 4096, ind=gb.FP8_E4M3) != (128, 256)       # 16-bit inputs only
+    p = gb.gemm_bt_plan(2048, 4096, 4096, gb.BF16, gb.BF16)
+    assert (p.threads, p.stages, p.lds_bytes) == (512, 3, 3 * (128 + 256) * 64 * 2)
+    for M, N, K, T, S in [(1024, 1024, 16384, 64, 4), (512, 1024, 32768, 32, 8), (300, 700, 30002, 18, 14),
+                          (1024, 2048, 8192, 128, 2)]:
+        p = gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.F32)
+        assert (p.bm, p.bn, p.split_tiles, p.grid) == (128, 128, T, T * S), (M, N, K)
+        assert p.workspace_bytes == 16384 + T * S * 128 * 128 * 4
+        assert gb.gemm_bt_workspace_size(M, N, K, gb.BF16, gb.F32) == p.workspace_bytes
+        assert gb.gemm_bt_plan(M, N, K, gb.BF16, gb.F32).split_tiles == 0  # gemm_bt never splits
+    for M, N, K in [(1000, 3000, 2050), (1024, 4096, 4096), (1024, 1024, 4096), (4096, 4096, 4096),
+                    (16, 8192, 8192), (768, 768, 8192)]:
+        assert gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.F32).split_tiles == 0, (M, N, K)
+        assert gb.gemm_bt_workspace_size(M, N, K, gb.BF16, gb.F32) == 0
+    assert gb.gemm_bt_plan_ws(1024, 1024, 16384, gb.FP8_E4M3, gb.F32).split_tiles == 0  # 16-bit inputs only
 
 
 def test_layout_tier_band():

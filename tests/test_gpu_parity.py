@@ -97,6 +97,11 @@ SHAPES = [
     (4096, 4096, 8), (4096, 4096, 130), (4900, 4100, 136), (4096, 4096, 200),
     # just above one wave of 256x256 tiles (289 of them): 128x128 tiles, ragged edges
     (4100, 4100, 136),
+    # 128x256 tiles (one wave of them, and 1.5 waves): whole tiles, ragged edges with a partial last K step,
+    # a K tail, C rows of 8-byte and 2-byte alignment
+    (2048, 4096, 136), (2000, 4000, 200), (2048, 4096, 130), (2048, 4004, 72), (2048, 3999, 64), (3072, 4096, 72),
+    # 304 tiles of 256x256 (1.19 waves, the edge of the band that takes smaller tiles)
+    (4864, 4096, 136),
 ]
 SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200)]
 
@@ -462,6 +467,10 @@ BATCHED = [
     (3, 130, 260, 160, "e4m3", "bf16", None, (16, 32, 0)),
     (3, 300, 200, 256, "i8", "i32", "b", (0, 0, 5)),
     (7, 64, 96, 48, "e5m2", "f32", "a", (0, 0, 0)),
+    # items stacked into 128x256 tiles: 68 items of 512x512 (272 tiles of 256x256, just above one wave) and
+    # 16 items of 512x1024 (one wave of 128x256 tiles)
+    (68, 512, 512, 136, "bf16", "bf16", None, (0, 0, 0)),
+    (16, 512, 1024, 72, "f16", "f32", None, (0, 0, 0)),
 ]
 
 
