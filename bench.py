@@ -6,14 +6,16 @@ i.i.d. N(0,1) rounded to bf16, seed 2, bf16 output), inputs resident in HBM.
 Prints ONE JSON line on stdout:
   value        TFLOP/s of the whole job (2·M·N·K per step / wall time of the
                K timed steps between two synchronisations)
-  timing       per-launch HIP-event times of the timed steps (median, min,
-               max, p10, p90, mean) and the untimed settle phase before them
+  timing       mean launch time of the timed steps (HIP events before and
+               after them), the spread of a second pass with an event after
+               every launch (median, min, max, p10, p90), and the untimed
+               settle phase before them
   clock        the GPU clock (per-XCD gfxclk) and socket power of the first
                amdsmi metrics snapshot the firmware takes under continued
                launches of the workload after the timed steps (the table
                refreshes about once per second), and % of peak at that clock
   roofline     the tiled MFMA kernel against the MI355X dense bf16 peak;
-               achieved = 2·M·N·K / the median launch time
+               achieved = 2·M·N·K / the mean launch time
   cpu_baseline the CPU oracle timed on a bounded sample of the same product,
                with the host's CPU model and core counts
   secondary    the other workloads (1024×4096×4096 f16, 16×8192×8192
@@ -22,7 +24,7 @@ Prints ONE JSON line on stdout:
                batch of 64 products of 512³ in one gemm_bt_batched call,
                4096³ with B stored K×N through gemm_bt_layout, and
                1024×1024×16384, which gemm_bt_ws splits along K), timed the
-               same way (median launch)
+               same way (us = mean launch time)
   copy_GBps    a plain 1 GiB device copy, as context for achievable HBM
 Diagnostics go to stderr.  Whatever --warmup is, the timed steps follow an
 untimed settle phase that runs launches until their time stops falling
@@ -270,38 +272,50 @@ class Case:
                 break
         return n, (time.perf_counter() - t0) * 1e3
 
-    def time(self, steps, warmup, sampler=None):
-        """`warmup` untimed steps, the settle phase, then `steps` timed steps, each bracketed by HIP events on
-        the launch stream (torch's current stream).  Returns a dict: wall seconds of the timed steps (between
-        two synchronisations), per-launch ms, the settle phase, and the host-clock window of the timed steps."""
+    def time(self, steps, warmup, settle=True):
+        """`warmup` untimed steps, the settle phase, then the `steps` timed steps, back to back between two
+        synchronisations, with one HIP event before and one after them on the launch stream (torch's current
+        stream): their mean is the average launch duration.  Then the same number of launches again, each
+        followed by an event of its own, for the spread: an event between two launches also holds the second
+        back by the dispatch gap, so those intervals run longer than the launches themselves (by about 1-6 us
+        on MI355X).  Returns a dict: wall seconds and event ms of the timed steps, the per-launch intervals of
+        the second pass, the settle phase, and the host-clock window of the timed steps."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         sh = stream.cuda_stream
         for i in range(warmup):
             self.step(i, sh)
         torch.cuda.synchronize()
-        settle_n, settle_ms = self.settle(stream)
+        settle_n, settle_ms = self.settle(stream) if settle else (0, 0.0)
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            self.step(i, sh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record(stream)
         for i in range(steps):
             self.step(i, sh)
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-        return {"wall_s": t1 - t0, "per_ms": per, "settle_launches": settle_n, "settle_ms": settle_ms,
-                "t0": t0, "t1": t1}
+        return {"wall_s": t1 - t0, "event_ms": e0.elapsed_time(e1), "per_ms": per, "settle_launches": settle_n,
+                "settle_ms": settle_ms, "t0": t0, "t1": t1}
 
 
 def timing_record(r):
     per_us = [x * 1e3 for x in r["per_ms"]]
-    return {"launches": len(per_us), "median_us": round(percentile(per_us, 0.5), 3),
-            "min_us": round(min(per_us), 3), "max_us": round(max(per_us), 3),
-            "p10_us": round(percentile(per_us, 0.1), 3), "p90_us": round(percentile(per_us, 0.9), 3),
-            "mean_us": round(sum(per_us) / len(per_us), 3), "settle_launches": r["settle_launches"],
-            "settle_ms": round(r["settle_ms"], 1)}
+    n = len(per_us)
+    return {"launches": n, "mean_us": round(r["event_ms"] * 1e3 / n, 3),
+            "per_launch_events": {"median_us": round(percentile(per_us, 0.5), 3), "min_us": round(min(per_us), 3),
+                                  "max_us": round(max(per_us), 3), "p10_us": round(percentile(per_us, 0.1), 3),
+                                  "p90_us": round(percentile(per_us, 0.9), 3)},
+            "settle_launches": r["settle_launches"], "settle_ms": round(r["settle_ms"], 1)}
 
 
 def cpu_info():
@@ -396,6 +410,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--mode", choices=["gemm", "copy"], default="gemm")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the settle phase and the clock reading (for counter-collection runs, where the "
+                         "profiler serializes every dispatch)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -422,17 +439,18 @@ def main():
     plan = case.plan
     log("plan", plan, "rotate", case.rotate, "device CUs", torch.cuda.get_device_properties(0).multi_processor_count)
     sampler = ClockSampler().start()
-    r = case.time(args.steps, args.warmup)
+    r = case.time(args.steps, args.warmup, settle=not args.no_settle)
     ms_per_step = r["wall_s"] / args.steps * 1e3
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     timing = timing_record(r)
-    achieved = w.flops / (timing["median_us"] * 1e-6) / 1e12
-    clock = clock_under_load(case, sampler, r["t1"], achieved)
+    achieved = w.flops / (timing["mean_us"] * 1e-6) / 1e12
+    clock = clock_under_load(case, sampler, r["t1"], achieved) if not args.no_settle else None
     sampler.stop()
-    log("wall ms/step %.4f  median launch %.3f us (min %.3f, p90 %.3f)  TFLOP/s %.1f (median launch %.1f)  settle "
-        "%d launches / %.1f ms  clock %s" % (ms_per_step, timing["median_us"], timing["min_us"], timing["p90_us"],
-                                             tflops, achieved, timing["settle_launches"], timing["settle_ms"],
-                                             clock))
+    pl = timing["per_launch_events"]
+    log("wall ms/step %.4f  mean launch %.3f us  per-launch events median %.3f (min %.3f, p90 %.3f)  TFLOP/s %.1f "
+        "(mean launch %.1f)  settle %d launches / %.1f ms  clock %s" % (
+            ms_per_step, timing["mean_us"], pl["median_us"], pl["min_us"], pl["p90_us"], tflops, achieved,
+            timing["settle_launches"], timing["settle_ms"], clock))
     traffic = load_traffic(w.name)
     out = {
         "metric": METRIC,
@@ -464,10 +482,12 @@ def main():
                      "batch64_sq512_bf16_bf16", "sq4096_nn_bf16_bf16", "splitk_m1024_n1024_k16384_bf16_bf16"):
             w2 = synth.WORKLOADS[name]
             c2 = Case(w2, torch, gb)
-            r2 = c2.time(max(50, args.steps // 2), args.warmup)
+            r2 = c2.time(max(50, args.steps // 2) if not args.no_settle else args.steps, args.warmup,
+                         settle=not args.no_settle)
             t2 = timing_record(r2)
-            us = t2["median_us"]
-            ent = {"us": us, "min_us": t2["min_us"], "p90_us": t2["p90_us"],
+            us = t2["mean_us"]
+            ent = {"us": us, "per_launch_events": t2["per_launch_events"], "launches": t2["launches"],
+                   "settle_launches": t2["settle_launches"],
                    "TFLOP/s": round(w2.flops / (us * 1e-6) / 1e12, 2),
                    "GB/s": round(w2.compulsory_bytes / (us * 1e-6) / 1e9, 1),
                    "rotated_input_sets": c2.rotate, "tile": [c2.plan["bm"], c2.plan["bn"], c2.plan["bk"]],

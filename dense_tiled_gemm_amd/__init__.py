@@ -33,7 +33,8 @@ OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_LAUNCH = 0, 1, 2, 3, 
 K_INNER, K_OUTER = 0, 1  # operand layouts of gemm_bt_layout
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgemm_bt.so")
+# GEMM_BT_LIB may name another build of this library (e.g. a build with the tuning variants, for measurements)
+LIB_PATH = os.environ.get("GEMM_BT_LIB") or os.path.join(_HERE, "libgemm_bt.so")
 EXPORTS = ("gemm_bt", "gemm_bt_batched", "gemm_bt_layout", "gemm_bt_batched_layout", "gemm_bt_status_string",
            "gemm_bt_version", "gemm_bt_plan", "gemm_bt_plan_batched", "gemm_bt_plan_layout",
            "gemm_bt_plan_batched_layout", "gemm_bt_tile_coord", "gemm_bt_ws", "gemm_bt_workspace_size",
@@ -65,6 +66,8 @@ class Plan(ctypes.Structure):
 def load():
     """Load the shared library (raises if it has not been built)."""
     global _lib
+    if _lib is not None:  # fast path for the raw calls below, made once per launch
+        return _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB_PATH):

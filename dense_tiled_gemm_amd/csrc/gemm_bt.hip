@@ -443,6 +443,10 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
     }
     const bool big = tiles_l >= num_cu;
     p->group_m = kGroupM;
+#ifdef GEMM_BT_TUNING
+    // tile-row band height of the banded order (GEMM_BT_GROUP_M=1 walks each die's run row by row)
+    if (const char* e = std::getenv("GEMM_BT_GROUP_M")) p->group_m = std::atoi(e) > 0 ? std::atoi(e) : kGroupM;
+#endif
     p->ksplit = 1;
     // the DMA kernel needs 4-byte aligned rows; a K tail that is not a whole
     // 16-byte chunk is added after its loop
