@@ -148,18 +148,20 @@ int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch,
 
 /*
  * C = A * B^T with a caller-provided workspace that lets the library split
- * the K range of output tiles over workgroups (stream-K: "Writing Mosaic GPU
- * kernels with Pallas", section "Cluster launch control", a persistent grid
- * with one workgroup per core that keeps every core busy to the end).  Where
- * the plain grid would leave compute units idle in its last wave of tiles
- * (e.g. 1000 x 3000 outputs in 192 tiles of 128 x 128 for 256 compute
- * units), a persistent grid of one workgroup per compute unit gives every
- * workgroup the same number of K steps; a tile computed in pieces by several
- * workgroups is added up by the last of them to finish, in K order, so the
- * result is the same bits on every run with the same sizes on the same
- * device.  The sum of each output is then formed in a different order than
- * gemm_bt's (pieces summed in fp32, then added), with the same accuracy
- * bound.  Where splitting does not pay, the call is exactly gemm_bt.
+ * the K range of output tiles over workgroups (the work split of stream-K:
+ * "Writing Mosaic GPU kernels with Pallas", section "Cluster launch
+ * control", a grid that keeps every core busy to the end).  Where 16-bit
+ * products would leave at least half the compute units without a 128 x 128
+ * tile and K is long (e.g. 1024 x 1024 x 16384: 64 tiles for 256 compute
+ * units), each of the T tiles is split into S = floor(CUs / T) pieces of
+ * consecutive K steps (at least 32 steps of 64 each), one piece per
+ * workgroup; the last of a tile's workgroups to finish adds the pieces in K
+ * order (piece 0 + 1 + ...), whatever the order of arrival, so the result
+ * is the same bits on every run with the same sizes on the same device.
+ * The sum of each output is then formed in a different order than gemm_bt's
+ * (pieces summed in fp32, then added), with the same accuracy bound.  Where
+ * no split is planned (every other shape, batches, 8-bit inputs, operands
+ * stored K-outer) the call is exactly gemm_bt.
  *   A, B, C, M, N, K, in_dtype, out_dtype, stream: as for gemm_bt
  *   workspace        device memory of at least workspace_bytes, 16-byte
  *                    aligned, owned by the caller, or NULL (then the call is
