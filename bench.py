@@ -479,7 +479,8 @@ def main():
         sec = {}
         for name in ("m1024_n4096_k4096_f16_f16", "skinny_m16_n8192_k8192_bf16_bf16", "sq512_bf16_f32",
                      "ragged_m1000_n3000_k2050_bf16_f32", "sq4096_e4m3_bf16", "sq4096_i8_i32",
-                     "batch64_sq512_bf16_bf16", "sq4096_nn_bf16_bf16", "splitk_m1024_n1024_k16384_bf16_bf16"):
+                     "batch64_sq512_bf16_bf16", "sq4096_nn_bf16_bf16", "splitk_m1024_n1024_k16384_bf16_bf16",
+                     "oddk_m1000_n3000_k2049_bf16_f32"):
             w2 = synth.WORKLOADS[name]
             c2 = Case(w2, torch, gb)
             r2 = c2.time(max(50, args.steps // 2) if not args.no_settle else args.steps, args.warmup,

@@ -1,5 +1,5 @@
 // dma_kernel.hpp -- LDS-tiled MFMA kernel for C = A * B^T with direct
-// global->LDS loads and a multi-stage LDS ring (gfx950, 16-byte aligned rows).
+// global->LDS loads and a multi-stage LDS ring (gfx950).
 //
 // Same computation and lane maps as staged_kernel (tiled_kernel.hpp); what
 // changes is how tiles reach LDS:
@@ -214,8 +214,10 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const u32 row_bytes = (u32)K * (u32)ESZ;
-    // Only whole 16-byte chunks go through the LDS DMA: k < Kf.  When rows are
-    // 4-byte aligned but K % 8 != 0, the last K - Kf (2, 4 or 6) elements of
+    // Only whole 16-byte chunks go through the LDS DMA: k < Kf.  Rows need no
+    // more than 2-byte alignment: the buffer unit accepts 16-byte loads at
+    // any even address (a chunk that straddles a 16-byte boundary costs a
+    // second access).  When K % 8 != 0, the last K - Kf (1 to 7) elements of
     // every row are added after the loop (see the tail below).
     const int Kf = K & ~(EPC - 1);
     const int nk_all = (Kf + BK - 1) / BK;  // K steps of a whole tile
@@ -266,22 +268,22 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     // k < Ke: the whole chunks of this K range (loads past it come back as zeros)
     const int Ke = min(Kf, ke * BK);
     const bool with_tail = ESZ == 2 && Kf != K && ke == nk_all;
-    // K tail (see after the loop): thread t fetches the last K - Kf elements
-    // (1 to 3 dwords; rows and K are 4-byte aligned here) of tile row t (A
-    // rows first, then B rows) now, so that their latency hides behind the
-    // main loop.  Being older than every ring load, they are also covered by
-    // each of the ring's vmcnt waits.
-    u32 tail_v[3] = {0u, 0u, 0u};
+    // K tail (see after the loop): thread t fetches the last K - Kf (1 to 7)
+    // elements of tile row t (A rows first, then B rows) now, one 16-bit
+    // load each (rows may be only 2-byte aligned), so that their latency
+    // hides behind the main loop.  Being older than every ring load, they are
+    // also covered by each of the ring's vmcnt waits.
+    u32 tail_v[4] = {0u, 0u, 0u, 0u};
     if (with_tail) {
         const int r = threadIdx.x;
         const bool in_a = r < BM;
         const bool valid = in_a ? r < rows_a : (r < BM + BN && r - BM < rows_b);
         if (valid) {
-            const u32* src = (const u32*)(in_a ? Ap + (size_t)(m0 + r) * K + Kf : Bp + (size_t)(n0 + r - BM) * K + Kf);
-            const int nd = (K - Kf) >> 1;
+            const u16* src = in_a ? Ap + (size_t)(m0 + r) * K + Kf : Bp + (size_t)(n0 + r - BM) * K + Kf;
+            const int t = K - Kf;
 #pragma unroll
-            for (int d = 0; d < 3; ++d)
-                if (d < nd) tail_v[d] = __builtin_nontemporal_load(src + d);
+            for (int e = 0; e < 7; ++e)
+                if (e < t) tail_v[e >> 1] |= (u32)__builtin_nontemporal_load(src + e) << (16 * (e & 1));
         }
     }
 
@@ -680,19 +682,19 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     wait_vmcnt<0>();  // the ring's last (out-of-range) loads still write LDS
 
     if (with_tail) {
-        // K tail: the last K - Kf (2, 4 or 6) elements of every row form one
+        // K tail: the last K - Kf (1 to 7) elements of every row form one
         // more K tile, zero-padded, written into LDS stage 0 in the same
         // swizzled layout and multiplied like the others.  It comes after all
         // whole chunks, so each sum still runs over k in order.
         barrier_no_fence();  // every wave is past its last read of the ring
         const int r = threadIdx.x;  // tile row r: A rows 0 .. BM-1, then B rows
         if (r < BM + BN) {
-            // chunk 0 holds elements Kf .. Kf+7 (the fetched dwords, zeros
+            // chunk 0 holds elements Kf .. Kf+7 (the fetched elements, zeros
             // past K and for rows past M or N); the other chunks are zero
 #pragma unroll
             for (int c = 0; c < CPR; ++c)
                 *(u32x4*)(lds + r * ROWB + ((c ^ swz_row<CPR, SWZ>(r)) * 16)) =
-                    c == 0 ? u32x4{tail_v[0], tail_v[1], tail_v[2], 0u} : u32x4{0u, 0u, 0u, 0u};
+                    c == 0 ? u32x4{tail_v[0], tail_v[1], tail_v[2], tail_v[3]} : u32x4{0u, 0u, 0u, 0u};
         }
         __syncthreads();
         Frag tb[FN], ta[FM];

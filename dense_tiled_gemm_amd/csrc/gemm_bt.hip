@@ -10,7 +10,9 @@
 #include "dma_kernel.hpp"
 #include "skinny_dma.hpp"
 #include "skinny_kernel.hpp"
-#include "tiled_kernel.hpp"
+#ifdef GEMM_BT_TUNING
+#include "tiled_kernel.hpp"  // register-staged loads: a measured alternative to the DMA kernel
+#endif
 #include "trans_kernel.hpp"
 
 namespace gbt {
@@ -25,14 +27,15 @@ __global__ void zero_fill_kernel(u16* __restrict__ c, size_t n16, long long sc) 
 
 enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3, KIND_DMA = 4, KIND_TRANS = 5 };
 
-// Tile shapes.  The aligned path (16-byte loads) uses dma_kernel; rows that
-// are not 16-byte aligned use the register-staged kernel with narrower loads.
+// Kernels.  Products with M > 16 run dma_kernel (direct global->LDS loads of
+// 16-byte chunks, from rows of any even alignment) in one of the tile shapes
+// of dma_variants().  Skinny products (M <= 16): 16-byte aligned rows use
+// skinny_dma_kernel (8 rows of B per single-wave workgroup, 256-element K
+// stages in a 3-deep LDS ring); other alignments use the register-streaming
+// skinny_kernel (32 rows, K split over 4 waves).  The tuning build also has
+// the register-staged tiled kernel (GEMM_BT_FORCE_TILE=STAGED):
 //   staged L: 256 x 256, 8 waves as 2 x 4 (each wave 128 x 64), BK 64, 2 stages.
 //   staged M: 128 x 128, 4 waves as 2 x 2 (each wave 64 x 64), BK 64, 2 stages.
-// Skinny (M <= 16): aligned rows use skinny_dma_kernel (32 rows of B per
-// workgroup, 256-element K stages in a 6-deep LDS ring, 4 waves); other
-// alignments use the register-streaming skinny_kernel (32 rows, K split over
-// 4 waves).
 struct TileCfg {
     int bm, bn, wm, wn;
 };
@@ -448,9 +451,9 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
     if (const char* e = std::getenv("GEMM_BT_GROUP_M")) p->group_m = std::atoi(e) > 0 ? std::atoi(e) : kGroupM;
 #endif
     p->ksplit = 1;
-    // the DMA kernel needs 4-byte aligned rows; a K tail that is not a whole
-    // 16-byte chunk is added after its loop
-    if (p->vec >= 2 && !forced_staged()) {
+    // the DMA kernel takes rows of any (2-byte) alignment; a K tail that is
+    // not a whole 16-byte chunk is added after its loop
+    if (!forced_staged()) {
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
         // 256x256 when that fills every CU (dma_large_tier); else 128x128
@@ -485,6 +488,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         p->lds_bytes = v.lds_bytes;
         if (allow_sk && f < 0 && batch == 1 && plan_split_rule(M, N, K, num_cu, p)) return GEMM_BT_OK;
     } else {
+        // tuning build only (GEMM_BT_FORCE_TILE=STAGED): the register-staged kernel
         const TileCfg c = big ? kCfgL : kCfgM;
         p->kernel = KIND_TILED;
         p->variant = big ? 0 : 1;
@@ -599,6 +603,7 @@ static const void* trans_fn_out(int out, int variant) {
 typedef void (*TiledFn)(const u16*, const u16*, void*, int, int, int, int, int, int, int);
 typedef void (*SkinnyFn)(const u16*, const u16*, void*, int, int, int, int);
 
+#ifdef GEMM_BT_TUNING
 template <int IN, int OUT, int VEC>
 static const void* tiled_fn(int cfg) {
     if (cfg == 0)
@@ -619,6 +624,8 @@ static const void* tiled_fn_out(int out, int cfg, int vec) {
     if (out == GEMM_BT_BF16) return tiled_fn_vec<IN, GEMM_BT_BF16>(cfg, vec);
     return tiled_fn_vec<IN, GEMM_BT_F16>(cfg, vec);
 }
+
+#endif
 
 template <int IN, int OUT>
 static const void* skinny_fn_vec(int vec) {
@@ -798,12 +805,14 @@ static int launch_inner(const void* A, const void* B, void* C, int64_t batch, in
             const unsigned gx = (unsigned)(p.split_tiles > 0 ? p.grid : p.grid * batch);
             void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store, &itm, &sa, &sb, &sc, &ska};
             e = hipLaunchKernel(fn, dim3(gx), dim3(p.threads), args, 0, s);
+#ifdef GEMM_BT_TUNING
         } else if (p.kernel == KIND_TILED) {
             const void* fn = in_dtype == GEMM_BT_BF16 ? tiled_fn_out<GEMM_BT_BF16>(out_dtype, p.variant, p.vec)
                                                       : tiled_fn_out<GEMM_BT_F16>(out_dtype, p.variant, p.vec);
             int tm = (int)(p.tiles_m * batch), tn = (int)p.tiles_n, gm = p.group_m, itm = (int)p.tiles_m;
             void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &tm, &tn, &gm, &vec_store, &itm, &sa, &sb, &sc};
             e = hipLaunchKernel(fn, dim3((unsigned)(p.grid * batch)), dim3(p.threads), args, 0, s);
+#endif
         } else {
             const void* fn;
             if (p.variant >= 1) {

@@ -219,8 +219,8 @@ int gemm_bt_version(void);
  */
 typedef struct {
     int kernel;       /* 0 = none (empty), 1 = zero fill (K == 0), 2 = LDS-tiled MFMA with register-staged
-                         loads (rows not 16-byte aligned), 3 = skinny streaming (M <= 16), 4 = LDS-tiled
-                         MFMA with direct global->LDS loads (16-byte aligned rows), 5 = LDS-tiled MFMA
+                         loads (no longer planned: kind 4 takes every row alignment), 3 = skinny streaming
+                         (M <= 16), 4 = LDS-tiled MFMA with direct global->LDS loads, 5 = LDS-tiled MFMA
                          with LDS transpose reads (an operand stored K-outer) */
     int variant;      /* tile-shape variant index within the kernel family */
     int bm, bn, bk;   /* workgroup tile (rows of C, columns of C, K step) */

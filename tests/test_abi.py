@@ -85,8 +85,9 @@ def test_batched_plan():
     assert gb.gemm_bt_plan_batched(4, 64, 64, 0, gb.BF16, gb.BF16).kernel == 1
     with pytest.raises(gb.GemmBtError):
         gb.gemm_bt_plan_batched(65536, 64, 64, 64, gb.BF16, gb.BF16)
-    # an item stride that breaks 16-byte alignment narrows the loads, or is refused for 8-bit inputs
-    assert gb.gemm_bt_plan_batched(2, 64, 64, 64, gb.BF16, gb.F32, a_align=2).kernel == 2
+    # an item stride that breaks 16-byte alignment: unaligned DMA loads for 16-bit inputs, refused for 8-bit ones
+    p = gb.gemm_bt_plan_batched(2, 64, 64, 64, gb.BF16, gb.F32, a_align=2)
+    assert (p.kernel, p.vec) == (4, 1)  # 2-byte aligned rows: the DMA kernel, unaligned 16-byte loads
     with pytest.raises(gb.GemmBtError):
         gb.gemm_bt_plan_batched(2, 64, 64, 64, gb.FP8_E4M3, gb.F32, b_align=8)
 
@@ -208,7 +209,8 @@ def test_plan_choices():
     assert (p.kernel, p.bm, p.bn, p.grid) == (4, 128, 128, 256)
     p = gb.gemm_bt_plan(1000, 3000, 2050, gb.BF16, gb.F32)  # 4-byte rows: DMA kernel + K tail
     assert (p.kernel, p.bm, p.bn, p.vec, p.tiles_m, p.tiles_n) == (4, 128, 128, 2, 8, 24)
-    assert gb.gemm_bt_plan(1000, 3000, 2049, gb.BF16, gb.F32).kernel == 2  # 2-byte rows: register-staged
+    p = gb.gemm_bt_plan(1000, 3000, 2049, gb.BF16, gb.F32)
+    assert (p.kernel, p.bm, p.vec) == (4, 128, 1)  # 2-byte aligned rows take the DMA kernel too
     p = gb.gemm_bt_plan(16, 8192, 8192, gb.BF16, gb.BF16)
     assert (p.kernel, p.bm, p.bn, p.ksplit, p.grid) == (3, 16, 8, 1, 1024)
     # several streaming workgroups fit on one CU

@@ -102,6 +102,10 @@ SHAPES = [
     (2048, 4096, 136), (2000, 4000, 200), (2048, 4096, 130), (2048, 4004, 72), (2048, 3999, 64), (3072, 4096, 72),
     # 304 tiles of 256x256 (1.19 waves, the edge of the band that takes smaller tiles)
     (4864, 4096, 136),
+    # odd K: rows only 2-byte aligned (every other row starts mid-dword), K tails of 1 to 7 elements, on
+    # every tile tier and with no whole chunk at all
+    (130, 264, 73), (300, 520, 1007), (64, 64, 7), (1000, 3000, 2051), (4096, 4096, 131), (2048, 4096, 135),
+    (4100, 4100, 137), (96, 200, 35),
 ]
 SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200)]
 
@@ -453,7 +457,7 @@ def run_batched(gb, Z, M, N, K, in_dtype, out_dtype, share=None, pad=(0, 0, 0), 
 
 
 # (Z, M, N, K, in, out, shared operand, element padding of A, B, C items): the 64x64, 128x128 and
-# 256x256 tiers, the register-staged kernel (odd K, or an odd item stride), both streaming kernels,
+# 256x256 tiers, 2-byte aligned rows (odd K, or an odd item stride), both streaming kernels,
 # 8-bit inputs, shared A and shared B
 BATCHED = [
     (3, 130, 260, 72, "bf16", "f32", None, (0, 0, 0)),
@@ -674,6 +678,7 @@ def test_graph_capture_replays_match_eager(gpu):
 @pytest.mark.parametrize("M,N,K,ind,outd", [
     (32, 40, 4194296, "bf16", "f32"),    # tiled kernel: 256 rows of K at the 32-bit panel limit (K % 8 == 0)
     (33, 24, 4194298, "f16", "f16"),     # tiled kernel with a K tail of 2
+    (40, 33, 4194303, "bf16", "f32"),    # the largest K: odd, rows 2-byte aligned, a K tail of 7
     (16, 24, 4194296, "bf16", "bf16"),   # streaming kernel (M <= 16)
     (32, 32, 8388592, "e4m3", "bf16"),   # 8-bit inputs: the largest K % 16 == 0 below the limit
 ])
@@ -815,7 +820,7 @@ def test_c_program_through_the_header(gpu):
 SK_CASES = [  # (M, N, K, in, out)
     (1024, 1024, 16384, "bf16", "bf16"), (512, 1024, 32768, "f16", "f16"), (1000, 1000, 8200, "bf16", "f32"),
     (300, 700, 30002, "bf16", "f32"), (130, 4100, 8192, "f16", "f16"), (200, 1999, 17000, "bf16", "f32"),
-    (64, 8192, 8192, "bf16", "bf16"), (1024, 2048, 8192, "f16", "f32"),
+    (64, 8192, 8192, "bf16", "bf16"), (1024, 2048, 8192, "f16", "f32"), (1024, 1024, 16383, "bf16", "f32"),
 ]
 
 
