@@ -9,7 +9,9 @@
 #include "common.hpp"
 #include "dma_kernel.hpp"
 #include "skinny_dma.hpp"
-#include "skinny_kernel.hpp"
+#ifdef GEMM_BT_TUNING
+#include "skinny_kernel.hpp"  // register streaming: a measured alternative to skinny_dma_kernel
+#endif
 #ifdef GEMM_BT_TUNING
 #include "tiled_kernel.hpp"  // register-staged loads: a measured alternative to the DMA kernel
 #endif
@@ -29,11 +31,11 @@ enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3, KIND_
 
 // Kernels.  Products with M > 16 run dma_kernel (direct global->LDS loads of
 // 16-byte chunks, from rows of any even alignment) in one of the tile shapes
-// of dma_variants().  Skinny products (M <= 16): 16-byte aligned rows use
-// skinny_dma_kernel (8 rows of B per single-wave workgroup, 256-element K
-// stages in a 3-deep LDS ring); other alignments use the register-streaming
-// skinny_kernel (32 rows, K split over 4 waves).  The tuning build also has
-// the register-staged tiled kernel (GEMM_BT_FORCE_TILE=STAGED):
+// of dma_variants().  Skinny products (M <= 16) run skinny_dma_kernel (8 rows
+// of B per single-wave workgroup, 256-element K stages in a 3-deep LDS ring,
+// rows of any even alignment too).  The tuning build also has the
+// register-streaming skinny_kernel (GEMM_BT_FORCE_SKINNY=REG: 32 rows, K split
+// over 4 waves) and the register-staged tiled kernel (GEMM_BT_FORCE_TILE=STAGED):
 //   staged L: 256 x 256, 8 waves as 2 x 4 (each wave 128 x 64), BK 64, 2 stages.
 //   staged M: 128 x 128, 4 waves as 2 x 2 (each wave 64 x 64), BK 64, 2 stages.
 struct TileCfg {
@@ -229,8 +231,10 @@ static const SkinnyVariant* skinny_variants(int* count) {
 }
 
 #ifdef GEMM_BT_TUNING
+constexpr int kSkinnyReg = -3;  // forced_skinny(): the register-streaming kernel
 static int forced_skinny() {
-    // Benchmarking aid: GEMM_BT_FORCE_SKINNY=<variant name>.
+    // Benchmarking aid: GEMM_BT_FORCE_SKINNY=<variant name>, or REG for the
+    // register-streaming kernel.
     static std::atomic<int> cached{-2};
     int v = cached.load(std::memory_order_relaxed);
     if (v == -2) {
@@ -240,6 +244,7 @@ static int forced_skinny() {
         const SkinnyVariant* vs = skinny_variants(&n);
         for (int i = 0; e && i < n; ++i)
             if (std::strcmp(e, vs[i].name) == 0) v = i;
+        if (e && std::strcmp(e, "REG") == 0) v = kSkinnyReg;
         cached.store(v, std::memory_order_relaxed);
     }
     return v;
@@ -275,6 +280,7 @@ static int forced_variant() {
 }
 #else
 // The production library takes no tuning overrides.
+constexpr int kSkinnyReg = -3;
 static int forced_skinny() { return -1; }
 static bool forced_staged() { return false; }
 static int forced_variant() { return -1; }
@@ -416,11 +422,13 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         p->kernel = KIND_SKINNY;
         p->bm = 16;
         p->tiles_m = 1;
-        if (p->vec == 8) {
+        // the streaming DMA kernel takes rows of any (2-byte) alignment; the
+        // register-streaming kernel is a tuning-build alternative
+        const int f = forced_skinny();
+        if (f != kSkinnyReg) {
             int n = 0;
             const SkinnyVariant* vs = skinny_variants(&n);
             int use = 0;
-            const int f = forced_skinny();
             if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
             const SkinnyVariant& v = vs[use];
             p->variant = 1 + use;
@@ -627,6 +635,7 @@ static const void* tiled_fn_out(int out, int cfg, int vec) {
 
 #endif
 
+#ifdef GEMM_BT_TUNING
 template <int IN, int OUT>
 static const void* skinny_fn_vec(int vec) {
     if (vec == 2) return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 2>;
@@ -639,6 +648,7 @@ static const void* skinny_fn_out(int out, int vec) {
     if (out == GEMM_BT_BF16) return skinny_fn_vec<IN, GEMM_BT_BF16>(vec);
     return skinny_fn_vec<IN, GEMM_BT_F16>(vec);
 }
+#endif
 
 // ---- device checks -------------------------------------------------------------
 
@@ -814,13 +824,15 @@ static int launch_inner(const void* A, const void* B, void* C, int64_t batch, in
             e = hipLaunchKernel(fn, dim3((unsigned)(p.grid * batch)), dim3(p.threads), args, 0, s);
 #endif
         } else {
-            const void* fn;
+            const void* fn = nullptr;
             if (p.variant >= 1) {
                 int n = 0;
                 fn = skinny_variants(&n)[p.variant - 1].fn[in_index(in_dtype)][out_index(out_dtype)];
             } else {
+#ifdef GEMM_BT_TUNING
                 fn = in_dtype == GEMM_BT_BF16 ? skinny_fn_out<GEMM_BT_BF16>(out_dtype, p.vec)
                                               : skinny_fn_out<GEMM_BT_F16>(out_dtype, p.vec);
+#endif
             }
             void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &vec_store, &sa, &sb, &sc};
             e = hipLaunchKernel(fn, dim3((unsigned)p.grid, gy), dim3(p.threads), args, 0, s);

@@ -1,5 +1,5 @@
-// skinny_dma.hpp -- streaming MFMA kernel for C = A * B^T with M <= 16 and
-// 16-byte aligned rows (gfx950).
+// skinny_dma.hpp -- streaming MFMA kernel for C = A * B^T with M <= 16
+// (gfx950).
 //
 // With at most 16 rows in A the product is bound by reading B once from HBM
 // (2 bytes per multiply-add pair): a 16-row tile has an arithmetic intensity
@@ -25,9 +25,14 @@
 //     of C) and A as second, fp32 accumulators; at the end the W partial sums
 //     are added through LDS in a fixed order, rounded once and stored masked
 //     to i < M, j < N;
-//   * rows of A past M and of B past N, and k >= K, read as zero through the
-//     buffer range check ("Chapter 7", section 4.3: zero the K overhang of
-//     both operands).
+//   * rows of A past M and of B past N, and chunks at k >= K, read as zero
+//     through the buffer range check ("Chapter 7", section 4.3: zero the K
+//     overhang of both operands);
+//   * rows need only 2-byte alignment: the LDS DMA moves the whole 16-byte
+//     chunks below Kf = K & ~7 from any even address, and the last K - Kf
+//     (1 to 7) elements of each row, fetched with 16-bit loads before the
+//     loop, form one more zero-padded k-block multiplied after it, so each
+//     sum still runs over k in increasing order.
 #pragma once
 
 #include "common.hpp"
@@ -94,15 +99,16 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
         kc[i] = c * 8;
         is_a[i] = a;
     }
-    const int nk = (K + KB - 1) / KB;
+    const int Kf = K & ~7;  // whole 16-byte chunks: through the LDS DMA
+    const int nk = (Kf + KB - 1) / KB;
     // ROT > 0: workgroup g walks the K steps starting at (g * ROT) mod nk and
     // wraps around, so that concurrent workgroups read different K offsets
-    const int k0 = ROT > 0 ? (int)(((long long)blockIdx.x * ROT) % nk) : 0;
+    const int k0 = ROT > 0 && nk > 0 ? (int)(((long long)blockIdx.x * ROT) % nk) : 0;
     auto issue = [&](int stage, int kstep) {
         const int kt = ROT > 0 ? (kstep + k0 >= nk ? kstep + k0 - nk : kstep + k0) : kstep;
         unsigned char* sbase = lds + stage * STAGE_BYTES;
         const u32 kbytes = (u32)kt * (u32)ROWB;
-        const int kleft = K - kt * KB;
+        const int kleft = Kf - kt * KB;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int j = wave + i * W;
@@ -118,6 +124,28 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
     // Operand reads: lane (r = l%16, q = l/16) reads row r of a 16-row block,
     // logical chunk 4*kb + q.
     const int r16 = lane & 15, q = lane >> 4;
+    // K tail: in the extra k-block, lanes with q = 0 hold elements Kf ..
+    // Kf + 7 of their row (zeros past K and for rows past M or N); the other
+    // lanes' chunks are zero.  Fetched now so the loads hide behind the loop.
+    const int tail = K - Kf;
+    u32x4 ta = {0u, 0u, 0u, 0u}, tb[NBLK];
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) tb[b] = u32x4{0u, 0u, 0u, 0u};
+    if (tail > 0 && wave == 0 && q == 0) {
+        auto fetch = [&](const u16* src) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 7; ++e)
+                if (e < tail) v[e >> 1] |= (u32)__builtin_nontemporal_load(src + e) << (16 * (e & 1));
+            return v;
+        };
+        if (r16 < rows_a) ta = fetch(A + (size_t)r16 * K + Kf);
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) {
+            const int br = 16 * b + (r16 % BR);  // B row of the operand's row r16 within this block
+            if (br < rows_b) tb[b] = fetch(B + (size_t)(n0 + br) * K + Kf);
+        }
+    }
     f32x4 acc[NBLK];
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -153,6 +181,9 @@ __global__ __launch_bounds__(64 * W) void skinny_dma_kernel(const u16* __restric
         ls = ls + 1 == STAGES ? 0 : ls + 1;
     }
     wait_vmcnt<0>();
+    if (tail > 0 && wave == 0)
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) acc[b] = Mfma<IN>::m16x16x32(tb[b], ta, acc[b]);
 
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) red[wave][b][lane] = acc[b];

@@ -215,7 +215,10 @@ def test_plan_choices():
     assert (p.kernel, p.bm, p.bn, p.ksplit, p.grid) == (3, 16, 8, 1, 1024)
     # several streaming workgroups fit on one CU
     assert 4 * p.lds_bytes <= 160 * 1024 and p.stages >= 3
-    assert gb.gemm_bt_plan(16, 8192, 8190, gb.BF16, gb.BF16).variant == 0  # narrow loads: register streaming
+    # rows that are not 16-byte aligned stream through the same kernel (unaligned DMA, K tail after the loop)
+    for K, al in ((8190, 256), (8191, 256), (8192, 2)):
+        q = gb.gemm_bt_plan(16, 8192, K, gb.BF16, gb.BF16, a_align=al)
+        assert (q.kernel, q.variant, q.bn, q.grid) == (3, 1, 8, 1024) and q.vec < 8
     # 8-bit float inputs: the LDS-DMA kernel with 128-element K steps, also for M <= 16
     for code in (gb.FP8_E4M3, gb.FP8_E5M2):
         p = gb.gemm_bt_plan(4096, 4096, 4096, code, gb.BF16)

@@ -107,7 +107,9 @@ SHAPES = [
     (130, 264, 73), (300, 520, 1007), (64, 64, 7), (1000, 3000, 2051), (4096, 4096, 131), (2048, 4096, 135),
     (4100, 4100, 137), (96, 200, 35),
 ]
-SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200)]
+SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200),
+          # K tails of 7 and 1 element, odd K with no whole chunk, 2-byte aligned rows
+          (16, 8192, 8191), (11, 300, 1001), (16, 1000, 7)]
 
 
 @pytest.mark.parametrize("in_dtype", ["bf16", "f16"])
