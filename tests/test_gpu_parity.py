@@ -624,11 +624,17 @@ def test_mm_wrapper_is_a_times_b(gpu):
 # ---------------------------------------------------------------- graph capture
 
 def test_graph_capture_replays_match_eager(gpu):
-    """Calls captured into a HIP graph (plain, batched, K-outer, int8, K = 0) replay bit for bit like eager
-    calls, several times, with eager work and synchronisation between the replays.  The library allocates
-    nothing and clears memory with a kernel, never a memset node."""
+    """Calls captured into a HIP graph (plain, batched, K-outer, int8, K = 0, split K through a workspace)
+    replay bit for bit like eager calls, several times, with eager work and synchronisation between the
+    replays.  The library allocates nothing and clears memory with a kernel, never a memset node; the split
+    kernel leaves its counters zero for the next replay."""
     say("graph capture")
     a, b = synth.make(300, 520, 136, "bf16", "normal", 1400)
+    ask, bsk = synth.make(1024, 1024, 8192, "bf16", "normal", 1403)
+    Ask, Bsk = to_dev(ask, "bf16"), to_dev(bsk, "bf16")
+    need = gpu.gemm_bt_workspace_size(1024, 1024, 8192, gpu.BF16, gpu.F32)
+    assert need > 0, "the split plan must be taken"
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     a3, b3 = synth.make_batched(3, 64, 96, 64, "f16", "normal", 1401)
     a8, b8 = synth.make(130, 260, 160, "i8", "int8", 1402)
     A, B = to_dev(a, "bf16"), to_dev(b, "bf16")
@@ -639,7 +645,8 @@ def test_graph_capture_replays_match_eager(gpu):
             torch.empty(300, 520, dtype=torch.float32, device="cuda"),
             torch.empty(3, 64, 96, dtype=torch.float16, device="cuda"),
             torch.empty(130, 260, dtype=torch.int32, device="cuda"),
-            torch.full((40, 24), float("nan"), dtype=torch.float32, device="cuda")]
+            torch.full((40, 24), float("nan"), dtype=torch.float32, device="cuda"),
+            torch.empty(1024, 1024, dtype=torch.float32, device="cuda")]
 
     def work(stream):
         s = stream.cuda_stream
@@ -650,6 +657,8 @@ def test_graph_capture_replays_match_eager(gpu):
                                    64 * 96, gpu.F16, gpu.F16, s) == 0
         assert gpu.gemm_bt(A8.data_ptr(), B8.data_ptr(), outs[3].data_ptr(), 130, 260, 160, gpu.INT8, gpu.INT32, s) == 0
         assert gpu.gemm_bt(A.data_ptr(), B.data_ptr(), outs[4].data_ptr(), 40, 24, 0, gpu.BF16, gpu.F32, s) == 0
+        assert gpu.gemm_bt_ws(Ask.data_ptr(), Bsk.data_ptr(), outs[5].data_ptr(), 1024, 1024, 8192, gpu.BF16,
+                              gpu.F32, ws.data_ptr(), need, s) == 0
 
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
@@ -673,6 +682,12 @@ def test_graph_capture_replays_match_eager(gpu):
     check_full(eager[1].cpu(), a, b, "bf16", "f32", "graph K-outer")
     assert np.array_equal(eager[3].cpu().numpy().astype(np.int64), oracle.gemm_bt_i8(a8, b8))
     assert (eager[4] == 0).all()
+    assert int(ws[:gpu.SK_COUNTER_BYTES].count_nonzero()) == 0
+    I, J = sample_entries(1024, 1024, np.random.default_rng(1404), tile=128)
+    ref = oracle.gemm_bt_entries(ask, bsk, "bf16", I, J)
+    norms = oracle.row_norms(ask, "bf16")[I] * oracle.row_norms(bsk, "bf16")[J]
+    rep = tolerance.check(f64(eager[5].cpu())[I, J], ref, norms, "f32")
+    assert rep.ok, ("graph split-K", rep)
 
 
 # ---------------------------------------------------------------- the largest supported K
