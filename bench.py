@@ -246,10 +246,12 @@ class Case:
         if st != self.gb.OK:
             raise self.gb.GemmBtError(st)
 
-    def settle(self, stream, batch=25, max_s=0.5, max_launches=4000, patience=3):
-        """Untimed launches until the per-launch time stops falling: batches of `batch` launches, stopping after
-        `patience` batches in a row that are no more than 0.5 % faster than the best so far, or at the bounds.
-        Returns (launches, ms)."""
+    def settle(self, stream, batch=25, min_ms=60.0, max_s=0.6, max_launches=6000, patience=3):
+        """Untimed launches until the per-launch time stops falling: batches of `batch` launches for at least
+        `min_ms` of load (from idle the 4096^3 launches take 124 us in the second batch and reach their steady
+        95-96 us only after 40-55 ms; 1024x4096x4096 first slows from 41 to 48 us, then settles near 39.5 us
+        after 30-40 ms), then until `patience` batches in a row are no more than 0.5 % faster than the best so
+        far, or at the bounds.  Returns (launches, ms)."""
         torch = self.torch
         sh = stream.cuda_stream
         e0 = torch.cuda.Event(enable_timing=True)
@@ -268,7 +270,8 @@ class Case:
                 best, stale = per, 0
             else:
                 stale += 1
-            if stale >= patience or time.perf_counter() - t0 > max_s or n >= max_launches:
+            elapsed = time.perf_counter() - t0
+            if (stale >= patience and elapsed * 1e3 >= min_ms) or elapsed > max_s or n >= max_launches:
                 break
         return n, (time.perf_counter() - t0) * 1e3
 
