@@ -173,6 +173,13 @@ def test_wide_tier_and_split_plans():
     assert tile(4096, 4096) == (256, 256)
     assert tile(512, 1024, K=72, batch=16) == (128, 256)         # items stacked: 256 tiles
     assert tile(2048, 4096, ind=gb.FP8_E4M3) != (128, 256)       # 16-bit inputs only
+    # 96x128 tiles for a single product when they make at most one wave and keep more CUs busy than 128x128
+    assert tile(768, 4096) == tile(3000, 1000) == tile(700, 3200) == (96, 128)   # 256, 256, 200 tiles
+    assert tile(1000, 3000) == tile(2048, 1536) == (128, 128)                      # 264 tiles of 96x128
+    assert tile(768, 4096, batch=2) == (128, 128)                                  # single products only
+    assert tile(768, 4096, ind=gb.FP8_E4M3) == (128, 128)                          # 16-bit inputs only
+    p = gb.gemm_bt_plan(768, 4096, 4096, gb.BF16, gb.BF16)
+    assert (p.threads, p.stages, p.grid, p.lds_bytes) == (256, 4, 256, 4 * (96 + 128) * 64 * 2)
     p = gb.gemm_bt_plan(2048, 4096, 4096, gb.BF16, gb.BF16)
     assert (p.threads, p.stages, p.lds_bytes) == (512, 3, 3 * (128 + 256) * 64 * 2)
     for M, N, K, T, S in [(1024, 1024, 16384, 64, 4), (512, 1024, 32768, 32, 8), (300, 700, 30002, 18, 14),

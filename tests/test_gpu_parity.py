@@ -102,6 +102,9 @@ SHAPES = [
     (2048, 4096, 136), (2000, 4000, 200), (2048, 4096, 130), (2048, 4004, 72), (2048, 3999, 64), (3072, 4096, 72),
     # 304 tiles of 256x256 (1.19 waves, the edge of the band that takes smaller tiles)
     (4864, 4096, 136),
+    # 96x128 tiles (at most one wave of them, more than 128x128 tiles would use): one exact wave, partial tile
+    # rows and columns with a K tail, odd K
+    (768, 4096, 136), (700, 3200, 130), (3000, 1000, 72), (760, 4000, 137),
     # odd K: rows only 2-byte aligned (every other row starts mid-dword), K tails of 1 to 7 elements, on
     # every tile tier and with no whole chunk at all
     (130, 264, 73), (300, 520, 1007), (64, 64, 7), (1000, 3000, 2051), (4096, 4096, 131), (2048, 4096, 135),
