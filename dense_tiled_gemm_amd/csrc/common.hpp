@@ -318,12 +318,19 @@ __device__ inline void store_tile(const typename AccBlock<MF>::type (&acc)[FN][F
 }
 
 // Physical 16-byte chunk of logical chunk c in row r of the parked output
-// tile (rows of CPR chunks): c ^ (r mod min(32, CPR)), except for 128-byte
-// rows (CPR 8), where rows r and r + 8 start in the same bank half: there
-// row bits 1..3 are XORed in instead, so the 16 rows of one parking pass
-// (8-byte writes of 16-bit outputs, 32 lanes per pass) fill all 64 banks.
+// tile (rows of CPR chunks).  The 16 rows of one parking pass (16-byte
+// writes of fp32 outputs 16 lanes per pass, 8-byte writes of 16-bit outputs
+// 32 lanes per pass) must fill all 64 banks, so rows that start at the same
+// bank offset get different chunks: c ^ (r mod min(32, CPR)) for rows of 256
+// bytes or more; for 128- and 384-byte rows (CPR 8 and 24, two bank offsets,
+// rows r and r + 2 alike) row bits 1..3 are XORed into the chunk's low 3
+// bits; for 192-byte rows (CPR 12, four bank offsets) row bits 2..3 into its
+// low 2 bits.  Each form permutes chunks inside aligned groups of 8 or 4, so
+// it is a bijection on the row.
 __host__ __device__ inline int epi_chunk(int c, int r, int cpr) {
-    return cpr == 8 ? c ^ ((r >> 1) & 7) : c ^ (r & ((cpr < 32 ? cpr : 32) - 1));
+    if (cpr == 8 || cpr == 24) return c ^ ((r >> 1) & 7);
+    if (cpr == 12) return c ^ ((r >> 2) & 3);
+    return c ^ (r & ((cpr < 32 ? cpr : 32) - 1));
 }
 
 // Store the workgroup's BM x BN tile through LDS so that each global store
@@ -347,8 +354,9 @@ __device__ inline void store_tile_lds(const typename AccBlock<MF>::type (&acc)[F
     constexpr int CPR = ROWB / 16;  // 16-byte chunks per tile row
     constexpr int P = BM * ROWB <= LDS_BYTES ? 1 : WM;
     constexpr int RP = BM / P;  // tile rows per pass
-    static_assert(CPR >= 8 && (CPR & (CPR - 1)) == 0, "row chunks");
+    static_assert(CPR == 12 || CPR == 24 || (CPR >= 8 && (CPR & (CPR - 1)) == 0), "row chunks");
     static_assert(RP * ROWB <= LDS_BYTES, "a pass must fit in LDS");
+    static_assert((RP * CPR) % NT == 0, "the row copy covers a pass in whole rounds of NT threads");
     const size_t c_origin = (size_t)m0 * N + n0;
     const size_t c_rest = (size_t)M * N - c_origin;
     const u32 c_bytes = (u32)min(c_rest * OSZ, (size_t)0x7FFFFFFF);

@@ -717,10 +717,10 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     // the finished tile at rows m0.., columns n0.. of Cp
     // (tid_r: the thread index, recomputed per call for the same reason as
     // lane_r in run)
-    // the whole-row epilogue needs rows of C that are a power-of-two number
-    // (>= 8) of 16-byte chunks; other tile widths store directly
+    // the whole-row epilogue takes tile rows of 8, 12, 16, 24 or 2^n 16-byte
+    // chunks (epi_chunk); other tile widths store directly
     constexpr int OCPR = BN * (store_type(OUT) == GEMM_BT_F32 ? 4 : 2) / 16;
-    constexpr bool WHOLE_ROWS = OCPR >= 8 && (OCPR & (OCPR - 1)) == 0;
+    constexpr bool WHOLE_ROWS = OCPR == 12 || OCPR == 24 || (OCPR >= 8 && (OCPR & (OCPR - 1)) == 0);
     auto store_c = [&](void* Cp, int m0, int n0, Acc& acc) {
         int tid_r = threadIdx.x;
         asm volatile("" : "+v"(tid_r));

@@ -108,8 +108,8 @@ static DmaVariant dma_variant(const char* name) {
     return v;
 }
 
-// Index 0 is the default for large grids, 7, 1 and 8 for smaller ones, 2 and
-// 6 for the smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
+// Index 0 is the default for large grids, 7, 1, 8 and 9 for smaller ones, 2
+// and 6 for the smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
 // (128-element K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32
 // MFMAs over 64-element substeps).
 // A build with GEMM_BT_TUNING defined adds the measured alternatives after
@@ -119,6 +119,7 @@ constexpr int kFp8Variants = 3;
 constexpr int kTiny16 = 6;  // 32 x 64 tiles (16-bit inputs), when even 64 x 64 tiles leave half the CUs idle
 constexpr int kWide16 = 7;  // 128 x 256 tiles (16-bit inputs, 8 waves of 64 x 64), see plan_impl
 constexpr int kShort16 = 8;  // 96 x 128 tiles (16-bit inputs, 4 waves of 48 x 64), see plan_impl
+constexpr int kNarrow16 = 9;  // 128 x 96 tiles (16-bit inputs, 4 waves of 64 x 48), see plan_impl
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
@@ -130,6 +131,7 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<32, 64, 64, 4, 2, 2, 2, 2, 0, 16, true>("T32x64"),
         dma_variant<128, 256, 64, 3, 2, 4, 2, 8, 0, 16, true>("H128x256s3"),
         dma_variant<96, 128, 64, 4, 2, 2, 2, 6, 0, 16, true>("M96x128s4"),
+        dma_variant<128, 96, 64, 4, 2, 2, 2, 6, 0, 16, true>("M128x96s4"),
 #ifdef GEMM_BT_TUNING
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
@@ -148,7 +150,6 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<256, 128, 64, 3, 4, 2, 2, 8, 0, 16>("H256x128s3"),
         dma_variant<128, 256, 64, 2, 2, 4, 2, 8, 0, 16>("H128x256s2"),
         dma_variant<128, 128, 64, 2, 2, 2, 2, 8, 0, 16>("M64s2"),
-        dma_variant<128, 96, 64, 4, 2, 2, 2, 6, 0, 16, true>("M64x96s4"),
 #endif
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
@@ -486,17 +487,26 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         const int64_t tiles_h = ((M + 127) / 128) * ((N + 255) / 256) * batch;
         if (use == 1 && tiles_h >= num_cu && (tiles_h % num_cu == 0 || tiles_h * 8 > (int64_t)num_cu * 11))
             use = kWide16;
-        // 96 x 128 tiles instead of 128 x 128 ones for a single product when
-        // they still make at most one wave and keep more CUs busy: the last
-        // quarter of the CUs then works instead of idling.  Measured (us,
-        // 128 x 128 vs 96 x 128, bf16 unless noted): 768x4096x4096 37.1 vs
-        // 33.6, 3000x1000x4096 37.0 vs 32.1, 1536x2048x4096 29.2 vs 26.4,
-        // 700x3200x4096 (150 vs 200 tiles) 33.2 vs 29.6, 1152x2048x4096 26.6 vs
-        // 23.6, 768x4096x2048 16.9 vs 15.9, 768x4096x8192 f16 69.4 vs 62.1,
-        // 760x4000x4104 48.3 vs 45.8; with more tiles than CUs it loses
-        // (1000x3000x2050, 264 tiles: 24.3 vs 41.3).
+        // 96 x 128 or 128 x 96 tiles instead of 128 x 128 ones for a single
+        // product when they still make at most one wave and keep more CUs
+        // busy: the CUs that would idle in the one wave then work.  Of the two,
+        // the one with more tiles within the wave (96 x 128 on a tie).
+        // Measured (us, 128 x 128 vs the narrower tile, bf16 unless noted):
+        // 96 x 128: 768x4096x4096 37.1 vs 33.6, 3000x1000x4096 37.0 vs 32.1,
+        // 1536x2048x4096 29.2 vs 26.4, 700x3200x4096 (150 vs 200 tiles) 33.2 vs
+        // 29.6, 1152x2048x4096 26.6 vs 23.6, 768x4096x2048 16.9 vs 15.9,
+        // 768x4096x8192 f16 69.4 vs 62.1, 760x4000x4104 48.3 vs 45.8;
+        // 128 x 96: 1024x3072x4096 36.4 vs 33.3, 2048x1536x2048 17.3 vs 16.1,
+        // 1000x3000x2048 -> f32 18.8 vs 17.7, 1000x3000x2050 -> f32 24.6 vs
+        // 24.0.  With more tiles than CUs either loses (1000x3000x2050 on 264
+        // tiles of 96 x 128: 24.3 vs 41.3).
         const int64_t tiles_s = ((M + 95) / 96) * ((N + 127) / 128);
-        if (use == 1 && batch == 1 && tiles_s <= num_cu && tiles_s > tiles_m128) use = kShort16;
+        const int64_t tiles_n96 = ((M + 127) / 128) * ((N + 95) / 96);
+        if (use == 1 && batch == 1) {
+            const int64_t best = tiles_s <= num_cu ? tiles_s : 0, alt = tiles_n96 <= num_cu ? tiles_n96 : 0;
+            if (alt > best && alt > tiles_m128) use = kNarrow16;
+            else if (best > tiles_m128) use = kShort16;
+        }
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];

@@ -20,7 +20,7 @@ int main() {
         std::printf("swz 4 2 %d %d\n", row, swz_row<4, 2>(row));
     }
     for (int row = 0; row < 64; ++row) std::printf("kouter %d %d\n", row, kouter_swz(row));
-    const int cprs[] = {8, 16, 32, 64};
+    const int cprs[] = {8, 12, 16, 24, 32, 64};
     for (int cpr : cprs)
         for (int row = 0; row < 64; ++row)
             for (int c = 0; c < cpr; ++c) std::printf("epi %d %d %d %d\n", cpr, row, c, epi_chunk(c, row, cpr));

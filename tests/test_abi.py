@@ -174,8 +174,11 @@ def test_wide_tier_and_split_plans():
     assert tile(512, 1024, K=72, batch=16) == (128, 256)         # items stacked: 256 tiles
     assert tile(2048, 4096, ind=gb.FP8_E4M3) != (128, 256)       # 16-bit inputs only
     # 96x128 tiles for a single product when they make at most one wave and keep more CUs busy than 128x128
-    assert tile(768, 4096) == tile(3000, 1000) == tile(700, 3200) == (96, 128)   # 256, 256, 200 tiles
-    assert tile(1000, 3000) == tile(2048, 1536) == (128, 128)                      # 264 tiles of 96x128
+    assert tile(768, 4096) == tile(3000, 1000) == tile(1536, 2048) == (96, 128)  # 256 tiles each
+    # or 128x96 tiles when those make more tiles within the wave (96x128: 264, 264, 264, 200 against 204)
+    assert tile(1000, 3000) == tile(2048, 1536) == tile(1024, 3072) == tile(700, 3200) == (128, 96)
+    assert tile(1500, 1500) == (96, 128)                                           # 192 either way: 96x128
+    assert tile(3000, 3000) == tile(1024, 4096) == (128, 128)                      # 576, 256 tiles of 128x128
     assert tile(768, 4096, batch=2) == (128, 128)                                  # single products only
     assert tile(768, 4096, ind=gb.FP8_E4M3) == (128, 128)                          # 16-bit inputs only
     p = gb.gemm_bt_plan(768, 4096, 4096, gb.BF16, gb.BF16)
@@ -215,7 +218,7 @@ def test_plan_choices():
     p = gb.gemm_bt_plan(1024, 4096, 4096, gb.F16, gb.F16)
     assert (p.kernel, p.bm, p.bn, p.grid) == (4, 128, 128, 256)
     p = gb.gemm_bt_plan(1000, 3000, 2050, gb.BF16, gb.F32)  # 4-byte rows: DMA kernel + K tail
-    assert (p.kernel, p.bm, p.bn, p.vec, p.tiles_m, p.tiles_n) == (4, 128, 128, 2, 8, 24)
+    assert (p.kernel, p.bm, p.bn, p.vec, p.tiles_m, p.tiles_n) == (4, 128, 96, 2, 8, 32)  # one wave of 128x96
     p = gb.gemm_bt_plan(1000, 3000, 2049, gb.BF16, gb.F32)
     assert (p.kernel, p.bm, p.vec) == (4, 128, 1)  # 2-byte aligned rows take the DMA kernel too
     p = gb.gemm_bt_plan(16, 8192, 8192, gb.BF16, gb.BF16)

@@ -105,6 +105,9 @@ SHAPES = [
     # 96x128 tiles (at most one wave of them, more than 128x128 tiles would use): one exact wave, partial tile
     # rows and columns with a K tail, odd K
     (768, 4096, 136), (700, 3200, 130), (3000, 1000, 72), (760, 4000, 137),
+    # 128x96 tiles (output rows of 12 or 24 16-byte chunks through the whole-row epilogue; C rows that are not
+    # whole chunks store directly): one exact wave with ragged edges, a K tail, odd N
+    (1000, 3000, 136), (2048, 1536, 72), (1024, 3072, 130), (1000, 2999, 72),
     # odd K: rows only 2-byte aligned (every other row starts mid-dword), K tails of 1 to 7 elements, on
     # every tile tier and with no whole chunk at all
     (130, 264, 73), (300, 520, 1007), (64, 64, 7), (1000, 3000, 2051), (4096, 4096, 131), (2048, 4096, 135),

@@ -140,7 +140,7 @@ def test_kouter_pair_swizzle_and_transpose_reads(maps, bx):
     assert plain > 1
 
 
-@pytest.mark.parametrize("osz,bn", [(4, 256), (4, 128), (2, 256), (2, 128), (2, 64), (4, 64)])
+@pytest.mark.parametrize("osz,bn", [(4, 256), (4, 128), (2, 256), (2, 128), (2, 64), (4, 64), (4, 96), (2, 96)])
 def test_epilogue_park_and_copy(maps, osz, bn):
     """The output tile parked in LDS: each wave writes its 16x16 accumulator blocks (lane l: row l % 16, 4
     columns from 4 (l // 16)) as 16 bytes (fp32) or 8 bytes (16-bit) per lane; then the workgroup copies whole
