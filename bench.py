@@ -22,15 +22,15 @@ Prints ONE JSON line on stdout:
                skinny, 512³, 1000×3000×2050, 4096³ with E4M3 inputs against
                the fp8 peak, 4096³ int8 -> int32 against the int8 peak, a
                batch of 64 products of 512³ in one gemm_bt_batched call,
-               4096³ with B stored K×N through gemm_bt_layout, and
-               1024×1024×16384, which gemm_bt_ws splits along K), timed the
+               4096³ with B stored K×N through gemm_bt_layout,
+               1024×1024×16384, which gemm_bt_ws splits along K, and
+               1000×3000×2049, whose rows are only 2-byte aligned), timed the
                same way (us = mean launch time)
   copy_GBps    a plain 1 GiB device copy, as context for achievable HBM
 Diagnostics go to stderr.  Whatever --warmup is, the timed steps follow an
-untimed settle phase that runs launches until their time stops falling
-(bounded at 0.5 s): from idle an MI355X needs about 25 ms of sustained GEMM
-launches before its clocks settle, and launches inside that ramp run up to
-15% slower.
+untimed settle phase of at least 60 ms that then runs until the launch time
+stops falling (bounded at 0.6 s): from idle the 4096³ launches take 124 us
+and reach their steady 95-96 us only after 40-55 ms of sustained load.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
   python bench.py --mode copy     # plain device copy of known size (counter calibration)
