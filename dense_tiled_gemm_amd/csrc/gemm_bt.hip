@@ -351,11 +351,19 @@ static bool plan_split(int64_t M, int64_t N, int64_t K, int variant, int num_cu,
     return true;
 }
 
-// Which split, if any (the measured rule; see plan_split)
-static bool plan_split_rule(int64_t M, int64_t N, int64_t K, int num_cu, gemm_bt_plan_t* p) {
+// Which split, if any (the measured rule; see plan_split).  plain_tiles is
+// the workgroup count of the plain plan.  When that already covers every CU
+// and M fills less than 3/4 of the split's 128-row tiles, the plain grid's
+// small tiles win: 64x8192x8192 41.0 us plain (256 tiles of 32 x 64) against
+// 43.2 split (128-row tiles half empty), while 100x4096x16384 (rows 78 %
+// full) splits at 47.7 against 65.4 and 64x4096x16384 (plain grid of 128)
+// at 46.3 against 67.4.
+static bool plan_split_rule(int64_t M, int64_t N, int64_t K, int num_cu, int64_t plain_tiles, gemm_bt_plan_t* p) {
 #ifdef GEMM_BT_TUNING
     if (const char* e = std::getenv("GEMM_BT_SPLIT_TILE")) return plan_split(M, N, K, std::atoi(e), num_cu, p);
 #endif
+    const int64_t rows = ((M + 127) / 128) * 128;
+    if (plain_tiles >= num_cu && M * 4 < rows * 3) return false;
     return plan_split(M, N, K, kSkVariant, num_cu, p);
 }
 
@@ -518,7 +526,8 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         p->stages = v.stages;
         p->threads = 64 * v.wm * v.wn;
         p->lds_bytes = v.lds_bytes;
-        if (allow_sk && f < 0 && batch == 1 && plan_split_rule(M, N, K, num_cu, p)) return GEMM_BT_OK;
+        const int64_t plain_tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
+        if (allow_sk && f < 0 && batch == 1 && plan_split_rule(M, N, K, num_cu, plain_tiles, p)) return GEMM_BT_OK;
     } else {
         // tuning build only (GEMM_BT_FORCE_TILE=STAGED): the register-staged kernel
         const TileCfg c = big ? kCfgL : kCfgM;

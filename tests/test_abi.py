@@ -197,6 +197,10 @@ def test_wide_tier_and_split_plans():
         assert gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.F32).split_tiles == 0, (M, N, K)
         assert gb.gemm_bt_workspace_size(M, N, K, gb.BF16, gb.F32) == 0
     assert gb.gemm_bt_plan_ws(1024, 1024, 16384, gb.FP8_E4M3, gb.F32).split_tiles == 0  # 16-bit inputs only
+    # thin products: no split when the plain grid already covers the CUs and M fills < 3/4 of the 128-row tiles
+    assert gb.gemm_bt_plan_ws(64, 8192, 8192, gb.BF16, gb.BF16).split_tiles == 0   # 256 tiles of 32x64
+    assert gb.gemm_bt_plan_ws(64, 4096, 16384, gb.BF16, gb.BF16).split_tiles == 32  # plain grid of 128
+    assert gb.gemm_bt_plan_ws(100, 4096, 16384, gb.BF16, gb.F32).split_tiles == 32  # rows 78 % full
 
 
 def test_layout_tier_band():
