@@ -10,10 +10,10 @@
 #include "dma_kernel.hpp"
 #include "skinny_dma.hpp"
 #ifdef GEMM_BT_TUNING
-#include "skinny_kernel.hpp"  // register streaming: a measured alternative to skinny_dma_kernel
-#endif
-#ifdef GEMM_BT_TUNING
-#include "tiled_kernel.hpp"  // register-staged loads: a measured alternative to the DMA kernel
+// measured alternatives: register streaming for M <= 16, register-staged
+// loads for the tiled kernel
+#include "skinny_kernel.hpp"
+#include "tiled_kernel.hpp"
 #endif
 #include "trans_kernel.hpp"
 
@@ -641,8 +641,6 @@ static const void* trans_fn_out(int out, int variant) {
 
 // ---- kernel selection --------------------------------------------------------
 
-typedef void (*TiledFn)(const u16*, const u16*, void*, int, int, int, int, int, int, int);
-typedef void (*SkinnyFn)(const u16*, const u16*, void*, int, int, int, int);
 
 #ifdef GEMM_BT_TUNING
 template <int IN, int OUT, int VEC>
@@ -666,9 +664,6 @@ static const void* tiled_fn_out(int out, int cfg, int vec) {
     return tiled_fn_vec<IN, GEMM_BT_F16>(cfg, vec);
 }
 
-#endif
-
-#ifdef GEMM_BT_TUNING
 template <int IN, int OUT>
 static const void* skinny_fn_vec(int vec) {
     if (vec == 2) return (const void*)&skinny_kernel<IN, OUT, kSkinnyNB, kSkinnyKS, 2>;
@@ -867,6 +862,7 @@ static int launch_inner(const void* A, const void* B, void* C, int64_t batch, in
                                               : skinny_fn_out<GEMM_BT_F16>(out_dtype, p.vec);
 #endif
             }
+            if (!fn) return GEMM_BT_ERR_UNSUPPORTED;  // no kernel of this plan in this build
             void* args[] = {&a, &b, &C, &Mi, &Ni, &Ki, &vec_store, &sa, &sb, &sc};
             e = hipLaunchKernel(fn, dim3((unsigned)p.grid, gy), dim3(p.threads), args, 0, s);
         }
