@@ -277,12 +277,15 @@ class Case:
 
     def time(self, steps, warmup, settle=True):
         """`warmup` untimed steps, the settle phase, then the `steps` timed steps, back to back between two
-        synchronisations, with one HIP event before and one after them on the launch stream (torch's current
-        stream): their mean is the average launch duration.  Then the same number of launches again, each
-        followed by an event of its own, for the spread: an event between two launches also holds the second
-        back by the dispatch gap, so those intervals run longer than the launches themselves (by about 1-6 us
-        on MI355X).  Returns a dict: wall seconds and event ms of the timed steps, the per-launch intervals of
-        the second pass, the settle phase, and the host-clock window of the timed steps."""
+        synchronisations (the host wall time of `value`).  Then the same number of launches again behind one
+        untimed lead launch, between two HIP events on the launch stream (torch's current stream): their mean
+        is the average launch duration.  (Started on an idle stream, the first event would be stamped while
+        the host is still issuing the first launch, and that gap, tens of us, would be averaged over the
+        launches.)  Then the same number of launches once more, each followed by an event of its own, for the
+        spread: an event between two launches also holds the second back by the dispatch gap, so those
+        intervals run longer than the launches themselves (by about 1-6 us on MI355X).  Returns a dict: wall
+        seconds of the timed steps, event ms of the second pass, the per-launch intervals of the third, the
+        settle phase, and the host-clock window of the timed steps."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         sh = stream.cuda_stream
@@ -291,15 +294,19 @@ class Case:
         torch.cuda.synchronize()
         settle_n, settle_ms = self.settle(stream) if settle else (0, 0.0)
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, sh)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
+        self.step(steps, sh)  # the lead launch: the stream is busy when e0 is stamped
         e0.record(stream)
         for i in range(steps):
             self.step(i, sh)
         e1.record(stream)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record(stream)
         for i in range(steps):
