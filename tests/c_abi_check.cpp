@@ -80,6 +80,43 @@ int main() {
     for (size_t i = 0; i < c2.size(); ++i) REQUIRE(c2[i] == a2[i] || (c2[i] | a2[i]) == 0x8000);  // +0 == -0
 
     REQUIRE(hipFree(dA) == hipSuccess && hipFree(dB) == hipSuccess && hipFree(dC) == hipSuccess);
+
+    // all-ones again on larger shapes (every entry is K exactly in f32): an odd K (rows only 2-byte aligned, a
+    // K tail of one element) on 1000 x 3000, and a long-K product through the split plan, first with a
+    // workspace of the reported size, then through the library's own scratch
+    auto ones = [](int64_t Mo, int64_t No, int64_t Ko, int mode) -> int {
+        std::vector<uint16_t> ha((size_t)(Mo > No ? Mo : No) * Ko, bf16_of(1));
+        std::vector<float> hc((size_t)Mo * No, -1.0f);
+        void *a, *b, *c, *ws = nullptr;
+        REQUIRE(hipMalloc(&a, (size_t)Mo * Ko * 2) == hipSuccess);
+        REQUIRE(hipMalloc(&b, (size_t)No * Ko * 2) == hipSuccess);
+        REQUIRE(hipMalloc(&c, hc.size() * 4) == hipSuccess);
+        REQUIRE(hipMemcpy(a, ha.data(), (size_t)Mo * Ko * 2, hipMemcpyHostToDevice) == hipSuccess);
+        REQUIRE(hipMemcpy(b, ha.data(), (size_t)No * Ko * 2, hipMemcpyHostToDevice) == hipSuccess);
+        size_t need = 0;
+        REQUIRE(gemm_bt_workspace_size(Mo, No, Ko, GEMM_BT_BF16, GEMM_BT_F32, &need) == GEMM_BT_OK);
+        if (mode == 0) {
+            REQUIRE(gemm_bt(a, b, c, Mo, No, Ko, GEMM_BT_BF16, GEMM_BT_F32, nullptr) == GEMM_BT_OK);
+        } else if (mode == 1) {
+            REQUIRE(need > 0);
+            REQUIRE(hipMalloc(&ws, need) == hipSuccess);
+            REQUIRE(hipMemset(ws, 0, need) == hipSuccess);
+            REQUIRE(gemm_bt_ws(a, b, c, Mo, No, Ko, GEMM_BT_BF16, GEMM_BT_F32, ws, need - 16, nullptr) ==
+                    GEMM_BT_ERR_INVALID_VALUE);
+            REQUIRE(gemm_bt_ws(a, b, c, Mo, No, Ko, GEMM_BT_BF16, GEMM_BT_F32, ws, need, nullptr) == GEMM_BT_OK);
+        } else {
+            REQUIRE(gemm_bt_noalloc(a, b, c, Mo, No, Ko, GEMM_BT_BF16, GEMM_BT_F32, nullptr) == GEMM_BT_OK);
+        }
+        REQUIRE(hipDeviceSynchronize() == hipSuccess);
+        REQUIRE(hipMemcpy(hc.data(), c, hc.size() * 4, hipMemcpyDeviceToHost) == hipSuccess);
+        for (size_t i = 0; i < hc.size(); ++i) REQUIRE(hc[i] == (float)Ko);
+        REQUIRE(hipFree(a) == hipSuccess && hipFree(b) == hipSuccess && hipFree(c) == hipSuccess);
+        if (ws) REQUIRE(hipFree(ws) == hipSuccess);
+        return 0;
+    };
+    REQUIRE(ones(1000, 3000, 2049, 0) == 0);
+    REQUIRE(ones(1024, 1024, 16384, 1) == 0);
+    REQUIRE(ones(1024, 1024, 16384, 2) == 0);
     std::printf("c_abi_check ok\n");
     return 0;
 }
