@@ -23,9 +23,11 @@ Prints ONE JSON line on stdout:
                the fp8 peak, 4096³ int8 -> int32 against the int8 peak, a
                batch of 64 products of 512³ in one gemm_bt_batched call,
                4096³ with B stored K×N through gemm_bt_layout,
-               1024×1024×16384, which gemm_bt_ws splits along K, and
-               1000×3000×2049, whose rows are only 2-byte aligned), timed the
-               same way (us = mean launch time)
+               1024×1024×16384, which gemm_bt_ws splits along K,
+               1000×3000×2049, whose rows are only 2-byte aligned, and the
+               thin 64×8192×8192, split along K on 64×64 tiles, against HBM
+               bandwidth like the skinny product), timed the same way (us =
+               mean launch time)
   copy_GBps    a plain 1 GiB device copy, as context for achievable HBM
 Diagnostics go to stderr.  Whatever --warmup is, the timed steps follow an
 untimed settle phase of at least 60 ms that then runs until the launch time
@@ -490,7 +492,7 @@ def main():
         for name in ("m1024_n4096_k4096_f16_f16", "skinny_m16_n8192_k8192_bf16_bf16", "sq512_bf16_f32",
                      "ragged_m1000_n3000_k2050_bf16_f32", "sq4096_e4m3_bf16", "sq4096_i8_i32",
                      "batch64_sq512_bf16_bf16", "sq4096_nn_bf16_bf16", "splitk_m1024_n1024_k16384_bf16_bf16",
-                     "oddk_m1000_n3000_k2049_bf16_f32"):
+                     "oddk_m1000_n3000_k2049_bf16_f32", "thin_m64_n8192_k8192_bf16_bf16"):
             w2 = synth.WORKLOADS[name]
             c2 = Case(w2, torch, gb)
             r2 = c2.time(max(50, args.steps // 2) if not args.no_settle else args.steps, args.warmup,
@@ -505,7 +507,7 @@ def main():
                    "grid": c2.plan["grid"]}
             if c2.plan.get("split_tiles"):
                 ent["split_tiles"] = c2.plan["split_tiles"]
-            if name.startswith("skinny"):
+            if name.startswith(("skinny", "thin")):  # bound by reading B once
                 ent["frac_hbm"] = round(ent["GB/s"] / PEAK_HBM_GBS, 4)
             elif w2.in_dtype in ("e4m3", "e5m2"):
                 ent["frac_mfma_fp8"] = round(ent["TFLOP/s"] / PEAK_FP8_TFLOPS, 4)

@@ -2,6 +2,7 @@
 // planning and kernel dispatch for C = A * B^T on gfx950.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -156,18 +157,20 @@ static const DmaVariant* dma_variants(int* count) {
     return v;
 }
 
-// Split-K form of the 128 x 128 tier (M64E4s4i, dma_variants() index 1): a
-// grid that splits the K range of every tile over several workgroups (16-bit
-// inputs, one item).  A tuning build also has the split form of the 128 x 256
-// tier (index 7; measured no faster: 1024x4096x4096 f16 43.1 us split 2 ways
-// against 42.9 us unsplit on 128 x 128 tiles).
+// Split-K forms of the 128 x 128 tier (M64E4s4i, dma_variants() index 1) and
+// of the 64 x 64 and 32 x 64 tiers (indices 2 and 6): a grid that splits the
+// K range of every tile over several workgroups (16-bit inputs, one item).  A
+// tuning build also has the split form of the 128 x 256 tier (index 7;
+// measured no faster: 1024x4096x4096 f16 43.1 us split 2 ways against 42.9 us
+// unsplit on 128 x 128 tiles).
 constexpr int kSkVariant = 1;
 template <int IN, int OUT>
 static const void* sk_fn_t(int variant) {
 #ifdef GEMM_BT_TUNING
     if (variant == 7) return (const void*)&dma_kernel<IN, OUT, 128, 256, 64, 3, 2, 4, 2, 8, 0, 16, 0, 0, 1>;
 #endif
-    (void)variant;
+    if (variant == 2) return (const void*)&dma_kernel<IN, OUT, 64, 64, 64, 4, 2, 2, 2, 4, 0, 16, 0, 0, 1>;
+    if (variant == kTiny16) return (const void*)&dma_kernel<IN, OUT, 32, 64, 64, 4, 2, 2, 2, 2, 0, 16, 0, 0, 1>;
     return (const void*)&dma_kernel<IN, OUT, 128, 128, 64, 4, 2, 2, 2, 8, 0, 16, 0, 0, 1>;
 }
 template <int IN>
@@ -310,31 +313,34 @@ static bool dma_large_tier(int64_t tiles_l, int num_cu, bool eight_bit) {
 }
 
 // Split plan (the stream-K kernel with one piece per workgroup) for 16-bit
-// inputs on the LDS-DMA path, one item, 128 x 128 tiles: when those tiles
-// would fill at most half the CUs (the plain plan then falls back to 64 x 64
-// or 32 x 64 tiles), each of the T tiles is split along K into
-// S = floor(CUs / T) pieces of at least kSkMinSteps K steps, and a grid of
-// T * S workgroups computes one piece each.  Every workgroup's run of
+// inputs on the LDS-DMA path, one item: when the tiles of `variant` would fill
+// at most half the CUs, each of the T tiles is split along K into
+// S = floor(CUs / T) pieces of at least kSkMinSteps K steps (with
+// fewer_pieces, into fewer pieces when K is too short for that many), and a
+// grid of T * S workgroups computes one piece each.  Every workgroup's run of
 // iterations then lies inside one tile, at the same K offset as the matching
 // pieces of the other tiles, so workgroups sharing an operand panel read it
-// in step, as in the plain grid.  Measured on 256 CUs, against the plain plan
-// (us): 512x1024x32768 61 vs 121, 1024x1024x16384 51 vs 73, 1024x2048x8192
-// 47 vs 62, 512x2048x8192 34 vs 39, 256x4096x8192 35 vs 41, 2048x1024x4096
-// 27 vs 29; with pieces of 16 steps it loses (1024x1024x4096 22 vs 18.5).
+// in step, as in the plain grid.  Measured on 256 CUs, 128 x 128 tiles
+// against the plain plan (us): 512x1024x32768 61 vs 121, 1024x1024x16384 51
+// vs 73, 1024x2048x8192 47 vs 62, 512x2048x8192 34 vs 39, 256x4096x8192 35
+// vs 41, 2048x1024x4096 27 vs 29; with pieces of 16 steps it loses
+// (1024x1024x4096 22 vs 18.5), and so it does in fewer pieces of 32 steps
+// (1024x1024x4096 in 2 pieces 22.3 vs 18.9, 256x4096x4096 28.5 vs 23.7).
 // With more tiles than half the CUs (e.g. 192 tiles of 1000x3000), pieces
 // that straddle tiles and start at different K offsets lose the panel reuse
 // and the split lost everywhere it was measured (1000x3000x2050 33 vs 26.5,
 // 1000x3000x8192 81 vs 65), so no split is planned there.
 // Fills p and returns true, or returns false and leaves p alone.
 constexpr int64_t kSkMinSteps = 32;
-static bool plan_split(int64_t M, int64_t N, int64_t K, int variant, int num_cu, gemm_bt_plan_t* p) {
+static bool plan_split(int64_t M, int64_t N, int64_t K, int variant, int num_cu, bool fewer_pieces,
+                       gemm_bt_plan_t* p) {
     int n = 0;
     const DmaVariant& v = dma_variants(&n)[variant];
     const int64_t T = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
     const int64_t nk = ((K & ~7LL) + 63) / 64;
-    if (T * 2 > num_cu) return false;
-    const int64_t S = num_cu / T;
-    if (nk < kSkMinSteps * S || T > kSkMaxTiles) return false;
+    if (T * 2 > num_cu || T > kSkMaxTiles) return false;
+    const int64_t S = fewer_pieces ? std::min<int64_t>(num_cu / T, nk / kSkMinSteps) : num_cu / T;
+    if (S < 2 || nk < kSkMinSteps * S) return false;
     p->kernel = KIND_DMA;
     p->variant = variant;
     p->bm = v.bm;
@@ -352,19 +358,29 @@ static bool plan_split(int64_t M, int64_t N, int64_t K, int variant, int num_cu,
 }
 
 // Which split, if any (the measured rule; see plan_split).  plain_tiles is
-// the workgroup count of the plain plan.  When that already covers every CU
-// and M fills less than 3/4 of the split's 128-row tiles, the plain grid's
-// small tiles win: 64x8192x8192 41.0 us plain (256 tiles of 32 x 64) against
-// 43.2 split (128-row tiles half empty), while 100x4096x16384 (rows 78 %
-// full) splits at 47.7 against 65.4 and 64x4096x16384 (plain grid of 128)
-// at 46.3 against 67.4.
+// the workgroup count of the plain plan.
+//  * Thin products (M <= 64): 32 x 64 tiles for M <= 32, else 64 x 64, split
+//    into as many pieces of 32 or more K steps as fill the CUs.  Per FLOP the
+//    small tiles re-read B once per 32 or 64 rows of A; splitting K instead
+//    of narrowing the tiles keeps that at once per row block and fills the
+//    CUs all the same.  Measured (us, plain plan vs split): 64x8192x8192
+//    40.6 vs 35.5, 48x8192x8192 42.6 vs 36.8, 17x8192x8192 39.8 vs 33.7,
+//    64x4096x16384 f16 48.3 (128 x 128 tiles split) vs 38.4, 64x3072x8192
+//    35.0 vs 20.7 (4 pieces), 32x4096x4096 20.7 vs 15.3 (2 pieces),
+//    64x1024x65536 244 vs 45; 32 x 64 against 64 x 64 tiles for M <= 32:
+//    24x8192x8192 35.3 vs 36.2, 32x4096x8192 23.1 vs 23.9.
+//  * Otherwise 128 x 128 tiles, except when the plain grid already covers
+//    every CU and M fills less than 3/4 of the 128-row tiles (their rows
+//    are then mostly padding): 100x4096x16384 (rows 78 % full) splits at 47.7
+//    against 65.4.
 static bool plan_split_rule(int64_t M, int64_t N, int64_t K, int num_cu, int64_t plain_tiles, gemm_bt_plan_t* p) {
 #ifdef GEMM_BT_TUNING
-    if (const char* e = std::getenv("GEMM_BT_SPLIT_TILE")) return plan_split(M, N, K, std::atoi(e), num_cu, p);
+    if (const char* e = std::getenv("GEMM_BT_SPLIT_TILE")) return plan_split(M, N, K, std::atoi(e), num_cu, false, p);
 #endif
+    if (M <= 64) return plan_split(M, N, K, M <= 32 ? kTiny16 : 2, num_cu, true, p);
     const int64_t rows = ((M + 127) / 128) * 128;
     if (plain_tiles >= num_cu && M * 4 < rows * 3) return false;
-    return plan_split(M, N, K, kSkVariant, num_cu, p);
+    return plan_split(M, N, K, kSkVariant, num_cu, false, p);
 }
 
 static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,

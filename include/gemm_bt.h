@@ -150,12 +150,17 @@ int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch,
  * C = A * B^T with a caller-provided workspace that lets the library split
  * the K range of output tiles over workgroups (the work split of stream-K:
  * "Writing Mosaic GPU kernels with Pallas", section "Cluster launch
- * control", a grid that keeps every core busy to the end).  Where 16-bit
- * products would leave at least half the compute units without a 128 x 128
- * tile and K is long (e.g. 1024 x 1024 x 16384: 64 tiles for 256 compute
- * units), each of the T tiles is split into S = floor(CUs / T) pieces of
+ * control", a grid that keeps every core busy to the end).  Where a 16-bit
+ * product would leave at least half the compute units without an output
+ * tile and K is long, each of its T tiles is split into S pieces of
  * consecutive K steps (at least 32 steps of 64 each), one piece per
- * workgroup; the last of a tile's workgroups to finish adds the pieces in K
+ * workgroup.  The tiles: 32 x 64 for M <= 32, 64 x 64 for M <= 64 (thin
+ * products, e.g. 64 x 8192 x 8192: 128 tiles, S = 2), else 128 x 128 (e.g.
+ * 1024 x 1024 x 16384: 64 tiles, S = 4); S = floor(CUs / T), for thin
+ * products at most K / 2048 (then S >= 2 is required), and for 128 x 128 tiles
+ * no split when M fills less than 3/4 of their rows while narrower tiles
+ * already give every compute unit a workgroup.  The last of a tile's
+ * workgroups to finish adds the pieces in K
  * order (piece 0 + 1 + ...), whatever the order of arrival, so the result
  * is the same bits on every run with the same sizes on the same device.
  * The sum of each output is then formed in a different order than gemm_bt's

@@ -69,8 +69,9 @@ class Workload:
 # The five measured shapes, seeds 0..4 in this order, the 4096³ product
 # with 8-bit E4M3 inputs (seed 5) and with int8 inputs and int32 output (seed 6),
 # a batch of 64 products of 512³ (seed 7), 4096³ with B stored K×N (seed 8),
-# 1024×1024×16384, whose 64 tiles the split plan divides along K (seed 9), and
-# the ragged shape with an odd K (rows only 2-byte aligned, a K tail of 1; seed 10).
+# 1024×1024×16384, whose 64 tiles the split plan divides along K (seed 9),
+# the ragged shape with an odd K (rows only 2-byte aligned, a K tail of 1; seed 10),
+# and the thin product 64×8192×8192 (64 × 64 tiles split along K; seed 11).
 WORKLOADS = {
     "sq512_bf16_f32": Workload("sq512_bf16_f32", 512, 512, 512, "bf16", "f32", "normal", 0),
     "m1024_n4096_k4096_f16_f16": Workload("m1024_n4096_k4096_f16_f16", 1024, 4096, 4096, "f16", "f16",
@@ -88,6 +89,8 @@ WORKLOADS = {
                                                     "bf16", "bf16", "normal", 9),
     "oddk_m1000_n3000_k2049_bf16_f32": Workload("oddk_m1000_n3000_k2049_bf16_f32", 1000, 3000, 2049,
                                                 "bf16", "f32", "uniform", 10),
+    "thin_m64_n8192_k8192_bf16_bf16": Workload("thin_m64_n8192_k8192_bf16_bf16", 64, 8192, 8192,
+                                               "bf16", "bf16", "normal", 11),
 }
 
 

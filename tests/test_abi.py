@@ -161,8 +161,9 @@ def test_tier_band_above_one_wave():
 
 def test_wide_tier_and_split_plans():
     """16-bit inputs: 128x256 tiles once they make whole waves or more than 1.375 waves (where 128x128 tiles
-    would otherwise be taken); the split plan (gemm_bt_ws) only where 128x128 tiles fill at most half the CUs and
-    each piece keeps at least 32 K steps, one piece per workgroup."""
+    would otherwise be taken); the split plan (gemm_bt_ws) only where its tiles (32x64 for M <= 32, 64x64 for
+    M <= 64, else 128x128) fill at most half the CUs and each piece keeps at least 32 K steps, one piece per
+    workgroup."""
     def tile(M, N, K=4096, batch=1, ind=gb.BF16):
         p = gb.gemm_bt_plan_batched(batch, M, N, K, ind, gb.BF16)
         return p.bm, p.bn
@@ -197,10 +198,19 @@ def test_wide_tier_and_split_plans():
         assert gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.F32).split_tiles == 0, (M, N, K)
         assert gb.gemm_bt_workspace_size(M, N, K, gb.BF16, gb.F32) == 0
     assert gb.gemm_bt_plan_ws(1024, 1024, 16384, gb.FP8_E4M3, gb.F32).split_tiles == 0  # 16-bit inputs only
-    # thin products: no split when the plain grid already covers the CUs and M fills < 3/4 of the 128-row tiles
-    assert gb.gemm_bt_plan_ws(64, 8192, 8192, gb.BF16, gb.BF16).split_tiles == 0   # 256 tiles of 32x64
-    assert gb.gemm_bt_plan_ws(64, 4096, 16384, gb.BF16, gb.BF16).split_tiles == 32  # plain grid of 128
+    # M > 64: no 128x128 split when the plain grid already covers the CUs and M fills < 3/4 of the 128-row tiles
+    assert gb.gemm_bt_plan_ws(65, 8192, 8192, gb.BF16, gb.BF16).split_tiles == 0    # 256 tiles of 64x64
     assert gb.gemm_bt_plan_ws(100, 4096, 16384, gb.BF16, gb.F32).split_tiles == 32  # rows 78 % full
+    # thin products (M <= 64): 32x64 (M <= 32) or 64x64 tiles, split into as many pieces of >= 32 K steps as
+    # fill the CUs, fewer when K is short
+    for M, N, K, bm, T, S in [(64, 8192, 8192, 64, 128, 2), (33, 8192, 8192, 64, 128, 2), (32, 8192, 4096, 32, 128, 2),
+                              (17, 8192, 8192, 32, 128, 2), (64, 4096, 16384, 64, 64, 4), (64, 3072, 8192, 64, 48, 4),
+                              (17, 4096, 4096, 32, 64, 2), (40, 6000, 8195, 64, 94, 2), (64, 1024, 65536, 64, 16, 16)]:
+        p = gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.BF16)
+        assert (p.bm, p.bn, p.split_tiles, p.grid) == (bm, 64, T, T * S), (M, N, K)
+        assert p.workspace_bytes == 16384 + T * S * bm * 64 * 4
+    for M, N, K in [(64, 8192, 2048), (64, 12288, 16384), (32, 12288, 8192), (16, 8192, 8192)]:
+        assert gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.BF16).split_tiles == 0, (M, N, K)  # K short, or >= 128 tiles
 
 
 def test_layout_tier_band():

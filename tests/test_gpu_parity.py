@@ -844,6 +844,9 @@ SK_CASES = [  # (M, N, K, in, out)
     (1024, 1024, 16384, "bf16", "bf16"), (512, 1024, 32768, "f16", "f16"), (1000, 1000, 8200, "bf16", "f32"),
     (300, 700, 30002, "bf16", "f32"), (130, 4100, 8192, "f16", "f16"), (200, 1999, 17000, "bf16", "f32"),
     (64, 4096, 16384, "bf16", "bf16"), (1024, 2048, 8192, "f16", "f32"), (1024, 1024, 16383, "bf16", "f32"),
+    # thin products: 64x64 and 32x64 tiles, ragged M, N and K, fewer pieces for short K, 16 pieces
+    (64, 8192, 8192, "bf16", "bf16"), (17, 4100, 4099, "f16", "f32"), (40, 6000, 8195, "bf16", "f32"),
+    (33, 3000, 8192, "f16", "f16"), (64, 1024, 65536, "bf16", "bf16"),
 ]
 
 

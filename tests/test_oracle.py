@@ -445,7 +445,7 @@ def test_synth_recipe():
     a, _ = synth.make(50, 4, wu.K, "bf16", wu.dist, wu.seed)
     v = indep_decode(a, "bf16")
     assert v.min() >= -1 and v.max() <= 1 and abs(v.std() - 1 / math.sqrt(3)) < 0.01
-    assert [x.seed for x in synth.WORKLOADS.values()] == [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
+    assert [x.seed for x in synth.WORKLOADS.values()] == list(range(12))
     w8 = synth.WORKLOADS["sq4096_e4m3_bf16"]
     a8, _ = synth.make(64, 4, w8.K, w8.in_dtype, w8.dist, w8.seed)
     assert a8.dtype == np.uint8 and w8.compulsory_bytes == 2 * 4096 * 4096 + 4096 * 4096 * 2
