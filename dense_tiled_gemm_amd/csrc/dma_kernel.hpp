@@ -37,16 +37,20 @@ namespace gbt {
 
 // 16-byte-chunk swizzle for tile rows of CPR chunks.  SWZ 0 disables it (for
 // measuring bank conflicts); SWZ 1 and 2 XOR 3 (CPR 8) or 2 (CPR 4) row bits
-// into the chunk index, starting at row bit 0/1 (CPR 8) or 1/2 (CPR 4).
+// into the chunk index, starting at row bit 0/1 (CPR 8) or 1/2 (CPR 4), and
+// for CPR 16 row bits 0..2 or 0..3.
 // gfx950's LDS has 64 four-byte banks (256 bytes per cycle): a ds_read_b128
 // is served 16 lanes at a time, so the 16 lanes of one MFMA operand read
 // (16 rows, same logical chunk) must hit 16 different 16-byte bank groups.
 // With 128-byte rows, row r starts at bank group 8*(r%2); XORing bits 1..3
 // of r into the chunk (SWZ 2) spreads rows r..r+15 over all 16 groups, while
 // bits 0..2 (SWZ 1, the form that suits 32 banks) leaves 2-way conflicts.
+// A 256-byte row covers all 64 banks, so every row starts at group 0 and
+// SWZ 2 XORs bits 0..3.
 template <int CPR, int SWZ>
 __host__ __device__ inline int swz_row(int row) {
     if constexpr (SWZ == 0) return 0;
+    else if constexpr (CPR == 16) return SWZ == 1 ? (row & 7) : (row & 15);
     else if constexpr (CPR == 8) return SWZ == 1 ? (row & 7) : ((row >> 1) & 7);
     else return SWZ == 1 ? ((row >> 1) & 3) : ((row >> 2) & 3);
 }
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     constexpr int STAGE_BYTES = (BM + BN) * ROWB;
     constexpr int PFI = PF > 0 ? (BM + BN) / (64 * W) : 0;  // prefetch instructions per wave per step
     constexpr int PEND = (STAGES - 2) * (LA + LB + PFI) + PFI;
-    static_assert(ROWB == 64 || ROWB == 128, "tile rows of 64 or 128 bytes");
+    static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "tile rows of 64, 128 or 256 bytes");
     static_assert(ESZ == 2 || MF == 32, "8-bit inputs use the 32x32x64 MFMA");
     static_assert((64 / MF) * (2 / ESZ) * 16 == KSUB * ESZ, "the lanes' fragments cover one substep's bytes once");
     static_assert(STAGES >= 2, "at least double buffering");

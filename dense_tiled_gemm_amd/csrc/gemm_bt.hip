@@ -109,10 +109,20 @@ static DmaVariant dma_variant(const char* name) {
     return v;
 }
 
+// Geometry of a tile form that runs only split along K (its kernels are the
+// split forms in sk_fn_t): no data-parallel entry points.
+template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ>
+static DmaVariant split_only_variant(const char* name) {
+    DmaVariant v = {name, BM, BN, BK, S, WM, WN, SWZ, S * (BM + BN) * BK * 2, {}};
+    return v;
+}
+
 // Index 0 is the default for large grids, 7, 1, 8 and 9 for smaller ones, 2
 // and 6 for the smallest (see plan_impl), 3..5 the same for 8-bit inputs, float or integer
 // (128-element K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32
-// MFMAs over 64-element substeps).
+// MFMAs over 64-element substeps); 10 and 11 run only split along K, for thin
+// products (plan_split_rule), with 128-element K steps of 16-bit inputs
+// (256-byte tile rows).
 // A build with GEMM_BT_TUNING defined adds the measured alternatives after
 // them (selected with GEMM_BT_FORCE_TILE=<name>, bf16->bf16 and f16->f16
 // only); the default library holds the production tile shapes only.
@@ -121,6 +131,8 @@ constexpr int kTiny16 = 6;  // 32 x 64 tiles (16-bit inputs), when even 64 x 64 
 constexpr int kWide16 = 7;  // 128 x 256 tiles (16-bit inputs, 8 waves of 64 x 64), see plan_impl
 constexpr int kShort16 = 8;  // 96 x 128 tiles (16-bit inputs, 4 waves of 48 x 64), see plan_impl
 constexpr int kNarrow16 = 9;  // 128 x 96 tiles (16-bit inputs, 4 waves of 64 x 48), see plan_impl
+constexpr int kThin64 = 10;   // 64 x 64 tiles of 256-byte rows, split along K only (thin products)
+constexpr int kThin32 = 11;   // 32 x 64 tiles of 256-byte rows, split along K only (thin products)
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
@@ -133,6 +145,8 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<128, 256, 64, 3, 2, 4, 2, 8, 0, 16, true>("H128x256s3"),
         dma_variant<96, 128, 64, 4, 2, 2, 2, 6, 0, 16, true>("M96x128s4"),
         dma_variant<128, 96, 64, 4, 2, 2, 2, 6, 0, 16, true>("M128x96s4"),
+        split_only_variant<64, 64, 128, 4, 2, 2, 2>("Q64B128s4"),
+        split_only_variant<32, 64, 128, 4, 2, 2, 2>("T32x64B128s4"),
 #ifdef GEMM_BT_TUNING
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
@@ -157,21 +171,26 @@ static const DmaVariant* dma_variants(int* count) {
     return v;
 }
 
-// Split-K forms of the 128 x 128 tier (M64E4s4i, dma_variants() index 1) and
-// of the 64 x 64 and 32 x 64 tiers (indices 2 and 6): a grid that splits the
-// K range of every tile over several workgroups (16-bit inputs, one item).  A
-// tuning build also has the split form of the 128 x 256 tier (index 7;
-// measured no faster: 1024x4096x4096 f16 43.1 us split 2 ways against 42.9 us
-// unsplit on 128 x 128 tiles).
+// Split-K forms (16-bit inputs, one item): a grid that splits the K range of
+// every tile over several workgroups.  The 128 x 128 tier (M64E4s4i,
+// dma_variants() index 1), and for thin products 64 x 64 and 32 x 64 tiles
+// with 128-element K steps (indices 10 and 11): each piece then streams 256
+// contiguous bytes of every B row per step instead of 128 (same box, us, 64-
+// against 128-element steps: 64x8192x8192 35.5 vs 34.8, 24x8192x8192 35.3 vs
+// 34.4, 32x4096x4096 15.5 vs 14.8, 64x4096x16384 f16 38.6 vs 37.8).  A tuning
+// build also has the split form of the 128 x 256 tier (index 7; measured no
+// faster: 1024x4096x4096 f16 43.1 us split 2 ways against 42.9 us unsplit on
+// 128 x 128 tiles).
 constexpr int kSkVariant = 1;
 template <int IN, int OUT>
 static const void* sk_fn_t(int variant) {
 #ifdef GEMM_BT_TUNING
     if (variant == 7) return (const void*)&dma_kernel<IN, OUT, 128, 256, 64, 3, 2, 4, 2, 8, 0, 16, 0, 0, 1>;
 #endif
-    if (variant == 2) return (const void*)&dma_kernel<IN, OUT, 64, 64, 64, 4, 2, 2, 2, 4, 0, 16, 0, 0, 1>;
-    if (variant == kTiny16) return (const void*)&dma_kernel<IN, OUT, 32, 64, 64, 4, 2, 2, 2, 2, 0, 16, 0, 0, 1>;
-    return (const void*)&dma_kernel<IN, OUT, 128, 128, 64, 4, 2, 2, 2, 8, 0, 16, 0, 0, 1>;
+    if (variant == kSkVariant) return (const void*)&dma_kernel<IN, OUT, 128, 128, 64, 4, 2, 2, 2, 8, 0, 16, 0, 0, 1>;
+    if (variant == kThin64) return (const void*)&dma_kernel<IN, OUT, 64, 64, 128, 4, 2, 2, 2, 4, 0, 16, 0, 0, 1>;
+    if (variant == kThin32) return (const void*)&dma_kernel<IN, OUT, 32, 64, 128, 4, 2, 2, 2, 2, 0, 16, 0, 0, 1>;
+    return nullptr;  // no split form of this tile
 }
 template <int IN>
 static const void* sk_fn_out(int out, int variant) {
@@ -375,9 +394,9 @@ static bool plan_split(int64_t M, int64_t N, int64_t K, int variant, int num_cu,
 //    against 65.4.
 static bool plan_split_rule(int64_t M, int64_t N, int64_t K, int num_cu, int64_t plain_tiles, gemm_bt_plan_t* p) {
 #ifdef GEMM_BT_TUNING
-    if (const char* e = std::getenv("GEMM_BT_SPLIT_TILE")) return plan_split(M, N, K, std::atoi(e), num_cu, false, p);
+    if (const char* e = std::getenv("GEMM_BT_SPLIT_TILE")) return plan_split(M, N, K, std::atoi(e), num_cu, true, p);
 #endif
-    if (M <= 64) return plan_split(M, N, K, M <= 32 ? kTiny16 : 2, num_cu, true, p);
+    if (M <= 64) return plan_split(M, N, K, M <= 32 ? kThin32 : kThin64, num_cu, true, p);
     const int64_t rows = ((M + 127) / 128) * 128;
     if (plain_tiles >= num_cu && M * 4 < rows * 3) return false;
     return plan_split(M, N, K, kSkVariant, num_cu, false, p);
@@ -853,6 +872,7 @@ static int launch_inner(const void* A, const void* B, void* C, int64_t batch, in
             int n = 0;
             const void* fn = p.split_tiles > 0 ? sk_fn(p.variant, in_dtype, out_dtype)
                                                : dma_variants(&n)[p.variant].fn[in_index(in_dtype)][out_index(out_dtype)];
+            if (!fn) return GEMM_BT_ERR_UNSUPPORTED;  // no kernel of this plan in this build
             SkArgs ska = sk_args(p, K, ws);
             // one grid row: the items stacked along the tile rows (stream-K: the persistent grid)
             int tm = (int)(p.tiles_m * batch), tn = (int)p.tiles_n, gm = p.group_m, itm = (int)p.tiles_m;

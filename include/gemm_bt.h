@@ -155,7 +155,8 @@ int gemm_bt_batched_layout(const void* A, const void* B, void* C, int64_t batch,
  * tile and K is long, each of its T tiles is split into S pieces of
  * consecutive K steps (at least 32 steps of 64 each), one piece per
  * workgroup.  The tiles: 32 x 64 for M <= 32, 64 x 64 for M <= 64 (thin
- * products, e.g. 64 x 8192 x 8192: 128 tiles, S = 2), else 128 x 128 (e.g.
+ * products, in K steps of 128, e.g. 64 x 8192 x 8192: 128 tiles, S = 2),
+ * else 128 x 128 (e.g.
  * 1024 x 1024 x 16384: 64 tiles, S = 4); S = floor(CUs / T), for thin
  * products at most K / 2048 (then S >= 2 is required), and for 128 x 128 tiles
  * no split when M fills less than 3/4 of their rows while narrower tiles

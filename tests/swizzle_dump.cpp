@@ -18,6 +18,9 @@ int main() {
         std::printf("swz 4 0 %d %d\n", row, swz_row<4, 0>(row));
         std::printf("swz 4 1 %d %d\n", row, swz_row<4, 1>(row));
         std::printf("swz 4 2 %d %d\n", row, swz_row<4, 2>(row));
+        std::printf("swz 16 0 %d %d\n", row, swz_row<16, 0>(row));
+        std::printf("swz 16 1 %d %d\n", row, swz_row<16, 1>(row));
+        std::printf("swz 16 2 %d %d\n", row, swz_row<16, 2>(row));
     }
     for (int row = 0; row < 64; ++row) std::printf("kouter %d %d\n", row, kouter_swz(row));
     const int cprs[] = {8, 12, 16, 24, 32, 64};

@@ -207,8 +207,9 @@ def test_wide_tier_and_split_plans():
                               (17, 8192, 8192, 32, 128, 2), (64, 4096, 16384, 64, 64, 4), (64, 3072, 8192, 64, 48, 4),
                               (17, 4096, 4096, 32, 64, 2), (40, 6000, 8195, 64, 94, 2), (64, 1024, 65536, 64, 16, 16)]:
         p = gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.BF16)
-        assert (p.bm, p.bn, p.split_tiles, p.grid) == (bm, 64, T, T * S), (M, N, K)
+        assert (p.bm, p.bn, p.bk, p.split_tiles, p.grid) == (bm, 64, 128, T, T * S), (M, N, K)  # 256-byte rows
         assert p.workspace_bytes == 16384 + T * S * bm * 64 * 4
+        assert p.lds_bytes == 4 * (bm + 64) * 128 * 2
     for M, N, K in [(64, 8192, 2048), (64, 12288, 16384), (32, 12288, 8192), (16, 8192, 8192)]:
         assert gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.BF16).split_tiles == 0, (M, N, K)  # K short, or >= 128 tiles
 

@@ -55,7 +55,7 @@ def split(lanes, per_pass):
     return [lanes[i:i + per_pass] for i in range(0, len(lanes), per_pass)]
 
 
-@pytest.mark.parametrize("cpr", [8, 4])
+@pytest.mark.parametrize("cpr", [16, 8, 4])
 @pytest.mark.parametrize("swz_kind", [0, 1, 2])
 def test_row_swizzle_is_a_bijection_on_each_window(maps, cpr, swz_kind):
     swz, _, _ = maps
@@ -81,7 +81,9 @@ def mfma_read_passes(swz, cpr, swz_kind, mf, ks, block):
     lanes = []
     for lane in range(64):
         row = block + lane % mf
-        if cpr == 8:
+        if cpr == 16:  # 256-byte rows (16x16x32 only): four substeps per row
+            chunk = 4 * ks + lane // 16
+        elif cpr == 8:
             chunk = (4 * ks + lane // 16) if mf == 16 else (2 * ks + lane // 32)
         else:
             chunk = (2 * (ks % 2) + lane // 16) % 4 if mf == 16 else (ks % 2) * 2 + lane // 32
@@ -102,6 +104,15 @@ def test_mfma_operand_reads(maps, mf):
     assert worst[2] == 1
     assert worst[1] == 2
     assert worst[0] == 8
+
+
+def test_mfma_operand_reads_256_byte_rows(maps):
+    """256-byte rows (the thin split tiles): each row spans all 64 banks, so without a swizzle the 16 rows of a pass
+    all read the same 16-byte bank group; XORing row bits 0..3 spreads them over the 16 groups."""
+    swz, _, _ = maps
+    worst = {kind: max(worst_bank(mfma_read_passes(swz, 16, kind, 16, ks, block))
+                       for ks in range(4) for block in range(0, 256, 16)) for kind in (0, 1, 2)}
+    assert worst[2] == 1 and worst[1] == 2 and worst[0] == 16
 
 
 def test_mfma_operand_reads_64_byte_rows(maps):
