@@ -32,7 +32,10 @@ enum Kind { KIND_NONE = 0, KIND_FILL = 1, KIND_TILED = 2, KIND_SKINNY = 3, KIND_
 
 // Kernels.  Products with M > 16 run dma_kernel (direct global->LDS loads of
 // 16-byte chunks, from rows of any even alignment) in one of the tile shapes
-// of dma_variants().  Skinny products (M <= 16) run skinny_dma_kernel (8 rows
+// of dma_variants(); through gemm_bt_ws and gemm_bt_noalloc, products that
+// leave half the CUs without a tile run its split-K form instead (128 x 128
+// tiles, or for M <= 64 thin tiles of 256-byte rows, see plan_split_rule).
+// Skinny products (M <= 16) run skinny_dma_kernel (8 rows
 // of B per single-wave workgroup, 256-element K stages in a 3-deep LDS ring,
 // rows of any even alignment too).  The tuning build also has the
 // register-streaming skinny_kernel (GEMM_BT_FORCE_SKINNY=REG: 32 rows, K split
