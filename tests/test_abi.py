@@ -212,6 +212,15 @@ def test_wide_tier_and_split_plans():
         assert p.lds_bytes == 4 * (bm + 64) * 128 * 2
     for M, N, K in [(64, 8192, 2048), (64, 12288, 16384), (32, 12288, 8192), (16, 8192, 8192)]:
         assert gb.gemm_bt_plan_ws(M, N, K, gb.BF16, gb.BF16).split_tiles == 0, (M, N, K)  # K short, or >= 128 tiles
+    # the tile height follows M across the thin range; every thin plan's workspace fits the no-allocation scratch
+    # (16 KiB of counters + 16 MiB of partial tiles)
+    for M in (17, 24, 32, 33, 48, 64):
+        for ind, outd in ((gb.BF16, gb.BF16), (gb.F16, gb.F32), (gb.BF16, gb.F16)):
+            p = gb.gemm_bt_plan_ws(M, 8192, 8192, ind, outd)
+            assert (p.bm, p.bk, p.split_tiles, p.grid) == (32 if M <= 32 else 64, 128, 128, 256), (M, ind, outd)
+            assert p.workspace_bytes <= 16384 + 16 * 2**20
+    assert gb.gemm_bt_plan_ws(64, 8192, 8192, gb.FP8_E4M3, gb.F32).split_tiles == 0  # 16-bit inputs only
+    assert gb.gemm_bt_plan_ws(64, 8192, 8192, gb.INT8, gb.INT32).split_tiles == 0
 
 
 def test_layout_tier_band():
