@@ -174,7 +174,7 @@ struct SkArgs {
 };
 
 template <int IN, int OUT, int BM, int BN, int BK, int STAGES, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0,
-          int MF = 32, int LDW = 0, int RING5 = 0, int SK = 0>
+          int MF = 32, int LDW = 0, int RING5 = 0, int SK = 0, int PH = 0>
 __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict__ A, const u16* __restrict__ B,
                                                           void* __restrict__ C, int M, int N, int K,
                                                           int tiles_m, int tiles_n, int group_m,
@@ -211,6 +211,10 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     constexpr int RING_BYTES = RING5 ? 5 * SLOT_BYTES : STAGES * STAGE_BYTES;
     static_assert(!RING5 || (BM == BN && STAGES == 2 && SCHED == 6 && PF == 0 && RING5 <= 2), "five-slot ring layout");
     static_assert(RING_BYTES + (PF > 0 ? W * 256 : 0) <= 160 * 1024, "LDS budget");
+    // PH: the line ring for rows that are 16-byte but not 128-byte aligned
+    // (see the loader below)
+    static_assert(!PH || (ESZ == 2 && CPR == 8 && !RING5 && SCHED >= 2 && PF == 0 && STAGES >= 3),
+                  "line ring: 16-bit inputs, 128-byte tile rows, an early-barrier ring of 3 or more stages");
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[RING_BYTES + (PF > 0 ? W * 256 : 0)];
 
@@ -265,6 +269,27 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     const int a_base = (wm * TM + fr) * ROWB;
     const int b_base = BM * ROWB + (wn * TN + fr) * ROWB;
     const int b_base0 = (wn * TN + fr) * ROWB;  // relative to the B tile
+    // PH (rows 16-byte aligned, row_bytes % 128 != 0): every 128-byte K
+    // segment of such a row straddles two cache lines.  The line ring loads
+    // whole aligned lines instead: stage kt holds line kt of each row, the
+    // aligned 128 bytes from the row's start rounded down to a line, plus
+    // kt * 128.  A row whose start lies ph 16-byte chunks into its line has
+    // logical chunk c of K segment kt in line kt (c + ph < 8) or kt + 1
+    // (c + ph >= 8).  The loader's lane that owns physical chunk P fetches
+    // logical chunk c = P ^ swz of segment kt, or of segment kt - 1 when
+    // c + ph >= 8 (its "carry"): that is line chunk (c + ph) % 8 of line kt,
+    // so every logical chunk sits at P = c ^ swz of the stage of its line and
+    // the operand reads stay one conflict-free ds_read_b128, from stage kt or
+    // kt + 1.  Rows 8 apart have the same phase (8 * row_bytes % 128 == 0),
+    // so a lane's phase is fixed for all its loads and fragment rows.
+    auto phase = [&](const u16* X, int64_t row) {
+        return (int)((((uintptr_t)X + (uint64_t)row * row_bytes) & 127u) >> 4);
+    };
+    const int ld_row = wave * RPI + lrow;  // this lane's first tile row in each load
+    const int carry_a = PH ? (lchunk + phase(Ap, (int64_t)m0 + ld_row)) >> 3 : 0;
+    const int carry_b = PH ? (lchunk + phase(Bp, (int64_t)n0 + ld_row)) >> 3 : 0;
+    const int ph_fa = PH ? phase(Ap, (int64_t)m0 + wm * TM + fr) : 0;
+    const int ph_fb = PH ? phase(Bp, (int64_t)n0 + wn * TN + fr) : 0;
 
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
     const i32x4 ra = rsrc_words((const unsigned char*)Ap + (size_t)m0 * row_bytes, (u32)rows_a * row_bytes);
@@ -338,10 +363,14 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     // The lane's fragment of k-substep ks from the row at `rowp`: one 16-byte
     // chunk (16-bit inputs) or two consecutive ones (8-bit inputs), logical
     // chunks (KSUB*ESZ/16)*ks + fhi*CPL + j, stored at chunk ^ fsw.
-    auto ld_frag = [&](const unsigned char* rowp, int ks) -> Frag {
+    // PH: the lane's chunk lies in the next stage (next - this bytes on) when
+    // its logical chunk plus the row's phase passes the line's end.
+    auto ld_frag = [&](const unsigned char* rowp, int ks, int ph = 0, int next = 0) -> Frag {
         constexpr int CPL = 2 / ESZ;  // chunks per lane per fragment
         const int c0 = (KSUB * ESZ / 16) * ks + fhi * CPL;
-        if constexpr (CPL == 1) {
+        if constexpr (PH) {
+            return *(const u32x4*)(rowp + (c0 + ph >= 8 ? next : 0) + ((c0 ^ fsw) * 16));
+        } else if constexpr (CPL == 1) {
             return *(const u32x4*)(rowp + ((c0 ^ fsw) * 16));
         } else {
             const u32x4 lo = *(const u32x4*)(rowp + ((c0 ^ fsw) * 16));
@@ -349,11 +378,16 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
             return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
     };
+    // bytes from a stage (or its B tile) to the same place in the next stage
+    auto next_stage = [&](const unsigned char* s) -> int {
+        return s + STAGE_BYTES < lds + STAGES * STAGE_BYTES ? STAGE_BYTES : -(STAGES - 1) * STAGE_BYTES;
+    };
     auto read_frags = [&](const unsigned char* s, int ks, Frag (&fb)[FN], Frag (&fa)[FM]) {
+        const int nx = PH ? next_stage(s) : 0;
 #pragma unroll
-        for (int i = 0; i < FN; ++i) fb[i] = ld_frag(s + b_base + MF * ROWB * i, ks);
+        for (int i = 0; i < FN; ++i) fb[i] = ld_frag(s + b_base + MF * ROWB * i, ks, ph_fb, nx);
 #pragma unroll
-        for (int j = 0; j < FM; ++j) fa[j] = ld_frag(s + a_base + MF * ROWB * j, ks);
+        for (int j = 0; j < FM; ++j) fa[j] = ld_frag(s + a_base + MF * ROWB * j, ks, ph_fa, nx);
     };
     auto mfma1 = [&](const Frag& b, const Frag& a, typename AB::type& c) {
         if constexpr (ESZ == 1) c = Mfma<IN>::m32x32x64(b, a, c);
@@ -428,6 +462,19 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         auto load_one = [&](int stage, int kt, int d) {
             if (!loader) return;
             unsigned char* sbase = lds + stage * STAGE_BYTES;
+            if constexpr (PH) {
+                // K segment (kb + kt - carry) of the lane's row; its full byte
+                // offset in the per-lane operand (none before the first segment)
+                const int carry = d < LAW ? carry_a : carry_b;
+                const int seg = kb + kt - carry;
+                const u32 base = l_off + (u32)(d < LAW ? d : d - LAW) * lw_stride;
+                const u32 off = seg >= 0 && seg * BK + l_kc < Ke ? base + (u32)seg * (u32)ROWB : kOutOfRange;
+                if (d < LAW)
+                    dma16(ra, sbase + (wave + d * LW) * 1024, off, 0u);
+                else
+                    dma16(rb, sbase + BM * ROWB + (wave + (d - LAW) * LW) * 1024, off, 0u);
+                return;
+            }
             const u32 kbytes = (u32)(kb + kt) * (u32)ROWB;
             const int kleft = Ke - (kb + kt) * BK;
             if (d < LAW)
@@ -442,12 +489,13 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         auto read_one = [&](const unsigned char* sta, const unsigned char* stb, int ks, auto rc, Frag (&fb)[FN],
                             Frag (&fa)[FM]) {
             constexpr int r = decltype(rc)::value;
+            const int nx = PH ? next_stage(sta) : 0;
             if constexpr (r == 0)
-                fb[0] = ld_frag(stb + b_base0, ks);
+                fb[0] = ld_frag(stb + b_base0, ks, ph_fb, nx);
             else if constexpr (r <= FM)
-                fa[r - 1] = ld_frag(sta + a_base + MF * ROWB * (r - 1), ks);
+                fa[r - 1] = ld_frag(sta + a_base + MF * ROWB * (r - 1), ks, ph_fa, nx);
             else
-                fb[r - FM] = ld_frag(stb + b_base0 + MF * ROWB * (r - FM), ks);
+                fb[r - FM] = ld_frag(stb + b_base0 + MF * ROWB * (r - FM), ks, ph_fb, nx);
         };
         // the NMMA MFMAs of one substep; after MFMA t it issues load d of the
         // refill if d * NMMA / CH == t (when do_load), and with ILR fragment
@@ -556,7 +604,8 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         for (int s = 0; s < STAGES - 1; ++s)
 #pragma unroll
             for (int d = 0; d < L; ++d) load_one(s, s, d);
-        wait_vmcnt<(STAGES - 2) * L>();
+        // tile 0 has landed (PH: tiles 0 and 1, the lines K segment 0 spans)
+        wait_vmcnt<(STAGES - 2 - (PH ? 1 : 0)) * L>();
         barrier_no_fence();
 #pragma unroll
         for (int d = 0; d < CH * HEADC; ++d) load_one(STAGES - 1, STAGES - 1, d);  // head chunks of tile STAGES - 1
@@ -577,7 +626,9 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
                 mma_refill(fb[ks % NSLOT], fa[ks % NSLOT], ps, kt + STAGES - 1, ks + FD < SPREAD ? ks + FD : -1,
                            s, ks + FD, fb[(ks + FD) % NSLOT], fa[(ks + FD) % NSLOT]);
             }
-            wait_vmcnt<(STAGES - 2) * L>();       // this wave's part of tile kt + 1 has landed
+            // this wave's part of tile kt + 1 has landed (PH: of kt + 2 too,
+            // the second line of K segment kt + 1)
+            wait_vmcnt<(STAGES - 2 - (PH ? 1 : 0)) * L>();
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done reading stage cs
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);

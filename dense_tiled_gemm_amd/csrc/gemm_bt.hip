@@ -82,7 +82,7 @@ static int out_index(int out_dtype) {
 static int out_size(int out_dtype) { return out_dtype == GEMM_BT_F32 || out_dtype == GEMM_BT_INT32 ? 4 : 2; }
 
 template <int BM, int BN, int BK, int S, int WM, int WN, int SWZ, int SCHED = 0, int PF = 0, int MF = 32,
-          bool ALL = false, int LDW = 0, int RING5 = 0, bool F8 = false>
+          bool ALL = false, int LDW = 0, int RING5 = 0, bool F8 = false, int PH = 0>
 static DmaVariant dma_variant(const char* name) {
     DmaVariant v = {name, BM, BN, BK, RING5 ? 5 : S, WM, WN, SWZ, 0, {}};
     // LDS: BK elements of 1 (8-bit inputs) or 2 bytes per tile row
@@ -100,13 +100,13 @@ static DmaVariant dma_variant(const char* name) {
             v.fn[4][3] = (const void*)&dma_kernel<GEMM_BT_INT8, GEMM_BT_INT32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
         }
     } else {
-        v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-        v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+        v.fn[0][1] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5, 0, PH>;
+        v.fn[1][2] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5, 0, PH>;
         if constexpr (ALL) {
-            v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-            v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-            v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
-            v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5>;
+            v.fn[0][0] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5, 0, PH>;
+            v.fn[0][2] = (const void*)&dma_kernel<GEMM_BT_BF16, GEMM_BT_F16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5, 0, PH>;
+            v.fn[1][0] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_F32, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5, 0, PH>;
+            v.fn[1][1] = (const void*)&dma_kernel<GEMM_BT_F16, GEMM_BT_BF16, BM, BN, BK, S, WM, WN, SWZ, SCHED, PF, MF, LDW, RING5, 0, PH>;
         }
     }
     return v;
@@ -125,7 +125,7 @@ static DmaVariant split_only_variant(const char* name) {
 // (128-element K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32
 // MFMAs over 64-element substeps); 10 and 11 run only split along K, for thin
 // products (plan_split_rule), with 128-element K steps of 16-bit inputs
-// (256-byte tile rows).
+// (256-byte tile rows); 12..14 are 1, 8 and 9 with the line ring.
 // A build with GEMM_BT_TUNING defined adds the measured alternatives after
 // them (selected with GEMM_BT_FORCE_TILE=<name>, bf16->bf16 and f16->f16
 // only); the default library holds the production tile shapes only.
@@ -136,6 +136,9 @@ constexpr int kShort16 = 8;  // 96 x 128 tiles (16-bit inputs, 4 waves of 48 x 6
 constexpr int kNarrow16 = 9;  // 128 x 96 tiles (16-bit inputs, 4 waves of 64 x 48), see plan_impl
 constexpr int kThin64 = 10;   // 64 x 64 tiles of 256-byte rows, split along K only (thin products)
 constexpr int kThin32 = 11;   // 32 x 64 tiles of 256-byte rows, split along K only (thin products)
+// The line-ring twins of the 128 x 128, 96 x 128 and 128 x 96 tiers (dma_kernel
+// PH = 1), for rows that are 16-byte but not 128-byte aligned.
+constexpr int kRing128 = 12, kRingShort = 13, kRingNarrow = 14;
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
@@ -150,6 +153,10 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<128, 96, 64, 4, 2, 2, 2, 6, 0, 16, true>("M128x96s4"),
         split_only_variant<64, 64, 128, 4, 2, 2, 2>("Q64B128s4"),
         split_only_variant<32, 64, 128, 4, 2, 2, 2>("T32x64B128s4"),
+        // the line ring (PH) twins of indices 1, 8 and 9
+        dma_variant<128, 128, 64, 4, 2, 2, 2, 8, 0, 16, true, 0, 0, false, 1>("M64E4s4iP"),
+        dma_variant<96, 128, 64, 4, 2, 2, 2, 6, 0, 16, true, 0, 0, false, 1>("M96x128s4P"),
+        dma_variant<128, 96, 64, 4, 2, 2, 2, 6, 0, 16, true, 0, 0, false, 1>("M128x96s4P"),
 #ifdef GEMM_BT_TUNING
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
@@ -168,6 +175,8 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<256, 128, 64, 3, 4, 2, 2, 8, 0, 16>("H256x128s3"),
         dma_variant<128, 256, 64, 2, 2, 4, 2, 8, 0, 16>("H128x256s2"),
         dma_variant<128, 128, 64, 2, 2, 2, 2, 8, 0, 16>("M64s2"),
+        dma_variant<128, 96, 64, 5, 2, 2, 2, 6, 0, 16, true, 0, 0, false, 1>("M128x96s5P"),
+        dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true, 0, 0, false, 1>("Q64E4m16P"),
 #endif
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
@@ -552,6 +561,20 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
             const int64_t best = tiles_s <= num_cu ? tiles_s : 0, alt = tiles_n96 <= num_cu ? tiles_n96 : 0;
             if (alt > best && alt > tiles_m128) use = kNarrow16;
             else if (best > tiles_m128) use = kShort16;
+        }
+        // Rows that are 16-byte aligned but not 128-byte aligned: the 128-row
+        // tiers load whole cache lines through the line ring (each 128-byte
+        // K segment of such a row spans two lines).  Measured (us, same box,
+        // plain vs line ring): 1024x4096x4104 f16 58.7 vs 44.5 (128 x 128),
+        // 768x4096x4104 50.3 vs 39.0 (96 x 128), 1000x3000x3000 -> f32 32.4 vs
+        // 28.7 and 1000x3000x2056 25.0 vs 22.8 (128 x 96).  It costs a stage of
+        // prefetch depth, so aligned rows keep the plain ring (1000x3000x2048
+        // 20.4 vs 22.2), and so do the 64 x 64 and 32 x 64 tiers (1000^3 10.6
+        // vs 11.4).
+        if (K % 8 == 0 && a_align % 16 == 0 && b_align % 16 == 0 && (K * 2) % 128 != 0) {
+            if (use == 1) use = kRing128;
+            else if (use == kShort16) use = kRingShort;
+            else if (use == kNarrow16) use = kRingNarrow;
         }
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;

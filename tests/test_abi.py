@@ -223,6 +223,26 @@ def test_wide_tier_and_split_plans():
     assert gb.gemm_bt_plan_ws(64, 8192, 8192, gb.INT8, gb.INT32).split_tiles == 0
 
 
+def test_line_ring_plans():
+    """Rows 16-byte aligned but not 128-byte aligned (K % 8 == 0, K % 64 != 0 for 16-bit inputs) take the line-ring
+    twins (variants 12..14) of the 128 x 128, 96 x 128 and 128 x 96 tiers; everything else keeps its plain tier."""
+    def plan(M, N, K, ind=gb.BF16, outd=gb.BF16, a_align=256, b_align=256, batch=1):
+        p = gb.gemm_bt_plan_batched(batch, M, N, K, ind, outd, a_align, b_align)
+        return p.variant, p.bm, p.bn, p.bk, p.stages
+    assert plan(1024, 4096, 4104, gb.F16, gb.F16) == (12, 128, 128, 64, 4)
+    assert plan(768, 4096, 4104) == (13, 96, 128, 64, 4)
+    assert plan(1000, 3000, 2056, gb.BF16, gb.F32) == (14, 128, 96, 64, 4)
+    assert plan(1000, 3000, 3000, gb.BF16, gb.F32)[0] == 14
+    assert plan(512, 1024, 4104, batch=8)[0] == 12                      # batch items, each 16-byte aligned
+    assert plan(1024, 4096, 4096, gb.F16, gb.F16)[0] == 1               # 128-byte aligned rows
+    assert plan(1024, 4096, 4104, gb.F16, gb.F16, a_align=8)[0] == 1    # A only 8-byte aligned
+    assert plan(1024, 4096, 4104, gb.F16, gb.F16, b_align=4)[0] == 1
+    assert plan(1000, 3000, 2050, gb.BF16, gb.F32)[0] == 9              # 4-byte aligned rows
+    assert plan(1000, 1000, 1000, gb.BF16, gb.F32)[0] == 2              # the 64 x 64 tier keeps its ring
+    assert plan(4096, 4096, 4104)[0] == 0                               # 256 x 256 (five-slot ring)
+    assert plan(1024, 4096, 4112, gb.FP8_E4M3, gb.BF16)[0] == 4         # 16-bit inputs only
+
+
 def test_layout_tier_band():
     """K-outer operands: 256x256 tiles at exactly one wave of them on 256 CUs and above 1.375 waves."""
     def bm(M, N, K=4096):

@@ -95,7 +95,7 @@ SHAPES = [
     (64, 4104, 200), (100, 2050, 134),
     # 256x256 tiles (five-slot ring): one K step, a K tail, ragged edges with three steps, a wrapped ring
     (4096, 4096, 8), (4096, 4096, 130), (4900, 4100, 136), (4096, 4096, 200),
-    # just above one wave of 256x256 tiles (289 of them): 128x128 tiles, ragged edges
+    # just above one wave of 256x256 tiles (289 of them): the 128x256 tier, ragged edges
     (4100, 4100, 136),
     # 128x256 tiles (one wave of them, and 1.5 waves): whole tiles, ragged edges with a partial last K step,
     # a K tail, C rows of 8-byte and 2-byte alignment
@@ -483,6 +483,10 @@ BATCHED = [
     # 16 items of 512x1024 (one wave of 128x256 tiles)
     (68, 512, 512, 136, "bf16", "bf16", None, (0, 0, 0)),
     (16, 512, 1024, 72, "f16", "f32", None, (0, 0, 0)),
+    # the line ring (128x128 tiles, rows 16-byte but not 128-byte aligned) on items whose bases sit at a
+    # different phase of the cache line each (an item stride of 139280 bytes), and with A shared
+    (9, 512, 512, 136, "bf16", "bf16", None, (8, 0, 0)),
+    (9, 512, 512, 136, "f16", "f32", "a", (0, 8, 0)),
 ]
 
 
@@ -500,6 +504,33 @@ def test_batched(gpu, case):
         else:
             rep = tolerance.check(f64(items[z]), cref[z], np.outer(nA[z], nB[z]), outd)
             assert rep.ok, (z, rep)
+
+
+LINE_RING = [(1024, 4096, 4104, "f16", "f16"), (768, 4096, 4104, "bf16", "bf16"), (1000, 3000, 3000, "bf16", "f32"),
+             (1540, 2050, 1000, "bf16", "bf16")]
+
+
+@pytest.mark.parametrize("case", range(len(LINE_RING)))
+def test_line_ring_large(gpu, case):
+    """Large products whose rows are 16-byte but not 128-byte aligned (the line ring on the 128x128, 96x128 and
+    128x96 tiers, up to 129 K steps): tile edges plus 20000 random entries against the oracle, and the integer
+    twin bit for bit on the same entries."""
+    M, N, K, ind, outd = LINE_RING[case]
+    plan = gpu.gemm_bt_plan(M, N, K, gpu._torch_code(TORCH_DT[ind]), gpu._torch_code(TORCH_DT[outd]))
+    say("line ring", M, N, K, ind, outd, "variant", plan.variant, "tile", plan.bm, plan.bn)
+    assert plan.variant in (12, 13, 14), "the case must take the line ring"
+    rng = np.random.default_rng(1700 + case)
+    I, J = sample_entries(M, N, rng)
+    a, b = synth.make(M, N, K, ind, "normal", 1700 + case)
+    c = f64(run_gpu(gpu, a, b, ind, outd))
+    ref = oracle.gemm_bt_entries(a, b, ind, I, J)
+    rep = tolerance.check(c[I, J], ref, oracle.row_norms(a, ind)[I] * oracle.row_norms(b, ind)[J], outd)
+    assert rep.ok, rep
+    ai, bi = synth.make(M, N, K, ind, "int", 1750 + case)
+    ci = run_gpu(gpu, ai, bi, ind, outd)
+    refi = oracle.round_to(oracle.gemm_bt_entries(ai, bi, ind, I, J), outd)
+    rep = tolerance.bit_exact(out_bits(ci)[I, J], refi, outd)
+    assert rep.ok, rep
 
 
 def test_batched_integer_bit_exact(gpu):
