@@ -189,10 +189,13 @@ static const DmaVariant* dma_variants(int* count) {
 // with 128-element K steps (indices 10 and 11): each piece then streams 256
 // contiguous bytes of every B row per step instead of 128 (same box, us, 64-
 // against 128-element steps: 64x8192x8192 35.5 vs 34.8, 24x8192x8192 35.3 vs
-// 34.4, 32x4096x4096 15.5 vs 14.8, 64x4096x16384 f16 38.6 vs 37.8).  A tuning
-// build also has the split form of the 128 x 256 tier (index 7; measured no
-// faster: 1024x4096x4096 f16 43.1 us split 2 ways against 42.9 us unsplit on
-// 128 x 128 tiles).
+// 34.4, 32x4096x4096 15.5 vs 14.8, 64x4096x16384 f16 38.6 vs 37.8); and the
+// 128 x 128 tier's line-ring twin (index 12) for rows 16-byte but not
+// 128-byte aligned (us, plain vs line ring: 1000x1000x8200 -> f32 39.4 vs
+// 32.8, 1024x1024x16392 68.0 vs 53.5, 512x1024x32776 f16 76.4 vs 60.5,
+// 256x4096x8200 42.5 vs 37.5).  A tuning build also has the split form of the
+// 128 x 256 tier (index 7; measured no faster: 1024x4096x4096 f16 43.1 us
+// split 2 ways against 42.9 us unsplit on 128 x 128 tiles).
 constexpr int kSkVariant = 1;
 template <int IN, int OUT>
 static const void* sk_fn_t(int variant) {
@@ -200,6 +203,7 @@ static const void* sk_fn_t(int variant) {
     if (variant == 7) return (const void*)&dma_kernel<IN, OUT, 128, 256, 64, 3, 2, 4, 2, 8, 0, 16, 0, 0, 1>;
 #endif
     if (variant == kSkVariant) return (const void*)&dma_kernel<IN, OUT, 128, 128, 64, 4, 2, 2, 2, 8, 0, 16, 0, 0, 1>;
+    if (variant == kRing128) return (const void*)&dma_kernel<IN, OUT, 128, 128, 64, 4, 2, 2, 2, 8, 0, 16, 0, 0, 1, 1>;
     if (variant == kThin64) return (const void*)&dma_kernel<IN, OUT, 64, 64, 128, 4, 2, 2, 2, 4, 0, 16, 0, 0, 1>;
     if (variant == kThin32) return (const void*)&dma_kernel<IN, OUT, 32, 64, 128, 4, 2, 2, 2, 2, 0, 16, 0, 0, 1>;
     return nullptr;  // no split form of this tile
@@ -404,14 +408,15 @@ static bool plan_split(int64_t M, int64_t N, int64_t K, int variant, int num_cu,
 //    every CU and M fills less than 3/4 of the 128-row tiles (their rows
 //    are then mostly padding): 100x4096x16384 (rows 78 % full) splits at 47.7
 //    against 65.4.
-static bool plan_split_rule(int64_t M, int64_t N, int64_t K, int num_cu, int64_t plain_tiles, gemm_bt_plan_t* p) {
+static bool plan_split_rule(int64_t M, int64_t N, int64_t K, int num_cu, int64_t plain_tiles, bool ring,
+                            gemm_bt_plan_t* p) {
 #ifdef GEMM_BT_TUNING
     if (const char* e = std::getenv("GEMM_BT_SPLIT_TILE")) return plan_split(M, N, K, std::atoi(e), num_cu, true, p);
 #endif
     if (M <= 64) return plan_split(M, N, K, M <= 32 ? kThin32 : kThin64, num_cu, true, p);
     const int64_t rows = ((M + 127) / 128) * 128;
     if (plain_tiles >= num_cu && M * 4 < rows * 3) return false;
-    return plan_split(M, N, K, kSkVariant, num_cu, false, p);
+    return plan_split(M, N, K, ring ? kRing128 : kSkVariant, num_cu, false, p);
 }
 
 static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,
@@ -539,8 +544,14 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         // 4608x4096x4096 153.5 vs 148.0, 4352x4096x8192 305 vs 281; just
         // above one wave no better (3000x3000x4096, 1.125 waves, 95.3 vs 95.2;
         // 2560x4096x4096, 1.25 waves, 93.9 vs 95.5).
+        // Rows that are 16-byte but not 128-byte aligned: the 128-row tiers
+        // below run their line-ring twins, and the 128 x 256 tier, whose
+        // three stages leave no room for the ring's extra one, gives way to
+        // 128 x 128 ring tiles (us, same box: 2048x4096x4104 84.5 vs 81.9,
+        // 3072x4096x4104 129.7 vs 114.3, 4100x4100x1000 87.2 vs 80.6).
+        const bool ring = K % 8 == 0 && a_align % 16 == 0 && b_align % 16 == 0 && (K * 2) % 128 != 0;
         const int64_t tiles_h = ((M + 127) / 128) * ((N + 255) / 256) * batch;
-        if (use == 1 && tiles_h >= num_cu && (tiles_h % num_cu == 0 || tiles_h * 8 > (int64_t)num_cu * 11))
+        if (use == 1 && !ring && tiles_h >= num_cu && (tiles_h % num_cu == 0 || tiles_h * 8 > (int64_t)num_cu * 11))
             use = kWide16;
         // 96 x 128 or 128 x 96 tiles instead of 128 x 128 ones for a single
         // product when they still make at most one wave and keep more CUs
@@ -571,7 +582,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         // prefetch depth, so aligned rows keep the plain ring (1000x3000x2048
         // 20.4 vs 22.2), and so do the 64 x 64 and 32 x 64 tiers (1000^3 10.6
         // vs 11.4).
-        if (K % 8 == 0 && a_align % 16 == 0 && b_align % 16 == 0 && (K * 2) % 128 != 0) {
+        if (ring) {
             if (use == 1) use = kRing128;
             else if (use == kShort16) use = kRingShort;
             else if (use == kNarrow16) use = kRingNarrow;
@@ -588,7 +599,8 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         p->threads = 64 * v.wm * v.wn;
         p->lds_bytes = v.lds_bytes;
         const int64_t plain_tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
-        if (allow_sk && f < 0 && batch == 1 && plan_split_rule(M, N, K, num_cu, plain_tiles, p)) return GEMM_BT_OK;
+        if (allow_sk && f < 0 && batch == 1 && plan_split_rule(M, N, K, num_cu, plain_tiles, ring, p))
+            return GEMM_BT_OK;
     } else {
         // tuning build only (GEMM_BT_FORCE_TILE=STAGED): the register-staged kernel
         const TileCfg c = big ? kCfgL : kCfgM;

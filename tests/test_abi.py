@@ -172,7 +172,8 @@ def test_wide_tier_and_split_plans():
     assert tile(2560, 4096) == tile(3000, 3000) == (128, 128)    # 320 (1.25 waves), 288 (1.125)
     assert tile(2048, 2048) == (128, 128)                        # 128 tiles of 128x256: half the CUs
     assert tile(4096, 4096) == (256, 256)
-    assert tile(512, 1024, K=72, batch=16) == (128, 256)         # items stacked: 256 tiles
+    assert tile(512, 1024, K=128, batch=16) == (128, 256)        # items stacked: 256 tiles
+    assert tile(512, 1024, K=72, batch=16) == (128, 128)         # 144-byte rows: the line ring's 128x128 tiles
     assert tile(2048, 4096, ind=gb.FP8_E4M3) != (128, 256)       # 16-bit inputs only
     # 96x128 tiles for a single product when they make at most one wave and keep more CUs busy than 128x128
     assert tile(768, 4096) == tile(3000, 1000) == tile(1536, 2048) == (96, 128)  # 256 tiles each
@@ -225,7 +226,8 @@ def test_wide_tier_and_split_plans():
 
 def test_line_ring_plans():
     """Rows 16-byte aligned but not 128-byte aligned (K % 8 == 0, K % 64 != 0 for 16-bit inputs) take the line-ring
-    twins (variants 12..14) of the 128 x 128, 96 x 128 and 128 x 96 tiers; everything else keeps its plain tier."""
+    twins (variants 12..14) of the 128 x 128, 96 x 128 and 128 x 96 tiers, 128 x 128 ring tiles where aligned rows
+    would take 128 x 256 ones, and the ring's split form; everything else keeps its plain tier."""
     def plan(M, N, K, ind=gb.BF16, outd=gb.BF16, a_align=256, b_align=256, batch=1):
         p = gb.gemm_bt_plan_batched(batch, M, N, K, ind, outd, a_align, b_align)
         return p.variant, p.bm, p.bn, p.bk, p.stages
@@ -240,6 +242,11 @@ def test_line_ring_plans():
     assert plan(1000, 3000, 2050, gb.BF16, gb.F32)[0] == 9              # 4-byte aligned rows
     assert plan(1000, 1000, 1000, gb.BF16, gb.F32)[0] == 2              # the 64 x 64 tier keeps its ring
     assert plan(4096, 4096, 4104)[0] == 0                               # 256 x 256 (five-slot ring)
+    assert plan(2048, 4096, 4104)[0] == plan(3072, 4096, 1000)[0] == 12  # ring 128 x 128 instead of 128 x 256
+    assert plan(2048, 4096, 4096)[0] == 7
+    for K, v in ((16392, 12), (8200, 12), (16384, 1)):                  # the split form follows the rows too
+        p = gb.gemm_bt_plan_ws(1024, 1024, K, gb.BF16, gb.BF16)
+        assert (p.variant, p.bm, p.split_tiles, p.grid) == (v, 128, 64, 256), K
     assert plan(1024, 4096, 4112, gb.FP8_E4M3, gb.BF16)[0] == 4         # 16-bit inputs only
 
 

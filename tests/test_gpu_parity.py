@@ -97,9 +97,11 @@ SHAPES = [
     (4096, 4096, 8), (4096, 4096, 130), (4900, 4100, 136), (4096, 4096, 200),
     # just above one wave of 256x256 tiles (289 of them): the 128x256 tier, ragged edges
     (4100, 4100, 136),
-    # 128x256 tiles (one wave of them, and 1.5 waves): whole tiles, ragged edges with a partial last K step,
-    # a K tail, C rows of 8-byte and 2-byte alignment
+    # 128x256 tiles (one wave of them, and 1.5 waves): whole tiles, ragged edges, a K tail, C rows of 8-byte and
+    # 2-byte alignment (K a multiple of 64: rows that are 16-byte but not 128-byte aligned take the line ring's
+    # 128x128 tiles instead, as the first, second, fourth and sixth do)
     (2048, 4096, 136), (2000, 4000, 200), (2048, 4096, 130), (2048, 4004, 72), (2048, 3999, 64), (3072, 4096, 72),
+    (2048, 4096, 128), (2000, 4000, 192), (2048, 4004, 64), (3072, 4096, 256),
     # 304 tiles of 256x256 (1.19 waves, the edge of the band that takes smaller tiles)
     (4864, 4096, 136),
     # 96x128 tiles (at most one wave of them, more than 128x128 tiles would use): one exact wave, partial tile
@@ -481,8 +483,8 @@ BATCHED = [
     (7, 64, 96, 48, "e5m2", "f32", "a", (0, 0, 0)),
     # items stacked into 128x256 tiles: 68 items of 512x512 (272 tiles of 256x256, just above one wave) and
     # 16 items of 512x1024 (one wave of 128x256 tiles)
-    (68, 512, 512, 136, "bf16", "bf16", None, (0, 0, 0)),
-    (16, 512, 1024, 72, "f16", "f32", None, (0, 0, 0)),
+    (68, 512, 512, 128, "bf16", "bf16", None, (0, 0, 0)),
+    (16, 512, 1024, 192, "f16", "f32", None, (0, 0, 0)),
     # the line ring (128x128 tiles, rows 16-byte but not 128-byte aligned) on items whose bases sit at a
     # different phase of the cache line each (an item stride of 139280 bytes), and with A shared
     (9, 512, 512, 136, "bf16", "bf16", None, (8, 0, 0)),
@@ -507,7 +509,7 @@ def test_batched(gpu, case):
 
 
 LINE_RING = [(1024, 4096, 4104, "f16", "f16"), (768, 4096, 4104, "bf16", "bf16"), (1000, 3000, 3000, "bf16", "f32"),
-             (1540, 2050, 1000, "bf16", "bf16")]
+             (1540, 2050, 1000, "bf16", "bf16"), (2048, 4096, 1000, "f16", "f16")]
 
 
 @pytest.mark.parametrize("case", range(len(LINE_RING)))
@@ -878,6 +880,8 @@ SK_CASES = [  # (M, N, K, in, out)
     # thin products: 64x64 and 32x64 tiles, ragged M, N and K, fewer pieces for short K, 16 pieces
     (64, 8192, 8192, "bf16", "bf16"), (17, 4100, 4099, "f16", "f32"), (40, 6000, 8195, "bf16", "f32"),
     (33, 3000, 8192, "f16", "f16"), (64, 1024, 65536, "bf16", "bf16"),
+    # the line ring's split form (rows 16-byte but not 128-byte aligned)
+    (512, 1024, 16392, "f16", "f16"), (300, 700, 30008, "bf16", "bf16"),
 ]
 
 

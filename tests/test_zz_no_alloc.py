@@ -49,7 +49,8 @@ def test_noalloc_matches_gemm_bt_ws(gpu):
     # split twice in a row, the second product smaller (fewer tiles, more pieces each)
     assert _both(gpu, 1024, 1024, 16384, "bf16", "bf16", 31) > 0
     assert _both(gpu, 300, 700, 30002, "bf16", "f32", 32) > 0
-    # a thin product: 64x64 tiles in pieces
+    # a thin product: 64x64 tiles in pieces; rows 16-byte but not 128-byte aligned: the line ring in pieces
     assert _both(gpu, 64, 8192, 8192, "bf16", "bf16", 34) > 0
+    assert _both(gpu, 1000, 1000, 8200, "bf16", "f32", 35) > 0
     # not split: the plain plan through the same entry point
     assert _both(gpu, 1000, 3000, 2050, "f16", "f16", 33) == 0
