@@ -125,7 +125,7 @@ static DmaVariant split_only_variant(const char* name) {
 // (128-element K steps: 128-byte tile rows, as for the 16-bit kernels; 32x32
 // MFMAs over 64-element substeps); 10 and 11 run only split along K, for thin
 // products (plan_split_rule), with 128-element K steps of 16-bit inputs
-// (256-byte tile rows); 12..14 are 1, 8 and 9 with the line ring.
+// (256-byte tile rows); 12..15 are 1, 8, 9 and 2 with the line ring.
 // A build with GEMM_BT_TUNING defined adds the measured alternatives after
 // them (selected with GEMM_BT_FORCE_TILE=<name>, bf16->bf16 and f16->f16
 // only); the default library holds the production tile shapes only.
@@ -136,9 +136,9 @@ constexpr int kShort16 = 8;  // 96 x 128 tiles (16-bit inputs, 4 waves of 48 x 6
 constexpr int kNarrow16 = 9;  // 128 x 96 tiles (16-bit inputs, 4 waves of 64 x 48), see plan_impl
 constexpr int kThin64 = 10;   // 64 x 64 tiles of 256-byte rows, split along K only (thin products)
 constexpr int kThin32 = 11;   // 32 x 64 tiles of 256-byte rows, split along K only (thin products)
-// The line-ring twins of the 128 x 128, 96 x 128 and 128 x 96 tiers (dma_kernel
-// PH = 1), for rows that are 16-byte but not 128-byte aligned.
-constexpr int kRing128 = 12, kRingShort = 13, kRingNarrow = 14;
+// The line-ring twins of the 128 x 128, 96 x 128, 128 x 96 and 64 x 64 tiers
+// (dma_kernel PH = 1), for rows that are 16-byte but not 128-byte aligned.
+constexpr int kRing128 = 12, kRingShort = 13, kRingNarrow = 14, kRing64 = 15;
 static const DmaVariant* dma_variants(int* count) {
     static const DmaVariant v[] = {
         dma_variant<256, 256, 64, 2, 2, 4, 2, 6, 0, 16, true, 0, 2>("L64E16iR5s"),
@@ -157,6 +157,7 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<128, 128, 64, 4, 2, 2, 2, 8, 0, 16, true, 0, 0, false, 1>("M64E4s4iP"),
         dma_variant<96, 128, 64, 4, 2, 2, 2, 6, 0, 16, true, 0, 0, false, 1>("M96x128s4P"),
         dma_variant<128, 96, 64, 4, 2, 2, 2, 6, 0, 16, true, 0, 0, false, 1>("M128x96s4P"),
+        dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true, 0, 0, false, 1>("Q64E4m16P"),
 #ifdef GEMM_BT_TUNING
         dma_variant<256, 256, 64, 2, 2, 4, 2, 2, 0, 16>("L64E16"),
         dma_variant<128, 128, 64, 4, 2, 2, 2, 4, 0, 16>("M64E4s4m16"),
@@ -176,7 +177,7 @@ static const DmaVariant* dma_variants(int* count) {
         dma_variant<128, 256, 64, 2, 2, 4, 2, 8, 0, 16>("H128x256s2"),
         dma_variant<128, 128, 64, 2, 2, 2, 2, 8, 0, 16>("M64s2"),
         dma_variant<128, 96, 64, 5, 2, 2, 2, 6, 0, 16, true, 0, 0, false, 1>("M128x96s5P"),
-        dma_variant<64, 64, 64, 4, 2, 2, 2, 4, 0, 16, true, 0, 0, false, 1>("Q64E4m16P"),
+
 #endif
     };
     *count = (int)(sizeof(v) / sizeof(v[0]));
@@ -580,12 +581,18 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         // 768x4096x4104 50.3 vs 39.0 (96 x 128), 1000x3000x3000 -> f32 32.4 vs
         // 28.7 and 1000x3000x2056 25.0 vs 22.8 (128 x 96).  It costs a stage of
         // prefetch depth, so aligned rows keep the plain ring (1000x3000x2048
-        // 20.4 vs 22.2), and so do the 64 x 64 and 32 x 64 tiers (1000^3 10.6
-        // vs 11.4).
+        // 20.4 vs 22.2), and so does the 64 x 64 tier while its tiles fit one
+        // workgroup per CU (1000x1000xK, 256 tiles: K = 1000 10.5 vs 11.1,
+        // 4000 20.0 vs 24.0); with more tiles than CUs two workgroups share a
+        // CU and the ring wins (1000x1500x3000 29.1 vs 23.2, 700x2000x3000
+        // 31.0 vs 22.6, 1000x2000x1000 14.5 vs 13.2).  The 32 x 64 tier, used
+        // only when even 64 x 64 tiles fill half the CUs, keeps its plain ring
+        // (500x500x1000 8.5 vs 10.0).
         if (ring) {
             if (use == 1) use = kRing128;
             else if (use == kShort16) use = kRingShort;
             else if (use == kNarrow16) use = kRingNarrow;
+            else if (use == 2 && tiles_q64 > num_cu) use = kRing64;
         }
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;

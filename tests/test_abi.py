@@ -226,7 +226,8 @@ def test_wide_tier_and_split_plans():
 
 def test_line_ring_plans():
     """Rows 16-byte aligned but not 128-byte aligned (K % 8 == 0, K % 64 != 0 for 16-bit inputs) take the line-ring
-    twins (variants 12..14) of the 128 x 128, 96 x 128 and 128 x 96 tiers, 128 x 128 ring tiles where aligned rows
+    twins (variants 12..15) of the 128 x 128, 96 x 128, 128 x 96 and (above one tile per CU) 64 x 64 tiers,
+    128 x 128 ring tiles where aligned rows
     would take 128 x 256 ones, and the ring's split form; everything else keeps its plain tier."""
     def plan(M, N, K, ind=gb.BF16, outd=gb.BF16, a_align=256, b_align=256, batch=1):
         p = gb.gemm_bt_plan_batched(batch, M, N, K, ind, outd, a_align, b_align)
@@ -240,7 +241,10 @@ def test_line_ring_plans():
     assert plan(1024, 4096, 4104, gb.F16, gb.F16, a_align=8)[0] == 1    # A only 8-byte aligned
     assert plan(1024, 4096, 4104, gb.F16, gb.F16, b_align=4)[0] == 1
     assert plan(1000, 3000, 2050, gb.BF16, gb.F32)[0] == 9              # 4-byte aligned rows
-    assert plan(1000, 1000, 1000, gb.BF16, gb.F32)[0] == 2              # the 64 x 64 tier keeps its ring
+    assert plan(1000, 1000, 1000, gb.BF16, gb.F32)[0] == 2              # 64 x 64: one tile per CU, plain ring
+    assert plan(1000, 1500, 3000)[0] == plan(700, 2000, 200)[0] == 15  # 64 x 64: more tiles than CUs, line ring
+    assert plan(1000, 2000, 1024)[0] == 2                               # ... on aligned rows, plain
+    assert plan(500, 500, 1000)[0] == 6                                 # 32 x 64 keeps its plain ring
     assert plan(4096, 4096, 4104)[0] == 0                               # 256 x 256 (five-slot ring)
     assert plan(2048, 4096, 4104)[0] == plan(3072, 4096, 1000)[0] == 12  # ring 128 x 128 instead of 128 x 256
     assert plan(2048, 4096, 4096)[0] == 7

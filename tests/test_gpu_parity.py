@@ -114,6 +114,8 @@ SHAPES = [
     # every tile tier and with no whole chunk at all
     (130, 264, 73), (300, 520, 1007), (64, 64, 7), (1000, 3000, 2051), (4096, 4096, 131), (2048, 4096, 135),
     (4100, 4100, 137), (96, 200, 35),
+    # the line ring on 64x64 tiles (more of them than CUs; rows 16-byte but not 128-byte aligned), ragged edges
+    (700, 2000, 200), (1000, 1500, 136), (1030, 1500, 72),
 ]
 SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200),
           # K tails of 7 and 1 element, odd K with no whole chunk, 2-byte aligned rows
@@ -509,18 +511,18 @@ def test_batched(gpu, case):
 
 
 LINE_RING = [(1024, 4096, 4104, "f16", "f16"), (768, 4096, 4104, "bf16", "bf16"), (1000, 3000, 3000, "bf16", "f32"),
-             (1540, 2050, 1000, "bf16", "bf16"), (2048, 4096, 1000, "f16", "f16")]
+             (1540, 2050, 1000, "bf16", "bf16"), (2048, 4096, 1000, "f16", "f16"), (1000, 1500, 3000, "f16", "f16")]
 
 
 @pytest.mark.parametrize("case", range(len(LINE_RING)))
 def test_line_ring_large(gpu, case):
-    """Large products whose rows are 16-byte but not 128-byte aligned (the line ring on the 128x128, 96x128 and
-    128x96 tiers, up to 129 K steps): tile edges plus 20000 random entries against the oracle, and the integer
-    twin bit for bit on the same entries."""
+    """Large products whose rows are 16-byte but not 128-byte aligned (the line ring on the 128x128, 96x128,
+    128x96 and 64x64 tiers, up to 129 K steps): tile edges plus 20000 random entries against the oracle, and the
+    integer twin bit for bit on the same entries."""
     M, N, K, ind, outd = LINE_RING[case]
     plan = gpu.gemm_bt_plan(M, N, K, gpu._torch_code(TORCH_DT[ind]), gpu._torch_code(TORCH_DT[outd]))
     say("line ring", M, N, K, ind, outd, "variant", plan.variant, "tile", plan.bm, plan.bn)
-    assert plan.variant in (12, 13, 14), "the case must take the line ring"
+    assert plan.variant in (12, 13, 14, 15), "the case must take the line ring"
     rng = np.random.default_rng(1700 + case)
     I, J = sample_entries(M, N, rng)
     a, b = synth.make(M, N, K, ind, "normal", 1700 + case)
