@@ -213,8 +213,9 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     static_assert(RING_BYTES + (PF > 0 ? W * 256 : 0) <= 160 * 1024, "LDS budget");
     // PH: the line ring for rows that are 16-byte but not 128-byte aligned
     // (see the loader below)
-    static_assert(!PH || (ESZ == 2 && CPR == 8 && !RING5 && SCHED >= 2 && PF == 0 && STAGES >= 3),
-                  "line ring: 16-bit inputs, 128-byte tile rows, an early-barrier ring of 3 or more stages");
+    static_assert(!PH || (ESZ == 2 && CPR == 8 && !RING5 && SCHED >= 2 && PF == 0 && STAGES >= 3 && LDW == 0),
+                  "line ring: 16-bit inputs, 128-byte tile rows, an early-barrier ring of 3 or more stages, "
+                  "every wave loading");
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[RING_BYTES + (PF > 0 ? W * 256 : 0)];
 

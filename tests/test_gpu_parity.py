@@ -410,6 +410,26 @@ def test_unaligned_pointers_and_odd_k(gpu):
         assert torch.isnan(bc[:off].cpu()).all() and torch.isnan(bc[off + M * N:].cpu()).all()
 
 
+def test_line_ring_shifted_bases(gpu):
+    """The line ring with operands that start 16, 48 or 112 bytes past a 128-byte line: every row's phase in its
+    line moves with the base, on the 128x128, 128x96 and 64x64 ring tiles, against the oracle in full."""
+    for (M, N, K, off) in [(1540, 2050, 136, 8), (1000, 3000, 72, 24), (1000, 1500, 136, 56), (1540, 2050, 200, 56)]:
+        a_bits, b_bits = synth.make(M, N, K, "bf16", "normal", 89)
+        plan = gpu.gemm_bt_plan(M, N, K, gpu.BF16, gpu.F32, 16, 16, 16)
+        say("ring shifted", M, N, K, "offset elems", off, "variant", plan.variant)
+        assert plan.variant in (12, 13, 14, 15), "the case must take the line ring"
+        ba = torch.zeros(M * K + off, dtype=torch.bfloat16, device="cuda")
+        bb = torch.zeros(N * K + off, dtype=torch.bfloat16, device="cuda")
+        ba[off:] = to_dev(a_bits, "bf16").reshape(-1)
+        bb[off:] = to_dev(b_bits, "bf16").reshape(-1)
+        c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        st = gpu.gemm_bt(ba.data_ptr() + 2 * off, bb.data_ptr() + 2 * off, c.data_ptr(), M, N, K, gpu.BF16, gpu.F32,
+                         torch.cuda.current_stream().cuda_stream)
+        assert st == gpu.OK
+        torch.cuda.synchronize()
+        check_full(c.cpu(), a_bits, b_bits, "bf16", "f32", (M, N, K, off))
+
+
 def test_deterministic_and_stream(gpu):
     w = synth.WORKLOADS["ragged_m1000_n3000_k2050_bf16_f32"]
     say("determinism", w.name)
