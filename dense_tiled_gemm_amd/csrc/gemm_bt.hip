@@ -574,6 +574,21 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
             if (alt > best && alt > tiles_m128) use = kNarrow16;
             else if (best > tiles_m128) use = kShort16;
         }
+        // Several waves of 128 x 128 tiles: every wave costs a full one, the
+        // last too, so 128 x 96 (or 96 x 128) tiles, whose waves take about
+        // 0.9 of the time, win when they need no more waves, i.e. when 0.9 *
+        // their waves < the 128 x 128 waves.  Measured (us, 128 x 128 vs
+        // 128 x 96): 3000^3 (576 vs 768 tiles, 3 waves each) 79.0 vs 70.9,
+        // 3072^3 75.5 vs 68.8; not where the narrower tiles need another wave
+        // (2000x7000x3000 107.6 vs 113.9, 5000x2000x2000 57.5 vs 65.0,
+        // 3000x4000x2048 54.3 vs 56.5).  Of the two, 128 x 96 (3000^3 70.9 vs
+        // 76.7 for 96 x 128).
+        if (use == 1 && batch == 1 && tiles_m128 > num_cu) {
+            const int64_t w128 = (tiles_m128 + num_cu - 1) / num_cu;
+            const int64_t wn = (tiles_n96 + num_cu - 1) / num_cu, ws = (tiles_s + num_cu - 1) / num_cu;
+            if (9 * wn < 10 * w128) use = kNarrow16;
+            else if (9 * ws < 10 * w128) use = kShort16;
+        }
         // Rows that are 16-byte aligned but not 128-byte aligned: the 128-row
         // tiers load whole cache lines through the line ring (each 128-byte
         // K segment of such a row spans two lines).  Measured (us, same box,

@@ -169,7 +169,8 @@ def test_wide_tier_and_split_plans():
         return p.bm, p.bn
     assert tile(2048, 4096) == (128, 256)                        # 256 tiles of 128x256: one wave
     assert tile(3072, 4096) == tile(4352, 4096) == (128, 256)    # 384 (1.5 waves), 544
-    assert tile(2560, 4096) == tile(3000, 3000) == (128, 128)    # 320 (1.25 waves), 288 (1.125)
+    assert tile(2560, 4096) == (128, 128)                        # 320 of 128x256 (1.25 waves)
+    assert tile(3000, 3000) == (128, 96)                         # 288 (1.125): 128x96 tiles in as many waves
     assert tile(2048, 2048) == (128, 128)                        # 128 tiles of 128x256: half the CUs
     assert tile(4096, 4096) == (256, 256)
     assert tile(512, 1024, K=128, batch=16) == (128, 256)        # items stacked: 256 tiles
@@ -180,9 +181,15 @@ def test_wide_tier_and_split_plans():
     # or 128x96 tiles when those make more tiles within the wave (96x128: 264, 264, 264, 200 against 204)
     assert tile(1000, 3000) == tile(2048, 1536) == tile(1024, 3072) == tile(700, 3200) == (128, 96)
     assert tile(1500, 1500) == (96, 128)                                           # 192 either way: 96x128
-    assert tile(3000, 3000) == tile(1024, 4096) == (128, 128)                      # 576, 256 tiles of 128x128
+    assert tile(1024, 4096) == (128, 128)                                          # 256 tiles of 128x128
     assert tile(768, 4096, batch=2) == (128, 128)                                  # single products only
     assert tile(768, 4096, ind=gb.FP8_E4M3) == (128, 128)                          # 16-bit inputs only
+    # several waves of 128x128 tiles: 128x96 (or 96x128) tiles when 0.9 x their waves < the 128x128 waves
+    assert tile(3072, 3072, K=3072) == tile(3072, 1536) == tile(1536, 6144) == (128, 96)  # 3, 2, 3 waves either way
+    assert tile(2880, 3200) == (96, 128)                   # 575 tiles (3 waves): 128x96 need 4, 96x128 3
+    assert tile(2000, 7000, K=3000) == tile(5000, 2000, K=2000) == (128, 128)  # the narrower tiles need a wave more
+    assert tile(2560, 2560) == (128, 128)
+    assert tile(3072, 1536, batch=2) != (128, 96)                                  # single products only
     p = gb.gemm_bt_plan(768, 4096, 4096, gb.BF16, gb.BF16)
     assert (p.threads, p.stages, p.grid, p.lds_bytes) == (256, 4, 256, 4 * (96 + 128) * 64 * 2)
     p = gb.gemm_bt_plan(2048, 4096, 4096, gb.BF16, gb.BF16)

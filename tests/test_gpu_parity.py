@@ -116,6 +116,8 @@ SHAPES = [
     (4100, 4100, 137), (96, 200, 35),
     # the line ring on 64x64 tiles (more of them than CUs; rows 16-byte but not 128-byte aligned), ragged edges
     (700, 2000, 200), (1000, 1500, 136), (1030, 1500, 72),
+    # several waves of 128x96 (plain and line ring) or 96x128 tiles in place of 128x128 ones, ragged edges
+    (3072, 1536, 64), (3000, 3000, 72), (2880, 3200, 64),
 ]
 SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200),
           # K tails of 7 and 1 element, odd K with no whole chunk, 2-byte aligned rows
