@@ -541,19 +541,40 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         // or more than 1.375 waves: per FLOP they load 3/4 of the bytes, and
         // one wave's MFMAs cover the other's loads.  Measured (us, 128 x 128
         // vs 128 x 256 tiles): 2048x4096x4096 76.4 vs 61.3, 2048x4096x8192 f16
-        // 140 vs 119, 2048x4096x2048 37.6 vs 33.4, 3072x4096x4096 102.6 vs 98.1,
-        // 4608x4096x4096 153.5 vs 148.0, 4352x4096x8192 305 vs 281; just
-        // above one wave no better (3000x3000x4096, 1.125 waves, 95.3 vs 95.2;
-        // 2560x4096x4096, 1.25 waves, 93.9 vs 95.5).
+        // 140 vs 119, 2048x4096x2048 37.6 vs 33.4, 4608x4096x4096 153.5 vs
+        // 148.0, 4352x4096x8192 305 vs 281; just above one wave no better
+        // (3000x3000x4096, 1.125 waves, 95.3 vs 95.2).
         // Rows that are 16-byte but not 128-byte aligned: the 128-row tiers
         // below run their line-ring twins, and the 128 x 256 tier, whose
         // three stages leave no room for the ring's extra one, gives way to
         // 128 x 128 ring tiles (us, same box: 2048x4096x4104 84.5 vs 81.9,
-        // 3072x4096x4104 129.7 vs 114.3, 4100x4100x1000 87.2 vs 80.6).
+        // 4100x4100x1000 87.2 vs 80.6).
         const bool ring = K % 8 == 0 && a_align % 16 == 0 && b_align % 16 == 0 && (K * 2) % 128 != 0;
         const int64_t tiles_h = ((M + 127) / 128) * ((N + 255) / 256) * batch;
+        // Less than one wave of 256 x 256 tiles where 128-row tiles of either
+        // width need more than one: the larger tiles win.  Per CU they load
+        // half the bytes per FLOP of 128 x 128 ones, and a partly filled wave
+        // runs each tile faster than a full one (the full chip is
+        // power-bound).  Since a 128 x 256 grid has at most twice the tiles,
+        // the 256 x 256 ones then fill more than half the CUs.  Measured (us,
+        // the 128-row plan vs 256 x 256): 2048x4352x4096 (136 tiles) 92.6 vs
+        // 75.5, 3000x3000x3072 (144) 68.9 vs 61.1, 2176x4224x4096 (153) 90.3
+        // vs 73.9, 2560x4096x4096 (160) 96.2 vs 77.4, 3072x4096x4096 (192;
+        // 128 x 256 tiles) 100.5 vs 85.4, 3584^3 (196) 87.4 vs 75.6.  Rows
+        // that take the line ring have no 256 x 256 twin of it: there the
+        // ring's 128-row tiles hold on to about 0.6 of the CUs (3000^3, 144
+        // tiles, 71.5 vs 76.2; 2100x4300x3000, 153, 81.0 vs 87.8;
+        // 4000x3000x5000, 192, 141.5 vs 124.3; 3072x4096x4104, 192, 108.7 vs
+        // 100.6; 2000x6000x3000, 192, 108.6 vs 76.3).
+        if (use == 1 && batch == 1 && tiles_l < num_cu && tiles_h > num_cu &&
+            (!ring || tiles_l * 5 >= (int64_t)num_cu * 3))
+            use = 0;
         if (use == 1 && !ring && tiles_h >= num_cu && (tiles_h % num_cu == 0 || tiles_h * 8 > (int64_t)num_cu * 11))
             use = kWide16;
+        // One wave of 128 x 256 tiles where 128 x 128 ones need two (us, 128
+        // x 128 vs 128 x 256): 2500^3 (400 vs 200 tiles) 66.2 vs 55.4,
+        // 1500x4500x3500 (432 vs 216) 94.2 vs 87.5, 2500x2500x2496 51.3 vs 44.6.
+        if (use == 1 && batch == 1 && !ring && tiles_h <= num_cu && tiles_m128 > num_cu) use = kWide16;
         // 96 x 128 or 128 x 96 tiles instead of 128 x 128 ones for a single
         // product when they still make at most one wave and keep more CUs
         // busy: the CUs that would idle in the one wave then work.  Of the two,

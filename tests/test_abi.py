@@ -160,17 +160,28 @@ def test_tier_band_above_one_wave():
 
 
 def test_wide_tier_and_split_plans():
-    """16-bit inputs: 128x256 tiles once they make whole waves or more than 1.375 waves (where 128x128 tiles
-    would otherwise be taken); the split plan (gemm_bt_ws) only where its tiles (32x64 for M <= 32, 64x64 for
+    """16-bit inputs: 256x256 tiles where fewer of them than CUs stand against more than one wave of 128-row tiles
+    of either width (for rows that take the line ring, once they fill 0.6 of the CUs); 128x256 tiles where they
+    make one wave and 128x128 ones would need two, and past one wave of 256x256 tiles once they make whole waves
+    or more than 1.375 waves; the split plan (gemm_bt_ws) only where its tiles (32x64 for M <= 32, 64x64 for
     M <= 64, else 128x128) fill at most half the CUs and each piece keeps at least 32 K steps, one piece per
     workgroup."""
     def tile(M, N, K=4096, batch=1, ind=gb.BF16):
         p = gb.gemm_bt_plan_batched(batch, M, N, K, ind, gb.BF16)
         return p.bm, p.bn
     assert tile(2048, 4096) == (128, 256)                        # 256 tiles of 128x256: one wave
-    assert tile(3072, 4096) == tile(4352, 4096) == (128, 256)    # 384 (1.5 waves), 544
-    assert tile(2560, 4096) == (128, 128)                        # 320 of 128x256 (1.25 waves)
-    assert tile(3000, 3000) == (128, 96)                         # 288 (1.125): 128x96 tiles in as many waves
+    assert tile(4352, 4096) == tile(4608, 4096) == (128, 256)    # 544 and 576 (272 and 288 of 256x256)
+    # 256x256: 192, 160, 136, 144 (odd K), 160 (4-byte rows) tiles; 128-row tiles over one wave
+    assert tile(3072, 4096) == tile(2560, 4096) == tile(2048, 4352) == tile(3000, 3000, K=3001) \
+        == tile(5000, 2000, K=2002) == tile(3072, 3072, K=3072) == (256, 256)
+    # line-ring rows: 160, 176, 192, 224 tiles of 256x256; under 0.6 of the CUs (144, 153) the ring's 128-row tiles
+    assert tile(2560, 3900, K=3000) == tile(2600, 3900, K=3000) == tile(4000, 3000, K=5000) \
+        == tile(2000, 7000, K=3000) == (256, 256)
+    assert tile(3000, 3000, K=3000) == tile(2100, 4300, K=3000) == (128, 96)
+    assert tile(2560, 2560) == tile(2816, 2816, K=2816) == tile(3072, 1536) == (128, 256)  # 200, 242, 144: one wave
+    assert tile(2500, 2500, K=2496) == (128, 256)
+    assert tile(2500, 2500, K=2504) == (128, 128)                # line-ring rows: no 128x256 twin
+    assert tile(3072, 3072, K=3072, batch=2) == (128, 256)       # stacked items: 576 tiles of 128x256
     assert tile(2048, 2048) == (128, 128)                        # 128 tiles of 128x256: half the CUs
     assert tile(4096, 4096) == (256, 256)
     assert tile(512, 1024, K=128, batch=16) == (128, 256)        # items stacked: 256 tiles
@@ -184,12 +195,11 @@ def test_wide_tier_and_split_plans():
     assert tile(1024, 4096) == (128, 128)                                          # 256 tiles of 128x128
     assert tile(768, 4096, batch=2) == (128, 128)                                  # single products only
     assert tile(768, 4096, ind=gb.FP8_E4M3) == (128, 128)                          # 16-bit inputs only
-    # several waves of 128x128 tiles: 128x96 (or 96x128) tiles when 0.9 x their waves < the 128x128 waves
-    assert tile(3072, 3072, K=3072) == tile(3072, 1536) == tile(1536, 6144) == (128, 96)  # 3, 2, 3 waves either way
-    assert tile(2880, 3200) == (96, 128)                   # 575 tiles (3 waves): 128x96 need 4, 96x128 3
-    assert tile(2000, 7000, K=3000) == tile(5000, 2000, K=2000) == (128, 128)  # the narrower tiles need a wave more
-    assert tile(2560, 2560) == (128, 128)
-    assert tile(3072, 1536, batch=2) != (128, 96)                                  # single products only
+    # several waves of 128x128 tiles (line-ring rows, 256x256 tiles under 0.6 of the CUs): 128x96 (or 96x128)
+    # tiles when 0.9 x their waves < the 128x128 waves
+    assert tile(3072, 1536, K=3000) == tile(2048, 4352, K=3000) == (128, 96)   # 2 and 3 waves either way
+    assert tile(1700, 3500, K=72) == (96, 128)             # 504 tiles (2 waves): 128x96 need 3
+    assert tile(3072, 1536, K=3000, batch=2) != (128, 96)                        # single products only
     p = gb.gemm_bt_plan(768, 4096, 4096, gb.BF16, gb.BF16)
     assert (p.threads, p.stages, p.grid, p.lds_bytes) == (256, 4, 256, 4 * (96 + 128) * 64 * 2)
     p = gb.gemm_bt_plan(2048, 4096, 4096, gb.BF16, gb.BF16)
@@ -253,7 +263,8 @@ def test_line_ring_plans():
     assert plan(1000, 2000, 1024)[0] == 2                               # ... on aligned rows, plain
     assert plan(500, 500, 1000)[0] == 6                                 # 32 x 64 keeps its plain ring
     assert plan(4096, 4096, 4104)[0] == 0                               # 256 x 256 (five-slot ring)
-    assert plan(2048, 4096, 4104)[0] == plan(3072, 4096, 1000)[0] == 12  # ring 128 x 128 instead of 128 x 256
+    assert plan(2048, 4096, 4104)[0] == plan(2000, 4000, 1000)[0] == 12  # ring 128 x 128 instead of 128 x 256
+    assert plan(3072, 4096, 1000)[0] == plan(3072, 4096, 4104)[0] == 0   # 192 tiles of 256 x 256: 0.75 of the CUs
     assert plan(2048, 4096, 4096)[0] == 7
     for K, v in ((16392, 12), (8200, 12), (16384, 1)):                  # the split form follows the rows too
         p = gb.gemm_bt_plan_ws(1024, 1024, K, gb.BF16, gb.BF16)

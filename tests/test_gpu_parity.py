@@ -97,11 +97,16 @@ SHAPES = [
     (4096, 4096, 8), (4096, 4096, 130), (4900, 4100, 136), (4096, 4096, 200),
     # just above one wave of 256x256 tiles (289 of them): the 128x256 tier, ragged edges
     (4100, 4100, 136),
-    # 128x256 tiles (one wave of them, and 1.5 waves): whole tiles, ragged edges, a K tail, C rows of 8-byte and
-    # 2-byte alignment (K a multiple of 64: rows that are 16-byte but not 128-byte aligned take the line ring's
-    # 128x128 tiles instead, as the first, second, fourth and sixth do)
-    (2048, 4096, 136), (2000, 4000, 200), (2048, 4096, 130), (2048, 4004, 72), (2048, 3999, 64), (3072, 4096, 72),
-    (2048, 4096, 128), (2000, 4000, 192), (2048, 4004, 64), (3072, 4096, 256),
+    # 128x256 tiles (one wave of them): whole tiles, ragged edges, a K tail, C rows of 8-byte and 2-byte alignment
+    # (K a multiple of 64: rows that are 16-byte but not 128-byte aligned take the line ring's 128x128 tiles
+    # instead, as the first, second and fourth do)
+    (2048, 4096, 136), (2000, 4000, 200), (2048, 4096, 130), (2048, 4004, 72), (2048, 3999, 64),
+    (2048, 4096, 128), (2000, 4000, 192), (2048, 4004, 64),
+    # fewer 256x256 tiles than CUs where 128-row tiles of either width need more than one wave: 192 tiles (rows
+    # that take the line ring elsewhere, and 512-byte rows), 156, 136, 144 with odd K, 160 with line-ring rows;
+    # then one wave of 128x256 tiles where 128x128 ones would need two
+    (3072, 4096, 72), (3072, 4096, 256), (2880, 3200, 64), (2048, 4352, 128), (3000, 3000, 73), (2560, 3900, 72),
+    (2560, 2560, 64), (3072, 1536, 64),
     # 304 tiles of 256x256 (1.19 waves, the edge of the band that takes smaller tiles)
     (4864, 4096, 136),
     # 96x128 tiles (at most one wave of them, more than 128x128 tiles would use): one exact wave, partial tile
@@ -116,8 +121,9 @@ SHAPES = [
     (4100, 4100, 137), (96, 200, 35),
     # the line ring on 64x64 tiles (more of them than CUs; rows 16-byte but not 128-byte aligned), ragged edges
     (700, 2000, 200), (1000, 1500, 136), (1030, 1500, 72),
-    # several waves of 128x96 (plain and line ring) or 96x128 tiles in place of 128x128 ones, ragged edges
-    (3072, 1536, 64), (3000, 3000, 72), (2880, 3200, 64),
+    # several waves of line-ring 128x96 or 96x128 tiles in place of 128x128 ones (rows 16-byte but not 128-byte
+    # aligned, 256x256 tiles under 0.6 of the CUs), ragged edges
+    (3000, 3000, 72), (2048, 4352, 136), (1700, 3500, 72),
 ]
 SKINNY = [(1, 100, 512), (16, 1000, 520), (5, 33, 35), (16, 8192, 64), (3, 4099, 2050), (16, 64, 8200),
           # K tails of 7 and 1 element, odd K with no whole chunk, 2-byte aligned rows
@@ -536,27 +542,43 @@ LINE_RING = [(1024, 4096, 4104, "f16", "f16"), (768, 4096, 4104, "bf16", "bf16")
              (1540, 2050, 1000, "bf16", "bf16"), (2048, 4096, 1000, "f16", "f16"), (1000, 1500, 3000, "f16", "f16")]
 
 
-@pytest.mark.parametrize("case", range(len(LINE_RING)))
-def test_line_ring_large(gpu, case):
-    """Large products whose rows are 16-byte but not 128-byte aligned (the line ring on the 128x128, 96x128,
-    128x96 and 64x64 tiers, up to 129 K steps): tile edges plus 20000 random entries against the oracle, and the
-    integer twin bit for bit on the same entries."""
-    M, N, K, ind, outd = LINE_RING[case]
+def sampled_large(gpu, M, N, K, ind, outd, seed, variants, what):
+    """Tile edges plus 20000 random entries against the oracle, and the integer twin bit for bit on the same
+    entries, after checking that the plan takes one of `variants`."""
     plan = gpu.gemm_bt_plan(M, N, K, gpu._torch_code(TORCH_DT[ind]), gpu._torch_code(TORCH_DT[outd]))
-    say("line ring", M, N, K, ind, outd, "variant", plan.variant, "tile", plan.bm, plan.bn)
-    assert plan.variant in (12, 13, 14, 15), "the case must take the line ring"
-    rng = np.random.default_rng(1700 + case)
+    say(what, M, N, K, ind, outd, "variant", plan.variant, "tile", plan.bm, plan.bn)
+    assert plan.variant in variants, (what, plan.variant)
+    rng = np.random.default_rng(seed)
     I, J = sample_entries(M, N, rng)
-    a, b = synth.make(M, N, K, ind, "normal", 1700 + case)
+    a, b = synth.make(M, N, K, ind, "normal", seed)
     c = f64(run_gpu(gpu, a, b, ind, outd))
     ref = oracle.gemm_bt_entries(a, b, ind, I, J)
     rep = tolerance.check(c[I, J], ref, oracle.row_norms(a, ind)[I] * oracle.row_norms(b, ind)[J], outd)
     assert rep.ok, rep
-    ai, bi = synth.make(M, N, K, ind, "int", 1750 + case)
+    ai, bi = synth.make(M, N, K, ind, "int", seed + 50)
     ci = run_gpu(gpu, ai, bi, ind, outd)
     refi = oracle.round_to(oracle.gemm_bt_entries(ai, bi, ind, I, J), outd)
     rep = tolerance.bit_exact(out_bits(ci)[I, J], refi, outd)
     assert rep.ok, rep
+
+
+@pytest.mark.parametrize("case", range(len(LINE_RING)))
+def test_line_ring_large(gpu, case):
+    """Large products whose rows are 16-byte but not 128-byte aligned: the line ring on the 128x128, 96x128,
+    128x96 and 64x64 tiers, up to 129 K steps."""
+    sampled_large(gpu, *LINE_RING[case], 1700 + case, (12, 13, 14, 15), "line ring")
+
+
+# fewer 256x256 tiles than CUs against more than one wave of 128-row tiles (odd K, line-ring rows, 4-byte rows),
+# and one wave of 128x256 tiles where 128x128 ones would need two, at full K
+PARTIAL_WAVE = [((3000, 3000, 3001, "bf16", "f32"), (0,)), ((2000, 7000, 3000, "f16", "f16"), (0,)),
+                ((5000, 2000, 2002, "bf16", "bf16"), (0,)), ((2560, 2560, 4096, "bf16", "bf16"), (7,))]
+
+
+@pytest.mark.parametrize("case", range(len(PARTIAL_WAVE)))
+def test_partial_wave_tiers_large(gpu, case):
+    shape, variants = PARTIAL_WAVE[case]
+    sampled_large(gpu, *shape, 1800 + case, variants, "partial wave")
 
 
 def test_batched_integer_bit_exact(gpu):
