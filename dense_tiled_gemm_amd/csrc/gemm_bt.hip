@@ -461,6 +461,16 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);
         int use = kFp8Variants + (dma_large_tier(tiles_l, num_cu, true) ? 0 : (tiles_m128 * 2 > num_cu ? 1 : 2));
+        // 256 x 256 tiles that fill at least half the CUs but not all, where
+        // 128 x 128 ones need more than one wave (as for 16-bit inputs; us,
+        // 128 x 128 vs 256 x 256, E4M3 -> bf16 and int8 -> int32):
+        // 2048x4352x4096 (136 tiles) 50.6 vs 39.5, 3072^3 (144) 42.8 vs 34.0
+        // and 46.1 vs 34.8, 2560x4096x4096 (160) 52.8 vs 43.3 and 55.5 vs
+        // 43.2, 2000x6000x3008 (192) 48.9 vs 39.4, 3072x4096x4096 (192) 56.2 vs
+        // 48.3 and 58.4 vs 47.7; at 100 tiles no better (2560^2x4096 36.2 vs
+        // 37.1).
+        if (use == kFp8Variants + 1 && tiles_l < num_cu && tiles_l * 2 >= num_cu && tiles_m128 > num_cu)
+            use = kFp8Variants;
         const int f = forced_variant();
         if (f >= 0 && vs[f].fn[in_index(in_dtype)][out_index(out_dtype)]) use = f;
         const DmaVariant& v = vs[use];
@@ -565,16 +575,22 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         // ring's 128-row tiles hold on to about 0.6 of the CUs (3000^3, 144
         // tiles, 71.5 vs 76.2; 2100x4300x3000, 153, 81.0 vs 87.8;
         // 4000x3000x5000, 192, 141.5 vs 124.3; 3072x4096x4104, 192, 108.7 vs
-        // 100.6; 2000x6000x3000, 192, 108.6 vs 76.3).
-        if (use == 1 && batch == 1 && tiles_l < num_cu && tiles_h > num_cu &&
+        // 100.6; 2000x6000x3000, 192, 108.6 vs 76.3).  Stacked items alike
+        // (items x M x N x K): 9x1024x1024x4096 (144) 109.5 vs 78.7,
+        // 10x1024x1024x2048 (160) 57.9 vs 44.7, 3x2048x2048x4096 (192) 102.6
+        // vs 85.3, 2x2048x3072x4096 (192) 106.3 vs 83.9, 6x1024x2048x3000
+        // (192, line ring) 89.6 vs 88.1.
+        if (use == 1 && tiles_l < num_cu && tiles_h > num_cu &&
             (!ring || tiles_l * 5 >= (int64_t)num_cu * 3))
             use = 0;
         if (use == 1 && !ring && tiles_h >= num_cu && (tiles_h % num_cu == 0 || tiles_h * 8 > (int64_t)num_cu * 11))
             use = kWide16;
         // One wave of 128 x 256 tiles where 128 x 128 ones need two (us, 128
         // x 128 vs 128 x 256): 2500^3 (400 vs 200 tiles) 66.2 vs 55.4,
-        // 1500x4500x3500 (432 vs 216) 94.2 vs 87.5, 2500x2500x2496 51.3 vs 44.6.
-        if (use == 1 && batch == 1 && !ring && tiles_h <= num_cu && tiles_m128 > num_cu) use = kWide16;
+        // 1500x4500x3500 (432 vs 216) 94.2 vs 87.5, 2500x2500x2496 51.3 vs 44.6,
+        // 4 items of 1024x1536x4096 (384 vs 192) 73.3 vs 55.4, 8 of
+        // 640x1024x4096 (320 vs 160) 69.9 vs 58.8.
+        if (use == 1 && !ring && tiles_h <= num_cu && tiles_m128 > num_cu) use = kWide16;
         // 96 x 128 or 128 x 96 tiles instead of 128 x 128 ones for a single
         // product when they still make at most one wave and keep more CUs
         // busy: the CUs that would idle in the one wave then work.  Of the two,
@@ -716,7 +732,20 @@ static int plan_layout_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int 
     // 128 x 128 tiles 8-17 % faster at 272-320 such tiles on 256 CUs, even at
     // 352, 4 % slower at 384)
     const int64_t tiles_l = ((M + 255) / 256) * ((N + 255) / 256) * batch;
-    const bool big = tiles_l == num_cu || tiles_l * 8 > (int64_t)num_cu * 11;
+    bool big = tiles_l == num_cu || tiles_l * 8 > (int64_t)num_cu * 11;
+    // and when fewer 256 x 256 tiles than CUs fill at least half of them where
+    // 128 x 128 ones need more than one wave (us, 128 vs 256, bf16, B stored
+    // K x N unless noted): 2048x4352x4096 (136 tiles) 124.8 vs 98.3, 3072^3
+    // (144) 82.2 vs 75.4, A stored K x M 84.0 vs 75.9, 2560x4096x4096 (160)
+    // 106.3 vs 96.1, 3072x4096x4096 (192) 112.4 vs 98.6, both stored K-outer
+    // 115.8 vs 108.0, 3 items of 2048x2048x4096 (192) 119.7 vs 103.3; at 100
+    // tiles no better (2560^2x4096 63.9 vs 97.2)
+    const int64_t tiles_128 = ((M + 127) / 128) * ((N + 127) / 128) * batch;
+    if (tiles_l < num_cu && tiles_l * 2 >= num_cu && tiles_128 > num_cu) big = true;
+#ifdef GEMM_BT_TUNING
+    // GEMM_BT_LAYOUT_TILE=128 or 256 forces the tile size
+    if (const char* e = std::getenv("GEMM_BT_LAYOUT_TILE")) big = std::atoi(e) == 256;
+#endif
     const int bt = big ? 256 : 128;
     p->kernel = KIND_TRANS;
     p->variant = (a_layout == GEMM_BT_K_OUTER ? 1 : 0) + (b_layout == GEMM_BT_K_OUTER ? 2 : 0) - 1 + (big ? 3 : 0);

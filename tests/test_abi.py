@@ -101,6 +101,11 @@ def test_layout_plan_and_validation():
         p = gb.gemm_bt_plan_layout(1000, 3000, 2048, la, lb, gb.BF16, gb.F32)
         assert (p.kernel, p.variant, p.bm, p.bn, p.tiles_m, p.tiles_n, p.grid) == (5, var, 128, 128, 8, 24, 192)
     assert gb.gemm_bt_plan_layout(200, 104, 301, KO, KO, gb.F16, gb.F16).kernel == 5  # any K when both are K-outer
+    # 256 x 256 tiles from half the CUs up where 128 x 128 ones need more than one wave (144 and 136 tiles), not below
+    assert gb.gemm_bt_plan_layout(3072, 3072, 3072, KI, KO, gb.BF16, gb.BF16).bm == 256
+    assert gb.gemm_bt_plan_layout(2048, 4352, 4096, KO, KO, gb.BF16, gb.BF16).bm == 256
+    assert gb.gemm_bt_plan_layout(2560, 2560, 4096, KI, KO, gb.BF16, gb.BF16).bm == 128
+    assert gb.gemm_bt_plan_batched_layout(3, 2048, 2048, 4096, KI, KO, gb.BF16, gb.BF16).bm == 256
     for la, lb, var in ((KO, KI, 3), (KI, KO, 4), (KO, KO, 5)):  # 256 x 256 tiles when they fill every CU
         p = gb.gemm_bt_plan_layout(4096, 4096, 4096, la, lb, gb.BF16, gb.BF16)
         assert (p.kernel, p.variant, p.bm, p.threads, p.grid, p.lds_bytes) == (5, var, 256, 512, 256, 128 * 1024)
@@ -160,9 +165,9 @@ def test_tier_band_above_one_wave():
 
 
 def test_wide_tier_and_split_plans():
-    """16-bit inputs: 256x256 tiles where fewer of them than CUs stand against more than one wave of 128-row tiles
-    of either width (for rows that take the line ring, once they fill 0.6 of the CUs); 128x256 tiles where they
-    make one wave and 128x128 ones would need two, and past one wave of 256x256 tiles once they make whole waves
+    """16-bit inputs (items stacked or not): 256x256 tiles where fewer of them than CUs stand against more than one
+    wave of 128-row tiles of either width (for rows that take the line ring, once they fill 0.6 of the CUs); 128x256
+    tiles where they make one wave and 128x128 ones would need two, and past one wave of 256x256 tiles once they make whole waves
     or more than 1.375 waves; the split plan (gemm_bt_ws) only where its tiles (32x64 for M <= 32, 64x64 for
     M <= 64, else 128x128) fill at most half the CUs and each piece keeps at least 32 K steps, one piece per
     workgroup."""
@@ -182,18 +187,24 @@ def test_wide_tier_and_split_plans():
     assert tile(2500, 2500, K=2496) == (128, 256)
     assert tile(2500, 2500, K=2504) == (128, 128)                # line-ring rows: no 128x256 twin
     assert tile(3072, 3072, K=3072, batch=2) == (128, 256)       # stacked items: 576 tiles of 128x256
+    assert tile(1024, 1024, batch=9) == tile(2048, 2048, batch=3) == (256, 256)   # stacked: 144 and 192 tiles
     assert tile(2048, 2048) == (128, 128)                        # 128 tiles of 128x256: half the CUs
     assert tile(4096, 4096) == (256, 256)
     assert tile(512, 1024, K=128, batch=16) == (128, 256)        # items stacked: 256 tiles
     assert tile(512, 1024, K=72, batch=16) == (128, 128)         # 144-byte rows: the line ring's 128x128 tiles
     assert tile(2048, 4096, ind=gb.FP8_E4M3) != (128, 256)       # 16-bit inputs only
+    # 8-bit inputs: 256x256 tiles from half the CUs up where 128x128 ones need more than one wave
+    i8 = lambda M, N: gb.gemm_bt_plan(M, N, 4096, gb.INT8, gb.INT32).bm
+    assert tile(3072, 3072, ind=gb.FP8_E4M3) == (256, 256) and i8(2048, 4352) == 256   # 144, 136 tiles
+    assert tile(2560, 2560, ind=gb.FP8_E4M3) == (128, 128) and i8(2048, 2048) == 128   # 100, 64 tiles
     # 96x128 tiles for a single product when they make at most one wave and keep more CUs busy than 128x128
     assert tile(768, 4096) == tile(3000, 1000) == tile(1536, 2048) == (96, 128)  # 256 tiles each
     # or 128x96 tiles when those make more tiles within the wave (96x128: 264, 264, 264, 200 against 204)
     assert tile(1000, 3000) == tile(2048, 1536) == tile(1024, 3072) == tile(700, 3200) == (128, 96)
     assert tile(1500, 1500) == (96, 128)                                           # 192 either way: 96x128
     assert tile(1024, 4096) == (128, 128)                                          # 256 tiles of 128x128
-    assert tile(768, 4096, batch=2) == (128, 128)                                  # single products only
+    assert tile(768, 2048, batch=2) == (128, 128)                                  # single products only
+    assert tile(768, 4096, batch=2) == (128, 256)          # stacked: one wave of 128x256, two of 128x128
     assert tile(768, 4096, ind=gb.FP8_E4M3) == (128, 128)                          # 16-bit inputs only
     # several waves of 128x128 tiles (line-ring rows, 256x256 tiles under 0.6 of the CUs): 128x96 (or 96x128)
     # tiles when 0.9 x their waves < the 128x128 waves

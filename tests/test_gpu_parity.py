@@ -159,7 +159,9 @@ def test_integer_bit_exact_sweep(gpu, in_dtype, out_dtype):
 # 8-bit inputs: the 64x64 tiles take it).
 FP8_SHAPES = [(1, 1, 16), (16, 16, 16), (17, 33, 64), (8, 1000, 64), (64, 64, 128), (130, 260, 160),
               (257, 513, 144), (300, 700, 1024), (1024, 1024, 256), (4096, 4096, 128), (4900, 4100, 272),
-              (4096, 4096, 400), (4350, 4090, 272)]
+              (4096, 4096, 400), (4350, 4090, 272),
+              # fewer 256x256 tiles than CUs (144, 132 and 136, ragged edges) where 128x128 ones need more than a wave
+              (3072, 3072, 64), (2600, 3000, 160), (2000, 4100, 272)]
 
 
 @pytest.mark.parametrize("in_dtype", ["e4m3", "e5m2"])
@@ -519,6 +521,11 @@ BATCHED = [
     # different phase of the cache line each (an item stride of 139280 bytes), and with A shared
     (9, 512, 512, 136, "bf16", "bf16", None, (8, 0, 0)),
     (9, 512, 512, 136, "f16", "f32", "a", (0, 8, 0)),
+    # fewer stacked 256x256 tiles than CUs against more than one wave of 128-row tiles (144 of them, the second
+    # with 4-byte rows, ragged edges and B shared), and one wave of 128x256 tiles where 128x128 ones need two
+    (9, 1024, 1024, 64, "bf16", "bf16", None, (0, 0, 0)),
+    (6, 1000, 1500, 130, "f16", "f32", "b", (0, 0, 8)),
+    (4, 1000, 1500, 64, "bf16", "bf16", None, (0, 0, 0)),
 ]
 
 
@@ -655,6 +662,8 @@ LAYOUTS = [
     (6152, 4096, 136, 1, 1, "bf16", "bf16"), (4096, 6152, 72, 1, 0, "f16", "f32"), (4096, 4096, 100, 1, 1, "bf16", "f16"),
     # just above one wave of 256 x 256 tiles (272 of them): 128 x 128 tiles, ragged edges
     (4104, 4096, 136, 1, 1, "bf16", "bf16"), (4096, 4104, 72, 1, 0, "f16", "f32"),
+    # fewer 256 x 256 tiles than CUs (144, 153, 192) where 128 x 128 ones need more than one wave, ragged edges
+    (3000, 3000, 72, 1, 0, "bf16", "bf16"), (2056, 4352, 136, 0, 1, "f16", "f32"), (3072, 4096, 64, 1, 1, "bf16", "f16"),
 ]
 
 
