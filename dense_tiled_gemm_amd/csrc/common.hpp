@@ -333,6 +333,23 @@ __host__ __device__ inline int epi_chunk(int c, int r, int cpr) {
     return c ^ (r & ((cpr < 32 ? cpr : 32) - 1));
 }
 
+// Bytes 16 - ph .. 31 - ph of the 32 bytes lo:hi (ph even, 0 <= ph < 16):
+// the 16 bytes that start ph bytes before hi.  A right shift of the 256-bit
+// value by 16 - ph bytes, done on named 64-bit words (no indexed array, which
+// the compiler would place in scratch memory).
+__device__ inline u32x4 window16(const u32x4 lo, const u32x4 hi, int ph) {
+    const uint64_t l0 = lo[0] | ((uint64_t)lo[1] << 32), l1 = lo[2] | ((uint64_t)lo[3] << 32);
+    const uint64_t h0 = hi[0] | ((uint64_t)hi[1] << 32), h1 = hi[2] | ((uint64_t)hi[3] << 32);
+    const int sh = 16 - ph;                 // bytes, 2 .. 16
+    const int q = sh >> 3, b = (sh & 7) * 8;  // whole words, then bits
+    const uint64_t x = q == 0 ? l0 : (q == 1 ? l1 : h0);
+    const uint64_t y = q == 0 ? l1 : (q == 1 ? h0 : h1);
+    const uint64_t z = q == 0 ? h0 : (q == 1 ? h1 : 0ull);
+    const uint64_t o0 = b ? (x >> b) | (y << (64 - b)) : x;
+    const uint64_t o1 = b ? (y >> b) | (z << (64 - b)) : y;
+    return u32x4{(u32)o0, (u32)(o0 >> 32), (u32)o1, (u32)(o1 >> 32)};
+}
+
 // Store the workgroup's BM x BN tile through LDS so that each global store
 // instruction writes whole rows: every wave first parks its accumulator
 // blocks (rounded to OUT) in LDS as a row-major tile, then the NT threads of
@@ -342,12 +359,19 @@ __host__ __device__ inline int epi_chunk(int c, int r, int cpr) {
 // chunk c ^ (r mod min(32, chunks per row)): the column-wise parking
 // writes of 16 or 32 rows then spread over the banks, and the row-wise reads
 // stay whole chunks.  A tile larger than LDS_BYTES goes in WM passes of one
-// wave row each.  Requires 16-byte aligned rows of C (N * sizeof(OUT) a
-// multiple of 16 and C 16-byte aligned); rows >= M and columns >= N are not
+// wave row each.  Unless `shifted`, requires 16-byte aligned rows of C
+// (N * sizeof(OUT) a multiple of 16 and C 16-byte aligned).  With `shifted`
+// (rows of any element alignment) each lane writes one 16-byte chunk that is
+// aligned in C: a tile row that starts `ph` bytes past a 16-byte boundary
+// touches one chunk more than it holds, chunk j taking the last ph bytes of
+// parked chunk j - 1 and the first 16 - ph of parked chunk j; the row's first
+// and last chunks, shared with the neighbouring tiles, and any chunk cut by
+// column N, go out element by element.  Rows >= M and columns >= N are not
 // written.  The caller guarantees that no wave still reads or fills `lds`.
 template <int OUT, int FN, int FM, int BM, int BN, int WM, int NT, int LDS_BYTES, int MF = 32>
 __device__ inline void store_tile_lds(const typename AccBlock<MF>::type (&acc)[FN][FM], unsigned char* lds, void* C,
-                                      int M, int N, int m0, int n0, int mw, int nw, int wm, int tid) {
+                                      int M, int N, int m0, int n0, int mw, int nw, int wm, int tid,
+                                      bool shifted = false) {
     typedef AccBlock<MF> AB;
     constexpr int OSZ = OUT == GEMM_BT_F32 ? 4 : 2;
     constexpr int ROWB = BN * OSZ;  // bytes per tile row
@@ -386,14 +410,48 @@ __device__ inline void store_tile_lds(const typename AccBlock<MF>::type (&acc)[F
                 }
         }
         __syncthreads();
+        if (!shifted) {
 #pragma unroll
-        for (int q0 = 0; q0 < RP * CPR; q0 += NT) {
-            const int q = q0 + tid;
-            const int r = q / CPR, c = q % CPR;
-            const u32x4 v = *(const u32x4*)(lds + r * ROWB + (epi_chunk(c, r, CPR) * 16));
-            const int row = p * RP + r, col = c * (16 / OSZ);
-            if (row < mlim && col < nlim)
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, ((u32)row * (u32)N + (u32)col) * OSZ, 0, kStoreNT);
+            for (int q0 = 0; q0 < RP * CPR; q0 += NT) {
+                const int q = q0 + tid;
+                const int r = q / CPR, c = q % CPR;
+                const u32x4 v = *(const u32x4*)(lds + r * ROWB + (epi_chunk(c, r, CPR) * 16));
+                const int row = p * RP + r, col = c * (16 / OSZ);
+                if (row < mlim && col < nlim)
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, ((u32)row * (u32)N + (u32)col) * OSZ, 0, kStoreNT);
+            }
+        } else {
+            constexpr int CH = CPR + 1;  // aligned chunks of C one tile row can touch
+            const int row_end = (nlim < BN ? nlim : BN) * OSZ;  // tile-row bytes inside C
+#pragma unroll
+            for (int q0 = 0; q0 < RP * CH; q0 += NT) {
+                const int q = q0 + tid;
+                const int r = q / CH, j = q % CH;
+                const int row = p * RP + r;
+                if (q >= RP * CH || row >= mlim) continue;
+                const u32 row_off = (u32)row * (u32)N * OSZ;  // tile row start, from the tile origin
+                const int ph = (int)(((uintptr_t)C + (c_origin * OSZ) + row_off) & 15u);
+                const int b0 = 16 * j - ph;  // tile-row byte at the start of aligned chunk j
+                if (b0 >= row_end || b0 + 16 <= 0) continue;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                const u32x4 lo = j > 0 ? *(const u32x4*)(lds + r * ROWB + (epi_chunk(j - 1, r, CPR) * 16)) : z;
+                const u32x4 hi = j < CPR ? *(const u32x4*)(lds + r * ROWB + (epi_chunk(j, r, CPR) * 16)) : z;
+                const u32x4 v = window16(lo, hi, ph);
+                if (b0 >= 0 && b0 + 16 <= row_end) {
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rc, row_off + (u32)b0, 0, kStoreNT);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16 / OSZ; ++e) {
+                        const int b = b0 + e * OSZ;
+                        if (b < 0 || b >= row_end) continue;
+                        if constexpr (OSZ == 4)
+                            __builtin_amdgcn_raw_buffer_store_b32(v[e], rc, row_off + (u32)b, 0, kStoreNT);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16((u16)(v[e >> 1] >> (16 * (e & 1))), rc,
+                                                                  row_off + (u32)b, 0, kStoreNT);
+                    }
+                }
+            }
         }
         if (p + 1 < P) __syncthreads();
     }

@@ -774,7 +774,8 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
     // (tid_r: the thread index, recomputed per call for the same reason as
     // lane_r in run)
     // the whole-row epilogue takes tile rows of 8, 12, 16, 24 or 2^n 16-byte
-    // chunks (epi_chunk); other tile widths store directly
+    // chunks (epi_chunk), for rows of C of any alignment (shifted when not
+    // 16-byte aligned: vec_store < 2); other tile widths store directly
     constexpr int OCPR = BN * (store_type(OUT) == GEMM_BT_F32 ? 4 : 2) / 16;
     constexpr bool WHOLE_ROWS = OCPR == 12 || OCPR == 24 || (OCPR >= 8 && (OCPR & (OCPR - 1)) == 0);
     auto store_c = [&](void* Cp, int m0, int n0, Acc& acc) {
@@ -782,13 +783,11 @@ __global__ __launch_bounds__(64 * WM * WN) void dma_kernel(const u16* __restrict
         asm volatile("" : "+v"(tid_r));
         if constexpr (!WHOLE_ROWS) {
             store_tile<store_type(OUT), FN, FM, MF>(acc, Cp, M, N, m0, n0, wm * TM, wn * TN, tid_r & 63, vec_store);
-        } else if (vec_store == 2) {
+        } else {
             // every wave is past its last LDS read and its loads have landed
             barrier_no_fence();
             store_tile_lds<store_type(OUT), FN, FM, BM, BN, WM, 64 * W, STAGES * STAGE_BYTES, MF>(
-                acc, lds, Cp, M, N, m0, n0, wm * TM, wn * TN, wm, tid_r);
-        } else {
-            store_tile<store_type(OUT), FN, FM, MF>(acc, Cp, M, N, m0, n0, wm * TM, wn * TN, tid_r & 63, vec_store);
+                acc, lds, Cp, M, N, m0, n0, wm * TM, wn * TN, wm, tid_r, vec_store != 2);
         }
     };
 
