@@ -48,7 +48,6 @@ struct TileCfg {
 constexpr TileCfg kCfgL = {256, 256, 2, 4};
 constexpr TileCfg kCfgM = {128, 128, 2, 2};
 constexpr int kSkinnyNB = 2, kSkinnyKS = 4;
-constexpr int kSwz = 2;
 constexpr int kGroupM = 4;
 
 // DMA-kernel variants: [in][out] entry points.
@@ -788,6 +787,7 @@ static const void* trans_fn_out(int out, int variant) {
 
 
 #ifdef GEMM_BT_TUNING
+constexpr int kSwz = 2;  // LDS swizzle of the register-staged kernel
 template <int IN, int OUT, int VEC>
 static const void* tiled_fn(int cfg) {
     if (cfg == 0)

@@ -26,7 +26,7 @@
 //       one transpose read touches fall in distinct bank ranges;
 //   * pipeline: two stages; the transfers for step k+1 go out before the
 //     MFMAs of step k, one s_waitcnt vmcnt(0) and one barrier per step;
-//   * epilogue: the shared store_tile / store_tile_lds.
+//   * epilogue: the shared whole-row store_tile_lds.
 // Requirements checked by the host: bf16 or f16 inputs, every operand row in
 // 16-byte chunks (K % 8 == 0 for a K-inner operand, M % 8 == 0 for a K-outer
 // A, N % 8 == 0 for a K-outer B) and 16-byte aligned A and B.
@@ -204,10 +204,9 @@ __global__ __launch_bounds__(64 * WM * WN) void trans_kernel(const u16* __restri
     }
 
     // the loop ended on a barrier: LDS is free for the whole-row epilogue
-    if (vec_store == 2)
-        store_tile_lds<OUT, FN, FM, BM, BN, WM, T, 2 * STAGE, 16>(acc, lds, C, M, N, m0, n0, wm * TM, wn * TN, wm, tid);
-    else
-        store_tile<OUT, FN, FM, 16>(acc, C, M, N, m0, n0, wm * TM, wn * TN, lane, vec_store);
+    // (shifted when rows of C are not 16-byte aligned)
+    store_tile_lds<OUT, FN, FM, BM, BN, WM, T, 2 * STAGE, 16>(acc, lds, C, M, N, m0, n0, wm * TM, wn * TN, wm, tid,
+                                                             vec_store != 2);
 }
 
 }  // namespace gbt

@@ -676,6 +676,8 @@ LAYOUTS = [
     (4104, 4096, 136, 1, 1, "bf16", "bf16"), (4096, 4104, 72, 1, 0, "f16", "f32"),
     # fewer 256 x 256 tiles than CUs (144, 153, 192) where 128 x 128 ones need more than one wave, ragged edges
     (3000, 3000, 72, 1, 0, "bf16", "bf16"), (2056, 4352, 136, 0, 1, "f16", "f32"), (3072, 4096, 64, 1, 1, "bf16", "f16"),
+    # rows of C 2- and 4-byte aligned (A stored K-outer, B K-inner with any N): the shifted whole-row epilogue
+    (1000, 1001, 136, 1, 0, "bf16", "bf16"), (512, 1003, 200, 1, 0, "f16", "f32"),
 ]
 
 
