@@ -584,6 +584,14 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
             use = 0;
         if (use == 1 && !ring && tiles_h >= num_cu && (tiles_h % num_cu == 0 || tiles_h * 8 > (int64_t)num_cu * 11))
             use = kWide16;
+        // From 1.2 up to 1.375 waves of 256 x 256 tiles, 128 x 256 ones (more
+        // than 2.4 waves) lose less to the last wave (us, 256 x 256 vs 128 x
+        // 256, same box): 4608^2x4096 (324 tiles) 159.2 vs 146.9, x2048 86.3
+        // vs 80.3, x8192 307.3 vs 304.5; 5120x4608x4096 (360) 158.5 vs 159.2;
+        // 5120^2x4096 (400) 163.2 vs 194.2, 5376^2x4096 (441) 172.7 vs 197.2.
+        if (use == 0 && !ring && tiles_l > num_cu && tiles_l * 8 <= (int64_t)num_cu * 11 &&
+            tiles_h * 8 > (int64_t)num_cu * 11)
+            use = kWide16;
         // One wave of 128 x 256 tiles where 128 x 128 ones need two (us, 128
         // x 128 vs 128 x 256): 2500^3 (400 vs 200 tiles) 66.2 vs 55.4,
         // 1500x4500x3500 (432 vs 216) 94.2 vs 87.5, 2500x2500x2496 51.3 vs 44.6,

@@ -150,13 +150,16 @@ def test_no_device_status_without_gpu():
 
 
 def test_tier_band_above_one_wave():
-    """256x256 tiles (DMA kernels) for exactly one wave of them on 256 CUs and above 1.2 waves (17/16 for 8-bit
-    inputs); 128x128 tiles in between, where the nearly empty last wave costs more."""
+    """256x256 tiles (DMA kernels) for exactly one wave of them on 256 CUs and above 1.375 waves (1.2 for rows that
+    take the line ring, 17/16 for 8-bit inputs); 128x256 (or 128x128) tiles in between, where the nearly empty last
+    wave costs more."""
     def bm(M, N, K=4096, ind=gb.BF16, outd=gb.BF16, batch=1):
         return gb.gemm_bt_plan_batched(batch, M, N, K, ind, outd).bm
     assert bm(4096, 4096) == 256                                  # 256 tiles: one wave
     assert bm(4352, 4096) == bm(4096, 4160) == bm(4864, 4096) == 128  # 272, 272, 304 tiles (128x256 ones)
-    assert bm(5120, 4096) == bm(4608, 4608) == 256                # 320, 324 tiles
+    assert bm(5120, 4096) == bm(4608, 4608) == 128                # 320, 324 tiles (128x256 ones)
+    assert bm(5120, 4608) == bm(5120, 5120) == 256                # 360, 400 tiles
+    assert bm(4608, 4608, K=4104) == 256                          # line-ring rows: above 1.2 waves
     assert bm(512, 512, 512, batch=68) == 128                     # 68 items x 4 tiles
     # 8-bit inputs: a narrower band, up to 17/16 waves
     assert bm(4352, 4096, ind=gb.FP8_E4M3) == bm(4352, 4096, ind=gb.INT8, outd=gb.INT32) == 128  # 272 tiles

@@ -577,9 +577,11 @@ def test_line_ring_large(gpu, case):
 
 
 # fewer 256x256 tiles than CUs against more than one wave of 128-row tiles (odd K, line-ring rows, 4-byte rows),
-# and one wave of 128x256 tiles where 128x128 ones would need two, at full K
+# one wave of 128x256 tiles where 128x128 ones would need two, and 128x256 tiles for 1.27 waves of 256x256 ones,
+# at full K
 PARTIAL_WAVE = [((3000, 3000, 3001, "bf16", "f32"), (0,)), ((2000, 7000, 3000, "f16", "f16"), (0,)),
-                ((5000, 2000, 2002, "bf16", "bf16"), (0,)), ((2560, 2560, 4096, "bf16", "bf16"), (7,))]
+                ((5000, 2000, 2002, "bf16", "bf16"), (0,)), ((2560, 2560, 4096, "bf16", "bf16"), (7,)),
+                ((4608, 4608, 4096, "bf16", "bf16"), (7,))]
 
 
 @pytest.mark.parametrize("case", range(len(PARTIAL_WAVE)))
