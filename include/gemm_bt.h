@@ -32,8 +32,9 @@
  * keeps no pointer after it returns and holds no state beyond a per-device
  * cache of device attributes.
  *
- * Asynchrony and errors.  gemm_bt enqueues its kernel on `stream` and returns
- * without waiting.  Argument errors are reported before anything is
+ * Asynchrony and errors.  gemm_bt enqueues its kernel on `stream` (two
+ * kernels in stream order for a plan with split_rows) and returns without
+ * waiting.  Argument errors are reported before anything is
  * enqueued.  A launch failure is reported as GEMM_BT_ERR_LAUNCH; a fault
  * inside the kernel shows at the caller's next synchronisation.  No call
  * throws, exits or aborts.  Calls are thread-safe.  C must not overlap A or B.
@@ -243,7 +244,10 @@ typedef struct {
     int64_t batch;    /* batch items (1 for gemm_bt) */
     int64_t split_tiles;     /* split plan: tiles whose K range is split over several workgroups (0: one
                                 workgroup per tile) */
-    int64_t workspace_bytes; /* workspace the plan needs (0 unless split_tiles > 0) */
+    int64_t workspace_bytes; /* workspace the plan needs (0 unless a launch of it splits tiles along K) */
+    int64_t split_rows;      /* > 0: the product runs as two launches in stream order, rows [0, split_rows)
+                                of C first, planned as the fields above describe (one wave of 256 x 256
+                                tiles), then the remaining rows on their own plan; 0: one launch */
 } gemm_bt_plan_t;
 
 int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,

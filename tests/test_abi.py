@@ -156,15 +156,40 @@ def test_tier_band_above_one_wave():
     def bm(M, N, K=4096, ind=gb.BF16, outd=gb.BF16, batch=1):
         return gb.gemm_bt_plan_batched(batch, M, N, K, ind, outd).bm
     assert bm(4096, 4096) == 256                                  # 256 tiles: one wave
-    assert bm(4352, 4096) == bm(4096, 4160) == bm(4864, 4096) == 128  # 272, 272, 304 tiles (128x256 ones)
-    assert bm(5120, 4096) == bm(4608, 4608) == 128                # 320, 324 tiles (128x256 ones)
+    # single products from just above one wave to 1.375 waves split their rows into two launches (the row split
+    # test below); stacked items take 128x256 (or 128x128) tiles
+    assert bm(2176, 4096, batch=2) == bm(2048, 4160, batch=2) == bm(2432, 4096, batch=2) == 128  # 288, 272, 304
+    assert bm(2560, 4096, batch=2) == bm(2304, 4608, batch=2) == 128  # 320, 324 tiles (128x256 ones)
     assert bm(5120, 4608) == bm(5120, 5120) == 256                # 360, 400 tiles
-    assert bm(4608, 4608, K=4104) == 256                          # line-ring rows: above 1.2 waves
+    assert bm(2304, 4608, K=4104, batch=2) == 256                 # line-ring rows: above 1.2 waves
     assert bm(512, 512, 512, batch=68) == 128                     # 68 items x 4 tiles
     # 8-bit inputs: a narrower band, up to 17/16 waves
     assert bm(4352, 4096, ind=gb.FP8_E4M3) == bm(4352, 4096, ind=gb.INT8, outd=gb.INT32) == 128  # 272 tiles
     assert bm(4608, 4096, ind=gb.FP8_E4M3) == bm(4864, 4096, ind=gb.INT8, outd=gb.INT32) == 256  # 288, 304
     assert bm(5120, 4096, ind=gb.FP8_E4M3) == 256
+
+
+def test_row_split_plans():
+    """A single 16-bit product with just over one wave of 256x256 tiles (up to 1.375 waves) runs as two launches:
+    R whole tile rows as one wave of 256x256 tiles (at least 7/8 of the CUs), then the remaining rows on their own
+    plan (split along K through gemm_bt_ws when that plan splits).  The plan describes the first launch."""
+    def plan(M, N, K=4096, ind=gb.BF16, outd=gb.BF16, batch=1):
+        p = gb.gemm_bt_plan_batched(batch, M, N, K, ind, outd)
+        return p.split_rows, p.bm, p.bn, p.grid
+    assert plan(4352, 4096) == plan(4160, 4096) == plan(5120, 4096) == (4096, 256, 256, 256)  # 272, 272, 320 tiles
+    assert plan(4608, 4608) == (3584, 256, 256, 252)        # 18 tile columns: 14 tile rows first
+    assert plan(4100, 4100, K=136) == (3840, 256, 256, 255)  # line-ring rows and ragged edges alike
+    assert plan(4096, 4096)[0] == plan(5120, 4608)[0] == 0   # one wave; 360 tiles (1.41 waves)
+    assert plan(2176, 4096, batch=2)[0] == 0                # stacked items: one launch
+    assert plan(4352, 4096, ind=gb.FP8_E4M3)[0] == plan(4352, 4096, ind=gb.INT8, outd=gb.INT32)[0] == 0
+    assert plan(512, 40000)[0] == 0                          # 157 tiles per tile row: the first launch under 7/8
+    # the workspace is that of the second launch's split plan
+    for M, rest in ((4608, 512), (4160, 64), (4352, 256)):
+        p = gb.gemm_bt_plan_ws(M, 4096, 4096, gb.BF16, gb.BF16)
+        r = gb.gemm_bt_plan_ws(rest, 4096, 4096, gb.BF16, gb.BF16)
+        assert p.split_rows == 4096 and r.split_rows == 0
+        assert p.workspace_bytes == r.workspace_bytes == gb.gemm_bt_workspace_size(M, 4096, 4096, gb.BF16, gb.BF16)
+    assert gb.gemm_bt_plan_ws(4160, 4096, 4096, gb.BF16, gb.BF16).workspace_bytes > 0
 
 
 def test_wide_tier_and_split_plans():
@@ -178,7 +203,7 @@ def test_wide_tier_and_split_plans():
         p = gb.gemm_bt_plan_batched(batch, M, N, K, ind, gb.BF16)
         return p.bm, p.bn
     assert tile(2048, 4096) == (128, 256)                        # 256 tiles of 128x256: one wave
-    assert tile(4352, 4096) == tile(4608, 4096) == (128, 256)    # 544 and 576 (272 and 288 of 256x256)
+    assert tile(2176, 4096, batch=2) == tile(2304, 4096, batch=2) == (128, 256)  # 544, 576 (272, 288 of 256x256)
     # 256x256: 192, 160, 136, 144 (odd K), 160 (4-byte rows) tiles; 128-row tiles over one wave
     assert tile(3072, 4096) == tile(2560, 4096) == tile(2048, 4352) == tile(3000, 3000, K=3001) \
         == tile(5000, 2000, K=2002) == tile(3072, 3072, K=3072) == (256, 256)

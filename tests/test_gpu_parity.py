@@ -577,11 +577,11 @@ def test_line_ring_large(gpu, case):
 
 
 # fewer 256x256 tiles than CUs against more than one wave of 128-row tiles (odd K, line-ring rows, 4-byte rows),
-# one wave of 128x256 tiles where 128x128 ones would need two, and 128x256 tiles for 1.27 waves of 256x256 ones,
-# at full K
+# one wave of 128x256 tiles where 128x128 ones would need two, and the row split of 1.27 waves of 256x256 tiles
+# (14 tile rows of 256x256, then 1024 rows on 128x96 tiles), at full K
 PARTIAL_WAVE = [((3000, 3000, 3001, "bf16", "f32"), (0,)), ((2000, 7000, 3000, "f16", "f16"), (0,)),
                 ((5000, 2000, 2002, "bf16", "bf16"), (0,)), ((2560, 2560, 4096, "bf16", "bf16"), (7,)),
-                ((4608, 4608, 4096, "bf16", "bf16"), (7,))]
+                ((4608, 4608, 4096, "bf16", "bf16"), (0,))]
 
 
 @pytest.mark.parametrize("case", range(len(PARTIAL_WAVE)))
@@ -995,6 +995,33 @@ def test_stream_k(gpu, case):
 
 def out_bits_t(c):
     return c.view(torch.int32) if c.dtype == torch.float32 else c.view(torch.int16)
+
+
+# row split: one wave of 256x256 tiles over the first rows, then the remaining rows (64 of them through the thin
+# split, 512 through the 128x128 split, 256 on the plain grid) through gemm_bt_ws, at full size
+ROW_SPLIT_WS = [(4160, 4096, 4096, "bf16", "bf16"), (4608, 4096, 4096, "f16", "f32"), (4352, 4096, 4104, "bf16", "bf16")]
+
+
+@pytest.mark.parametrize("case", range(len(ROW_SPLIT_WS)))
+def test_row_split_ws_large(gpu, case):
+    M, N, K, ind, outd = ROW_SPLIT_WS[case]
+    plan = gpu.gemm_bt_plan_ws(M, N, K, gpu._torch_code(TORCH_DT[ind]), gpu._torch_code(TORCH_DT[outd]))
+    say("row split ws", M, N, K, ind, outd, "split rows", plan.split_rows, "workspace", plan.workspace_bytes)
+    assert plan.split_rows == 4096
+    seed = 2000 + case
+    rng = np.random.default_rng(seed)
+    I, J = sample_entries(M, N, rng)
+    a, b = synth.make(M, N, K, ind, "normal", seed)
+    c, ws = run_ws(gpu, a, b, ind, outd)
+    c = f64(c)
+    ref = oracle.gemm_bt_entries(a, b, ind, I, J)
+    rep = tolerance.check(c[I, J], ref, oracle.row_norms(a, ind)[I] * oracle.row_norms(b, ind)[J], outd)
+    assert rep.ok, rep
+    ai, bi = synth.make(M, N, K, ind, "int", seed + 50)
+    ci, _ = run_ws(gpu, ai, bi, ind, outd, ws)
+    refi = oracle.round_to(oracle.gemm_bt_entries(ai, bi, ind, I, J), outd)
+    rep = tolerance.bit_exact(out_bits(ci)[I, J], refi, outd)
+    assert rep.ok, rep
 
 
 def test_stream_k_fallback_and_refusals(gpu):
