@@ -453,6 +453,36 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         p->grid = g < 4096 ? g : 4096;
         return GEMM_BT_OK;
     }
+    // Row split: a single product with just over one wave of 256 x 256 tiles
+    // (up to 1.375 waves) runs as two launches on the stream, the first
+    // R * 256 rows as one wave of 256 x 256 tiles (R tile rows, at least 7/8
+    // of the CUs) and the remaining rows on their own plan, split along K
+    // where that plan allows.  Every tier that covers the whole product in
+    // one grid leaves most CUs idle in its last wave.  Same box, us (the
+    // 128 x 256 plan vs the sum of the two launches): 4352x4096x4096 147.7 vs
+    // 97.8 + 23.7, 4160x4096x4096 145.6 vs 97.8 + 17.5, 4608x4096x4096 146.1
+    // vs 97.8 + 30.0, 4352^2x4096 148.9 vs 97.8 + 34.4, 5120x4096x4096 152.4
+    // vs 97.8 + 41.1, 4352x4096x2048 79.3 vs 55.2 + 12.1; 8-bit inputs alike
+    // (E4M3 -> bf16: 4352x4096x4096 84.1 vs 55.6 + 12.4, 4608x4096x4096 86.1
+    // vs 55.6 + 19.1, 5120x4096x4096 85.9 vs 55.6 + 23.6).  Past 1.375 waves
+    // the second launch costs more than the last wave saves (6144x4096x4096
+    // 163.2 vs 97.8 + 62.6, 5120^2x4096 166.4 vs 131.1 + 57.5).
+    if (batch == 1 && !forced_staged() && forced_variant() < 0 && tiles_l > num_cu &&
+        tiles_l * 8 <= (int64_t)num_cu * 11) {
+        const int64_t tn = (N + 255) / 256;
+        const int64_t m1 = (num_cu / tn) * 256;
+        if ((num_cu / tn) * tn * 8 >= (int64_t)num_cu * 7 && m1 < M) {
+            gemm_bt_plan_t rest;
+            int st = plan_impl(1, M - m1, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, allow_sk,
+                               &rest);
+            if (st != GEMM_BT_OK) return st;
+            st = plan_impl(1, m1, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, allow_sk, p);
+            if (st != GEMM_BT_OK) return st;
+            p->split_rows = m1;
+            if (rest.workspace_bytes > p->workspace_bytes) p->workspace_bytes = rest.workspace_bytes;
+            return GEMM_BT_OK;
+        }
+    }
     if (is_8bit(in_dtype)) {
         // 8-bit inputs: whole 16-byte chunks only (K a multiple of 16, A and B
         // 16-byte aligned), always the LDS-DMA kernel
@@ -535,32 +565,6 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
     p->ksplit = 1;
     // the DMA kernel takes rows of any (2-byte) alignment; a K tail that is
     // not a whole 16-byte chunk is added after its loop
-    // Row split: a single product with just over one wave of 256 x 256 tiles
-    // (up to 1.375 waves) runs as two launches on the stream, the first
-    // R * 256 rows as one wave of 256 x 256 tiles (R tile rows, at least 7/8
-    // of the CUs) and the remaining rows on their own plan, split along K
-    // where that plan allows.  Every tier that covers the whole product in
-    // one grid leaves most CUs idle in its last wave.  Same box, us (the
-    // 128 x 256 plan vs the sum of the two launches): 4352x4096x4096 147.7 vs
-    // 97.8 + 23.7, 4160x4096x4096 145.6 vs 97.8 + 17.5, 4608x4096x4096 146.1
-    // vs 97.8 + 30.0, 4352^2x4096 148.9 vs 97.8 + 34.4, 5120x4096x4096 152.4
-    // vs 97.8 + 41.1, 4352x4096x2048 79.3 vs 55.2 + 12.1.
-    if (batch == 1 && !is_8bit(in_dtype) && !forced_staged() && forced_variant() < 0 && tiles_l > num_cu &&
-        tiles_l * 8 <= (int64_t)num_cu * 11) {
-        const int64_t tn = (N + 255) / 256;
-        const int64_t m1 = (num_cu / tn) * 256;
-        if ((num_cu / tn) * tn * 8 >= (int64_t)num_cu * 7 && m1 < M) {
-            gemm_bt_plan_t rest;
-            int st = plan_impl(1, M - m1, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, allow_sk,
-                               &rest);
-            if (st != GEMM_BT_OK) return st;
-            st = plan_impl(1, m1, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, allow_sk, p);
-            if (st != GEMM_BT_OK) return st;
-            p->split_rows = m1;
-            if (rest.workspace_bytes > p->workspace_bytes) p->workspace_bytes = rest.workspace_bytes;
-            return GEMM_BT_OK;
-        }
-    }
     if (!forced_staged()) {
         int n = 0;
         const DmaVariant* vs = dma_variants(&n);

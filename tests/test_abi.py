@@ -164,13 +164,14 @@ def test_tier_band_above_one_wave():
     assert bm(2304, 4608, K=4104, batch=2) == 256                 # line-ring rows: above 1.2 waves
     assert bm(512, 512, 512, batch=68) == 128                     # 68 items x 4 tiles
     # 8-bit inputs: a narrower band, up to 17/16 waves
-    assert bm(4352, 4096, ind=gb.FP8_E4M3) == bm(4352, 4096, ind=gb.INT8, outd=gb.INT32) == 128  # 272 tiles
-    assert bm(4608, 4096, ind=gb.FP8_E4M3) == bm(4864, 4096, ind=gb.INT8, outd=gb.INT32) == 256  # 288, 304
+    # (stacked items: single products in this band split their rows)
+    assert bm(256, 4096, ind=gb.FP8_E4M3, batch=17) == bm(256, 4096, ind=gb.INT8, outd=gb.INT32, batch=17) == 128
+    assert bm(256, 4096, ind=gb.FP8_E4M3, batch=18) == bm(256, 4096, ind=gb.INT8, outd=gb.INT32, batch=19) == 256
     assert bm(5120, 4096, ind=gb.FP8_E4M3) == 256
 
 
 def test_row_split_plans():
-    """A single 16-bit product with just over one wave of 256x256 tiles (up to 1.375 waves) runs as two launches:
+    """A single product with just over one wave of 256x256 tiles (up to 1.375 waves) runs as two launches:
     R whole tile rows as one wave of 256x256 tiles (at least 7/8 of the CUs), then the remaining rows on their own
     plan (split along K through gemm_bt_ws when that plan splits).  The plan describes the first launch."""
     def plan(M, N, K=4096, ind=gb.BF16, outd=gb.BF16, batch=1):
@@ -181,7 +182,7 @@ def test_row_split_plans():
     assert plan(4100, 4100, K=136) == (3840, 256, 256, 255)  # line-ring rows and ragged edges alike
     assert plan(4096, 4096)[0] == plan(5120, 4608)[0] == 0   # one wave; 360 tiles (1.41 waves)
     assert plan(2176, 4096, batch=2)[0] == 0                # stacked items: one launch
-    assert plan(4352, 4096, ind=gb.FP8_E4M3)[0] == plan(4352, 4096, ind=gb.INT8, outd=gb.INT32)[0] == 0
+    assert plan(4352, 4096, ind=gb.FP8_E4M3)[0] == plan(4352, 4096, ind=gb.INT8, outd=gb.INT32)[0] == 4096  # 8-bit
     assert plan(512, 40000)[0] == 0                          # 157 tiles per tile row: the first launch under 7/8
     # the workspace is that of the second launch's split plan
     for M, rest in ((4608, 512), (4160, 64), (4352, 256)):
