@@ -57,7 +57,8 @@ class Plan(ctypes.Structure):
                 ("ksplit", ctypes.c_int), ("stages", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("tiles_m", ctypes.c_int64),
                 ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64), ("batch", ctypes.c_int64),
-                ("split_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("split_rows", ctypes.c_int64)]
+                ("split_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("split_rows", ctypes.c_int64),
+                ("split_items", ctypes.c_int64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

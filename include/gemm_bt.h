@@ -33,8 +33,8 @@
  * cache of device attributes.
  *
  * Asynchrony and errors.  gemm_bt enqueues its kernel on `stream` (two
- * kernels in stream order for a plan with split_rows) and returns without
- * waiting.  Argument errors are reported before anything is
+ * kernels in stream order for a plan with split_rows or split_items) and
+ * returns without waiting.  Argument errors are reported before anything is
  * enqueued.  A launch failure is reported as GEMM_BT_ERR_LAUNCH; a fault
  * inside the kernel shows at the caller's next synchronisation.  No call
  * throws, exits or aborts.  Calls are thread-safe.  C must not overlap A or B.
@@ -248,6 +248,9 @@ typedef struct {
     int64_t split_rows;      /* > 0: the product runs as two launches in stream order, rows [0, split_rows)
                                 of C first, planned as the fields above describe (one wave of 256 x 256
                                 tiles), then the remaining rows on their own plan; 0: one launch */
+    int64_t split_items;     /* > 0: stacked items run as two launches in stream order, items
+                                [0, split_items) first, planned as the fields above describe (one wave of
+                                256 x 256 tiles), then the remaining items on their own plan; 0: one launch */
 } gemm_bt_plan_t;
 
 int gemm_bt_plan(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, int a_align,

@@ -162,11 +162,12 @@ def test_tier_band_above_one_wave():
     assert bm(2560, 4096, batch=2) == bm(2304, 4608, batch=2) == 128  # 320, 324 tiles (128x256 ones)
     assert bm(5120, 4608) == bm(5120, 5120) == 256                # 360, 400 tiles
     assert bm(2304, 4608, K=4104, batch=2) == 256                 # line-ring rows: above 1.2 waves
-    assert bm(512, 512, 512, batch=68) == 128                     # 68 items x 4 tiles
+    assert bm(1536, 3072, 512, batch=4) == 128                    # 4 items x 72 tiles: 3 of them under 7/8
     # 8-bit inputs: a narrower band, up to 17/16 waves
-    # (stacked items: single products in this band split their rows)
-    assert bm(256, 4096, ind=gb.FP8_E4M3, batch=17) == bm(256, 4096, ind=gb.INT8, outd=gb.INT32, batch=17) == 128
-    assert bm(256, 4096, ind=gb.FP8_E4M3, batch=18) == bm(256, 4096, ind=gb.INT8, outd=gb.INT32, batch=19) == 256
+    # (items of 68 and 72 tiles, 272 and 288 in all: single products and items that fill 7/8 of the CUs in one
+    # wave split instead)
+    assert bm(1024, 4352, ind=gb.FP8_E4M3, batch=4) == bm(1024, 4352, ind=gb.INT8, outd=gb.INT32, batch=4) == 128
+    assert bm(1536, 3072, ind=gb.FP8_E4M3, batch=4) == bm(1536, 3072, ind=gb.INT8, outd=gb.INT32, batch=4) == 256
     assert bm(5120, 4096, ind=gb.FP8_E4M3) == 256
 
 
@@ -184,6 +185,14 @@ def test_row_split_plans():
     assert plan(2176, 4096, batch=2)[0] == 0                # stacked items: one launch
     assert plan(4352, 4096, ind=gb.FP8_E4M3)[0] == plan(4352, 4096, ind=gb.INT8, outd=gb.INT32)[0] == 4096  # 8-bit
     assert plan(512, 40000)[0] == 0                          # 157 tiles per tile row: the first launch under 7/8
+    # stacked items split by items: the first floor(CUs / tiles per item) of them as one wave
+    def items(batch, M, N, K=4096):
+        p = gb.gemm_bt_plan_batched(batch, M, N, K, gb.BF16, gb.BF16)
+        return p.split_items, p.split_rows, p.bm, p.grid
+    assert items(17, 256, 4096) == (16, 0, 256, 16) and items(9, 512, 4096) == (8, 0, 256, 32)
+    assert items(68, 512, 512, 128) == (64, 0, 256, 4) and items(5, 1024, 4096, 2048) == (4, 0, 256, 64)
+    assert items(4, 1536, 3072)[0] == 0                      # 72 tiles per item: 3 items fill under 7/8
+    assert items(16, 256, 4096)[0] == items(2, 2176, 4096)[0] == 0  # one wave; 144 tiles per item
     # the workspace is that of the second launch's split plan
     for M, rest in ((4608, 512), (4160, 64), (4352, 256)):
         p = gb.gemm_bt_plan_ws(M, 4096, 4096, gb.BF16, gb.BF16)

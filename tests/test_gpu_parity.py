@@ -526,6 +526,10 @@ BATCHED = [
     (9, 1024, 1024, 64, "bf16", "bf16", None, (0, 0, 0)),
     (6, 1000, 1500, 130, "f16", "f32", "b", (0, 0, 8)),
     (4, 1000, 1500, 64, "bf16", "bf16", None, (0, 0, 0)),
+    # just past one wave of 256x256 tiles: the first items as one wave, then the rest in a second launch (16 + 1
+    # items with B shared and C rows padded, 4 + 1 with A shared and 144-byte rows; 64 + 4 above)
+    (17, 256, 4096, 64, "f16", "f32", "b", (0, 0, 8)),
+    (5, 1024, 4096, 72, "bf16", "bf16", "a", (0, 16, 0)),
 ]
 
 
