@@ -454,7 +454,7 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
         return GEMM_BT_OK;
     }
     // Row split: a single product with just over one wave of 256 x 256 tiles
-    // (up to 1.375 waves) runs as two launches on the stream, the first
+    // (up to 1.375 waves; W waves up to W + 0.375) runs as two launches on the stream, the first
     // R * 256 rows as one wave of 256 x 256 tiles (R tile rows, at least 7/8
     // of the CUs) and the remaining rows on their own plan, split along K
     // where that plan allows.  Every tier that covers the whole product in
@@ -466,12 +466,19 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
     // (E4M3 -> bf16: 4352x4096x4096 84.1 vs 55.6 + 12.4, 4608x4096x4096 86.1
     // vs 55.6 + 19.1, 5120x4096x4096 85.9 vs 55.6 + 23.6).  Past 1.375 waves
     // the second launch costs more than the last wave saves (6144x4096x4096
-    // 163.2 vs 97.8 + 62.6, 5120^2x4096 166.4 vs 131.1 + 57.5).
-    if (batch == 1 && !forced_staged() && forced_variant() < 0 && tiles_l > num_cu &&
-        tiles_l * 8 <= (int64_t)num_cu * 11) {
+    // 163.2 vs 97.8 + 62.6, 5120^2x4096 166.4 vs 131.1 + 57.5).  Likewise
+    // just past W >= 2 whole waves: the first launch is W waves (8448x4096x4096
+    // 253.1 vs 191.3 + 23.6, 8704x4096x4096 251.3 vs 191.3 + 29.9,
+    // 9216x4096x4096 251.6 vs 191.3 + 40.7, 8448x4096x2048 134.7 vs 102.8 +
+    // 11.8, 12544x4096x4096 340.1 vs 280.3 + 23.6).
+    const int64_t waves_l = tiles_l / num_cu;  // whole waves of 256 x 256 tiles
+    const bool split_band = waves_l >= 1 && tiles_l % num_cu != 0 &&
+                            (tiles_l - waves_l * num_cu) * 8 <= (int64_t)num_cu * 3;
+    if (batch == 1 && !forced_staged() && forced_variant() < 0 && split_band) {
         const int64_t tn = (N + 255) / 256;
-        const int64_t m1 = (num_cu / tn) * 256;
-        if ((num_cu / tn) * tn * 8 >= (int64_t)num_cu * 7 && m1 < M) {
+        const int64_t r1 = waves_l * num_cu / tn;  // tile rows of the first launch
+        const int64_t m1 = r1 * 256;
+        if (r1 * tn * 8 >= waves_l * num_cu * 7 && m1 < M) {
             gemm_bt_plan_t rest;
             int st = plan_impl(1, M - m1, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, allow_sk,
                                &rest);
@@ -483,17 +490,16 @@ static int plan_impl(int64_t batch, int64_t M, int64_t N, int64_t K, int in_dtyp
             return GEMM_BT_OK;
         }
     }
-    // Item split: stacked items in the same band run the first
-    // floor(CUs / tiles per item) items as one wave of 256 x 256 tiles (at
+    // Item split: stacked items in the same bands run the first
+    // floor(W * CUs / tiles per item) items as W waves of 256 x 256 tiles (at
     // least 7/8 of the CUs), then the remaining items (us, one launch on
     // 128 x 256 tiles vs the sum of the two launches): 17 items of
     // 256x4096x4096 192.1 vs 138.9 + 21.2, 9 of 512x4096x4096 171.2 vs 108.9 +
     // 33.8, 5 of 1024x4096x2048 85.6 vs 55.2 + 19.1.
-    if (batch > 1 && !forced_staged() && forced_variant() < 0 && tiles_l > num_cu &&
-        tiles_l * 8 <= (int64_t)num_cu * 11) {
+    if (batch > 1 && !forced_staged() && forced_variant() < 0 && split_band) {
         const int64_t ti = tiles_l / batch;  // 256 x 256 tiles per item
-        const int64_t z1 = num_cu / ti;
-        if (z1 >= 1 && z1 < batch && z1 * ti * 8 >= (int64_t)num_cu * 7) {
+        const int64_t z1 = waves_l * num_cu / ti;
+        if (z1 >= 1 && z1 < batch && z1 * ti * 8 >= waves_l * num_cu * 7) {
             gemm_bt_plan_t rest;
             int st = plan_impl(batch - z1, M, N, K, in_dtype, out_dtype, a_align, b_align, c_align, num_cu, allow_sk,
                                &rest);

@@ -182,6 +182,10 @@ def test_row_split_plans():
     assert plan(4608, 4608) == (3584, 256, 256, 252)        # 18 tile columns: 14 tile rows first
     assert plan(4100, 4100, K=136) == (3840, 256, 256, 255)  # line-ring rows and ragged edges alike
     assert plan(4096, 4096)[0] == plan(5120, 4608)[0] == 0   # one wave; 360 tiles (1.41 waves)
+    # just past W whole waves: W waves first
+    assert plan(8448, 4096) == plan(9728, 4096) == (8192, 256, 256, 512)  # 528, 608 tiles
+    assert plan(12544, 4096) == (12288, 256, 256, 768)
+    assert plan(8192, 4096)[0] == plan(9984, 4096)[0] == plan(6144, 4096)[0] == 0  # 2, 2.44, 1.5 waves
     assert plan(2176, 4096, batch=2)[0] == 0                # stacked items: one launch
     assert plan(4352, 4096, ind=gb.FP8_E4M3)[0] == plan(4352, 4096, ind=gb.INT8, outd=gb.INT32)[0] == 4096  # 8-bit
     assert plan(512, 40000)[0] == 0                          # 157 tiles per tile row: the first launch under 7/8
@@ -192,6 +196,7 @@ def test_row_split_plans():
     assert items(17, 256, 4096) == (16, 0, 256, 16) and items(9, 512, 4096) == (8, 0, 256, 32)
     assert items(68, 512, 512, 128) == (64, 0, 256, 4) and items(5, 1024, 4096, 2048) == (4, 0, 256, 64)
     assert items(4, 1536, 3072)[0] == 0                      # 72 tiles per item: 3 items fill under 7/8
+    assert items(33, 256, 4096)[0] == 32 and items(33, 256, 2048, 64)[0] == 32  # 528 and 264 tiles
     assert items(16, 256, 4096)[0] == items(2, 2176, 4096)[0] == 0  # one wave; 144 tiles per item
     # the workspace is that of the second launch's split plan
     for M, rest in ((4608, 512), (4160, 64), (4352, 256)):

@@ -530,6 +530,7 @@ BATCHED = [
     # items with B shared and C rows padded, 4 + 1 with A shared and 144-byte rows; 64 + 4 above)
     (17, 256, 4096, 64, "f16", "f32", "b", (0, 0, 8)),
     (5, 1024, 4096, 72, "bf16", "bf16", "a", (0, 16, 0)),
+    (33, 256, 2048, 64, "bf16", "bf16", None, (0, 0, 0)),  # 32 items as one wave, then 1
 ]
 
 
@@ -585,7 +586,7 @@ def test_line_ring_large(gpu, case):
 # (14 tile rows of 256x256, then 1024 rows on 128x96 tiles), at full K
 PARTIAL_WAVE = [((3000, 3000, 3001, "bf16", "f32"), (0,)), ((2000, 7000, 3000, "f16", "f16"), (0,)),
                 ((5000, 2000, 2002, "bf16", "bf16"), (0,)), ((2560, 2560, 4096, "bf16", "bf16"), (7,)),
-                ((4608, 4608, 4096, "bf16", "bf16"), (0,))]
+                ((4608, 4608, 4096, "bf16", "bf16"), (0,)), ((8448, 4100, 2048, "f16", "f16"), (0,))]
 
 
 @pytest.mark.parametrize("case", range(len(PARTIAL_WAVE)))
